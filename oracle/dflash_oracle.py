@@ -1,0 +1,341 @@
+"""Plain CPU oracle of the DFlash2 draft-block path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product (the HIP library and its
+Python binding) imports, calls or links this module; only the tests,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` do.
+It shares no code, table or constant with the HIP path.
+
+Every function is the plain definition written out, slowly and readably, in
+numpy float64 (bf16 and fp32 inputs decode to float64 exactly), except the
+walk, whose precision the pages fix at fp32.  Sources (page titles; sections):
+
+  [DF2]  "[Spec] DFlash2: local convolution + candidate selector"
+         (sglang PR 35371): executive summary (the edge formula and the
+         lossless q contract), implementation breakdown (the six config
+         fields, their pairing, the unary transform, the deterministic
+         top-k), and the code excerpts for the grouped conv, the selector
+         lattice hand-off, the draft sampler and the walk kernel.
+  [DSP]  "DSpark padded-vocab d2t fix" (vllm PR 55133): logical vocab
+         200058 vs physical 201024, and the requirement that padded ids are
+         never sampled.
+
+Readings where the pages are silent (each listed again in the design doc):
+  * conv: coefficient index is the OUTPUT token i with tap t, applied to
+    x[i - t]; delta carries a tap axis, delta[i, t, g]; block position is the
+    flat token index modulo the block size.
+  * transform: y = m * z, then y = cap * tanh(y / cap) when cap > 0; entries
+    that are -inf stay -inf.  The transform's body is not printed, so its
+    exact form is "parity unpinned" beyond identity, bounds, symmetry and
+    slope at 0.
+  * top-k order: transformed value descending, ties by lowest token id; ids
+    at or beyond the logical vocab are never selected.
+  * lattice: A and B are [V, r] per-token tables, project(h) = P h with
+    P [r, H]; slot 0's predecessor is the anchor.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+F32 = np.float32
+
+
+# ---------------------------------------------------------------------------
+# Number formats (decoding/rounding only; no method arithmetic)
+# ---------------------------------------------------------------------------
+
+def round_to_bf16(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (ties to even), returned as
+    float64.  bfloat16 = 1 sign, 8 exponent bits (the fp32 range), 8
+    significant bits.  Done directly from float64 (no detour through fp32,
+    which would round twice)."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.array(v, copy=True)
+    finite = np.isfinite(v) & (v != 0)
+    f, e = np.frexp(v[finite])          # v = f * 2**e, 0.5 <= |f| < 1
+    # normal bf16: 8 significant bits -> step 2**(e-8); below 2**-126 the
+    # step is fixed at 2**-133 (subnormals).
+    step_exp = np.maximum(e - 8, -133)
+    q = np.rint(np.ldexp(f, e - step_exp))   # rint = round half to even
+    r = np.ldexp(q, step_exp)
+    r[np.abs(r) >= 2.0 ** 128] = np.copysign(np.inf, r[np.abs(r) >= 2.0 ** 128])
+    # the largest bf16 is (2 - 2**-7) * 2**127; anything that rounds above it
+    # is infinite (handled by the line above since q*2**step would be 2**128)
+    out[finite] = r
+    return out
+
+
+def round_to_dtype(v: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return round_to_bf16(v)
+    if dtype == "f32":
+        return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# Config contract  [DF2] implementation breakdown (config fields, pairing) and
+# the grouped-conv module constructor (hidden % group_size).
+# ---------------------------------------------------------------------------
+
+def validate_config(conv_kernel_size: int, conv_group_size: int, selector_rank: int,
+                    selector_top_k: int, output_multiplier: float = 1.0,
+                    final_logit_softcapping: float = 0.0, hidden_size: Optional[int] = None,
+                    block_size: Optional[int] = None) -> None:
+    """Raise ValueError if the draft config breaks the pages' contract.
+
+    The conv fields come as a pair and so do the selector fields: both zero
+    (feature off) or both positive.  A conv group size must divide the hidden
+    width.  Multiplier must be positive and finite (the top-k order is taken
+    on raw logits, which needs a strictly increasing transform) and the
+    softcap non-negative (0 = off)."""
+    if (conv_kernel_size > 0) != (conv_group_size > 0) or conv_kernel_size < 0 or conv_group_size < 0:
+        raise ValueError("conv_kernel_size and conv_group_size must be set together")
+    if (selector_rank > 0) != (selector_top_k > 0) or selector_rank < 0 or selector_top_k < 0:
+        raise ValueError("selector_rank and selector_top_k must be set together")
+    if not (math.isfinite(output_multiplier) and output_multiplier > 0):
+        raise ValueError("output_multiplier must be finite and > 0")
+    if not (math.isfinite(final_logit_softcapping) and final_logit_softcapping >= 0):
+        raise ValueError("final_logit_softcapping must be finite and >= 0")
+    if hidden_size is not None and conv_group_size > 0 and hidden_size % conv_group_size:
+        raise ValueError("conv_group_size must divide hidden_size")
+    if block_size is not None and block_size < 1:
+        raise ValueError("block_size must be >= 1")
+
+
+# ---------------------------------------------------------------------------
+# Step 1: block-causal grouped dynamic depthwise convolution
+# [DF2] code excerpt of the grouped conv: out[i,c] = sum_t (base + delta) x[i-t,c],
+# with taps that reach before the start of the token's block zeroed.
+# ---------------------------------------------------------------------------
+
+def conv(x: np.ndarray, base: np.ndarray, delta: np.ndarray, block_size: int,
+         group_size: int) -> np.ndarray:
+    """x [N, H], base [T, H], delta [N, T, G] -> out [N, H] (float64).
+
+    Walks each block on its own (the block start is r * B), so the in-block
+    position is the loop index j, with no modulo or bit trick."""
+    x = np.asarray(x, np.float64)
+    base = np.asarray(base, np.float64)
+    delta = np.asarray(delta, np.float64)
+    N, H = x.shape
+    T = base.shape[0]
+    if N % block_size:
+        raise ValueError("token count must be a whole number of blocks")
+    out = np.zeros((N, H))
+    for b0 in range(0, N, block_size):
+        for j in range(block_size):
+            i = b0 + j
+            for t in range(min(T, j + 1)):          # taps before the block start are zero
+                coeff = base[t] + np.repeat(delta[i, t], group_size)   # channel c uses group c // gs
+                out[i] += coeff * x[i - t]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Step 2: unary transform  [DF2] implementation breakdown: output_multiplier
+# and final_logit_softcapping jointly define the unary logit transform.
+# ---------------------------------------------------------------------------
+
+def transform(z: np.ndarray, multiplier: float, softcap: float) -> np.ndarray:
+    z = np.asarray(z, np.float64)
+    y = multiplier * z
+    if softcap > 0:
+        y = softcap * np.tanh(y / softcap)
+    return np.where(np.isneginf(z), -np.inf, y)
+
+
+# ---------------------------------------------------------------------------
+# Step 3: per-slot top-K  [DF2] implementation breakdown (deterministic top-k)
+# and [DSP] (padded ids must never be sampled).
+# ---------------------------------------------------------------------------
+
+def topk(logits: np.ndarray, valid_vocab: int, top_k: int, multiplier: float,
+         softcap: float):
+    """logits [rows, V] -> ids [rows, K] int64, unary [rows, K] float64.
+
+    Each row is fully sorted by (eligible first, value descending, id
+    ascending) and the first K entries are taken.  Eligible = id <
+    valid_vocab.  The transform is strictly increasing for multiplier > 0, so
+    ranking the raw logit equals ranking the transformed value (taken on the
+    exact input values; -0 and +0 are equal)."""
+    z = np.asarray(logits, np.float64)
+    rows, V = z.shape
+    if np.isnan(z).any():
+        raise ValueError("NaN logits are outside the method's domain")
+    if not (0 < top_k <= valid_vocab <= V):
+        raise ValueError("need 0 < top_k <= valid_vocab <= vocab")
+    ids = np.arange(V)
+    ineligible = ids >= valid_vocab
+    out_ids = np.empty((rows, top_k), np.int64)
+    for n in range(rows):
+        order = np.lexsort((ids, -z[n], ineligible))   # last key is the primary key
+        out_ids[n] = order[:top_k]
+    unary = transform(np.take_along_axis(z, out_ids, axis=1), multiplier, softcap)
+    return out_ids, unary
+
+
+# ---------------------------------------------------------------------------
+# Step 4 and 5: rank-r projection and the selector lattice
+# [DF2] executive summary: edge(p -> c) = <A[p] (.) project(h), B[c]> + unary[c],
+# scored over adjacent slots; slot 0's predecessor is the verified anchor
+# (draft-sampler code excerpt: position 0 of the block is the anchor).
+# ---------------------------------------------------------------------------
+
+def project(h: np.ndarray, proj: np.ndarray) -> np.ndarray:
+    """h [..., H], proj [r, H] -> u [..., r] = P h (float64 matmul)."""
+    return np.asarray(h, np.float64) @ np.asarray(proj, np.float64).T
+
+
+def lattice(ids: np.ndarray, unary: np.ndarray, u: np.ndarray, anchor: np.ndarray,
+            sel_a: np.ndarray, sel_b: np.ndarray) -> np.ndarray:
+    """ids [R,S,K], unary [R,S,K], u [R,S,r], anchor [R], A,B [V,r]
+    -> scores [R,S,K(prev),K(cur)] float64."""
+    A = np.asarray(sel_a, np.float64)
+    Bt = np.asarray(sel_b, np.float64)
+    R, S, K = ids.shape
+    scores = np.empty((R, S, K, K))
+    for r in range(R):
+        for s in range(S):
+            prev = np.full(K, anchor[r]) if s == 0 else ids[r, s - 1]
+            left = A[prev] * u[r, s]                       # A[p] (.) project(h), one row per p
+            scores[r, s] = left @ Bt[ids[r, s]].T + unary[r, s][None, :]
+    return scores
+
+
+def lattice_error_scale(ids, unary, h, proj, anchor, sel_a, sel_b):
+    """Magnitudes that bound the rounding error of an fp32 evaluation of each
+    lattice entry (used by the tests to derive a tolerance, not part of the
+    method): M1[r,s,j,c] = sum_k |A_pk||B_ck| sum_h |P_kh h_h|,
+    M2[r,s,j,c] = sum_k |A_pk u_k B_ck| + |unary_c|."""
+    A = np.abs(np.asarray(sel_a, np.float64))
+    Bt = np.abs(np.asarray(sel_b, np.float64))
+    absu = np.abs(np.asarray(h, np.float64)) @ np.abs(np.asarray(proj, np.float64)).T
+    u = project(h, proj)
+    R, S, K = ids.shape
+    M1 = np.empty((R, S, K, K))
+    M2 = np.empty((R, S, K, K))
+    for r in range(R):
+        for s in range(S):
+            prev = np.full(K, anchor[r]) if s == 0 else ids[r, s - 1]
+            M1[r, s] = (A[prev] * absu[r, s]) @ Bt[ids[r, s]].T
+            M2[r, s] = (A[prev] * np.abs(u[r, s])) @ Bt[ids[r, s]].T + np.abs(unary[r, s])[None, :]
+    return M1, M2
+
+
+# ---------------------------------------------------------------------------
+# Step 6: the per-request walk  [DF2] walk-kernel code excerpt and executive
+# summary (greedy rows emit a point mass; sampled rows return the softmax q
+# they drew from).  The pages' walk loads scores as fp32 and draws with fp32
+# uniforms, so this walk is evaluated in fp32, in the pages' order: divide by
+# the temperature, subtract the row max, exponentiate, normalise by the sum,
+# accumulate the CDF, and count the CDF entries at or below the uniform.
+# Sums and the CDF run left to right.  exp is the fp32 value nearest e^x
+# (float64 exp rounded once).  Temperatures are clamped to >= 1e-5, as the
+# sampler's staging step does.
+# ---------------------------------------------------------------------------
+
+def _softmax_cdf_f32(row: np.ndarray, temperature: float):
+    t = max(F32(temperature), F32(1e-5))
+    scaled = (row.astype(F32) / t).astype(F32)
+    shifted = (scaled - scaled.max()).astype(F32)
+    e = np.exp(shifted.astype(np.float64)).astype(F32)
+    total = F32(0)
+    for v in e:                                   # left-to-right sum
+        total = F32(total + v)
+    p = (e / total).astype(F32)
+    cdf = np.empty_like(p)
+    acc = F32(0)
+    for j, v in enumerate(p):                     # left-to-right CDF
+        acc = F32(acc + v)
+        cdf[j] = acc
+    return p, cdf
+
+
+def walk(scores: np.ndarray, ids: np.ndarray, uniforms: np.ndarray,
+         temperatures: np.ndarray, greedy: np.ndarray, return_margins: bool = False):
+    """scores [R,S,K,K] (fp32 values), ids [R,S,K], uniforms [R,S] fp32,
+    temperatures [R], greedy [R] bool -> tokens [R,S] int64, q [R,S,K] fp32,
+    idx [R,S] int64 (+ margins [R,S] float64: greedy top1 - top2, sampled
+    min_j |u - C_j| over the boundaries that can change the draw)."""
+    sc = np.asarray(scores).astype(F32)
+    R, S, K = ids.shape
+    tokens = np.empty((R, S), np.int64)
+    idxs = np.empty((R, S), np.int64)
+    q = np.zeros((R, S, K), F32)
+    margins = np.full((R, S), np.inf)
+    for r in range(R):
+        prev = 0                                  # start from the anchor's row
+        for s in range(S):
+            row = sc[r, s, prev]
+            if greedy[r]:
+                best = row.max()
+                idx = int(np.flatnonzero(row == best)[0])      # lowest index among ties
+                q[r, s, idx] = 1.0
+                if K > 1:
+                    margins[r, s] = float(best) - float(np.sort(row)[-2])
+            else:
+                u = F32(uniforms[r, s])
+                p, cdf = _softmax_cdf_f32(row, float(temperatures[r]))
+                idx = min(int(np.count_nonzero(u >= cdf)), K - 1)
+                q[r, s] = p
+                if K > 1:
+                    margins[r, s] = float(np.min(np.abs(np.float64(u) - cdf[: K - 1].astype(np.float64))))
+            tokens[r, s] = ids[r, s, idx]
+            idxs[r, s] = idx
+            prev = idx
+    if return_margins:
+        return tokens, q, idxs, margins
+    return tokens, q, idxs
+
+
+def path_probability(scores: np.ndarray, temperature: float, path) -> float:
+    """Probability (float64) that a sampled walk over one request's scores
+    [S,K,K] follows ``path`` (candidate indices per slot): the product of the
+    per-slot softmax(row / T) entries along the path, starting from row 0."""
+    t = max(float(F32(temperature)), float(F32(1e-5)))
+    prev, prob = 0, 1.0
+    for s, c in enumerate(path):
+        row = np.asarray(scores[s, prev], np.float64) / t
+        w = np.exp(row - row.max())
+        prob *= w[c] / w.sum()
+        prev = c
+    return prob
+
+
+# ---------------------------------------------------------------------------
+# Whole block  [DF2] draft-sampler code excerpt: drop the anchor position,
+# select candidates per slot, build the lattice, walk.
+# ---------------------------------------------------------------------------
+
+def propose_block(inp: Dict[str, np.ndarray], *, block_size: int, group_size: int,
+                  valid_vocab: int, top_k: int, multiplier: float, softcap: float,
+                  dtype: str, side: int = 0, h_override: Optional[np.ndarray] = None):
+    """End-to-end oracle from raw inputs (all float64 arrays holding the input
+    bits).  Returns a dict with conv_out (float64), conv_out_q (rounded to the
+    storage dtype), ids, unary, u, scores, tokens, q, idx, margins.
+
+    The proposal hidden state of slot s of request r is conv-output row
+    r*B + 1 + s (a stand-in for the draft stack, which sits between the conv
+    and the selector on the pages and is outside this path)."""
+    x = inp["x"]
+    T = inp["base"].shape[1]
+    base = inp["base"][side]
+    delta = inp["delta"][:, side]
+    out = conv(x, base, delta, block_size, group_size)
+    out_q = round_to_dtype(out, dtype)
+    R = x.shape[0] // block_size
+    S = block_size - 1
+    H = x.shape[1]
+    h = (out_q if h_override is None else h_override).reshape(R, block_size, H)[:, 1:, :]
+    ids, unary = topk(inp["logits"], valid_vocab, top_k, multiplier, softcap)
+    ids = ids.reshape(R, S, top_k)
+    unary = unary.reshape(R, S, top_k)
+    u = project(h, inp["proj"])
+    scores = lattice(ids, unary, u, inp["anchor"], inp["sel_a"], inp["sel_b"])
+    tokens, q, idx, margins = walk(scores.astype(F32), ids, inp["uniforms"], inp["temperatures"],
+                                   inp["greedy_mask"], return_margins=True)
+    return dict(conv_out=out, conv_out_q=out_q, h=h, ids=ids, unary=unary, u=u, scores=scores,
+                tokens=tokens, q=q, idx=idx, margins=margins)
