@@ -1,0 +1,272 @@
+"""Thin Python binding of libdflash.so (argument marshalling only).
+
+Every function has the name of the C entry point it calls, takes torch
+tensors that already live on the GPU, passes their device pointers and the
+current HIP stream, and returns the output tensors it allocated with torch.
+No step of the computation runs here: if the library is missing, importing
+this module's functions raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libdflash.so")
+
+DFLASH_OK = 0
+DFLASH_ERR_INVALID_ARG = -1
+DFLASH_ERR_UNSUPPORTED = -2
+DFLASH_ERR_WORKSPACE = -3
+DFLASH_ERR_LAUNCH = -4
+DFLASH_F32 = 0
+DFLASH_BF16 = 1
+MAX_TOP_K = 32
+
+_c_i32, _c_i64, _c_f32, _c_size, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+
+class DraftConfig(ctypes.Structure):
+    """Mirror of dflash_draft_config."""
+    _fields_ = [
+        ("conv_kernel_size", _c_i32),
+        ("conv_group_size", _c_i32),
+        ("selector_rank", _c_i32),
+        ("selector_top_k", _c_i32),
+        ("output_multiplier", _c_f32),
+        ("final_logit_softcapping", _c_f32),
+        ("block_size", _c_i32),
+        ("hidden_size", _c_i32),
+    ]
+
+
+class BlockArgs(ctypes.Structure):
+    """Mirror of dflash_block_args."""
+    _fields_ = [
+        ("x", _c_vp), ("conv_base", _c_vp), ("conv_delta", _c_vp), ("delta_row_stride", _c_i64),
+        ("logits", _c_vp), ("logits_row_stride", _c_i64), ("vocab", _c_i64), ("valid_vocab", _c_i64),
+        ("anchor_ids", _c_vp), ("sel_a", _c_vp), ("sel_b", _c_vp), ("proj", _c_vp),
+        ("uniforms", _c_vp), ("temperatures", _c_vp), ("greedy_mask", _c_vp),
+        ("conv_out", _c_vp), ("ids_out", _c_vp), ("unary_out", _c_vp), ("tokens_out", _c_vp),
+        ("q_out", _c_vp), ("scores_out", _c_vp),
+        ("workspace", _c_vp), ("workspace_bytes", _c_size),
+        ("stage_events", _c_vp),
+        ("n_req", _c_i32), ("dtype", _c_i32),
+    ]
+
+
+_SIGNATURES = {
+    "dflash_abi_version": (_c_i32, []),
+    "dflash_validate_config": (_c_i32, [ctypes.POINTER(DraftConfig)]),
+    "dflash_last_error": (ctypes.c_char_p, []),
+    "dflash_conv": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp]),
+    "dflash_topk_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i32]),
+    "dflash_topk": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_f32, _c_f32, _c_i32, _c_vp, _c_vp,
+                             _c_vp, _c_size, _c_vp]),
+    "dflash_lattice_workspace_size": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32]),
+    "dflash_lattice": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32,
+                                _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_vp, _c_vp, _c_size, _c_vp]),
+    "dflash_walk": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp]),
+    "dflash_propose_block_workspace_size": (_c_size, [ctypes.POINTER(DraftConfig), _c_i32, _c_i64]),
+    "dflash_propose_block": (_c_i32, [ctypes.POINTER(DraftConfig), ctypes.POINTER(BlockArgs), _c_vp]),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdflash.so (built in-tree by ``block_draft_proposal_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m block_draft_proposal_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def last_error() -> str:
+    return lib().dflash_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != DFLASH_OK:
+        raise DFlashError(status, last_error())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DFLASH_BF16
+    if t.dtype == torch.float32:
+        return DFLASH_F32
+    raise TypeError(f"unsupported float dtype {t.dtype}")
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _need_inner_contiguous(t: torch.Tensor, name: str):
+    if t.dim() > 1 and t.shape[0] > 0 and not t[0].is_contiguous():
+        raise ValueError(f"{name}: every row must be contiguous")
+
+
+def make_config(*, taps: int, group_size: int, rank: int, top_k: int, multiplier: float = 1.0,
+                softcap: float = 0.0, block_size: int, hidden: int) -> DraftConfig:
+    return DraftConfig(taps, group_size, rank, top_k, multiplier, softcap, block_size, hidden)
+
+
+def dflash_validate_config(cfg: DraftConfig) -> None:
+    _check(lib().dflash_validate_config(ctypes.byref(cfg)))
+
+
+def dflash_conv(x: torch.Tensor, base: torch.Tensor, delta: torch.Tensor, *, block_size: int,
+                group_size: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """x [N, H]; base [T, H]; delta [N, T, G] (rows may be strided, e.g. one
+    side of a packed [N, 2, T, G] projection).  Returns out [N, H]."""
+    if not (x.is_contiguous() and base.is_contiguous()):
+        raise ValueError("x and base must be contiguous")
+    _need_inner_contiguous(delta, "delta")
+    N, H = x.shape
+    T = base.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().dflash_conv(_p(x), _p(base), _p(delta), delta.stride(0) if N else T * (H // group_size), _p(out),
+                             N, H, group_size, T, block_size, _dtype_code(x), _stream(stream)))
+    return out
+
+
+def dflash_topk(logits: torch.Tensor, *, top_k: int, valid_vocab: Optional[int] = None,
+                multiplier: float = 1.0, softcap: float = 0.0, vocab: Optional[int] = None,
+                ids_out=None, unary_out=None, workspace=None, stream=None):
+    """logits [rows, >= vocab] (row stride = logits.stride(0)).  Returns
+    (ids int64 [rows, K], unary fp32 [rows, K])."""
+    rows = logits.shape[0]
+    vocab = logits.shape[1] if vocab is None else vocab
+    valid_vocab = vocab if valid_vocab is None else valid_vocab
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [rows, V] with contiguous rows")
+    dev = logits.device
+    ids_out = torch.empty((rows, top_k), dtype=torch.int64, device=dev) if ids_out is None else ids_out
+    unary_out = torch.empty((rows, top_k), dtype=torch.float32, device=dev) if unary_out is None else unary_out
+    ws_bytes = lib().dflash_topk_workspace_size(rows, valid_vocab, top_k)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib().dflash_topk(_p(logits), logits.stride(0), rows, vocab, valid_vocab, top_k, multiplier, softcap,
+                             _dtype_code(logits), _p(ids_out), _p(unary_out), _p(workspace),
+                             workspace.numel(), _stream(stream)))
+    return ids_out, unary_out
+
+
+def dflash_lattice(ids: torch.Tensor, unary: torch.Tensor, hidden: torch.Tensor, anchor: torch.Tensor,
+                   sel_a: torch.Tensor, sel_b: torch.Tensor, proj: torch.Tensor, *, scores_out=None,
+                   workspace=None, stream=None) -> torch.Tensor:
+    """ids, unary [R, S, K]; hidden [R, S, H] (strided views allowed, rows
+    contiguous); anchor [R]; sel_a, sel_b [V, r]; proj [r, H].
+    Returns scores fp32 [R, S, K, K]."""
+    R, S, K = ids.shape
+    H = hidden.shape[-1]
+    r = proj.shape[0]
+    if hidden.stride(-1) != 1:
+        raise ValueError("hidden rows must be contiguous")
+    for t, n in ((ids, "ids"), (unary, "unary"), (anchor, "anchor"), (sel_a, "sel_a"), (sel_b, "sel_b"),
+                 (proj, "proj")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    dev = ids.device
+    scores_out = torch.empty((R, S, K, K), dtype=torch.float32, device=dev) if scores_out is None else scores_out
+    ws_bytes = lib().dflash_lattice_workspace_size(R, S, r, H)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib().dflash_lattice(_p(ids), _p(unary), _p(hidden), hidden.stride(0), hidden.stride(1), _p(anchor),
+                                _p(sel_a), _p(sel_b), _p(proj), R, S, K, H, r, sel_a.shape[0],
+                                _dtype_code(hidden), _p(scores_out), _p(workspace), workspace.numel(),
+                                _stream(stream)))
+    return scores_out
+
+
+def dflash_walk(scores: torch.Tensor, ids: torch.Tensor, uniforms: torch.Tensor, temperatures: torch.Tensor,
+                greedy_mask: torch.Tensor, *, tokens_out=None, q_out=None, stream=None):
+    """scores [R, S, K, K] fp32; ids [R, S, K]; uniforms [R, S]; temperatures
+    [R]; greedy_mask [R] bool/uint8.  Returns (tokens int64 [R, S], q fp32 [R, S, K])."""
+    R, S, K = ids.shape
+    for t, n in ((scores, "scores"), (ids, "ids"), (uniforms, "uniforms"), (temperatures, "temperatures"),
+                 (greedy_mask, "greedy_mask")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    if greedy_mask.element_size() != 1:
+        raise TypeError("greedy_mask must be bool or uint8")
+    dev = ids.device
+    tokens_out = torch.empty((R, S), dtype=torch.int64, device=dev) if tokens_out is None else tokens_out
+    q_out = torch.empty((R, S, K), dtype=torch.float32, device=dev) if q_out is None else q_out
+    _check(lib().dflash_walk(_p(scores), _p(ids), _p(uniforms), _p(temperatures), _p(greedy_mask), R, S, K,
+                             _p(tokens_out), _p(q_out), _stream(stream)))
+    return tokens_out, q_out
+
+
+def propose_block_workspace_size(cfg: DraftConfig, n_req: int, valid_vocab: int) -> int:
+    return lib().dflash_propose_block_workspace_size(ctypes.byref(cfg), n_req, valid_vocab)
+
+
+def dflash_propose_block(cfg: DraftConfig, *, x, conv_base, conv_delta, logits, anchor, sel_a, sel_b, proj,
+                         uniforms, temperatures, greedy_mask, valid_vocab: Optional[int] = None,
+                         vocab: Optional[int] = None, keep_scores: bool = False,
+                         outputs: Optional[Dict[str, torch.Tensor]] = None, workspace=None,
+                         stage_events: Optional[Sequence] = None, stream=None) -> Dict[str, torch.Tensor]:
+    """One draft block.  conv_base [T, H]; conv_delta [N, T, G] (rows may be
+    strided: one side of the packed projection).  Returns a dict with
+    conv_out, ids, unary, tokens, q (and scores when keep_scores)."""
+    B, H, K = cfg.block_size, cfg.hidden_size, cfg.selector_top_k
+    S = B - 1
+    N = x.shape[0]
+    R = N // B
+    vocab = logits.shape[1] if vocab is None else vocab
+    valid_vocab = vocab if valid_vocab is None else valid_vocab
+    dev = x.device
+    _need_inner_contiguous(conv_delta, "conv_delta")
+    if logits.stride(-1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    o = dict(outputs or {})
+    o.setdefault("conv_out", torch.empty_like(x))
+    o.setdefault("ids", torch.empty((R, S, K), dtype=torch.int64, device=dev))
+    o.setdefault("unary", torch.empty((R, S, K), dtype=torch.float32, device=dev))
+    o.setdefault("tokens", torch.empty((R, S), dtype=torch.int64, device=dev))
+    o.setdefault("q", torch.empty((R, S, K), dtype=torch.float32, device=dev))
+    if keep_scores:
+        o.setdefault("scores", torch.empty((R, S, K, K), dtype=torch.float32, device=dev))
+    if workspace is None:
+        nbytes = propose_block_workspace_size(cfg, max(R, 1), valid_vocab)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    ev_arr = None
+    if stage_events is not None:
+        ev_arr = (ctypes.c_void_p * 8)(*[ctypes.c_void_p(e.cuda_event) for e in stage_events])
+    args = BlockArgs(
+        _p(x), _p(conv_base), _p(conv_delta), conv_delta.stride(0),
+        _p(logits), logits.stride(0), vocab, valid_vocab,
+        _p(anchor), _p(sel_a), _p(sel_b), _p(proj),
+        _p(uniforms), _p(temperatures), _p(greedy_mask),
+        _p(o["conv_out"]), _p(o["ids"]), _p(o["unary"]), _p(o["tokens"]), _p(o["q"]), _p(o.get("scores")),
+        _p(workspace), workspace.numel(),
+        ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None,
+        R, _dtype_code(x))
+    _check(lib().dflash_propose_block(ctypes.byref(cfg), ctypes.byref(args), _stream(stream)))
+    return o

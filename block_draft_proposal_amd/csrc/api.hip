@@ -1,0 +1,368 @@
+// C ABI of the DFlash2 draft-block library: host-side validation and launch
+// sequencing.  Every check runs on the host before anything is enqueued.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "dflash.h"
+#include "dflash_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return DFLASH_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int elem_bytes(int32_t dtype) { return dtype == DFLASH_BF16 ? 2 : 4; }
+bool dtype_ok(int32_t dtype) { return dtype == DFLASH_F32 || dtype == DFLASH_BF16; }
+hipStream_t as_hip(dflash_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DFLASH_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return DFLASH_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+constexpr int64_t kMaxVocab = (int64_t)1 << 24;
+constexpr size_t kLatticeLdsMax = 64 * 1024;
+
+size_t lattice_lds(int K, int r) {
+  const size_t used = (size_t)(r + K * (r + 1) + r * K);
+  return ((used + 1) & ~(size_t)1) * sizeof(float) + 2 * (size_t)K * sizeof(int64_t);
+}
+
+// ---------------------------------------------------------------------------
+int check_conv(const void* x, const void* base, const void* delta, int64_t delta_row_stride,
+               const void* out, int64_t n_tokens, int32_t hidden, int32_t group_size, int32_t taps,
+               int32_t block_size, int32_t dtype) {
+  if (!dtype_ok(dtype)) return fail(DFLASH_ERR_INVALID_ARG, "dflash_conv: unknown dtype %d", dtype);
+  if (n_tokens < 0) return fail(DFLASH_ERR_INVALID_ARG, "dflash_conv: n_tokens < 0");
+  if (hidden <= 0 || group_size <= 0 || taps <= 0 || block_size <= 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "dflash_conv: hidden, group_size, taps, block_size must be > 0");
+  if (hidden % group_size)
+    return fail(DFLASH_ERR_INVALID_ARG, "dflash_conv: conv_group_size=%d must divide hidden_size=%d",
+                group_size, hidden);
+  const int vec = dtype == DFLASH_BF16 ? 8 : 4;
+  if (hidden % vec)
+    return fail(DFLASH_ERR_UNSUPPORTED, "dflash_conv: hidden must be a multiple of %d", vec);
+  if (n_tokens % block_size)
+    return fail(DFLASH_ERR_INVALID_ARG, "dflash_conv: n_tokens=%lld is not a whole number of blocks of %d",
+                (long long)n_tokens, block_size);
+  const int64_t groups = hidden / group_size;
+  if (delta_row_stride < (int64_t)taps * groups)
+    return fail(DFLASH_ERR_INVALID_ARG, "dflash_conv: delta_row_stride < taps * groups");
+  if (n_tokens == 0) return DFLASH_OK;
+  if (!x || !base || !delta || !out) return fail(DFLASH_ERR_INVALID_ARG, "dflash_conv: null pointer");
+  if (!aligned16(x) || !aligned16(base) || !aligned16(out))
+    return fail(DFLASH_ERR_INVALID_ARG, "dflash_conv: x, base and out must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(delta) % elem_bytes(dtype))
+    return fail(DFLASH_ERR_INVALID_ARG, "dflash_conv: delta misaligned");
+  const size_t bytes = (size_t)n_tokens * hidden * elem_bytes(dtype);
+  if (overlaps(x, bytes, out, bytes)) return fail(DFLASH_ERR_INVALID_ARG, "dflash_conv: out overlaps x");
+  return DFLASH_OK;
+}
+
+int check_topk(const void* logits, int64_t row_stride, int64_t n_rows, int64_t vocab, int64_t valid_vocab,
+               int32_t top_k, float mult, float cap, int32_t dtype, const void* ids_out,
+               const void* unary_out, const dflash::TopkPlan& plan, const void* ws, size_t ws_bytes,
+               const char* who) {
+  if (!dtype_ok(dtype)) return fail(DFLASH_ERR_INVALID_ARG, "%s: unknown dtype %d", who, dtype);
+  if (n_rows < 0) return fail(DFLASH_ERR_INVALID_ARG, "%s: n_rows < 0", who);
+  if (top_k < 1) return fail(DFLASH_ERR_INVALID_ARG, "%s: top_k must be >= 1", who);
+  if (top_k > DFLASH_MAX_TOP_K) return fail(DFLASH_ERR_UNSUPPORTED, "%s: top_k > %d", who, DFLASH_MAX_TOP_K);
+  if (!(valid_vocab >= top_k && valid_vocab <= vocab && vocab <= row_stride))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: need top_k <= valid_vocab <= vocab <= row_stride", who);
+  if (vocab >= kMaxVocab) return fail(DFLASH_ERR_UNSUPPORTED, "%s: vocab must be < 2^24", who);
+  if (!(std::isfinite(mult) && mult > 0.f))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: output_multiplier must be finite and > 0", who);
+  if (!(std::isfinite(cap) && cap >= 0.f))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: final_logit_softcapping must be finite and >= 0", who);
+  if ((int64_t)plan.chunks * top_k > dflash::kTopkMergeCap)
+    return fail(DFLASH_ERR_UNSUPPORTED, "%s: valid_vocab too large for top_k=%d", who, top_k);
+  if (n_rows == 0) return DFLASH_OK;
+  if (!logits || !ids_out || !unary_out) return fail(DFLASH_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!aligned16(logits) || (row_stride * elem_bytes(dtype)) % 16)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: logits rows must be 16-byte aligned", who);
+  if ((reinterpret_cast<uintptr_t>(ids_out) & 7) || (reinterpret_cast<uintptr_t>(unary_out) & 3))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: misaligned output", who);
+  if (ws_bytes < plan.bytes || (plan.bytes && !ws))
+    return fail(DFLASH_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu needed", who, ws_bytes, plan.bytes);
+  if (reinterpret_cast<uintptr_t>(ws) & 255)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", who);
+  return DFLASH_OK;
+}
+
+int check_select(const int64_t* ids, const float* unary, const void* hidden, int64_t req_stride,
+                 int64_t slot_stride, const int64_t* anchor, const void* sel_a, const void* sel_b,
+                 const void* proj, int32_t n_req, int32_t slots, int32_t top_k, int32_t hidden_size,
+                 int32_t rank, int64_t vocab, int32_t dtype, const char* who) {
+  if (!dtype_ok(dtype)) return fail(DFLASH_ERR_INVALID_ARG, "%s: unknown dtype %d", who, dtype);
+  if (n_req < 0 || slots < 0) return fail(DFLASH_ERR_INVALID_ARG, "%s: n_req and slots must be >= 0", who);
+  if (top_k < 1) return fail(DFLASH_ERR_INVALID_ARG, "%s: top_k must be >= 1", who);
+  if (top_k > DFLASH_MAX_TOP_K) return fail(DFLASH_ERR_UNSUPPORTED, "%s: top_k > %d", who, DFLASH_MAX_TOP_K);
+  if (rank < 1 || hidden_size < 1 || vocab < 1)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: rank, hidden_size and vocab must be >= 1", who);
+  const int vec = dtype == DFLASH_BF16 ? 8 : 4;
+  if (hidden_size % vec) return fail(DFLASH_ERR_UNSUPPORTED, "%s: hidden_size must be a multiple of %d", who, vec);
+  if (dtype == DFLASH_BF16 && rank > 128) return fail(DFLASH_ERR_UNSUPPORTED, "%s: bf16 rank > 128", who);
+  if (lattice_lds(top_k, rank) > kLatticeLdsMax)
+    return fail(DFLASH_ERR_UNSUPPORTED, "%s: top_k x rank too large for one workgroup's LDS", who);
+  if (vocab >= ((int64_t)1 << 31)) return fail(DFLASH_ERR_UNSUPPORTED, "%s: vocab must be < 2^31", who);
+  if (req_stride < 0 || slot_stride < 0) return fail(DFLASH_ERR_INVALID_ARG, "%s: negative stride", who);
+  if ((int64_t)n_req * slots == 0) return DFLASH_OK;
+  if (!ids || !unary || !hidden || !anchor || !sel_a || !sel_b || !proj)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: null pointer", who);
+  const int e = elem_bytes(dtype);
+  if (!aligned16(hidden) || (req_stride * e) % 16 || (slot_stride * e) % 16 || !aligned16(proj))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: hidden rows and proj must be 16-byte aligned", who);
+  if ((reinterpret_cast<uintptr_t>(sel_a) % e) || (reinterpret_cast<uintptr_t>(sel_b) % e))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: selector tables misaligned", who);
+  return DFLASH_OK;
+}
+
+int check_walk(const float* scores, const int64_t* ids, const float* uniforms, const float* temperatures,
+               const uint8_t* greedy, int32_t n_req, int32_t slots, int32_t top_k, const int64_t* tokens,
+               const float* q, const char* who) {
+  if (n_req < 0 || slots < 0) return fail(DFLASH_ERR_INVALID_ARG, "%s: n_req and slots must be >= 0", who);
+  if (top_k < 1) return fail(DFLASH_ERR_INVALID_ARG, "%s: top_k must be >= 1", who);
+  if (top_k > DFLASH_MAX_TOP_K) return fail(DFLASH_ERR_UNSUPPORTED, "%s: top_k > %d", who, DFLASH_MAX_TOP_K);
+  if ((int64_t)n_req * slots == 0) return DFLASH_OK;
+  if (!scores || !ids || !uniforms || !temperatures || !greedy || !tokens || !q)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: null pointer", who);
+  return DFLASH_OK;
+}
+
+int record(void* const* events, int idx, hipStream_t s) {
+  if (!events) return DFLASH_OK;
+  const hipError_t e = hipEventRecord(reinterpret_cast<hipEvent_t>(events[idx]), s);
+  if (e != hipSuccess) return fail(DFLASH_ERR_LAUNCH, "stage event record failed: %s", hipGetErrorString(e));
+  return DFLASH_OK;
+}
+
+struct BlockLayout {
+  dflash::TopkPlan topk;
+  dflash::ProjPlan proj;
+  size_t proj_off, scores_off, bytes;
+};
+
+BlockLayout block_layout(const dflash_draft_config* cfg, int32_t n_req, int64_t valid_vocab) {
+  BlockLayout L{};
+  const int32_t slots = cfg->block_size - 1;
+  const int64_t rows = (int64_t)n_req * slots;
+  const int32_t K = cfg->selector_top_k;
+  L.topk = dflash::plan_topk(rows, valid_vocab, K);
+  // dtype only changes the projection split; size for the larger (bf16) plan
+  const dflash::ProjPlan pb = dflash::plan_proj((int32_t)rows, cfg->selector_rank, cfg->hidden_size, DFLASH_BF16);
+  const dflash::ProjPlan pf = dflash::plan_proj((int32_t)rows, cfg->selector_rank, cfg->hidden_size, DFLASH_F32);
+  L.proj_off = align256(L.topk.bytes);
+  L.scores_off = L.proj_off + align256(pb.bytes > pf.bytes ? pb.bytes : pf.bytes);
+  L.bytes = L.scores_off + align256((size_t)rows * K * K * sizeof(float));
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash_abi_version(void) { return DFLASH_ABI_VERSION; }
+
+const char* dflash_last_error(void) { return g_last_error.c_str(); }
+
+int dflash_validate_config(const dflash_draft_config* c) {
+  if (!c) return fail(DFLASH_ERR_INVALID_ARG, "dflash_validate_config: null config");
+  if (c->conv_kernel_size < 0 || c->conv_group_size < 0 || c->selector_rank < 0 || c->selector_top_k < 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "draft config: negative field");
+  if ((c->conv_kernel_size > 0) != (c->conv_group_size > 0))
+    return fail(DFLASH_ERR_INVALID_ARG, "draft config: conv_kernel_size and conv_group_size must be set together");
+  if ((c->selector_rank > 0) != (c->selector_top_k > 0))
+    return fail(DFLASH_ERR_INVALID_ARG, "draft config: selector_rank and selector_top_k must be set together");
+  if (!(std::isfinite(c->output_multiplier) && c->output_multiplier > 0.f))
+    return fail(DFLASH_ERR_INVALID_ARG, "draft config: output_multiplier must be finite and > 0");
+  if (!(std::isfinite(c->final_logit_softcapping) && c->final_logit_softcapping >= 0.f))
+    return fail(DFLASH_ERR_INVALID_ARG, "draft config: final_logit_softcapping must be finite and >= 0");
+  if (c->block_size < 1) return fail(DFLASH_ERR_INVALID_ARG, "draft config: block_size must be >= 1");
+  if (c->hidden_size < 1) return fail(DFLASH_ERR_INVALID_ARG, "draft config: hidden_size must be >= 1");
+  if (c->conv_group_size > 0 && c->hidden_size % c->conv_group_size)
+    return fail(DFLASH_ERR_INVALID_ARG, "draft config: conv_group_size=%d must divide hidden_size=%d",
+                c->conv_group_size, c->hidden_size);
+  if (c->selector_top_k > DFLASH_MAX_TOP_K)
+    return fail(DFLASH_ERR_UNSUPPORTED, "draft config: selector_top_k > %d", DFLASH_MAX_TOP_K);
+  return ok();
+}
+
+int dflash_conv(const void* x, const void* base, const void* delta, int64_t delta_row_stride, void* out,
+                int64_t n_tokens, int32_t hidden, int32_t group_size, int32_t taps, int32_t block_size,
+                int32_t dtype, dflash_stream_t stream) {
+  int st = check_conv(x, base, delta, delta_row_stride, out, n_tokens, hidden, group_size, taps, block_size,
+                      dtype);
+  if (st != DFLASH_OK) return st;
+  if (n_tokens == 0) return ok();
+  dflash::ConvArgs a{x, base, delta, delta_row_stride, out, n_tokens, hidden, group_size, taps, block_size,
+                     dtype, nullptr, 0};
+  st = launch_status(dflash::launch_conv(a, as_hip(stream)), "dflash_conv");
+  return st == DFLASH_OK ? ok() : st;
+}
+
+size_t dflash_topk_workspace_size(int64_t n_rows, int64_t valid_vocab, int32_t top_k) {
+  if (n_rows <= 0 || valid_vocab <= 0 || top_k <= 0) return 0;
+  return dflash::plan_topk(n_rows, valid_vocab, top_k).bytes;
+}
+
+int dflash_topk(const void* logits, int64_t row_stride, int64_t n_rows, int64_t vocab, int64_t valid_vocab,
+                int32_t top_k, float output_multiplier, float softcap, int32_t dtype, int64_t* ids_out,
+                float* unary_out, void* workspace, size_t workspace_bytes, dflash_stream_t stream) {
+  const dflash::TopkPlan plan = dflash::plan_topk(n_rows > 0 ? n_rows : 0, valid_vocab > 0 ? valid_vocab : 1,
+                                                  top_k > 0 ? top_k : 1);
+  int st = check_topk(logits, row_stride, n_rows, vocab, valid_vocab, top_k, output_multiplier, softcap, dtype,
+                      ids_out, unary_out, plan, workspace, workspace_bytes, "dflash_topk");
+  if (st != DFLASH_OK) return st;
+  if (n_rows == 0) return ok();
+  dflash::TopkArgs a{logits, row_stride, n_rows, vocab, valid_vocab, top_k, output_multiplier, softcap,
+                     dtype, ids_out, unary_out, workspace, false};
+  st = launch_status(dflash::launch_topk_zero(a, plan, as_hip(stream)), "dflash_topk");
+  if (st != DFLASH_OK) return st;
+  st = launch_status(dflash::launch_topk(a, plan, as_hip(stream)), "dflash_topk");
+  return st == DFLASH_OK ? ok() : st;
+}
+
+size_t dflash_lattice_workspace_size(int32_t n_req, int32_t slots, int32_t rank, int32_t hidden_size) {
+  if (n_req <= 0 || slots <= 0 || rank <= 0 || hidden_size <= 0) return 0;
+  const dflash::ProjPlan pb = dflash::plan_proj(n_req * slots, rank, hidden_size, DFLASH_BF16);
+  const dflash::ProjPlan pf = dflash::plan_proj(n_req * slots, rank, hidden_size, DFLASH_F32);
+  return pb.bytes > pf.bytes ? pb.bytes : pf.bytes;
+}
+
+int dflash_lattice(const int64_t* ids, const float* unary, const void* hidden, int64_t hidden_req_stride,
+                   int64_t hidden_slot_stride, const int64_t* anchor_ids, const void* sel_a, const void* sel_b,
+                   const void* proj, int32_t n_req, int32_t slots, int32_t top_k, int32_t hidden_size,
+                   int32_t rank, int64_t vocab, int32_t dtype, float* scores_out, void* workspace,
+                   size_t workspace_bytes, dflash_stream_t stream) {
+  int st = check_select(ids, unary, hidden, hidden_req_stride, hidden_slot_stride, anchor_ids, sel_a, sel_b,
+                        proj, n_req, slots, top_k, hidden_size, rank, vocab, dtype, "dflash_lattice");
+  if (st != DFLASH_OK) return st;
+  if ((int64_t)n_req * slots == 0) return ok();
+  if (!scores_out) return fail(DFLASH_ERR_INVALID_ARG, "dflash_lattice: null scores_out");
+  const dflash::ProjPlan plan = dflash::plan_proj(n_req * slots, rank, hidden_size, dtype);
+  if (workspace_bytes < plan.bytes || !workspace)
+    return fail(DFLASH_ERR_WORKSPACE, "dflash_lattice: workspace of %zu bytes < %zu needed", workspace_bytes,
+                plan.bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(DFLASH_ERR_INVALID_ARG, "dflash_lattice: workspace must be 256-byte aligned");
+  dflash::SelectArgs a{ids, unary, hidden, hidden_req_stride, hidden_slot_stride, anchor_ids, sel_a, sel_b,
+                       proj, n_req, slots, top_k, hidden_size, rank, vocab, dtype,
+                       static_cast<float*>(workspace), scores_out};
+  st = launch_status(dflash::launch_proj(a, plan, as_hip(stream)), "dflash_lattice(projection)");
+  if (st != DFLASH_OK) return st;
+  st = launch_status(dflash::launch_lattice(a, plan, as_hip(stream)), "dflash_lattice");
+  return st == DFLASH_OK ? ok() : st;
+}
+
+int dflash_walk(const float* scores, const int64_t* ids, const float* uniforms, const float* temperatures,
+                const uint8_t* greedy_mask, int32_t n_req, int32_t slots, int32_t top_k, int64_t* tokens_out,
+                float* q_out, dflash_stream_t stream) {
+  int st = check_walk(scores, ids, uniforms, temperatures, greedy_mask, n_req, slots, top_k, tokens_out, q_out,
+                      "dflash_walk");
+  if (st != DFLASH_OK) return st;
+  if ((int64_t)n_req * slots == 0) return ok();
+  dflash::WalkArgs a{scores, ids, uniforms, temperatures, greedy_mask, n_req, slots, top_k, tokens_out, q_out};
+  st = launch_status(dflash::launch_walk(a, as_hip(stream)), "dflash_walk");
+  return st == DFLASH_OK ? ok() : st;
+}
+
+size_t dflash_propose_block_workspace_size(const dflash_draft_config* cfg, int32_t n_req, int64_t valid_vocab) {
+  if (!cfg || n_req <= 0 || valid_vocab <= 0 || cfg->block_size < 2 || cfg->selector_top_k <= 0 ||
+      cfg->selector_rank <= 0 || cfg->hidden_size <= 0)
+    return 0;
+  return block_layout(cfg, n_req, valid_vocab).bytes;
+}
+
+int dflash_propose_block(const dflash_draft_config* cfg, const dflash_block_args* a, dflash_stream_t stream) {
+  const char* who = "dflash_propose_block";
+  if (!a) return fail(DFLASH_ERR_INVALID_ARG, "%s: null args", who);
+  int st = dflash_validate_config(cfg);
+  if (st != DFLASH_OK) return st;
+  if (cfg->conv_kernel_size == 0 || cfg->selector_top_k == 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: needs both the conv and the selector enabled", who);
+  if (cfg->block_size < 2) return fail(DFLASH_ERR_INVALID_ARG, "%s: block_size must be >= 2", who);
+  if (a->n_req < 0) return fail(DFLASH_ERR_INVALID_ARG, "%s: n_req < 0", who);
+  const int32_t B = cfg->block_size, S = B - 1, H = cfg->hidden_size, K = cfg->selector_top_k;
+  const int32_t r = cfg->selector_rank, T = cfg->conv_kernel_size, gs = cfg->conv_group_size;
+  const int64_t N = (int64_t)a->n_req * B, rows = (int64_t)a->n_req * S;
+  if (rows >= ((int64_t)1 << 31)) return fail(DFLASH_ERR_UNSUPPORTED, "%s: too many slot rows", who);
+  st = check_conv(a->x, a->conv_base, a->conv_delta, a->delta_row_stride, a->conv_out, N, H, gs, T, B, a->dtype);
+  if (st != DFLASH_OK) return st;
+  const BlockLayout L = block_layout(cfg, a->n_req > 0 ? a->n_req : 1, a->valid_vocab > 0 ? a->valid_vocab : 1);
+  st = check_topk(a->logits, a->logits_row_stride, rows, a->vocab, a->valid_vocab, K, cfg->output_multiplier,
+                  cfg->final_logit_softcapping, a->dtype, a->ids_out, a->unary_out, L.topk, a->workspace,
+                  a->workspace_bytes, who);
+  if (st != DFLASH_OK) return st;
+  st = check_select(a->ids_out, a->unary_out, a->conv_out, (int64_t)B * H, H, a->anchor_ids, a->sel_a, a->sel_b,
+                    a->proj, a->n_req, S, K, H, r, a->vocab, a->dtype, who);
+  if (st != DFLASH_OK) return st;
+  st = check_walk(a->scores_out ? a->scores_out : reinterpret_cast<const float*>(16), a->ids_out, a->uniforms,
+                  a->temperatures, a->greedy_mask, a->n_req, S, K, a->tokens_out, a->q_out, who);
+  if (st != DFLASH_OK) return st;
+  if (a->n_req == 0) return ok();
+  if (a->workspace_bytes < L.bytes || !a->workspace)
+    return fail(DFLASH_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu needed", who, a->workspace_bytes, L.bytes);
+  if (reinterpret_cast<uintptr_t>(a->workspace) & 255)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", who);
+
+  hipStream_t s = as_hip(stream);
+  char* ws = static_cast<char*>(a->workspace);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(ws + L.topk.counters_offset);
+  float* scores = a->scores_out ? a->scores_out : reinterpret_cast<float*>(ws + L.scores_off);
+  void* const* ev = a->stage_events;
+
+  // stage 0: conv (also clears the top-K row tickets)
+  if ((st = record(ev, 0, s)) != DFLASH_OK) return st;
+  dflash::ConvArgs ca{a->x, a->conv_base, a->conv_delta, a->delta_row_stride, a->conv_out, N, H, gs, T, B,
+                      a->dtype, counters, (int32_t)rows};
+  if ((st = launch_status(dflash::launch_conv(ca, s), who)) != DFLASH_OK) return st;
+  if ((st = record(ev, 1, s)) != DFLASH_OK) return st;
+  // stage 1: transform + top-K
+  if ((st = record(ev, 2, s)) != DFLASH_OK) return st;
+  dflash::TopkArgs ta{a->logits, a->logits_row_stride, rows, a->vocab, a->valid_vocab, K, cfg->output_multiplier,
+                      cfg->final_logit_softcapping, a->dtype, a->ids_out, a->unary_out, a->workspace, true};
+  if ((st = launch_status(dflash::launch_topk(ta, L.topk, s), who)) != DFLASH_OK) return st;
+  if ((st = record(ev, 3, s)) != DFLASH_OK) return st;
+  // stage 2: projection of the slot rows of the conv output
+  const dflash::ProjPlan pp = dflash::plan_proj((int32_t)rows, r, H, a->dtype);
+  const void* hidden = static_cast<const char*>(a->conv_out) + (size_t)H * (a->dtype == DFLASH_BF16 ? 2 : 4);
+  dflash::SelectArgs sa{a->ids_out, a->unary_out, hidden, (int64_t)B * H, (int64_t)H, a->anchor_ids, a->sel_a,
+                        a->sel_b, a->proj, a->n_req, S, K, H, r, a->vocab, a->dtype,
+                        reinterpret_cast<float*>(ws + L.proj_off), scores};
+  if ((st = record(ev, 4, s)) != DFLASH_OK) return st;
+  if ((st = launch_status(dflash::launch_proj(sa, pp, s), who)) != DFLASH_OK) return st;
+  if ((st = record(ev, 5, s)) != DFLASH_OK) return st;
+  // stage 3: lattice + walk
+  if ((st = record(ev, 6, s)) != DFLASH_OK) return st;
+  if ((st = launch_status(dflash::launch_lattice(sa, pp, s), who)) != DFLASH_OK) return st;
+  dflash::WalkArgs wa{scores, a->ids_out, a->uniforms, a->temperatures, a->greedy_mask, a->n_req, S, K,
+                      a->tokens_out, a->q_out};
+  if ((st = launch_status(dflash::launch_walk(wa, s), who)) != DFLASH_OK) return st;
+  if ((st = record(ev, 7, s)) != DFLASH_OK) return st;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// Internal declarations of the DFlash2 HIP library: device helpers shared by
+// the kernels and the host-side launchers called by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace dflash {
+
+// ---------------------------------------------------------------------------
+// bfloat16 storage helpers (raw 16-bit patterns)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {               // bf16 storage
+  static constexpr int kVec = 8;                  // elements per 16-byte vector
+  __device__ static float load(const uint16_t* p) { return bf16_to_f32(*p); }
+  __device__ static float to_f32(uint16_t v) { return bf16_to_f32(v); }
+};
+template <> struct Elem<float> {
+  static constexpr int kVec = 4;
+  __device__ static float load(const float* p) { return *p; }
+  __device__ static float to_f32(float v) { return v; }
+};
+
+// Unpack one 16-byte vector into fp32 values.
+__device__ __forceinline__ void unpack16(const uint4& v, float (&o)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack16(const uint4& v, float (&o)[4]) {
+  o[0] = __uint_as_float(v.x);
+  o[1] = __uint_as_float(v.y);
+  o[2] = __uint_as_float(v.z);
+  o[3] = __uint_as_float(v.w);
+}
+
+// ---------------------------------------------------------------------------
+// Wave (64-lane) reductions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (each returns hipSuccess or the launch error)
+// ---------------------------------------------------------------------------
+struct ConvArgs {
+  const void* x;
+  const void* base;
+  const void* delta;
+  int64_t delta_row_stride;
+  void* out;
+  int64_t n_tokens;
+  int32_t hidden, group_size, taps, block_size;
+  int32_t dtype;          // DFLASH_F32 / DFLASH_BF16
+  uint32_t* zero_ptr;     // optional: this many u32 words are cleared by the launch
+  int32_t zero_count;
+};
+hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
+
+struct TopkPlan {
+  int64_t n_rows, valid_vocab;
+  int32_t top_k;
+  int32_t chunks;           // row chunks, one workgroup each
+  size_t parts_offset;      // byte offsets inside the workspace
+  size_t counters_offset;
+  size_t bytes;             // total workspace bytes
+};
+TopkPlan plan_topk(int64_t n_rows, int64_t valid_vocab, int32_t top_k);
+// Max row chunks times top_k a row merge can hold.
+constexpr int kTopkMergeCap = 2048;
+
+struct TopkArgs {
+  const void* logits;
+  int64_t row_stride, n_rows, vocab, valid_vocab;
+  int32_t top_k;
+  float multiplier, softcap;
+  int32_t dtype;
+  int64_t* ids_out;
+  float* unary_out;
+  void* workspace;
+  bool counters_zeroed;     // true when an earlier launch on the stream cleared them
+};
+hipError_t launch_topk_zero(const TopkArgs& a, const TopkPlan& p, hipStream_t stream);
+hipError_t launch_topk(const TopkArgs& a, const TopkPlan& p, hipStream_t stream);
+
+struct ProjPlan {
+  int32_t n_rows, rank, hidden;
+  int32_t row_tiles, ksplit, kslice;   // split of the contraction over workgroups
+  size_t bytes;                        // fp32 partials [ksplit][n_rows][rank]
+};
+ProjPlan plan_proj(int32_t n_rows, int32_t rank, int32_t hidden, int32_t dtype);
+
+struct SelectArgs {
+  const int64_t* ids;
+  const float* unary;
+  const void* hidden;
+  int64_t hidden_req_stride, hidden_slot_stride;
+  const int64_t* anchor;
+  const void* sel_a;
+  const void* sel_b;
+  const void* proj;
+  int32_t n_req, slots, top_k, hidden_size, rank;
+  int64_t vocab;
+  int32_t dtype;
+  float* u_parts;           // workspace: ProjPlan::bytes
+  float* scores;            // [n_req, slots, K, K]
+};
+hipError_t launch_proj(const SelectArgs& a, const ProjPlan& p, hipStream_t stream);
+hipError_t launch_lattice(const SelectArgs& a, const ProjPlan& p, hipStream_t stream);
+
+struct WalkArgs {
+  const float* scores;
+  const int64_t* ids;
+  const float* uniforms;
+  const float* temperatures;
+  const uint8_t* greedy;
+  int32_t n_req, slots, top_k;
+  int64_t* tokens;
+  float* q;
+};
+hipError_t launch_walk(const WalkArgs& a, hipStream_t stream);
+
+}  // namespace dflash

@@ -1,0 +1,186 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, its structs have the layout the binding mirrors, and the
+host-side validation rejects contract violations (the DFlash2 pages' config
+pairing and hidden % group_size errors) before anything is launched.  No
+call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_draft_proposal_amd as D
+from block_draft_proposal_amd import binding as Bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point():
+    names = _declared_functions()
+    assert "dflash_propose_block" in names and len(names) == 11
+    lib = D.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(Bd.EXPORTED) == names
+    out = subprocess.run(["nm", "-D", "--defined-only", D.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, flags=re.M), n
+
+
+def test_abi_version():
+    assert D.lib().dflash_abi_version() == 1
+
+
+def test_struct_layout_matches_c(tmp_path):
+    fields_cfg = [f for f, _ in Bd.DraftConfig._fields_]
+    fields_args = [f for f, _ in Bd.BlockArgs._fields_]
+    src = ['#include <stdio.h>', '#include <stddef.h>', '#include "dflash.h"', "int main(void){"]
+    src.append('printf("cfg %zu\\n", sizeof(dflash_draft_config));')
+    src.append('printf("args %zu\\n", sizeof(dflash_block_args));')
+    for f in fields_cfg:
+        src.append(f'printf("cfg.{f} %zu\\n", offsetof(dflash_draft_config, {f}));')
+    for f in fields_args:
+        src.append(f'printf("args.{f} %zu\\n", offsetof(dflash_block_args, {f}));')
+    src.append("return 0;}")
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True).stdout.splitlines())
+    assert int(got["cfg"]) == ctypes.sizeof(Bd.DraftConfig)
+    assert int(got["args"]) == ctypes.sizeof(Bd.BlockArgs)
+    for f in fields_cfg:
+        assert int(got[f"cfg.{f}"]) == getattr(Bd.DraftConfig, f).offset, f
+    for f in fields_args:
+        assert int(got[f"args.{f}"]) == getattr(Bd.BlockArgs, f).offset, f
+
+
+def _cfg(**kw):
+    base = dict(taps=4, group_size=64, rank=64, top_k=8, multiplier=1.0, softcap=30.0, block_size=16, hidden=4096)
+    base.update(kw)
+    return D.make_config(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0),
+    (dict(taps=0, group_size=0), 0),
+    (dict(rank=0, top_k=0), 0),
+    (dict(taps=4, group_size=0), -1),
+    (dict(taps=0, group_size=64), -1),
+    (dict(rank=0, top_k=8), -1),
+    (dict(rank=64, top_k=0), -1),
+    (dict(group_size=48), -1),                  # 48 does not divide 4096
+    (dict(multiplier=0.0), -1),
+    (dict(multiplier=float("nan")), -1),
+    (dict(softcap=-1.0), -1),
+    (dict(block_size=0), -1),
+    (dict(top_k=33), -2),
+])
+def test_validate_config(kw, code):
+    cfg = _cfg(**kw)
+    assert D.lib().dflash_validate_config(ctypes.byref(cfg)) == code
+    if code:
+        assert D.last_error()
+
+
+FAKE = 1 << 20          # never dereferenced: validation fails first
+
+
+def test_conv_validation():
+    L = D.lib()
+    # hidden % group_size
+    assert L.dflash_conv(FAKE, FAKE, FAKE, 4 * 85, FAKE + (1 << 24), 16, 4096, 48, 4, 16, 1, None) == -1
+    assert "must divide" in D.last_error()
+    # ragged token count
+    assert L.dflash_conv(FAKE, FAKE, FAKE, 4 * 64, FAKE + (1 << 24), 17, 4096, 64, 4, 16, 1, None) == -1
+    # delta stride too small
+    assert L.dflash_conv(FAKE, FAKE, FAKE, 3 * 64, FAKE + (1 << 24), 16, 4096, 64, 4, 16, 1, None) == -1
+    # misaligned x
+    assert L.dflash_conv(FAKE + 2, FAKE, FAKE, 4 * 64, FAKE + (1 << 24), 16, 4096, 64, 4, 16, 1, None) == -1
+    # out overlapping x
+    assert L.dflash_conv(FAKE, FAKE, FAKE, 4 * 64, FAKE + 64, 16, 4096, 64, 4, 16, 1, None) == -1
+    # null pointer
+    assert L.dflash_conv(None, FAKE, FAKE, 4 * 64, FAKE + (1 << 24), 16, 4096, 64, 4, 16, 1, None) == -1
+    # bad dtype
+    assert L.dflash_conv(FAKE, FAKE, FAKE, 4 * 64, FAKE + (1 << 24), 16, 4096, 64, 4, 16, 7, None) == -1
+    # hidden not a multiple of the 16-byte vector
+    assert L.dflash_conv(FAKE, FAKE, FAKE, 4 * 1, FAKE + (1 << 24), 16, 4, 4, 4, 16, 1, None) == -2
+    # empty input is a no-op
+    assert L.dflash_conv(None, None, None, 4 * 64, None, 0, 4096, 64, 4, 16, 1, None) == 0
+
+
+def test_topk_validation():
+    L = D.lib()
+    ws = L.dflash_topk_workspace_size(480, 151936, 8)
+    assert ws > 0
+    args = lambda **k: dict(dict(logits=FAKE, stride=151936, rows=480, vocab=151936, valid=151936, k=8, m=1.0,
+                                 cap=30.0, dtype=1, ids=FAKE, unary=FAKE, ws=FAKE, wsb=ws), **k)
+
+    def call(a):
+        return L.dflash_topk(a["logits"], a["stride"], a["rows"], a["vocab"], a["valid"], a["k"], a["m"],
+                             a["cap"], a["dtype"], a["ids"], a["unary"], a["ws"], a["wsb"], None)
+
+    assert call(args(k=0)) == -1
+    assert call(args(k=33)) == -2
+    assert call(args(valid=4)) == -1                 # K > valid_vocab
+    assert call(args(valid=151937)) == -1            # valid_vocab > vocab
+    assert call(args(stride=151935)) == -1           # row stride < vocab
+    assert call(args(m=0.0)) == -1
+    assert call(args(m=-1.0)) == -1
+    assert call(args(cap=-2.0)) == -1
+    assert call(args(wsb=ws - 1)) == -3
+    assert call(args(logits=FAKE + 8)) == -1         # misaligned rows
+    assert call(args(stride=151937, vocab=151936)) == -1
+    assert call(args(vocab=1 << 24, valid=1 << 24, stride=1 << 24)) == -2
+    assert call(args(rows=0, logits=None, ids=None, unary=None, ws=None, wsb=0)) == 0
+
+
+def test_lattice_and_walk_validation():
+    L = D.lib()
+    # rank beyond what the bf16 projection supports
+    assert L.dflash_lattice(FAKE, FAKE, FAKE, 16 * 4096, 4096, FAKE, FAKE, FAKE, FAKE, 32, 15, 8, 4096, 256, 151936,
+                            1, FAKE, FAKE, 1 << 30, None) == -2
+    # hidden row stride misaligned
+    assert L.dflash_lattice(FAKE, FAKE, FAKE, 16 * 4096 + 1, 4096, FAKE, FAKE, FAKE, FAKE, 32, 15, 8, 4096, 64,
+                            151936, 1, FAKE, FAKE, 1 << 30, None) == -1
+    # workspace too small
+    need = L.dflash_lattice_workspace_size(32, 15, 64, 4096)
+    assert L.dflash_lattice(FAKE, FAKE, FAKE, 16 * 4096, 4096, FAKE, FAKE, FAKE, FAKE, 32, 15, 8, 4096, 64, 151936,
+                            1, FAKE, FAKE, need - 1, None) == -3
+    assert L.dflash_walk(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 3, 0, FAKE, FAKE, None) == -1
+    assert L.dflash_walk(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 3, 40, FAKE, FAKE, None) == -2
+    assert L.dflash_walk(None, FAKE, FAKE, FAKE, FAKE, 4, 3, 4, FAKE, FAKE, None) == -1
+    assert L.dflash_walk(None, None, None, None, None, 0, 3, 4, None, None, None) == 0
+
+
+def test_propose_block_validation():
+    L = D.lib()
+    cfg = _cfg()
+    args = Bd.BlockArgs()
+    args.n_req = 32
+    args.dtype = 1
+    assert L.dflash_propose_block(ctypes.byref(cfg), ctypes.byref(args), None) == -1   # null pointers
+    bad = _cfg(taps=0, group_size=0)
+    assert L.dflash_propose_block(ctypes.byref(bad), ctypes.byref(args), None) == -1
+    assert "conv and the selector" in D.last_error()
+    bad = _cfg(block_size=1)
+    assert L.dflash_propose_block(ctypes.byref(bad), ctypes.byref(args), None) == -1
+    assert L.dflash_propose_block_workspace_size(ctypes.byref(cfg), 32, 151936) > 0
+
+
+def test_error_message_is_per_call():
+    L = D.lib()
+    cfg = _cfg(group_size=48)
+    assert L.dflash_validate_config(ctypes.byref(cfg)) == -1
+    assert "divide" in D.last_error()
+    cfg = _cfg()
+    assert L.dflash_validate_config(ctypes.byref(cfg)) == 0
+    assert D.last_error() == ""

@@ -1,0 +1,174 @@
+"""GPU tests of dflash_propose_block, the whole draft block ("[Spec]
+DFlash2", draft-sampler excerpt): it must equal the chain of the four entry
+points bit for bit, repeat bit for bit, and agree end to end with the oracle
+run from the raw inputs (ids exact; every walk decision whose margin clears
+the rounding band of the fp32 lattice must match; decisions inside the band
+are counted and the oracle continues from the GPU's choice)."""
+import numpy as np
+import pytest
+import torch
+
+import block_draft_proposal_amd as D
+import workloads as W
+from gpu_helpers import CONV_TOL, DEV, conv_rel_err, f64, require_gpu, sample_indices, say
+from oracle import dflash_oracle as O
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -24
+
+
+def _cfg(w: W.Workload):
+    return D.make_config(taps=w.taps, group_size=w.group_size, rank=w.rank, top_k=w.top_k,
+                         multiplier=w.multiplier, softcap=w.softcap, block_size=w.block_size, hidden=w.hidden)
+
+
+def _propose(w, inp, keep_scores=True, **kw):
+    return D.dflash_propose_block(_cfg(w), x=inp["x"], conv_base=inp["base"][0], conv_delta=inp["delta"][:, 0],
+                                  logits=inp["logits"], anchor=inp["anchor"], sel_a=inp["sel_a"],
+                                  sel_b=inp["sel_b"], proj=inp["proj"], uniforms=inp["uniforms"],
+                                  temperatures=inp["temperatures"], greedy_mask=inp["greedy_mask"],
+                                  valid_vocab=w.valid_vocab, keep_scores=keep_scores, **kw)
+
+
+def _chain(w, inp):
+    conv = D.dflash_conv(inp["x"], inp["base"][0], inp["delta"][:, 0], block_size=w.block_size,
+                         group_size=w.group_size)
+    ids, unary = D.dflash_topk(inp["logits"], top_k=w.top_k, valid_vocab=w.valid_vocab, multiplier=w.multiplier,
+                               softcap=w.softcap)
+    R, S, K = w.n_req, w.slots, w.top_k
+    ids, unary = ids.view(R, S, K), unary.view(R, S, K)
+    hid = conv.view(R, w.block_size, w.hidden)[:, 1:, :]
+    scores = D.dflash_lattice(ids, unary, hid, inp["anchor"], inp["sel_a"], inp["sel_b"], inp["proj"])
+    tok, q = D.dflash_walk(scores, ids, inp["uniforms"], inp["temperatures"], inp["greedy_mask"])
+    return dict(conv_out=conv, ids=ids, unary=unary, scores=scores, tokens=tok, q=q)
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_fused_equals_chain_and_repeats(name):
+    require_gpu()
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w, device=DEV)
+    say(f"dflash_propose_block {name} (fused vs chain)")
+    a = _propose(w, inp)
+    b = _propose(w, inp)
+    c = _chain(w, inp)
+    torch.cuda.synchronize()
+    for k in ("conv_out", "ids", "unary", "scores", "tokens", "q"):
+        assert torch.equal(a[k], b[k]), ("repeat", k)
+        assert torch.equal(a[k], c[k]), ("chain", k)
+    # the scores-in-workspace variant gives the same tokens and q
+    d = _propose(w, inp, keep_scores=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a["tokens"], d["tokens"]) and torch.equal(a["q"], d["q"])
+
+
+def _e2e(w: W.Workload, req_sample):
+    inp = W.make_inputs(w, device=DEV)
+    say(f"dflash_propose_block {w.name} (end to end vs oracle)")
+    out = _propose(w, inp)
+    torch.cuda.synchronize()
+    R, B, S, K, H = w.n_req, w.block_size, w.slots, w.top_k, w.hidden
+    reqs = np.arange(R) if req_sample is None else sample_indices(R, req_sample, seed=2)
+    tok_rows = np.concatenate([np.arange(r * B, (r + 1) * B) for r in reqs])
+    slot_rows = np.concatenate([np.arange(r * S, (r + 1) * S) for r in reqs])
+    ti = torch.from_numpy(tok_rows).to(DEV)
+    si = torch.from_numpy(slot_rows).to(DEV)
+    ri = torch.from_numpy(reqs).to(DEV)
+    host = dict(x=f64(inp["x"][ti]), base=f64(inp["base"]), delta=f64(inp["delta"][ti]),
+                logits=f64(inp["logits"][si]), anchor=inp["anchor"][ri].cpu().numpy(),
+                sel_a=f64(inp["sel_a"]), sel_b=f64(inp["sel_b"]), proj=f64(inp["proj"]),
+                uniforms=inp["uniforms"][ri].cpu().numpy(), temperatures=inp["temperatures"][ri].cpu().numpy(),
+                greedy_mask=inp["greedy_mask"][ri].cpu().numpy())
+    ref = O.propose_block(host, block_size=B, group_size=w.group_size, valid_vocab=w.valid_vocab, top_k=K,
+                          multiplier=w.multiplier, softcap=w.softcap, dtype=w.dtype)
+    # conv
+    assert conv_rel_err(f64(out["conv_out"][ti]), ref["conv_out"]) <= CONV_TOL[w.dtype]
+    # ids exact, unary close
+    np.testing.assert_array_equal(out["ids"][ri].cpu().numpy(), ref["ids"])
+    assert np.all(np.abs(f64(out["unary"][ri]) - ref["unary"]) <= 1e-5 * (1 + np.abs(ref["unary"])))
+    # scores: fp64 oracle (from the oracle's own rounded conv output) vs GPU
+    got_scores = f64(out["scores"][ri])
+    M1, M2 = O.lattice_error_scale(ref["ids"], ref["unary"], ref["h"], host["proj"], host["anchor"],
+                                   host["sel_a"], host["sel_b"])
+    # band: fp32 rounding of both accumulations, plus the effect of the conv
+    # outputs that the two sides rounded to different storage values
+    # (M3 = sum_k |A_pk||B_ck| sum_h |P_kh| |h_gpu - h_ref|), plus the unary
+    # tolerance
+    h_gpu = f64(out["conv_out"][ti]).reshape(len(reqs), B, H)[:, 1:, :]
+    dh = np.abs(h_gpu - ref["h"])
+    M3, _ = O.lattice_error_scale(ref["ids"], ref["unary"], dh, host["proj"], host["anchor"], host["sel_a"],
+                                  host["sel_b"])
+    band = ((H + 8) * U * M1 + (w.rank + 8) * U * M2 + M3
+            + 1e-5 * (1 + np.abs(ref["unary"]))[:, :, None, :])
+    print(f"[e2e] {w.name}: conv outputs rounded differently: {int(np.count_nonzero(dh))} of {dh.size}",
+          flush=True)
+    assert np.all(np.abs(got_scores - ref["scores"]) <= band), float(np.max(np.abs(got_scores - ref["scores"]) / band))
+    # walk decisions
+    got_tok = out["tokens"][ri].cpu().numpy()
+    got_q = out["q"][ri].cpu().numpy()
+    greedy = host["greedy_mask"]
+    near = 0
+    for i, r in enumerate(reqs):
+        prev = 0
+        for s in range(S):
+            row_ref = ref["scores"][i, s, prev]
+            row_band = band[i, s, prev]
+            idx = int(np.flatnonzero(out["ids"][r, s].cpu().numpy() == got_tok[i, s])[0])
+            if greedy[i]:
+                best = int(np.argmax(row_ref))
+                if idx != best:
+                    # allowed only if the two are within the rounding band
+                    assert row_ref[best] - row_ref[idx] <= row_band[best] + row_band[idx], (r, s)
+                    near += 1
+                assert got_q[i, s, idx] == 1.0
+            else:
+                t = max(float(host["temperatures"][i]), 1e-5)
+                x = row_ref / t
+                p = np.exp(x - x.max()); p /= p.sum()
+                cdf = np.cumsum(p)
+                u = float(host["uniforms"][i, s])
+                want = min(int(np.count_nonzero(u >= cdf)), K - 1)
+                if idx != want:
+                    # the CDF shift from score rounding: |dC| <= sum_j p_j |dx_j| * 2
+                    dc = 2 * np.sum(p * row_band / t) + 4e-6
+                    lo = cdf[min(idx, want)]
+                    assert abs(u - lo) <= dc, (r, s, u, lo, dc)
+                    near += 1
+                np.testing.assert_allclose(got_q[i, s], p, atol=max(1e-5, 4 * float(np.max(row_band / t))))
+            prev = idx
+    return near
+
+
+@pytest.mark.parametrize("name,reqs", [("tiny_fp32", None), ("bf16_b16_v151936", 8),
+                                       ("nonpow2_b10_v151936", 8), ("padded_v201024_k16", 6),
+                                       ("stress_r1024_k32", 4)])
+def test_end_to_end_against_oracle(name, reqs):
+    require_gpu()
+    near = _e2e(W.WORKLOADS[name], reqs)
+    print(f"[e2e] {name}: decisions inside the rounding band: {near}", flush=True)
+
+
+def test_stage_events_are_recorded():
+    require_gpu()
+    w = W.WORKLOADS["bf16_b16_v151936"]
+    inp = W.make_inputs(w, device=DEV)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    say("dflash_propose_block with stage events")
+    out = _propose(w, inp, stage_events=ev)
+    torch.cuda.synchronize()
+    times = [ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(4)]
+    assert all(t >= 0 for t in times)
+    assert times[1] > 0
+    assert out["tokens"].shape == (w.n_req, w.slots)
+
+
+def test_zero_requests_is_a_no_op():
+    require_gpu()
+    w = W.WORKLOADS["tiny_fp32"].replace(n_req=0)
+    inp = W.make_inputs(w, device=DEV)
+    out = _propose(w, inp)
+    torch.cuda.synchronize()
+    assert out["tokens"].shape == (0, w.slots)
