@@ -97,8 +97,6 @@ int check_topk(const void* logits, int64_t row_stride, int64_t n_rows, int64_t v
     return fail(DFLASH_ERR_INVALID_ARG, "%s: output_multiplier must be finite and > 0", who);
   if (!(std::isfinite(cap) && cap >= 0.f))
     return fail(DFLASH_ERR_INVALID_ARG, "%s: final_logit_softcapping must be finite and >= 0", who);
-  if ((int64_t)plan.chunks * top_k > dflash::kTopkMergeCap)
-    return fail(DFLASH_ERR_UNSUPPORTED, "%s: valid_vocab too large for top_k=%d", who, top_k);
   if (n_rows == 0) return DFLASH_OK;
   if (!logits || !ids_out || !unary_out) return fail(DFLASH_ERR_INVALID_ARG, "%s: null pointer", who);
   if (!aligned16(logits) || (row_stride * elem_bytes(dtype)) % 16)
@@ -107,7 +105,7 @@ int check_topk(const void* logits, int64_t row_stride, int64_t n_rows, int64_t v
     return fail(DFLASH_ERR_INVALID_ARG, "%s: misaligned output", who);
   if (ws_bytes < plan.bytes || (plan.bytes && !ws))
     return fail(DFLASH_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu needed", who, ws_bytes, plan.bytes);
-  if (reinterpret_cast<uintptr_t>(ws) & 255)
+  if (plan.bytes && (reinterpret_cast<uintptr_t>(ws) & 255))
     return fail(DFLASH_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", who);
   return DFLASH_OK;
 }
@@ -218,7 +216,7 @@ int dflash_conv(const void* x, const void* base, const void* delta, int64_t delt
   if (st != DFLASH_OK) return st;
   if (n_tokens == 0) return ok();
   dflash::ConvArgs a{x, base, delta, delta_row_stride, out, n_tokens, hidden, group_size, taps, block_size,
-                     dtype, nullptr, 0};
+                     dtype};
   st = launch_status(dflash::launch_conv(a, as_hip(stream)), "dflash_conv");
   return st == DFLASH_OK ? ok() : st;
 }
@@ -238,9 +236,7 @@ int dflash_topk(const void* logits, int64_t row_stride, int64_t n_rows, int64_t 
   if (st != DFLASH_OK) return st;
   if (n_rows == 0) return ok();
   dflash::TopkArgs a{logits, row_stride, n_rows, vocab, valid_vocab, top_k, output_multiplier, softcap,
-                     dtype, ids_out, unary_out, workspace, false};
-  st = launch_status(dflash::launch_topk_zero(a, plan, as_hip(stream)), "dflash_topk");
-  if (st != DFLASH_OK) return st;
+                     dtype, ids_out, unary_out, workspace};
   st = launch_status(dflash::launch_topk(a, plan, as_hip(stream)), "dflash_topk");
   return st == DFLASH_OK ? ok() : st;
 }
@@ -330,20 +326,19 @@ int dflash_propose_block(const dflash_draft_config* cfg, const dflash_block_args
 
   hipStream_t s = as_hip(stream);
   char* ws = static_cast<char*>(a->workspace);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(ws + L.topk.counters_offset);
   float* scores = a->scores_out ? a->scores_out : reinterpret_cast<float*>(ws + L.scores_off);
   void* const* ev = a->stage_events;
 
-  // stage 0: conv (also clears the top-K row tickets)
+  // stage 0: conv
   if ((st = record(ev, 0, s)) != DFLASH_OK) return st;
   dflash::ConvArgs ca{a->x, a->conv_base, a->conv_delta, a->delta_row_stride, a->conv_out, N, H, gs, T, B,
-                      a->dtype, counters, (int32_t)rows};
+                      a->dtype};
   if ((st = launch_status(dflash::launch_conv(ca, s), who)) != DFLASH_OK) return st;
   if ((st = record(ev, 1, s)) != DFLASH_OK) return st;
   // stage 1: transform + top-K
   if ((st = record(ev, 2, s)) != DFLASH_OK) return st;
   dflash::TopkArgs ta{a->logits, a->logits_row_stride, rows, a->vocab, a->valid_vocab, K, cfg->output_multiplier,
-                      cfg->final_logit_softcapping, a->dtype, a->ids_out, a->unary_out, a->workspace, true};
+                      cfg->final_logit_softcapping, a->dtype, a->ids_out, a->unary_out, a->workspace};
   if ((st = launch_status(dflash::launch_topk(ta, L.topk, s), who)) != DFLASH_OK) return st;
   if ((st = record(ev, 3, s)) != DFLASH_OK) return st;
   // stage 2: projection of the slot rows of the conv output

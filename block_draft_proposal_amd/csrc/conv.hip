@@ -66,12 +66,9 @@ template <typename TIO, int TAPS, bool ONE_GROUP>
 __global__ __launch_bounds__(kThreads) void conv_kernel(const TIO* __restrict__ x,
                                                         const TIO* __restrict__ base,
                                                         const TIO* __restrict__ delta,
-                                                        TIO* __restrict__ out, ConvGeom g,
-                                                        uint32_t* __restrict__ zero_ptr,
-                                                        int32_t zero_count) {
+                                                        TIO* __restrict__ out, ConvGeom g) {
   constexpr int VEC = Elem<TIO>::kVec;
   const int64_t unit = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (unit < zero_count) zero_ptr[unit] = 0u;
   if (unit >= g.units) return;
 
   const int v = (int)(unit % g.nvec);
@@ -135,12 +132,9 @@ template <typename TIO>
 __global__ __launch_bounds__(kThreads) void conv_kernel_any_taps(const TIO* __restrict__ x,
                                                                  const TIO* __restrict__ base,
                                                                  const TIO* __restrict__ delta,
-                                                                 TIO* __restrict__ out, ConvGeom g,
-                                                                 uint32_t* __restrict__ zero_ptr,
-                                                                 int32_t zero_count) {
+                                                                 TIO* __restrict__ out, ConvGeom g) {
   constexpr int VEC = Elem<TIO>::kVec;
   const int64_t unit = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (unit < zero_count) zero_ptr[unit] = 0u;
   if (unit >= g.units) return;
   const int v = (int)(unit % g.nvec);
   const int64_t rest = unit / g.nvec;
@@ -169,19 +163,16 @@ __global__ __launch_bounds__(kThreads) void conv_kernel_any_taps(const TIO* __re
 
 template <typename TIO, int TAPS>
 hipError_t launch_t(const ConvArgs& a, const ConvGeom& g, hipStream_t s) {
-  const int64_t work = g.units > a.zero_count ? g.units : a.zero_count;
-  const dim3 grid((unsigned)((work + kThreads - 1) / kThreads));
+  const dim3 grid((unsigned)((g.units + kThreads - 1) / kThreads));
   const bool one_group = (a.group_size % Elem<TIO>::kVec) == 0;
   const TIO* x = static_cast<const TIO*>(a.x);
   const TIO* b = static_cast<const TIO*>(a.base);
   const TIO* d = static_cast<const TIO*>(a.delta);
   TIO* o = static_cast<TIO*>(a.out);
   if (one_group)
-    hipLaunchKernelGGL((conv_kernel<TIO, TAPS, true>), grid, dim3(kThreads), 0, s, x, b, d, o, g,
-                       a.zero_ptr, a.zero_count);
+    hipLaunchKernelGGL((conv_kernel<TIO, TAPS, true>), grid, dim3(kThreads), 0, s, x, b, d, o, g);
   else
-    hipLaunchKernelGGL((conv_kernel<TIO, TAPS, false>), grid, dim3(kThreads), 0, s, x, b, d, o, g,
-                       a.zero_ptr, a.zero_count);
+    hipLaunchKernelGGL((conv_kernel<TIO, TAPS, false>), grid, dim3(kThreads), 0, s, x, b, d, o, g);
   return hipGetLastError();
 }
 
@@ -197,12 +188,10 @@ hipError_t launch_dtype(const ConvArgs& a, const ConvGeom& g, hipStream_t s) {
     case 7: return launch_t<TIO, 7>(a, g, s);
     case 8: return launch_t<TIO, 8>(a, g, s);
     default: {
-      const int64_t work = g.units > a.zero_count ? g.units : a.zero_count;
-      const dim3 grid((unsigned)((work + kThreads - 1) / kThreads));
+      const dim3 grid((unsigned)((g.units + kThreads - 1) / kThreads));
       hipLaunchKernelGGL((conv_kernel_any_taps<TIO>), grid, dim3(kThreads), 0, s,
                          static_cast<const TIO*>(a.x), static_cast<const TIO*>(a.base),
-                         static_cast<const TIO*>(a.delta), static_cast<TIO*>(a.out), g, a.zero_ptr,
-                         a.zero_count);
+                         static_cast<const TIO*>(a.delta), static_cast<TIO*>(a.out), g);
       return hipGetLastError();
     }
   }
@@ -231,7 +220,7 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
   g.run_len = run;
   g.runs_per_block = (a.block_size + run - 1) / run;
   g.units = nblocks * g.runs_per_block * g.nvec;
-  if (g.units == 0 && a.zero_count == 0) return hipSuccess;
+  if (g.units == 0) return hipSuccess;
   return a.dtype == DFLASH_BF16 ? launch_dtype<uint16_t>(a, g, stream)
                                 : launch_dtype<float>(a, g, stream);
 }

@@ -87,21 +87,20 @@ struct ConvArgs {
   int64_t n_tokens;
   int32_t hidden, group_size, taps, block_size;
   int32_t dtype;          // DFLASH_F32 / DFLASH_BF16
-  uint32_t* zero_ptr;     // optional: this many u32 words are cleared by the launch
-  int32_t zero_count;
 };
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 
 struct TopkPlan {
   int64_t n_rows, valid_vocab;
   int32_t top_k;
-  int32_t chunks;           // row chunks, one workgroup each
-  size_t parts_offset;      // byte offsets inside the workspace
-  size_t counters_offset;
-  size_t bytes;             // total workspace bytes
+  int32_t chunks;           // 16384-value chunks per row
+  int32_t segs;             // workgroups per row (1: no merge kernel)
+  int32_t chunks_per_seg;
+  size_t parts_offset;      // byte offset of the per-segment partials in the workspace
+  size_t bytes;             // total workspace bytes (0 when segs == 1)
 };
 TopkPlan plan_topk(int64_t n_rows, int64_t valid_vocab, int32_t top_k);
-// Max row chunks times top_k a row merge can hold.
+// LDS slots for one chunk's new candidates, and for a row merge.
 constexpr int kTopkMergeCap = 2048;
 
 struct TopkArgs {
@@ -113,9 +112,7 @@ struct TopkArgs {
   int64_t* ids_out;
   float* unary_out;
   void* workspace;
-  bool counters_zeroed;     // true when an earlier launch on the stream cleared them
 };
-hipError_t launch_topk_zero(const TopkArgs& a, const TopkPlan& p, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, const TopkPlan& p, hipStream_t stream);
 
 struct ProjPlan {

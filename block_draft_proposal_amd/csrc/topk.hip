@@ -8,29 +8,28 @@
 //   ordered by (value descending, id ascending); unary = T(z) of those ids.
 // T is strictly increasing, so selection compares the raw logits exactly.
 //
-// Design (HBM-bound stream, one pass over the logits):
+// Design (HBM-bound stream, one pass over the logits, no cross-workgroup
+// synchronisation):
 //  * Every value becomes an order-preserving unsigned key (-0 and +0 share a
 //    key; a position outside the logical vocabulary has key 0, below every
 //    real value), and every (key, id) pair a 56-bit composite
 //    key << 24 | (2^24 - 1 - id) whose order is exactly (value desc, id asc)
 //    and which is unique within a row.
-//  * A row is cut into chunks of 16384 values; one 256-thread workgroup reads
-//    a chunk (64 values per thread, all 16-byte loads in flight at once, each
-//    wave load one contiguous 1 KiB) and turns it into keys in registers
-//    (bf16 keys packed two per register, built with packed 16-bit ops).
-//  * Threshold: split the workgroup into P >= K thread groups; the minimum of
-//    the groups' maxima is a key that at least K distinct values reach, so the
-//    chunk's top-K all have keys >= it.  On random data only a few dozen
-//    values pass; a packed saturating subtract tests two keys per instruction,
+//  * One 256-thread workgroup owns a row (or, when rows are too few to fill
+//    the chip, a segment of a row; a small second kernel then merges the
+//    segments).  It streams the row in chunks of 16384 values, 64 per thread
+//    as eight 16-byte loads, so each wave load is one contiguous 1 KiB; the
+//    next chunk's loads are issued before the current chunk is processed.
+//    bf16 keys are built and kept two per register with packed 16-bit ops.
+//  * The running K best composites live in LDS.  For the first chunk the
+//    threshold is the minimum over P >= K thread groups of the group maxima
+//    (at least K distinct values reach it); once K are held, a later value
+//    must beat the K-th key strictly (its id is larger than every held id).
+//    A packed saturating subtract tests two keys per instruction; the few
 //    survivors are compacted into LDS and ranked exactly by counting.
-//  * If too many pass (mass ties), an exact bisection on the key, then on the
-//    id among the tied key, narrows the set to exactly K.  That path re-reads
-//    the chunk (cache-resident) instead of holding extra registers.
-//  * Each workgroup writes its chunk's K best composites; the last workgroup
-//    of a row to finish (atomic ticket) ranks the row's chunks x K candidates,
-//    decodes ids and values, applies the transform in fp32 and writes the row.
-//  * Workgroups of one row are placed on one XCD (round-robin dispatch across
-//    the 8 XCDs), so the merge reads partials from the same L2.
+//  * If a chunk yields more survivors than LDS holds (mass ties), an exact
+//    bisection on the key, then on the id among the tied key, narrows the
+//    chunk to exactly its K best; that path re-reads the chunk from cache.
 #include "dflash.h"
 #include "dflash_internal.h"
 
@@ -39,14 +38,19 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPerThread = 64;
-constexpr int kChunk = kThreads * kPerThread;   // values per workgroup
-constexpr int kCap = kTopkMergeCap;             // LDS candidate slots
+constexpr int kChunk = kThreads * kPerThread;   // values per chunk
+constexpr int kCap = kTopkMergeCap;             // LDS slots for new candidates
+constexpr int kMaxK = DFLASH_MAX_TOP_K;
 constexpr uint32_t kIdMask = 0xffffffu;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, int64_t id) {
   return ((uint64_t)key << 24) | (uint64_t)(kIdMask - (uint32_t)id);
+}
+__device__ __forceinline__ uint32_t composite_key(uint64_t c) { return (uint32_t)(c >> 24); }
+__device__ __forceinline__ int64_t composite_id(uint64_t c) {
+  return (int64_t)(kIdMask - (uint32_t)(c & kIdMask));
 }
 
 // bf16 bits -> key in [1, 0xffff]: negatives map to 0x10000 - bits (so -0
@@ -74,21 +78,23 @@ __device__ __forceinline__ float f32_key_value(uint32_t k) {
   return __uint_as_float(b);
 }
 
-// Keys of one thread's 64 chunk values.  Value i (0..63) sits at
+// One thread's 64 values of a chunk.  Value i (0..63) sits at
 // id = c_start + ((i / VEC) * 256 + tid) * VEC + i % VEC.
-template <typename TIO> struct ChunkKeys;
+template <typename TIO> struct Chunk;
 
-template <> struct ChunkKeys<uint16_t> {
+template <> struct Chunk<uint16_t> {
   static constexpr int VEC = 8, L = kPerThread / VEC, W = kPerThread / 2;
-  uint32_t w[W];    // word j holds keys of values 2j (low half) and 2j+1 (high half)
+  uint4 raw[L];      // loaded bits
+  uint32_t w[W];     // packed keys: word j = values 2j (low half), 2j+1 (high half)
 
-  __device__ void load(const uint16_t* rowp, int64_t c_start, int64_t valid, int tid) {
-    uint4 raw[L];
+  __device__ void issue(const uint16_t* rowp, int64_t c_start, int64_t valid, int tid) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
       const int64_t e0 = c_start + ((int64_t)l * kThreads + tid) * VEC;
       raw[l] = (e0 + VEC <= valid) ? *reinterpret_cast<const uint4*>(rowp + e0) : make_uint4(0u, 0u, 0u, 0u);
     }
+  }
+  __device__ void make_keys(const uint16_t* rowp, int64_t c_start, int64_t valid, int tid) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
       const int64_t e0 = c_start + ((int64_t)l * kThreads + tid) * VEC;
@@ -113,9 +119,10 @@ template <> struct ChunkKeys<uint16_t> {
     for (int j = 1; j < W; ++j) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[j]));
     return max((uint32_t)m.x, (uint32_t)m.y);
   }
-  // Calls f(key, value index) for every key >= tau (tau >= 1).
-  template <class F> __device__ void for_each_ge(uint32_t tau, F&& f) const {
-    const u16x2 t = {(unsigned short)(tau - 1), (unsigned short)(tau - 1)};
+  // Calls f(key, value index) for every key >= tau (1 <= tau <= 0x10000).
+  template <class F> __device__ void for_each_ge(uint64_t tau, F&& f) const {
+    const unsigned short t1 = (unsigned short)(tau - 1);
+    const u16x2 t = {t1, t1};
 #pragma unroll
     for (int j = 0; j < W; ++j) {
       const u16x2 d = __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, w[j]), t);
@@ -125,32 +132,32 @@ template <> struct ChunkKeys<uint16_t> {
       }
     }
   }
+  static constexpr uint64_t kKeyLimit = 0x10000u;   // keys are < this
   __device__ static uint32_t key_at(const uint16_t* p) { return bf16_key(*p); }
   __device__ static float value(uint32_t k) { return bf16_key_value(k); }
 };
 
-template <> struct ChunkKeys<float> {
+template <> struct Chunk<float> {
   static constexpr int VEC = 4, L = kPerThread / VEC;
+  uint4 raw[L];
   uint32_t w[kPerThread];
 
-  __device__ void load(const float* rowp, int64_t c_start, int64_t valid, int tid) {
+  __device__ void issue(const float* rowp, int64_t c_start, int64_t valid, int tid) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
       const int64_t e0 = c_start + ((int64_t)l * kThreads + tid) * VEC;
-      uint4 r = (e0 + VEC <= valid) ? *reinterpret_cast<const uint4*>(rowp + e0) : make_uint4(0u, 0u, 0u, 0u);
-      w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
+      raw[l] = (e0 + VEC <= valid) ? *reinterpret_cast<const uint4*>(rowp + e0) : make_uint4(0u, 0u, 0u, 0u);
     }
+  }
+  __device__ void make_keys(const float* rowp, int64_t c_start, int64_t valid, int tid) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
       const int64_t e0 = c_start + ((int64_t)l * kThreads + tid) * VEC;
-      if (e0 + VEC <= valid) {
+      const uint32_t r4[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[l * 4 + q] = f32_key(w[l * 4 + q]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          w[l * 4 + q] = (e0 + q < valid) ? f32_key(__float_as_uint(rowp[e0 + q])) : 0u;
-      }
+      for (int q = 0; q < 4; ++q)
+        w[l * 4 + q] = (e0 + VEC <= valid) ? f32_key(r4[q])
+                       : (e0 + q < valid) ? f32_key(__float_as_uint(rowp[e0 + q])) : 0u;
     }
   }
   __device__ uint32_t max_key() const {
@@ -159,23 +166,24 @@ template <> struct ChunkKeys<float> {
     for (int j = 0; j < kPerThread; ++j) m = max(m, w[j]);
     return m;
   }
-  template <class F> __device__ void for_each_ge(uint32_t tau, F&& f) const {
+  template <class F> __device__ void for_each_ge(uint64_t tau, F&& f) const {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j)
-      if (w[j] >= tau) f(w[j], j);
+      if ((uint64_t)w[j] >= tau) f(w[j], j);
   }
+  static constexpr uint64_t kKeyLimit = 0x100000000ull;
   __device__ static uint32_t key_at(const float* p) { return f32_key(__float_as_uint(*p)); }
   __device__ static float value(uint32_t k) { return f32_key_value(k); }
 };
 
 struct Shared {
-  uint64_t cand[kCap];
+  uint64_t pool[kMaxK + kCap];   // [0, nbest): held best; then new candidates
+  uint64_t best_tmp[kMaxK];
   uint32_t tmax[kThreads];
   uint32_t gmax[64];
   uint32_t red[kThreads / 64];
-  uint32_t count;
-  uint32_t tau;
-  uint32_t last;
+  uint32_t count;                // new candidates appended this chunk
+  uint32_t tau_lo, tau_hi;       // threshold (64-bit, split)
 };
 
 __device__ __forceinline__ int64_t value_id(int64_t c_start, int i, int vec) {
@@ -200,12 +208,12 @@ __device__ uint32_t block_sum(uint32_t v, Shared& sh) {
 template <typename TIO>
 __device__ uint32_t count_pass(const TIO* rowp, int64_t c_start, int64_t valid, int mode, uint64_t lo_key,
                                uint32_t key_eq, int64_t id_bound, Shared& sh) {
-  constexpr int VEC = ChunkKeys<TIO>::VEC;
+  constexpr int VEC = Chunk<TIO>::VEC;
   uint32_t c = 0;
   for (int i = 0; i < kPerThread; ++i) {
     const int64_t id = value_id(c_start, i, VEC);
     if (id >= valid) continue;
-    const uint32_t k = ChunkKeys<TIO>::key_at(rowp + id);
+    const uint32_t k = Chunk<TIO>::key_at(rowp + id);
     if (mode == 0) c += ((uint64_t)k >= lo_key) ? 1u : 0u;
     else if (mode == 1) c += (k > key_eq) ? 1u : 0u;
     else c += (k == key_eq && id < id_bound) ? 1u : 0u;
@@ -213,25 +221,26 @@ __device__ uint32_t count_pass(const TIO* rowp, int64_t c_start, int64_t valid, 
   return block_sum(c, sh);
 }
 
-// Exact narrowing when more than kCap values reach the first threshold:
-// leaves exactly the chunk's top-K composites in sh.cand[0..K) and sets
-// sh.count = K (or the number of real values, if fewer).
+// Exact narrowing when a chunk yields more than kCap candidates: replaces the
+// new candidates (pool[nbest, ...)) by exactly the chunk's K best (or all its
+// real values if fewer) and sets sh.count to their number.
 template <typename TIO>
-__device__ __noinline__ void narrow_exact(const TIO* rowp, int64_t c_start, int64_t valid, int K, uint32_t tau,
-                                          uint32_t top_key, Shared& sh) {
-  constexpr int VEC = ChunkKeys<TIO>::VEC;
-  uint64_t lo = tau, hi = (uint64_t)top_key + 1;      // count(>= lo) >= K > count(>= hi)
-  while (hi - lo > 1) {
-    const uint64_t mid = lo + (hi - lo) / 2;
-    if (count_pass(rowp, c_start, valid, 0, mid, 0, 0, sh) >= (uint32_t)K) lo = mid; else hi = mid;
-  }
-  const uint32_t kt = (uint32_t)lo;
-  const uint32_t c_ge = count_pass(rowp, c_start, valid, 0, kt, 0, 0, sh);
-  int64_t id_bound = INT64_MAX;                       // ties at kt: only ids below this
-  if (c_ge > (uint32_t)kCap) {
+__device__ __noinline__ void narrow_exact(const TIO* rowp, int64_t c_start, int64_t valid, int K, int nbest,
+                                          Shared& sh) {
+  constexpr int VEC = Chunk<TIO>::VEC;
+  const uint32_t n_real = count_pass(rowp, c_start, valid, 0, 1, 0, 0, sh);
+  uint32_t kt = 1;                                     // take every real value when there are few
+  int64_t id_bound = INT64_MAX;
+  if (n_real > (uint32_t)K) {
+    uint64_t lo = 1, hi = Chunk<TIO>::kKeyLimit;       // count(>= lo) >= K > count(>= hi)
+    while (hi - lo > 1) {
+      const uint64_t mid = lo + (hi - lo) / 2;
+      if (count_pass(rowp, c_start, valid, 0, mid, 0, 0, sh) >= (uint32_t)K) lo = mid; else hi = mid;
+    }
+    kt = (uint32_t)lo;
     const uint32_t c_gt = count_pass(rowp, c_start, valid, 1, 0, kt, 0, sh);
-    const uint32_t need = (uint32_t)K - c_gt;
-    int64_t lo_i = c_start, hi_i = c_start + kChunk;  // count(id < lo_i) < need <= count(id < hi_i)
+    const uint32_t need = (uint32_t)K - c_gt;          // ties at kt to take, lowest ids first
+    int64_t lo_i = c_start, hi_i = c_start + kChunk;   // count(id < lo_i) < need <= count(id < hi_i)
     while (hi_i - lo_i > 1) {
       const int64_t mid = lo_i + (hi_i - lo_i) / 2;
       if (count_pass(rowp, c_start, valid, 2, 0, kt, mid, sh) >= need) hi_i = mid; else lo_i = mid;
@@ -244,133 +253,148 @@ __device__ __noinline__ void narrow_exact(const TIO* rowp, int64_t c_start, int6
   for (int i = 0; i < kPerThread; ++i) {
     const int64_t id = value_id(c_start, i, VEC);
     if (id >= valid) continue;
-    const uint32_t k = ChunkKeys<TIO>::key_at(rowp + id);
+    const uint32_t k = Chunk<TIO>::key_at(rowp + id);
     if (k > kt || (k == kt && id < id_bound)) {
       const uint32_t pos = atomicAdd(&sh.count, 1u);
-      if (pos < (uint32_t)kCap) sh.cand[pos] = composite(k, id);
+      if (pos < (uint32_t)kCap) sh.pool[nbest + pos] = composite(k, id);
     }
   }
   __syncthreads();
 }
 
-// Rank the first n LDS candidates (unique nonzero composites) and write the
-// best k in order to dst[0..k); positions without a candidate get 0.
-__device__ void rank_to_global(const Shared& sh, int n, int k, uint64_t* dst) {
-  if (n > kCap) n = kCap;                 // cannot happen (see narrow_exact); keeps LDS reads in bounds
+// Keep the K best of pool[0, n) in pool[0, min(n, K)) (sorted, best first).
+__device__ void keep_best(Shared& sh, int n, int K) {
   for (int i = threadIdx.x; i < n; i += kThreads) {
-    const uint64_t c = sh.cand[i];
+    const uint64_t c = sh.pool[i];
     int rank = 0;
-    for (int j = 0; j < n; ++j) rank += (sh.cand[j] > c) ? 1 : 0;
-    if (rank < k) dst[rank] = c;
+    for (int j = 0; j < n; ++j) rank += (sh.pool[j] > c) ? 1 : 0;
+    if (rank < K) sh.best_tmp[rank] = c;
   }
-  for (int r = n + (int)threadIdx.x; r < k; r += kThreads) dst[r] = 0;
+  __syncthreads();
+  const int m = n < K ? n : K;
+  for (int i = threadIdx.x; i < m; i += kThreads) sh.pool[i] = sh.best_tmp[i];
+  __syncthreads();
+}
+
+__device__ __forceinline__ float unary_transform(float z, float mult, float cap) {
+  float y = mult * z;
+  if (cap > 0.f) y = cap * tanhf(y / cap);
+  return (z == -INFINITY) ? -INFINITY : y;     // masked entries stay masked
 }
 
 template <typename TIO>
-__global__ __launch_bounds__(kThreads) void topk_kernel(const TIO* __restrict__ logits,
-                                                        int64_t row_stride, int64_t valid_vocab,
-                                                        int64_t n_rows, int32_t K, int32_t chunks,
-                                                        float mult, float cap,
-                                                        uint64_t* __restrict__ parts,
-                                                        uint32_t* __restrict__ counters,
-                                                        int64_t* __restrict__ ids_out,
-                                                        float* __restrict__ unary_out) {
-  constexpr int VEC = ChunkKeys<TIO>::VEC;
+__global__ __launch_bounds__(kThreads) void topk_rows_kernel(const TIO* __restrict__ logits, int64_t row_stride,
+                                                             int64_t valid_vocab, int32_t K, int32_t chunks,
+                                                             int32_t segs, int32_t chunks_per_seg, float mult,
+                                                             float cap, uint64_t* __restrict__ parts,
+                                                             int64_t* __restrict__ ids_out,
+                                                             float* __restrict__ unary_out) {
   __shared__ Shared sh;
   const int tid = threadIdx.x;
-
-  // XCD-aware placement: workgroup b runs on XCD b % 8; give each XCD a
-  // contiguous range of (row, chunk) work items so a row's chunks share an L2.
-  const int64_t total = n_rows * chunks;
-  const int64_t per_xcd = (int64_t)gridDim.x / 8;
-  const int64_t vid = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (vid >= total) return;
-  const int64_t row = vid / chunks;
-  const int chunk = (int)(vid % chunks);
-  const int64_t c_start = (int64_t)chunk * kChunk;
+  const int64_t row = blockIdx.x / segs;
+  const int seg = (int)(blockIdx.x % segs);
+  const int c_begin = seg * chunks_per_seg;
+  const int c_end = min(chunks, c_begin + chunks_per_seg);
   const TIO* rowp = logits + row * row_stride;
-
-  ChunkKeys<TIO> keys;
-  keys.load(rowp, c_start, valid_vocab, tid);
-
-  // ---- threshold from group maxima ---------------------------------------
   int groups = 1;
   while (groups < K) groups <<= 1;               // P = next power of two >= K
   const int gsize = kThreads / groups;           // threads per group (>= 8)
-  sh.tmax[tid] = keys.max_key();
-  if (tid == 0) sh.count = 0;
-  __syncthreads();
-  if (tid < groups) {
-    uint32_t g = 0;
-    for (int i = 0; i < gsize; ++i) g = max(g, sh.tmax[tid * gsize + i]);
-    sh.gmax[tid] = g;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t tau = 0xffffffffu;
-    int nonempty = 0;
-    for (int g = 0; g < groups; ++g) {
-      if (sh.gmax[g] != 0) { ++nonempty; tau = min(tau, sh.gmax[g]); }
+
+  int nbest = 0;                                 // held best composites (uniform)
+  Chunk<TIO> cur;
+  if (c_begin < c_end) cur.issue(rowp, (int64_t)c_begin * kChunk, valid_vocab, tid);
+  for (int c = c_begin; c < c_end; ++c) {
+    const int64_t c_start = (int64_t)c * kChunk;
+    Chunk<TIO> next;
+    if (c + 1 < c_end) next.issue(rowp, c_start + kChunk, valid_vocab, tid);   // prefetch
+    cur.make_keys(rowp, c_start, valid_vocab, tid);
+
+    // ---- threshold --------------------------------------------------------
+    if (nbest < K) {
+      sh.tmax[tid] = cur.max_key();
+      __syncthreads();
+      if (tid < groups) {
+        uint32_t g = 0;
+        for (int i = 0; i < gsize; ++i) g = max(g, sh.tmax[tid * gsize + i]);
+        sh.gmax[tid] = g;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t tau = 0xffffffffu;
+        int nonempty = 0;
+        for (int g = 0; g < groups; ++g)
+          if (sh.gmax[g] != 0) { ++nonempty; tau = min(tau, sh.gmax[g]); }
+        const uint64_t t = (nonempty >= K) ? (uint64_t)tau : 1u;   // too few: every real value
+        sh.tau_lo = (uint32_t)t;
+        sh.tau_hi = (uint32_t)(t >> 32);
+        sh.count = 0;
+      }
+    } else if (tid == 0) {
+      // later values have larger ids than every held one: they must beat the
+      // K-th key strictly
+      const uint64_t t = (uint64_t)composite_key(sh.pool[K - 1]) + 1;
+      sh.tau_lo = (uint32_t)t;
+      sh.tau_hi = (uint32_t)(t >> 32);
+      sh.count = 0;
     }
-    sh.tau = (nonempty >= K) ? tau : 1u;         // too few: every real value
-  }
-  __syncthreads();
-  const uint32_t tau = sh.tau;
+    __syncthreads();
+    const uint64_t tau = ((uint64_t)sh.tau_hi << 32) | sh.tau_lo;
 
-  // ---- compact the keys >= tau -------------------------------------------
-  keys.for_each_ge(tau, [&](uint32_t k, int i) {
-    const uint32_t pos = atomicAdd(&sh.count, 1u);
-    if (pos < (uint32_t)kCap) sh.cand[pos] = composite(k, value_id(c_start, i, VEC));
-  });
-  __syncthreads();
-  uint32_t n = sh.count;
-  if (n > (uint32_t)kCap) {
-    uint32_t top = 0;
-    for (int g = 0; g < groups; ++g) top = max(top, sh.gmax[g]);
-    narrow_exact<TIO>(rowp, c_start, valid_vocab, K, tau, top, sh);
-    n = sh.count;
-  }
-
-  // ---- this chunk's K best -> partials ---------------------------------
-  uint64_t* my_parts = parts + ((size_t)row * chunks + chunk) * K;
-  rank_to_global(sh, (int)n, K, my_parts);
-
-  // ---- last workgroup of the row merges ----------------------------------
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t ticket = atomicAdd(&counters[row], 1u);
-    sh.last = (ticket == (uint32_t)chunks - 1) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!sh.last) return;
-  __threadfence();
-  const int m = chunks * K;
-  const uint64_t* row_parts = parts + (size_t)row * chunks * K;
-  for (int i = tid; i < m; i += kThreads) sh.cand[i] = row_parts[i];
-  __syncthreads();
-  for (int i = tid; i < m; i += kThreads) {
-    const uint64_t c = sh.cand[i];
-    if (c == 0) continue;                       // empty slot of a short chunk
-    int rank = 0;
-    for (int j = 0; j < m; ++j) rank += (sh.cand[j] > c) ? 1 : 0;
-    if (rank < K) {
-      const uint32_t key = (uint32_t)(c >> 24);
-      const int64_t id = (int64_t)(kIdMask - (uint32_t)(c & kIdMask));
-      const float z = ChunkKeys<TIO>::value(key);
-      float y = mult * z;
-      if (cap > 0.f) y = cap * tanhf(y / cap);
-      if (z == -INFINITY) y = -INFINITY;      // masked entries stay masked
-      ids_out[row * K + rank] = id;
-      unary_out[row * K + rank] = y;
+    // ---- compact the survivors behind the held best -----------------------
+    if (tau < Chunk<TIO>::kKeyLimit) {
+      cur.for_each_ge(tau, [&](uint32_t k, int i) {
+        const uint32_t pos = atomicAdd(&sh.count, 1u);
+        if (pos < (uint32_t)kCap) sh.pool[nbest + pos] = composite(k, value_id(c_start, i, Chunk<TIO>::VEC));
+      });
     }
+    __syncthreads();
+    uint32_t n = sh.count;
+    if (n > (uint32_t)kCap) {
+      narrow_exact<TIO>(rowp, c_start, valid_vocab, K, nbest, sh);
+      n = sh.count;
+    }
+    if (n > 0) {
+      keep_best(sh, nbest + (int)n, K);
+      nbest = min(K, nbest + (int)n);
+    }
+    if (c + 1 < c_end) cur = next;
   }
-  if (tid == 0) counters[row] = 0u;           // leave the ticket cleared
+
+  // ---- output -----------------------------------------------------------
+  if (segs == 1) {
+    for (int i = tid; i < nbest; i += kThreads) {
+      const uint64_t c = sh.pool[i];
+      ids_out[row * K + i] = composite_id(c);
+      unary_out[row * K + i] = unary_transform(Chunk<TIO>::value(composite_key(c)), mult, cap);
+    }
+  } else {
+    uint64_t* dst = parts + ((size_t)row * segs + seg) * K;
+    for (int i = tid; i < K; i += kThreads) dst[i] = i < nbest ? sh.pool[i] : 0ull;
+  }
 }
 
-__global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+// Merge of the per-segment K best (rows split over several workgroups).
+template <typename TIO>
+__global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __restrict__ parts, int32_t K,
+                                                              int32_t segs, float mult, float cap,
+                                                              int64_t* __restrict__ ids_out,
+                                                              float* __restrict__ unary_out) {
+  __shared__ uint64_t cand[kCap];
+  const int64_t row = blockIdx.x;
+  const int m = segs * K;
+  const uint64_t* src = parts + (size_t)row * m;
+  for (int i = threadIdx.x; i < m; i += kThreads) cand[i] = src[i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < m; i += kThreads) {
+    const uint64_t c = cand[i];
+    if (c == 0) continue;                      // empty slot of a short segment
+    int rank = 0;
+    for (int j = 0; j < m; ++j) rank += (cand[j] > c) ? 1 : 0;
+    if (rank < K) {
+      ids_out[row * K + rank] = composite_id(c);
+      unary_out[row * K + rank] = unary_transform(Chunk<TIO>::value(composite_key(c)), mult, cap);
+    }
+  }
 }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -384,38 +408,43 @@ TopkPlan plan_topk(int64_t n_rows, int64_t valid_vocab, int32_t top_k) {
   p.top_k = top_k;
   p.chunks = (int32_t)((valid_vocab + kChunk - 1) / kChunk);
   if (p.chunks < 1) p.chunks = 1;
+  // One workgroup per row once rows cover the chip; otherwise split rows so
+  // that about 512 workgroups stream, and merge the segments afterwards.
+  int segs = 1;
+  if (n_rows > 0 && n_rows < 256) {
+    segs = (int)((512 + n_rows - 1) / n_rows);
+    if (segs > p.chunks) segs = p.chunks;
+    if (segs * top_k > kCap) segs = kCap / top_k;
+    if (segs < 1) segs = 1;
+  }
+  p.segs = segs;
+  p.chunks_per_seg = (p.chunks + segs - 1) / segs;
+  p.segs = (p.chunks + p.chunks_per_seg - 1) / p.chunks_per_seg;   // no empty segments
   p.parts_offset = 0;
-  p.counters_offset = align256((size_t)n_rows * p.chunks * top_k * sizeof(uint64_t));
-  p.bytes = p.counters_offset + align256((size_t)n_rows * sizeof(uint32_t));
-  if (n_rows == 0) p.bytes = 0;
+  p.bytes = (p.segs > 1 && n_rows > 0) ? align256((size_t)n_rows * p.segs * top_k * sizeof(uint64_t)) : 0;
   return p;
-}
-
-hipError_t launch_topk_zero(const TopkArgs& a, const TopkPlan& p, hipStream_t stream) {
-  if (p.n_rows == 0) return hipSuccess;
-  uint32_t* counters = reinterpret_cast<uint32_t*>(static_cast<char*>(a.workspace) + p.counters_offset);
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((p.n_rows + 255) / 256)), dim3(256), 0, stream,
-                     counters, p.n_rows);
-  return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkArgs& a, const TopkPlan& p, hipStream_t stream) {
   if (p.n_rows == 0) return hipSuccess;
-  char* ws = static_cast<char*>(a.workspace);
-  uint64_t* parts = reinterpret_cast<uint64_t*>(ws + p.parts_offset);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(ws + p.counters_offset);
-  const int64_t work = p.n_rows * p.chunks;
-  const int64_t grid = (work + 7) / 8 * 8;     // whole rounds over the 8 XCDs
+  uint64_t* parts = reinterpret_cast<uint64_t*>(static_cast<char*>(a.workspace) + p.parts_offset);
+  const dim3 grid((unsigned)(p.n_rows * p.segs));
   if (a.dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(topk_kernel<uint16_t>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(a.logits), a.row_stride, a.valid_vocab, p.n_rows,
-                       a.top_k, p.chunks, a.multiplier, a.softcap, parts, counters, a.ids_out,
-                       a.unary_out);
+    hipLaunchKernelGGL(topk_rows_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(a.logits), a.row_stride, a.valid_vocab, a.top_k, p.chunks,
+                       p.segs, p.chunks_per_seg, a.multiplier, a.softcap, parts, a.ids_out, a.unary_out);
   else
-    hipLaunchKernelGGL(topk_kernel<float>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                       static_cast<const float*>(a.logits), a.row_stride, a.valid_vocab, p.n_rows,
-                       a.top_k, p.chunks, a.multiplier, a.softcap, parts, counters, a.ids_out,
-                       a.unary_out);
+    hipLaunchKernelGGL(topk_rows_kernel<float>, grid, dim3(kThreads), 0, stream,
+                       static_cast<const float*>(a.logits), a.row_stride, a.valid_vocab, a.top_k, p.chunks,
+                       p.segs, p.chunks_per_seg, a.multiplier, a.softcap, parts, a.ids_out, a.unary_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.segs == 1) return e;
+  if (a.dtype == DFLASH_BF16)
+    hipLaunchKernelGGL(topk_merge_kernel<uint16_t>, dim3((unsigned)p.n_rows), dim3(kThreads), 0, stream, parts,
+                       a.top_k, p.segs, a.multiplier, a.softcap, a.ids_out, a.unary_out);
+  else
+    hipLaunchKernelGGL(topk_merge_kernel<float>, dim3((unsigned)p.n_rows), dim3(kThreads), 0, stream, parts,
+                       a.top_k, p.segs, a.multiplier, a.softcap, a.ids_out, a.unary_out);
   return hipGetLastError();
 }
 

@@ -119,9 +119,10 @@ def test_conv_validation():
 
 def test_topk_validation():
     L = D.lib()
-    ws = L.dflash_topk_workspace_size(480, 151936, 8)
+    assert L.dflash_topk_workspace_size(480, 151936, 8) == 0      # one workgroup per row: no partials
+    ws = L.dflash_topk_workspace_size(100, 151936, 8)              # rows split over workgroups
     assert ws > 0
-    args = lambda **k: dict(dict(logits=FAKE, stride=151936, rows=480, vocab=151936, valid=151936, k=8, m=1.0,
+    args = lambda **k: dict(dict(logits=FAKE, stride=151936, rows=100, vocab=151936, valid=151936, k=8, m=1.0,
                                  cap=30.0, dtype=1, ids=FAKE, unary=FAKE, ws=FAKE, wsb=ws), **k)
 
     def call(a):
