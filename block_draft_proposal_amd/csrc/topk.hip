@@ -15,32 +15,38 @@
 //    real value), and every (key, id) pair a 56-bit composite
 //    key << 24 | (2^24 - 1 - id) whose order is exactly (value desc, id asc)
 //    and which is unique within a row.
-//  * One 256-thread workgroup owns a row (or, when rows are too few to fill
-//    the chip, a segment of a row; a small second kernel then merges the
-//    segments).  It streams the row in chunks of 16384 values, 64 per thread
-//    as eight 16-byte loads, so each wave load is one contiguous 1 KiB; the
-//    next chunk's loads are issued before the current chunk is processed.
-//    bf16 keys are built and kept two per register with packed 16-bit ops.
-//  * The running K best composites live in LDS.  For the first chunk the
-//    threshold is the minimum over P >= K thread groups of the group maxima
-//    (at least K distinct values reach it); once K are held, a later value
-//    must beat the K-th key strictly (its id is larger than every held id).
-//    A packed saturating subtract tests two keys per instruction; the few
-//    survivors are compacted into LDS and ranked exactly by counting.
+//  * A workgroup of 8 waves owns a row (or, when rows are too few to fill the
+//    chip, a segment of one; a small second kernel then merges segments).
+//    The row is cut into wave-chunks of 4096 values, dealt round-robin to the
+//    8 waves; every wave streams its chunks on its own -- 64 values per lane
+//    as eight 16-byte loads, each wave load one contiguous 1 KiB, the next
+//    chunk's loads issued before the current chunk is processed -- and keeps
+//    its own K best in LDS.  No workgroup barrier until the final merge.
+//  * bf16 keys are built and tested two per register with packed 16-bit ops.
+//  * Threshold: on a wave's first chunk, the K-th largest of the 64 lane maxima
+//    (at least K distinct values reach it); once a wave holds K values, a later
+//    value of that wave must beat its K-th key strictly (its id is larger than
+//    every id the wave holds).  The few survivors are compacted into LDS and
+//    ranked exactly by counting.
 //  * If a chunk yields more survivors than LDS holds (mass ties), an exact
 //    bisection on the key, then on the id among the tied key, narrows the
 //    chunk to exactly its K best; that path re-reads the chunk from cache.
+//  * The 8 sorted per-wave lists are merged with one barrier: each entry's
+//    rank is its own index plus, per other list, a binary-searched count of
+//    larger entries.
 #include "dflash.h"
 #include "dflash_internal.h"
 
 namespace dflash {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kPerThread = 64;
-constexpr int kChunk = kThreads * kPerThread;   // values per chunk
-constexpr int kCap = kTopkMergeCap;             // LDS slots for new candidates
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kPerLane = 64;                   // values per lane per wave-chunk
+constexpr int kWaveChunk = 64 * kPerLane;      // 4096 values
+constexpr int kWaveCap = 256;                  // LDS slots for one chunk's new candidates
 constexpr int kMaxK = DFLASH_MAX_TOP_K;
+constexpr int kMergeThreads = 256;
 constexpr uint32_t kIdMask = 0xffffffu;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -78,30 +84,65 @@ __device__ __forceinline__ float f32_key_value(uint32_t k) {
   return __uint_as_float(b);
 }
 
-// One thread's 64 values of a chunk.  Value i (0..63) sits at
-// id = c_start + ((i / VEC) * 256 + tid) * VEC + i % VEC.
+// Within a wave: make LDS writes of all lanes visible to all lanes.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One lane's 64 values of a wave-chunk.  Value i (0..63) sits at
+// id = c_start + ((i / VEC) * 64 + lane) * VEC + i % VEC.
 template <typename TIO> struct Chunk;
 
 template <> struct Chunk<uint16_t> {
-  static constexpr int VEC = 8, L = kPerThread / VEC, W = kPerThread / 2;
-  uint4 raw[L];      // loaded bits
-  uint32_t w[W];     // packed keys: word j = values 2j (low half), 2j+1 (high half)
+  static constexpr int VEC = 8, L = kPerLane / VEC, W = kPerLane / 2;
+  uint32_t w[W];     // raw bits after issue(), packed keys after make_keys()
 
-  __device__ void issue(const uint16_t* rowp, int64_t c_start, int64_t valid, int tid) {
+  // `full` (wave-uniform): the whole wave-chunk lies below the logical vocab
+  // end, so every load is unconditional and the key conversion branch-free
+  // (keeps the wait for this chunk's loads from draining the prefetch).
+  __device__ void issue(const uint16_t* rowp, int64_t c_start, int64_t valid, int lane, bool full) {
+    if (full) {
+      const uint4* p = reinterpret_cast<const uint4*>(rowp + c_start) + lane;
 #pragma unroll
-    for (int l = 0; l < L; ++l) {
-      const int64_t e0 = c_start + ((int64_t)l * kThreads + tid) * VEC;
-      raw[l] = (e0 + VEC <= valid) ? *reinterpret_cast<const uint4*>(rowp + e0) : make_uint4(0u, 0u, 0u, 0u);
+      for (int l = 0; l < L; ++l) {
+        const uint4 r = p[l * 64];
+        w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
+      }
+    } else {
+#pragma unroll
+      for (int l = 0; l < L; ++l) {
+        const int64_t e0 = c_start + ((int64_t)l * 64 + lane) * VEC;
+        const uint4 r = (e0 + VEC <= valid) ? *reinterpret_cast<const uint4*>(rowp + e0) : make_uint4(0u, 0u, 0u, 0u);
+        w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
+      }
     }
   }
-  __device__ void make_keys(const uint16_t* rowp, int64_t c_start, int64_t valid, int tid) {
+  __device__ void issue_full(const uint16_t* rowp, int64_t c_start, int lane) {
+    const uint4* p = reinterpret_cast<const uint4*>(rowp + c_start) + lane;
 #pragma unroll
     for (int l = 0; l < L; ++l) {
-      const int64_t e0 = c_start + ((int64_t)l * kThreads + tid) * VEC;
-      const uint32_t r4[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
+      const uint4 r = p[l * 64];
+      w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
+    }
+  }
+  __device__ void keys_full() {
+#pragma unroll
+    for (int j = 0; j < W; ++j) w[j] = bf16_key2(w[j]);
+  }
+  __device__ void make_keys(const uint16_t* rowp, int64_t c_start, int64_t valid, int lane, bool full) {
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < W; ++j) w[j] = bf16_key2(w[j]);
+      return;
+    }
+#pragma unroll
+    for (int l = 0; l < L; ++l) {
+      const int64_t e0 = c_start + ((int64_t)l * 64 + lane) * VEC;
       if (e0 + VEC <= valid) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[l * 4 + q] = bf16_key2(r4[q]);
+        for (int q = 0; q < 4; ++q) w[l * 4 + q] = bf16_key2(w[l * 4 + q]);
       } else {   // the one vector that straddles the logical end, or beyond it
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -119,7 +160,7 @@ template <> struct Chunk<uint16_t> {
     for (int j = 1; j < W; ++j) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[j]));
     return max((uint32_t)m.x, (uint32_t)m.y);
   }
-  // Calls f(key, value index) for every key >= tau (1 <= tau <= 0x10000).
+  // Calls f(key, value index) for every key >= tau (1 <= tau < 0x10000).
   template <class F> __device__ void for_each_ge(uint64_t tau, F&& f) const {
     const unsigned short t1 = (unsigned short)(tau - 1);
     const u16x2 t = {t1, t1};
@@ -132,148 +173,183 @@ template <> struct Chunk<uint16_t> {
       }
     }
   }
+  // On raw bits (before make_keys): calls f(key, value index) for every
+  // positive value whose bits, read as int16, are >= r (1 <= r <= 0x7fff).
+  // A positive value's key is bits | 0x8000, so this selects key >= r + 0x8000;
+  // negative values (int16 < 0) never pass.  One packed signed max tests two
+  // values.
+  static constexpr bool kHasRawFilter = true;
+  template <class F> __device__ void for_each_raw_ge(uint32_t r, F&& f) const {
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    const short r1 = (short)(r - 1);
+    const s16x2 t = {r1, r1};
+    const uint32_t t32 = __builtin_bit_cast(uint32_t, t);
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      const s16x2 x = __builtin_bit_cast(s16x2, w[j]);
+      const s16x2 m = __builtin_elementwise_max(x, t);
+      if (__builtin_bit_cast(uint32_t, m) != t32) {
+        if (x.x > r1) f((w[j] & 0xffffu) | 0x8000u, 2 * j);
+        if (x.y > r1) f((w[j] >> 16) | 0x8000u, 2 * j + 1);
+      }
+    }
+  }
   static constexpr uint64_t kKeyLimit = 0x10000u;   // keys are < this
   __device__ static uint32_t key_at(const uint16_t* p) { return bf16_key(*p); }
   __device__ static float value(uint32_t k) { return bf16_key_value(k); }
 };
 
 template <> struct Chunk<float> {
-  static constexpr int VEC = 4, L = kPerThread / VEC;
-  uint4 raw[L];
-  uint32_t w[kPerThread];
+  static constexpr int VEC = 4, L = kPerLane / VEC;
+  uint32_t w[kPerLane];
 
-  __device__ void issue(const float* rowp, int64_t c_start, int64_t valid, int tid) {
+  __device__ void issue(const float* rowp, int64_t c_start, int64_t valid, int lane, bool full) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
-      const int64_t e0 = c_start + ((int64_t)l * kThreads + tid) * VEC;
-      raw[l] = (e0 + VEC <= valid) ? *reinterpret_cast<const uint4*>(rowp + e0) : make_uint4(0u, 0u, 0u, 0u);
+      const int64_t e0 = c_start + ((int64_t)l * 64 + lane) * VEC;
+      const uint4 r = (full || e0 + VEC <= valid) ? *reinterpret_cast<const uint4*>(rowp + e0)
+                                                  : make_uint4(0u, 0u, 0u, 0u);
+      w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
     }
   }
-  __device__ void make_keys(const float* rowp, int64_t c_start, int64_t valid, int tid) {
+  __device__ void issue_full(const float* rowp, int64_t c_start, int lane) {
+    const uint4* p = reinterpret_cast<const uint4*>(rowp + c_start) + lane;
 #pragma unroll
     for (int l = 0; l < L; ++l) {
-      const int64_t e0 = c_start + ((int64_t)l * kThreads + tid) * VEC;
-      const uint32_t r4[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
+      const uint4 r = p[l * 64];
+      w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
+    }
+  }
+  __device__ void keys_full() {
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) w[j] = f32_key(w[j]);
+  }
+  __device__ void make_keys(const float* rowp, int64_t c_start, int64_t valid, int lane, bool full) {
+#pragma unroll
+    for (int l = 0; l < L; ++l) {
+      const int64_t e0 = c_start + ((int64_t)l * 64 + lane) * VEC;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        w[l * 4 + q] = (e0 + VEC <= valid) ? f32_key(r4[q])
+        w[l * 4 + q] = (full || e0 + VEC <= valid) ? f32_key(w[l * 4 + q])
                        : (e0 + q < valid) ? f32_key(__float_as_uint(rowp[e0 + q])) : 0u;
     }
   }
   __device__ uint32_t max_key() const {
     uint32_t m = 0;
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) m = max(m, w[j]);
+    for (int j = 0; j < kPerLane; ++j) m = max(m, w[j]);
     return m;
   }
   template <class F> __device__ void for_each_ge(uint64_t tau, F&& f) const {
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j)
+    for (int j = 0; j < kPerLane; ++j)
       if ((uint64_t)w[j] >= tau) f(w[j], j);
   }
+  static constexpr bool kHasRawFilter = false;
+  template <class F> __device__ void for_each_raw_ge(uint32_t, F&&) const {}
   static constexpr uint64_t kKeyLimit = 0x100000000ull;
   __device__ static uint32_t key_at(const float* p) { return f32_key(__float_as_uint(*p)); }
   __device__ static float value(uint32_t k) { return f32_key_value(k); }
 };
 
-struct Shared {
-  uint64_t pool[kMaxK + kCap];   // [0, nbest): held best; then new candidates
-  uint64_t best_tmp[kMaxK];
-  uint32_t tmax[kThreads];
-  uint32_t gmax[64];
-  uint32_t red[kThreads / 64];
-  uint32_t count;                // new candidates appended this chunk
-  uint32_t tau_lo, tau_hi;       // threshold (64-bit, split)
+struct WaveLds {
+  uint64_t pool[kMaxK + kWaveCap];   // [0, nbest): held best (sorted); then new candidates
+  uint64_t tmp[kMaxK];
+  uint32_t count;
+  uint32_t nbest;
 };
 
-__device__ __forceinline__ int64_t value_id(int64_t c_start, int i, int vec) {
-  return c_start + ((int64_t)(i / vec) * kThreads + threadIdx.x) * vec + (i % vec);
+struct Shared {
+  WaveLds wave[kWaves];
+};
+
+__device__ __forceinline__ int64_t value_id(int64_t c_start, int i, int vec, int lane) {
+  return c_start + ((int64_t)(i / vec) * 64 + lane) * vec + (i % vec);
 }
 
-// Workgroup-wide sum of one value per thread (all threads must call).
-__device__ uint32_t block_sum(uint32_t v, Shared& sh) {
-  v = wave_sum_u32(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < kThreads / 64; ++i) s += sh.red[i];
-  return s;
-}
-
-// Counts, over this thread's chunk values re-read from memory, those with
+// Counts, over this lane's chunk values re-read from memory, those with
 // key >= lo_key (mode 0), key > key_eq (mode 1), or key == key_eq and
-// id < id_bound (mode 2); then sums over the workgroup.
+// id < id_bound (mode 2); then sums over the wave.
 template <typename TIO>
-__device__ uint32_t count_pass(const TIO* rowp, int64_t c_start, int64_t valid, int mode, uint64_t lo_key,
-                               uint32_t key_eq, int64_t id_bound, Shared& sh) {
+__device__ uint32_t count_pass(const TIO* rowp, int64_t c_start, int64_t valid, int lane, int mode,
+                               uint64_t lo_key, uint32_t key_eq, int64_t id_bound) {
   constexpr int VEC = Chunk<TIO>::VEC;
   uint32_t c = 0;
-  for (int i = 0; i < kPerThread; ++i) {
-    const int64_t id = value_id(c_start, i, VEC);
+  for (int i = 0; i < kPerLane; ++i) {
+    const int64_t id = value_id(c_start, i, VEC, lane);
     if (id >= valid) continue;
     const uint32_t k = Chunk<TIO>::key_at(rowp + id);
     if (mode == 0) c += ((uint64_t)k >= lo_key) ? 1u : 0u;
     else if (mode == 1) c += (k > key_eq) ? 1u : 0u;
     else c += (k == key_eq && id < id_bound) ? 1u : 0u;
   }
-  return block_sum(c, sh);
+  return wave_sum_u32(c);
 }
 
-// Exact narrowing when a chunk yields more than kCap candidates: replaces the
-// new candidates (pool[nbest, ...)) by exactly the chunk's K best (or all its
-// real values if fewer) and sets sh.count to their number.
+// Exact narrowing when a wave-chunk yields more than kWaveCap candidates:
+// replaces the new candidates (pool[nbest, ...)) by exactly the chunk's K
+// best (or all its real values if fewer); returns their number.
 template <typename TIO>
-__device__ __noinline__ void narrow_exact(const TIO* rowp, int64_t c_start, int64_t valid, int K, int nbest,
-                                          Shared& sh) {
+__device__ __noinline__ uint32_t narrow_exact(const TIO* rowp, int64_t c_start, int64_t valid, int lane, int K,
+                                              int nbest, WaveLds& wl) {
   constexpr int VEC = Chunk<TIO>::VEC;
-  const uint32_t n_real = count_pass(rowp, c_start, valid, 0, 1, 0, 0, sh);
+  const uint32_t n_real = count_pass(rowp, c_start, valid, lane, 0, 1, 0, 0);
   uint32_t kt = 1;                                     // take every real value when there are few
   int64_t id_bound = INT64_MAX;
   if (n_real > (uint32_t)K) {
     uint64_t lo = 1, hi = Chunk<TIO>::kKeyLimit;       // count(>= lo) >= K > count(>= hi)
     while (hi - lo > 1) {
       const uint64_t mid = lo + (hi - lo) / 2;
-      if (count_pass(rowp, c_start, valid, 0, mid, 0, 0, sh) >= (uint32_t)K) lo = mid; else hi = mid;
+      if (count_pass(rowp, c_start, valid, lane, 0, mid, 0, 0) >= (uint32_t)K) lo = mid; else hi = mid;
     }
     kt = (uint32_t)lo;
-    const uint32_t c_gt = count_pass(rowp, c_start, valid, 1, 0, kt, 0, sh);
+    const uint32_t c_gt = count_pass(rowp, c_start, valid, lane, 1, 0, kt, 0);
     const uint32_t need = (uint32_t)K - c_gt;          // ties at kt to take, lowest ids first
-    int64_t lo_i = c_start, hi_i = c_start + kChunk;   // count(id < lo_i) < need <= count(id < hi_i)
+    int64_t lo_i = c_start, hi_i = c_start + kWaveChunk;  // count(id < lo_i) < need <= count(id < hi_i)
     while (hi_i - lo_i > 1) {
       const int64_t mid = lo_i + (hi_i - lo_i) / 2;
-      if (count_pass(rowp, c_start, valid, 2, 0, kt, mid, sh) >= need) hi_i = mid; else lo_i = mid;
+      if (count_pass(rowp, c_start, valid, lane, 2, 0, kt, mid) >= need) hi_i = mid; else lo_i = mid;
     }
     id_bound = hi_i;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) sh.count = 0;
-  __syncthreads();
-  for (int i = 0; i < kPerThread; ++i) {
-    const int64_t id = value_id(c_start, i, VEC);
+  wave_sync();
+  if (lane == 0) wl.count = 0;
+  wave_sync();
+  for (int i = 0; i < kPerLane; ++i) {
+    const int64_t id = value_id(c_start, i, VEC, lane);
     if (id >= valid) continue;
     const uint32_t k = Chunk<TIO>::key_at(rowp + id);
     if (k > kt || (k == kt && id < id_bound)) {
-      const uint32_t pos = atomicAdd(&sh.count, 1u);
-      if (pos < (uint32_t)kCap) sh.pool[nbest + pos] = composite(k, id);
+      const uint32_t pos = atomicAdd(&wl.count, 1u);
+      if (pos < (uint32_t)kWaveCap) wl.pool[nbest + pos] = composite(k, id);
     }
   }
-  __syncthreads();
+  wave_sync();
+  return __builtin_amdgcn_readfirstlane(wl.count);
 }
 
 // Keep the K best of pool[0, n) in pool[0, min(n, K)) (sorted, best first).
-__device__ void keep_best(Shared& sh, int n, int K) {
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    const uint64_t c = sh.pool[i];
+__device__ void keep_best(WaveLds& wl, int n, int K, int lane) {
+  for (int i = lane; i < n; i += 64) {
+    const uint64_t c = wl.pool[i];
     int rank = 0;
-    for (int j = 0; j < n; ++j) rank += (sh.pool[j] > c) ? 1 : 0;
-    if (rank < K) sh.best_tmp[rank] = c;
+    for (int j = 0; j < n; ++j) rank += (wl.pool[j] > c) ? 1 : 0;
+    if (rank < K) wl.tmp[rank] = c;
   }
-  __syncthreads();
+  wave_sync();
   const int m = n < K ? n : K;
-  for (int i = threadIdx.x; i < m; i += kThreads) sh.pool[i] = sh.best_tmp[i];
-  __syncthreads();
+  for (int i = lane; i < m; i += 64) wl.pool[i] = wl.tmp[i];
+  wave_sync();
+}
+
+// Number of entries of the sorted (descending) list l[0, n) greater than c.
+__device__ __forceinline__ int count_greater(const uint64_t* l, int n, uint64_t c) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (l[mid] > c) lo = mid + 1; else hi = mid;
+  }
+  return lo;
 }
 
 __device__ __forceinline__ float unary_transform(float z, float mult, float cap) {
@@ -283,109 +359,177 @@ __device__ __forceinline__ float unary_transform(float z, float mult, float cap)
 }
 
 template <typename TIO>
-__global__ __launch_bounds__(kThreads) void topk_rows_kernel(const TIO* __restrict__ logits, int64_t row_stride,
-                                                             int64_t valid_vocab, int32_t K, int32_t chunks,
-                                                             int32_t segs, int32_t chunks_per_seg, float mult,
-                                                             float cap, uint64_t* __restrict__ parts,
-                                                             int64_t* __restrict__ ids_out,
-                                                             float* __restrict__ unary_out) {
+__device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, int64_t row_stride,
+                                               int64_t valid_vocab, int32_t K, int32_t wchunks, int32_t segs,
+                                               int32_t wchunks_per_seg, float mult, float cap,
+                                               uint64_t* __restrict__ parts, int64_t* __restrict__ ids_out,
+                                               float* __restrict__ unary_out) {
   __shared__ Shared sh;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  // wave index through readfirstlane: provably uniform, so chunk bounds and
+  // tests below are scalar and the loads need no exec masking
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  WaveLds& wl = sh.wave[wave];
   const int64_t row = blockIdx.x / segs;
   const int seg = (int)(blockIdx.x % segs);
-  const int c_begin = seg * chunks_per_seg;
-  const int c_end = min(chunks, c_begin + chunks_per_seg);
+  const int c_begin = seg * wchunks_per_seg;
+  const int c_end = min(wchunks, c_begin + wchunks_per_seg);
   const TIO* rowp = logits + row * row_stride;
-  int groups = 1;
-  while (groups < K) groups <<= 1;               // P = next power of two >= K
-  const int gsize = kThreads / groups;           // threads per group (>= 8)
 
-  int nbest = 0;                                 // held best composites (uniform)
-  Chunk<TIO> cur;
-  if (c_begin < c_end) cur.issue(rowp, (int64_t)c_begin * kChunk, valid_vocab, tid);
-  for (int c = c_begin; c < c_end; ++c) {
-    const int64_t c_start = (int64_t)c * kChunk;
-    Chunk<TIO> next;
-    if (c + 1 < c_end) next.issue(rowp, c_start + kChunk, valid_vocab, tid);   // prefetch
-    cur.make_keys(rowp, c_start, valid_vocab, tid);
+  int nbest = 0;                                 // held best composites (wave-uniform)
 
-    // ---- threshold --------------------------------------------------------
-    if (nbest < K) {
-      sh.tmax[tid] = cur.max_key();
-      __syncthreads();
-      if (tid < groups) {
-        uint32_t g = 0;
-        for (int i = 0; i < gsize; ++i) g = max(g, sh.tmax[tid * gsize + i]);
-        sh.gmax[tid] = g;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t tau = 0xffffffffu;
-        int nonempty = 0;
-        for (int g = 0; g < groups; ++g)
-          if (sh.gmax[g] != 0) { ++nonempty; tau = min(tau, sh.gmax[g]); }
-        const uint64_t t = (nonempty >= K) ? (uint64_t)tau : 1u;   // too few: every real value
-        sh.tau_lo = (uint32_t)t;
-        sh.tau_hi = (uint32_t)(t >> 32);
-        sh.count = 0;
-      }
-    } else if (tid == 0) {
-      // later values have larger ids than every held one: they must beat the
-      // K-th key strictly
-      const uint64_t t = (uint64_t)composite_key(sh.pool[K - 1]) + 1;
-      sh.tau_lo = (uint32_t)t;
-      sh.tau_hi = (uint32_t)(t >> 32);
-      sh.count = 0;
-    }
-    __syncthreads();
-    const uint64_t tau = ((uint64_t)sh.tau_hi << 32) | sh.tau_lo;
-
-    // ---- compact the survivors behind the held best -----------------------
-    if (tau < Chunk<TIO>::kKeyLimit) {
-      cur.for_each_ge(tau, [&](uint32_t k, int i) {
-        const uint32_t pos = atomicAdd(&sh.count, 1u);
-        if (pos < (uint32_t)kCap) sh.pool[nbest + pos] = composite(k, value_id(c_start, i, Chunk<TIO>::VEC));
-      });
-    }
-    __syncthreads();
-    uint32_t n = sh.count;
-    if (n > (uint32_t)kCap) {
-      narrow_exact<TIO>(rowp, c_start, valid_vocab, K, nbest, sh);
-      n = sh.count;
-    }
+  constexpr int VEC = Chunk<TIO>::VEC;
+  // Appends a survivor (key, value index i of chunk c_start) behind the held best.
+  auto push = [&](uint32_t k, int i, uint32_t id_base) {
+    const uint32_t pos = atomicAdd(&wl.count, 1u);
+    // ids < 2^24: a 32-bit lane base plus the value's compile-time offset
+    const uint32_t id = id_base + (uint32_t)((i / VEC) * 64 * VEC + i % VEC);
+    if (pos < (uint32_t)kWaveCap) wl.pool[nbest + pos] = ((uint64_t)k << 24) | (uint64_t)(kIdMask - id);
+  };
+  // After the survivors of one chunk are in the pool: exact narrowing if they
+  // overflowed, then keep the wave's K best.
+  auto update = [&](int64_t c_start) {
+    wave_sync();
+    uint32_t n = __builtin_amdgcn_readfirstlane(wl.count);
+    if (n > (uint32_t)kWaveCap) n = narrow_exact<TIO>(rowp, c_start, valid_vocab, lane, K, nbest, wl);
     if (n > 0) {
-      keep_best(sh, nbest + (int)n, K);
+      keep_best(wl, nbest + (int)n, K, lane);
       nbest = min(K, nbest + (int)n);
     }
-    if (c + 1 < c_end) cur = next;
-  }
-
-  // ---- output -----------------------------------------------------------
-  if (segs == 1) {
-    for (int i = tid; i < nbest; i += kThreads) {
-      const uint64_t c = sh.pool[i];
-      ids_out[row * K + i] = composite_id(c);
-      unary_out[row * K + i] = unary_transform(Chunk<TIO>::value(composite_key(c)), mult, cap);
+  };
+  // General path: `ch` holds keys.  Threshold, compaction, update.
+  auto process_keys = [&](const Chunk<TIO>& ch, int64_t c_start) {
+    uint64_t tau;
+    if (nbest < K) {
+      // K-th largest lane maximum (ties by lane): at least K values reach it
+      const uint32_t m = ch.max_key();
+      int rank = 0;
+      for (int o = 0; o < 64; ++o) {
+        const uint32_t v = (uint32_t)__shfl((int)m, o, 64);
+        rank += (v > m || (v == m && o < lane)) ? 1 : 0;
+      }
+      const int nonzero = __popcll(__ballot(m != 0));
+      const unsigned long long at = __ballot(rank == K - 1);
+      tau = (nonzero >= K) ? (uint64_t)(uint32_t)__shfl((int)m, __ffsll((long long)at) - 1, 64) : 1u;
+    } else {
+      // a later value has a larger id than every held one: it must beat the
+      // K-th key strictly
+      tau = (uint64_t)composite_key(wl.pool[K - 1]) + 1;
     }
-  } else {
-    uint64_t* dst = parts + ((size_t)row * segs + seg) * K;
-    for (int i = tid; i < K; i += kThreads) dst[i] = i < nbest ? sh.pool[i] : 0ull;
+    if (lane == 0) wl.count = 0;
+    wave_sync();
+    const uint32_t id_base = (uint32_t)c_start + (uint32_t)lane * VEC;
+    if (tau < Chunk<TIO>::kKeyLimit) ch.for_each_ge(tau, [&](uint32_t k, int i) { push(k, i, id_base); });
+    update(c_start);
+  };
+  // One full chunk whose raw bits are in `ch`.
+  auto process_full = [&](Chunk<TIO>& ch, int64_t c_start) {
+    if (Chunk<TIO>::kHasRawFilter && nbest == K) {
+      const uint32_t tau = composite_key(wl.pool[K - 1]) + 1;   // strict, as above
+      if (tau > 0x8000u && tau < 0x10000u) {                     // a positive threshold
+        if (lane == 0) wl.count = 0;
+        wave_sync();
+        const uint32_t id_base = (uint32_t)c_start + (uint32_t)lane * VEC;
+        ch.for_each_raw_ge(tau - 0x8000u, [&](uint32_t k, int i) { push(k, i, id_base); });
+        update(c_start);
+        return;
+      }
+    }
+    ch.keys_full();
+    process_keys(ch, c_start);
+  };
+
+  // Wave-chunks below n_full lie entirely inside the logical vocabulary; at
+  // most the row's last chunk is partial.  The loop over full chunks always
+  // issues the next chunk's loads (the last iteration re-reads its own chunk,
+  // a cache hit), so the wait for the current chunk is an exact in-order
+  // count and the next chunk's loads stay in flight while this one is
+  // processed.
+  const int n_full = (int)(valid_vocab / kWaveChunk);
+  const int full_end = min(c_end, n_full);
+  int c = c_begin + wave;
+  if (c < full_end) {
+    Chunk<TIO> cur;
+    cur.issue_full(rowp, (int64_t)c * kWaveChunk, lane);
+    for (; c < full_end; c += kWaves) {
+      const int64_t c_start = (int64_t)c * kWaveChunk;
+      const int c_next = (c + kWaves < full_end) ? c + kWaves : c;
+      Chunk<TIO> next;
+      next.issue_full(rowp, (int64_t)c_next * kWaveChunk, lane);
+      process_full(cur, c_start);
+      cur = next;
+    }
   }
+  if (c < c_end) {                               // the partial last chunk of the row
+    Chunk<TIO> tail;
+    const int64_t c_start = (int64_t)c * kWaveChunk;
+    tail.issue(rowp, c_start, valid_vocab, lane, false);
+    tail.make_keys(rowp, c_start, valid_vocab, lane, false);
+    process_keys(tail, c_start);
+  }
+  if (lane == 0) wl.nbest = (uint32_t)nbest;
+  __syncthreads();
+
+  // ---- merge the 8 sorted wave lists --------------------------------------
+  if (threadIdx.x < kWaves * K) {
+    const int w = threadIdx.x / K, i = threadIdx.x % K;
+    const int nw = (int)sh.wave[w].nbest;
+    if (i < nw) {
+      const uint64_t cval = sh.wave[w].pool[i];
+      int rank = i;
+      for (int o = 0; o < kWaves; ++o)
+        if (o != w) rank += count_greater(sh.wave[o].pool, (int)sh.wave[o].nbest, cval);
+      if (rank < K) {
+        if (segs == 1) {
+          ids_out[row * K + rank] = composite_id(cval);
+          unary_out[row * K + rank] = unary_transform(Chunk<TIO>::value(composite_key(cval)), mult, cap);
+        } else {
+          parts[((size_t)row * segs + seg) * K + rank] = cval;
+        }
+      }
+    }
+  }
+  if (segs > 1) {
+    // a segment with fewer than K real values leaves empty slots
+    int total = 0;
+    for (int w = 0; w < kWaves; ++w) total += (int)sh.wave[w].nbest;
+    for (int i = total + (int)threadIdx.x; i < K; i += kThreads) parts[((size_t)row * segs + seg) * K + i] = 0ull;
+  }
+}
+
+// bf16: at most 128 VGPRs so that 4 waves share each SIMD.
+__global__ __launch_bounds__(kThreads, 4) void topk_rows_bf16(const uint16_t* __restrict__ logits, int64_t row_stride,
+                                                            int64_t valid_vocab, int32_t K, int32_t wchunks,
+                                                            int32_t segs, int32_t wchunks_per_seg, float mult,
+                                                            float cap, uint64_t* __restrict__ parts,
+                                                            int64_t* __restrict__ ids_out,
+                                                            float* __restrict__ unary_out) {
+  topk_rows_body<uint16_t>(logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap, parts,
+                           ids_out, unary_out);
+}
+__global__ __launch_bounds__(kThreads) void topk_rows_f32(const float* __restrict__ logits, int64_t row_stride,
+                                                          int64_t valid_vocab, int32_t K, int32_t wchunks,
+                                                          int32_t segs, int32_t wchunks_per_seg, float mult,
+                                                          float cap, uint64_t* __restrict__ parts,
+                                                          int64_t* __restrict__ ids_out,
+                                                          float* __restrict__ unary_out) {
+  topk_rows_body<float>(logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap, parts,
+                        ids_out, unary_out);
 }
 
 // Merge of the per-segment K best (rows split over several workgroups).
 template <typename TIO>
-__global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __restrict__ parts, int32_t K,
-                                                              int32_t segs, float mult, float cap,
-                                                              int64_t* __restrict__ ids_out,
-                                                              float* __restrict__ unary_out) {
-  __shared__ uint64_t cand[kCap];
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const uint64_t* __restrict__ parts, int32_t K,
+                                                                   int32_t segs, float mult, float cap,
+                                                                   int64_t* __restrict__ ids_out,
+                                                                   float* __restrict__ unary_out) {
+  __shared__ uint64_t cand[kTopkMergeCap];
   const int64_t row = blockIdx.x;
   const int m = segs * K;
   const uint64_t* src = parts + (size_t)row * m;
-  for (int i = threadIdx.x; i < m; i += kThreads) cand[i] = src[i];
+  for (int i = threadIdx.x; i < m; i += kMergeThreads) cand[i] = src[i];
   __syncthreads();
-  for (int i = threadIdx.x; i < m; i += kThreads) {
+  for (int i = threadIdx.x; i < m; i += kMergeThreads) {
     const uint64_t c = cand[i];
     if (c == 0) continue;                      // empty slot of a short segment
     int rank = 0;
@@ -406,18 +550,18 @@ TopkPlan plan_topk(int64_t n_rows, int64_t valid_vocab, int32_t top_k) {
   p.n_rows = n_rows;
   p.valid_vocab = valid_vocab;
   p.top_k = top_k;
-  p.chunks = (int32_t)((valid_vocab + kChunk - 1) / kChunk);
+  p.chunks = (int32_t)((valid_vocab + kWaveChunk - 1) / kWaveChunk);   // wave-chunks per row
   if (p.chunks < 1) p.chunks = 1;
-  // One workgroup per row once rows cover the chip; otherwise split rows so
-  // that about 512 workgroups stream, and merge the segments afterwards.
+  // One workgroup (8 waves) per row once rows give the chip about 4096 waves;
+  // otherwise split rows into segments and merge them in a second kernel.
   int segs = 1;
-  if (n_rows > 0 && n_rows < 256) {
-    segs = (int)((512 + n_rows - 1) / n_rows);
-    if (segs > p.chunks) segs = p.chunks;
-    if (segs * top_k > kCap) segs = kCap / top_k;
+  if (n_rows > 0 && n_rows * kWaves < 3072) {
+    segs = (int)((4096 / kWaves + n_rows - 1) / n_rows);
+    const int max_by_chunks = (p.chunks + kWaves - 1) / kWaves;         // >= 1 wave-chunk per wave
+    if (segs > max_by_chunks) segs = max_by_chunks;
+    if (segs * top_k > kTopkMergeCap) segs = kTopkMergeCap / top_k;
     if (segs < 1) segs = 1;
   }
-  p.segs = segs;
   p.chunks_per_seg = (p.chunks + segs - 1) / segs;
   p.segs = (p.chunks + p.chunks_per_seg - 1) / p.chunks_per_seg;   // no empty segments
   p.parts_offset = 0;
@@ -430,21 +574,21 @@ hipError_t launch_topk(const TopkArgs& a, const TopkPlan& p, hipStream_t stream)
   uint64_t* parts = reinterpret_cast<uint64_t*>(static_cast<char*>(a.workspace) + p.parts_offset);
   const dim3 grid((unsigned)(p.n_rows * p.segs));
   if (a.dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(topk_rows_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(topk_rows_bf16, grid, dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(a.logits), a.row_stride, a.valid_vocab, a.top_k, p.chunks,
                        p.segs, p.chunks_per_seg, a.multiplier, a.softcap, parts, a.ids_out, a.unary_out);
   else
-    hipLaunchKernelGGL(topk_rows_kernel<float>, grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(topk_rows_f32, grid, dim3(kThreads), 0, stream,
                        static_cast<const float*>(a.logits), a.row_stride, a.valid_vocab, a.top_k, p.chunks,
                        p.segs, p.chunks_per_seg, a.multiplier, a.softcap, parts, a.ids_out, a.unary_out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.segs == 1) return e;
   if (a.dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(topk_merge_kernel<uint16_t>, dim3((unsigned)p.n_rows), dim3(kThreads), 0, stream, parts,
-                       a.top_k, p.segs, a.multiplier, a.softcap, a.ids_out, a.unary_out);
+    hipLaunchKernelGGL(topk_merge_kernel<uint16_t>, dim3((unsigned)p.n_rows), dim3(kMergeThreads), 0, stream,
+                       parts, a.top_k, p.segs, a.multiplier, a.softcap, a.ids_out, a.unary_out);
   else
-    hipLaunchKernelGGL(topk_merge_kernel<float>, dim3((unsigned)p.n_rows), dim3(kThreads), 0, stream, parts,
-                       a.top_k, p.segs, a.multiplier, a.softcap, a.ids_out, a.unary_out);
+    hipLaunchKernelGGL(topk_merge_kernel<float>, dim3((unsigned)p.n_rows), dim3(kMergeThreads), 0, stream,
+                       parts, a.top_k, p.segs, a.multiplier, a.softcap, a.ids_out, a.unary_out);
   return hipGetLastError();
 }
 
