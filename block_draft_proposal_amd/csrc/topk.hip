@@ -10,37 +10,41 @@
 //
 // Design (HBM-bound stream, one pass over the logits, no cross-workgroup
 // synchronisation):
-//  * Every value becomes an order-preserving unsigned key (-0 and +0 share a
-//    key; a position outside the logical vocabulary has key 0, below every
-//    real value), and every (key, id) pair a 56-bit composite
+//  * Every value has an order-preserving unsigned key (-0 and +0 share a key;
+//    a position outside the logical vocabulary has key 0, below every real
+//    value), and every (key, id) pair a 56-bit composite
 //    key << 24 | (2^24 - 1 - id) whose order is exactly (value desc, id asc)
 //    and which is unique within a row.
-//  * A workgroup of 8 waves owns a row (or, when rows are too few to fill the
-//    chip, a segment of one; a small second kernel then merges segments).
-//    The row is cut into wave-chunks of 4096 values, dealt round-robin to the
-//    8 waves; every wave streams its chunks on its own -- 64 values per lane
-//    as eight 16-byte loads, each wave load one contiguous 1 KiB, the next
-//    chunk's loads issued before the current chunk is processed -- and keeps
-//    its own K best in LDS.  No workgroup barrier until the final merge.
-//  * bf16 keys are built and tested two per register with packed 16-bit ops.
-//  * Threshold: on a wave's first chunk, the K-th largest of the 64 lane maxima
-//    (at least K distinct values reach it); once a wave holds K values, a later
-//    value of that wave must beat its K-th key strictly (its id is larger than
-//    every id the wave holds).  The few survivors are compacted into LDS and
-//    ranked exactly by counting.
+//  * A workgroup of 4 waves owns a row (or, when rows are very few, a segment
+//    of one; a small second kernel then merges segments).  The row is cut
+//    into wave-chunks of 4096 values dealt round-robin to the waves; every
+//    wave streams its chunks on its own -- 64 values per lane as eight
+//    16-byte loads, each wave load one contiguous 1 KiB, the next chunk's
+//    loads in flight while the current chunk is processed -- and keeps its
+//    own K best in LDS.  No workgroup barrier until the final merge.
+//  * Threshold: on a wave's first chunk, the K-th largest of its 64 lane
+//    maxima (found bit by bit with ballot counts; those K lanes hold K
+//    distinct values that reach it); afterwards a value must beat the wave's
+//    K-th key strictly (its id is larger than every id the wave holds).
+//  * bf16: while that threshold is a positive value, the filter runs on the
+//    raw bits (a positive bf16 read as int16 orders like its value), one
+//    packed signed max per two values; keys are built only for survivors.
+//    Otherwise (and for fp32) keys are built per value.
+//  * Survivors are compacted into LDS; the wave's sorted list is updated with
+//    ranks from a binary search in the held list plus a count among the new.
 //  * If a chunk yields more survivors than LDS holds (mass ties), an exact
 //    bisection on the key, then on the id among the tied key, narrows the
 //    chunk to exactly its K best; that path re-reads the chunk from cache.
-//  * The 8 sorted per-wave lists are merged with one barrier: each entry's
-//    rank is its own index plus, per other list, a binary-searched count of
-//    larger entries.
+//  * The sorted per-wave lists are merged with one barrier: each entry's rank
+//    is its own index plus, per other list, a binary-searched count of larger
+//    entries.
 #include "dflash.h"
 #include "dflash_internal.h"
 
 namespace dflash {
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kPerLane = 64;                   // values per lane per wave-chunk
 constexpr int kWaveChunk = 64 * kPerLane;      // 4096 values
@@ -173,6 +177,15 @@ template <> struct Chunk<uint16_t> {
       }
     }
   }
+  // On raw bits: the largest lane value read as int16 (the largest positive
+  // value, when the lane has one).
+  __device__ int raw_max_i16() const {
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    s16x2 m = __builtin_bit_cast(s16x2, w[0]);
+#pragma unroll
+    for (int j = 1; j < W; ++j) m = __builtin_elementwise_max(m, __builtin_bit_cast(s16x2, w[j]));
+    return max((int)m.x, (int)m.y);
+  }
   // On raw bits (before make_keys): calls f(key, value index) for every
   // positive value whose bits, read as int16, are >= r (1 <= r <= 0x7fff).
   // A positive value's key is bits | 0x8000, so this selects key >= r + 0x8000;
@@ -195,6 +208,7 @@ template <> struct Chunk<uint16_t> {
     }
   }
   static constexpr uint64_t kKeyLimit = 0x10000u;   // keys are < this
+  static constexpr int kKeyBits = 16;
   __device__ static uint32_t key_at(const uint16_t* p) { return bf16_key(*p); }
   __device__ static float value(uint32_t k) { return bf16_key_value(k); }
 };
@@ -246,8 +260,10 @@ template <> struct Chunk<float> {
       if ((uint64_t)w[j] >= tau) f(w[j], j);
   }
   static constexpr bool kHasRawFilter = false;
+  __device__ int raw_max_i16() const { return 0; }
   template <class F> __device__ void for_each_raw_ge(uint32_t, F&&) const {}
   static constexpr uint64_t kKeyLimit = 0x100000000ull;
+  static constexpr int kKeyBits = 32;
   __device__ static uint32_t key_at(const float* p) { return f32_key(__float_as_uint(*p)); }
   __device__ static float value(uint32_t k) { return f32_key_value(k); }
 };
@@ -328,20 +344,6 @@ __device__ __noinline__ uint32_t narrow_exact(const TIO* rowp, int64_t c_start, 
   return __builtin_amdgcn_readfirstlane(wl.count);
 }
 
-// Keep the K best of pool[0, n) in pool[0, min(n, K)) (sorted, best first).
-__device__ void keep_best(WaveLds& wl, int n, int K, int lane) {
-  for (int i = lane; i < n; i += 64) {
-    const uint64_t c = wl.pool[i];
-    int rank = 0;
-    for (int j = 0; j < n; ++j) rank += (wl.pool[j] > c) ? 1 : 0;
-    if (rank < K) wl.tmp[rank] = c;
-  }
-  wave_sync();
-  const int m = n < K ? n : K;
-  for (int i = lane; i < m; i += 64) wl.pool[i] = wl.tmp[i];
-  wave_sync();
-}
-
 // Number of entries of the sorted (descending) list l[0, n) greater than c.
 __device__ __forceinline__ int count_greater(const uint64_t* l, int n, uint64_t c) {
   int lo = 0, hi = n;
@@ -352,10 +354,49 @@ __device__ __forceinline__ int count_greater(const uint64_t* l, int n, uint64_t 
   return lo;
 }
 
+// Merge n new candidates pool[nb, nb + n) into the held sorted list
+// pool[0, nb) and keep the best min(nb + n, K), sorted, in pool[0, ...).
+// A held entry's new rank is its index plus the new candidates above it; a
+// new candidate's rank is a binary search in the held list plus the new
+// candidates above it (composites are unique, so ranks are distinct).
+__device__ void keep_best(WaveLds& wl, int nb, int n, int K, int lane) {
+  const uint64_t* held = wl.pool;
+  const uint64_t* fresh = wl.pool + nb;
+  for (int i = lane; i < nb; i += 64) {
+    const uint64_t c = held[i];
+    int rank = i;
+    for (int j = 0; j < n; ++j) rank += (fresh[j] > c) ? 1 : 0;
+    if (rank < K) wl.tmp[rank] = c;
+  }
+  for (int i = lane; i < n; i += 64) {
+    const uint64_t c = fresh[i];
+    int rank = count_greater(held, nb, c);
+    for (int j = 0; j < n; ++j) rank += (fresh[j] > c) ? 1 : 0;
+    if (rank < K) wl.tmp[rank] = c;
+  }
+  wave_sync();
+  const int m = nb + n < K ? nb + n : K;
+  for (int i = lane; i < m; i += 64) wl.pool[i] = wl.tmp[i];
+  wave_sync();
+}
+
 __device__ __forceinline__ float unary_transform(float z, float mult, float cap) {
   float y = mult * z;
   if (cap > 0.f) y = cap * tanhf(y / cap);
   return (z == -INFINITY) ? -INFINITY : y;     // masked entries stay masked
+}
+
+// K-th largest of the 64 lane values m (unsigned, below 2^bits): the largest
+// t with #{lanes : m >= t} >= K, found bit by bit with ballot counts.  Those
+// K lanes each hold a distinct value >= t.  Returns 0 when fewer than K
+// lanes have m >= 1.
+__device__ __forceinline__ uint32_t kth_largest_lane(uint32_t m, int K, int bits) {
+  uint32_t t = 0;
+  for (int b = bits - 1; b >= 0; --b) {
+    const uint32_t cand = t | (1u << b);
+    if (__popcll(__ballot(m >= cand)) >= K) t = cand;
+  }
+  return t;
 }
 
 template <typename TIO>
@@ -393,7 +434,7 @@ __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, i
     uint32_t n = __builtin_amdgcn_readfirstlane(wl.count);
     if (n > (uint32_t)kWaveCap) n = narrow_exact<TIO>(rowp, c_start, valid_vocab, lane, K, nbest, wl);
     if (n > 0) {
-      keep_best(wl, nbest + (int)n, K, lane);
+      keep_best(wl, nbest, (int)n, K, lane);
       nbest = min(K, nbest + (int)n);
     }
   };
@@ -401,16 +442,10 @@ __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, i
   auto process_keys = [&](const Chunk<TIO>& ch, int64_t c_start) {
     uint64_t tau;
     if (nbest < K) {
-      // K-th largest lane maximum (ties by lane): at least K values reach it
-      const uint32_t m = ch.max_key();
-      int rank = 0;
-      for (int o = 0; o < 64; ++o) {
-        const uint32_t v = (uint32_t)__shfl((int)m, o, 64);
-        rank += (v > m || (v == m && o < lane)) ? 1 : 0;
-      }
-      const int nonzero = __popcll(__ballot(m != 0));
-      const unsigned long long at = __ballot(rank == K - 1);
-      tau = (nonzero >= K) ? (uint64_t)(uint32_t)__shfl((int)m, __ffsll((long long)at) - 1, 64) : 1u;
+      // K-th largest lane maximum: at least K values reach it (key 0 =
+      // no real value; too few real lanes -> every real value)
+      const uint32_t t = kth_largest_lane(ch.max_key(), K, Chunk<TIO>::kKeyBits);
+      tau = t ? (uint64_t)t : 1u;
     } else {
       // a later value has a larger id than every held one: it must beat the
       // K-th key strictly
@@ -422,15 +457,26 @@ __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, i
     if (tau < Chunk<TIO>::kKeyLimit) ch.for_each_ge(tau, [&](uint32_t k, int i) { push(k, i, id_base); });
     update(c_start);
   };
-  // One full chunk whose raw bits are in `ch`.
+  // One full chunk whose raw bits are in `ch`.  bf16: while the threshold is
+  // a positive value the filter runs on raw bits (keys are built only for
+  // survivors); otherwise the chunk goes through the key path.
   auto process_full = [&](Chunk<TIO>& ch, int64_t c_start) {
-    if (Chunk<TIO>::kHasRawFilter && nbest == K) {
-      const uint32_t tau = composite_key(wl.pool[K - 1]) + 1;   // strict, as above
-      if (tau > 0x8000u && tau < 0x10000u) {                     // a positive threshold
+    if (Chunk<TIO>::kHasRawFilter) {
+      int r = 0;                                                 // raw int16 threshold, >= 1 when usable
+      if (nbest == K) {
+        const uint32_t tau = composite_key(wl.pool[K - 1]) + 1;   // strict, as above
+        if (tau > 0x8000u && tau < 0x10000u) r = (int)(tau - 0x8000u);
+      } else if (nbest == 0) {
+        // first chunk: K-th largest positive raw lane maximum (a positive
+        // int16 orders like its value); 0 when fewer than K lanes hold a
+        // positive value
+        r = (int)kth_largest_lane((uint32_t)max(ch.raw_max_i16(), 0), K, 15);
+      }
+      if (r >= 1) {
         if (lane == 0) wl.count = 0;
         wave_sync();
         const uint32_t id_base = (uint32_t)c_start + (uint32_t)lane * VEC;
-        ch.for_each_raw_ge(tau - 0x8000u, [&](uint32_t k, int i) { push(k, i, id_base); });
+        ch.for_each_raw_ge((uint32_t)r, [&](uint32_t k, int i) { push(k, i, id_base); });
         update(c_start);
         return;
       }
@@ -449,15 +495,20 @@ __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, i
   const int full_end = min(c_end, n_full);
   int c = c_begin + wave;
   if (c < full_end) {
-    Chunk<TIO> cur;
-    cur.issue_full(rowp, (int64_t)c * kWaveChunk, lane);
-    for (; c < full_end; c += kWaves) {
-      const int64_t c_start = (int64_t)c * kWaveChunk;
-      const int c_next = (c + kWaves < full_end) ? c + kWaves : c;
-      Chunk<TIO> next;
-      next.issue_full(rowp, (int64_t)c_next * kWaveChunk, lane);
-      process_full(cur, c_start);
-      cur = next;
+    // two buffers, alternating roles, so that no chunk is copied
+    Chunk<TIO> a, b;
+    a.issue_full(rowp, (int64_t)c * kWaveChunk, lane);
+    while (true) {
+      int c_next = (c + kWaves < full_end) ? c + kWaves : c;
+      b.issue_full(rowp, (int64_t)c_next * kWaveChunk, lane);
+      process_full(a, (int64_t)c * kWaveChunk);
+      c += kWaves;
+      if (c >= full_end) break;
+      c_next = (c + kWaves < full_end) ? c + kWaves : c;
+      a.issue_full(rowp, (int64_t)c_next * kWaveChunk, lane);
+      process_full(b, (int64_t)c * kWaveChunk);
+      c += kWaves;
+      if (c >= full_end) break;
     }
   }
   if (c < c_end) {                               // the partial last chunk of the row
@@ -470,7 +521,7 @@ __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, i
   if (lane == 0) wl.nbest = (uint32_t)nbest;
   __syncthreads();
 
-  // ---- merge the 8 sorted wave lists --------------------------------------
+  // ---- merge the sorted wave lists ----------------------------------------
   if (threadIdx.x < kWaves * K) {
     const int w = threadIdx.x / K, i = threadIdx.x % K;
     const int nw = (int)sh.wave[w].nbest;
@@ -552,11 +603,12 @@ TopkPlan plan_topk(int64_t n_rows, int64_t valid_vocab, int32_t top_k) {
   p.top_k = top_k;
   p.chunks = (int32_t)((valid_vocab + kWaveChunk - 1) / kWaveChunk);   // wave-chunks per row
   if (p.chunks < 1) p.chunks = 1;
-  // One workgroup (8 waves) per row once rows give the chip about 4096 waves;
-  // otherwise split rows into segments and merge them in a second kernel.
+  // One workgroup (4 waves) per row; only when rows are very few are they
+  // split into segments (merged by a second kernel), since the merge launch
+  // costs more than the extra parallelism gains for a few hundred rows.
   int segs = 1;
-  if (n_rows > 0 && n_rows * kWaves < 3072) {
-    segs = (int)((4096 / kWaves + n_rows - 1) / n_rows);
+  if (n_rows > 0 && n_rows < 128) {
+    segs = (int)((512 + n_rows - 1) / n_rows);
     const int max_by_chunks = (p.chunks + kWaves - 1) / kWaves;         // >= 1 wave-chunk per wave
     if (segs > max_by_chunks) segs = max_by_chunks;
     if (segs * top_k > kTopkMergeCap) segs = kTopkMergeCap / top_k;
