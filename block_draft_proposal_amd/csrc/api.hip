@@ -350,12 +350,16 @@ int dflash_propose_block(const dflash_draft_config* cfg, const dflash_block_args
   if ((st = record(ev, 4, s)) != DFLASH_OK) return st;
   if ((st = launch_status(dflash::launch_proj(sa, pp, s), who)) != DFLASH_OK) return st;
   if ((st = record(ev, 5, s)) != DFLASH_OK) return st;
-  // stage 3: lattice + walk
+  // stage 3: lattice + walk (one kernel when a request's lattice fits in LDS)
   if ((st = record(ev, 6, s)) != DFLASH_OK) return st;
-  if ((st = launch_status(dflash::launch_lattice(sa, pp, s), who)) != DFLASH_OK) return st;
   dflash::WalkArgs wa{scores, a->ids_out, a->uniforms, a->temperatures, a->greedy_mask, a->n_req, S, K,
                       a->tokens_out, a->q_out};
-  if ((st = launch_status(dflash::launch_walk(wa, s), who)) != DFLASH_OK) return st;
+  if (dflash::lattice_walk_fits(sa)) {
+    if ((st = launch_status(dflash::launch_lattice_walk(sa, pp, wa, a->scores_out, s), who)) != DFLASH_OK) return st;
+  } else {
+    if ((st = launch_status(dflash::launch_lattice(sa, pp, s), who)) != DFLASH_OK) return st;
+    if ((st = launch_status(dflash::launch_walk(wa, s), who)) != DFLASH_OK) return st;
+  }
   if ((st = record(ev, 7, s)) != DFLASH_OK) return st;
   return ok();
 }

@@ -28,11 +28,13 @@ template <> struct Elem<uint16_t> {               // bf16 storage
   static constexpr int kVec = 8;                  // elements per 16-byte vector
   __device__ static float load(const uint16_t* p) { return bf16_to_f32(*p); }
   __device__ static float to_f32(uint16_t v) { return bf16_to_f32(v); }
+  __device__ static uint16_t nan_value() { return 0x7fc0u; }
 };
 template <> struct Elem<float> {
   static constexpr int kVec = 4;
   __device__ static float load(const float* p) { return *p; }
   __device__ static float to_f32(float v) { return v; }
+  __device__ static float nan_value() { return __builtin_nanf(""); }
 };
 
 // Unpack one 16-byte vector into fp32 values.
@@ -115,6 +117,11 @@ struct TopkArgs {
 };
 hipError_t launch_topk(const TopkArgs& a, const TopkPlan& p, hipStream_t stream);
 
+constexpr int kMaxTopK = 32;   // DFLASH_MAX_TOP_K
+
+// Most slices the projection's contraction is split into (their partial
+// sums are added by the consumer, in slice order).
+constexpr int kMaxProjSplit = 32;
 struct ProjPlan {
   int32_t n_rows, rank, hidden;
   int32_t row_tiles, ksplit, kslice;   // split of the contraction over workgroups
@@ -151,5 +158,14 @@ struct WalkArgs {
   float* q;
 };
 hipError_t launch_walk(const WalkArgs& a, hipStream_t stream);
+
+// Lattice and walk in one kernel (one workgroup per request) when the
+// request's lattice and its staging fit in LDS; bit-identical to
+// launch_lattice followed by launch_walk.  scores_out may be null.
+constexpr size_t kLatticeWalkLdsMax = 64 * 1024;
+size_t lattice_walk_lds_bytes(int slots, int top_k, int rank, int dtype);
+bool lattice_walk_fits(const struct SelectArgs& a);   // LDS size, rank multiple of a vector, 16-byte tables
+hipError_t launch_lattice_walk(const SelectArgs& a, const ProjPlan& p, const WalkArgs& w, float* scores_out,
+                               hipStream_t stream);
 
 }  // namespace dflash

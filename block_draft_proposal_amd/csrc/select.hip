@@ -36,6 +36,15 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kRowsPerWG = 64;       // 4 waves x 16 rows
 
+// Exact n / d for 0 <= n, d < 2^16 (d >= 1) by one multiply-high:
+// q = (n * ceil(2^32 / d)) >> 32.  The error n * (M d - 2^32) / (d 2^32) is
+// below 1/d, so the floor is exact.
+struct FastDiv {
+  uint64_t m;
+  __device__ explicit FastDiv(int d) : m(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d) {}
+  __device__ int quot(int n) const { return (int)(((uint64_t)(uint32_t)n * m) >> 32); }
+};
+
 __device__ __forceinline__ const void* hidden_row(const void* hidden, int64_t req_stride,
                                                   int64_t slot_stride, int32_t slots, int row,
                                                   int elem_bytes) {
@@ -107,6 +116,22 @@ __global__ __launch_bounds__(kThreads) void proj_f32_kernel(const float* __restr
   u_parts[t] = acc;
 }
 
+// u[n][k] = sum over the projection slices sp = 0..ksplit-1 of
+// u_parts[sp][n][k], added in slice order.  All slice loads are issued before
+// the first add (ksplit <= kMaxProjSplit).
+__device__ __forceinline__ float sum_proj_slices(const float* __restrict__ u_parts, int ksplit, int64_t n_rows,
+                                                 int r, int64_t n, int k) {
+  float v[kMaxProjSplit];
+#pragma unroll
+  for (int sp = 0; sp < kMaxProjSplit; ++sp)
+    if (sp < ksplit) v[sp] = u_parts[((int64_t)sp * n_rows + n) * r + k];
+  float u = v[0];
+#pragma unroll
+  for (int sp = 1; sp < kMaxProjSplit; ++sp)
+    if (sp < ksplit) u += v[sp];
+  return u;
+}
+
 template <typename TIO>
 __device__ __forceinline__ float load_f32(const TIO* p, int64_t i) { return Elem<TIO>::to_f32(p[i]); }
 
@@ -122,11 +147,7 @@ __device__ void lattice_block(const int64_t* __restrict__ ids, const float* __re
   const int tid = threadIdx.x;
   const int n = req * slots + s;
   const int wstride = r + 1;                         // padded row of w (LDS banks)
-  for (int k = tid; k < r; k += kThreads) {
-    float u = u_parts[(int64_t)n * r + k];
-    for (int sp = 1; sp < ksplit; ++sp) u += u_parts[((int64_t)sp * n_rows + n) * r + k];
-    s_u[k] = u;
-  }
+  for (int k = tid; k < r; k += kThreads) s_u[k] = sum_proj_slices(u_parts, ksplit, n_rows, r, n, k);
   for (int j = tid; j < K; j += kThreads) {
     s_pred[j] = (s == 0) ? anchor[req] : ids[((int64_t)req * slots + s - 1) * K + j];
     s_cand[j] = ids[(int64_t)n * K + j];
@@ -173,38 +194,87 @@ __global__ __launch_bounds__(kThreads) void lattice_kernel(const int64_t* __rest
                      s_u, s_w, s_bt, s_ids, s_ids + K, scores + (int64_t)n * K * K);
 }
 
+// Lane j's value of v, as a wave-uniform value.
+__device__ __forceinline__ float lane_value(float v, int j) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+}
+
 // One walk decision on a wave: lane j (< K) holds row[j].  Returns the chosen
-// index (same on every lane) and sets q (this lane's probability).
-__device__ __forceinline__ int walk_decide(float v, int lane, int K, bool greedy, float temp,
-                                           float u, float& q) {
+// index (wave-uniform) and sets q (this lane's probability).  Maxima are
+// exact in any order (tree); the normalising sum and the CDF run left to
+// right over the candidates, as the definition is evaluated.
+__device__ __forceinline__ int walk_decide(float v, int lane, int K, bool greedy, float temp, float u,
+                                           float& q) {
   const bool on = lane < K;
   if (greedy) {
-    const float best = wave_max_f32(on ? v : -INFINITY);
-    int idx = wave_min_i32((on && v == best) ? lane : K);
-    if (idx > K - 1) idx = 0;             // all-NaN row: no maximum; stay in range
+    // first maximum in candidate order = lowest index among ties
+    float best = lane_value(v, 0);
+    int idx = 0;
+    for (int j = 1; j < K; ++j) {
+      const float x = lane_value(v, j);
+      if (x > best) { best = x; idx = j; }
+    }
     q = (lane == idx) ? 1.f : 0.f;
     return idx;
   }
   const float t = fmaxf(temp, 1e-5f);
   const float xs = v / t;
-  const float mx = wave_max_f32(on ? xs : -INFINITY);
+  float mx = lane_value(xs, 0);
+  for (int j = 1; j < K; ++j) mx = fmaxf(mx, lane_value(xs, j));
   // exp rounded once to fp32 (from the fp64 exponential)
   const float e = on ? (float)exp((double)(xs - mx)) : 0.f;
   float total = 0.f;
-  for (int j = 0; j < K; ++j) total += __shfl(e, j, 64);        // left to right
+  for (int j = 0; j < K; ++j) total += lane_value(e, j);          // left to right
   const float p = e / total;
   float cdf = 0.f;
-  for (int j = 0; j < K; ++j) {
-    const float pj = __shfl(p, j, 64);
-    if (j <= lane) cdf += pj;                                     // C_lane, left to right
+  int cnt = 0;
+  for (int j = 0; j < K; ++j) {                                     // C_j left to right
+    cdf += lane_value(p, j);
+    cnt += (u >= cdf) ? 1 : 0;
   }
-  const unsigned long long hit = __ballot(on && u >= cdf);
-  const int cnt = __popcll(hit);
   q = on ? p : 0.f;
   return cnt < K - 1 ? cnt : K - 1;
 }
 
-constexpr int kWalkLdsFloats = 16384;   // 64 KiB: S * K * K staged when it fits
+// The same decision for one lattice row evaluated by a single thread:
+// row[0..K) in, q[0..K) out (q may alias row).  Same operations in the same
+// order as walk_decide, so the two give identical bits.
+__device__ __forceinline__ int row_decide(const float* row, float* q, int K, bool greedy, float temp, float u) {
+  if (greedy) {
+    float best = row[0];
+    int idx = 0;
+    for (int c = 1; c < K; ++c) {
+      const float x = row[c];
+      if (x > best) { best = x; idx = c; }
+    }
+    for (int c = 0; c < K; ++c) q[c] = (c == idx) ? 1.f : 0.f;
+    return idx;
+  }
+  const float t = fmaxf(temp, 1e-5f);
+  float mx = row[0] / t;
+  for (int c = 1; c < K; ++c) mx = fmaxf(mx, row[c] / t);
+  float total = 0.f;
+  for (int c = 0; c < K; ++c) {
+    const float e = (float)exp((double)(row[c] / t - mx));
+    q[c] = e;
+    total += e;                                                   // left to right
+  }
+  float cdf = 0.f;
+  int cnt = 0;
+  for (int c = 0; c < K; ++c) {
+    const float p = q[c] / total;
+    q[c] = p;
+    cdf += p;                                                     // C_c left to right
+    cnt += (u >= cdf) ? 1 : 0;
+  }
+  return cnt < K - 1 ? cnt : K - 1;
+}
+
+constexpr int kWalkLdsBytes = 64 * 1024;   // scores + ids + uniforms of a request, staged when they fit
+
+__device__ __forceinline__ size_t walk_stage_bytes(int slots, int K) {
+  return (size_t)slots * K * K * sizeof(float) + (size_t)slots * K * sizeof(int64_t) + (size_t)slots * sizeof(float);
+}
 
 __global__ __launch_bounds__(kThreads) void walk_kernel(const float* __restrict__ scores,
                                                         const int64_t* __restrict__ ids,
@@ -214,29 +284,205 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(const float* __restrict_
                                                         int32_t slots, int32_t K,
                                                         int64_t* __restrict__ tokens,
                                                         float* __restrict__ q_out) {
-  extern __shared__ float s_sc[];
+  extern __shared__ __align__(16) unsigned char walk_smem[];
   const int req = blockIdx.x;
   const int64_t per_req = (int64_t)slots * K * K;
   const float* src = scores + (int64_t)req * per_req;
-  const bool staged = per_req <= kWalkLdsFloats;
+  const int64_t* ids_r = ids + (int64_t)req * slots * K;
+  const float* uni_r = uniforms + (int64_t)req * slots;
+  // layout: ids (8-byte) first, then scores, then uniforms
+  int64_t* s_ids = reinterpret_cast<int64_t*>(walk_smem);
+  float* s_sc = reinterpret_cast<float*>(s_ids + (int64_t)slots * K);
+  float* s_u = s_sc + per_req;
+  const bool staged = walk_stage_bytes(slots, K) <= (size_t)kWalkLdsBytes;
   if (staged) {
     for (int64_t i = threadIdx.x; i < per_req; i += kThreads) s_sc[i] = src[i];
+    for (int i = threadIdx.x; i < slots * K; i += kThreads) s_ids[i] = ids_r[i];
+    for (int i = threadIdx.x; i < slots; i += kThreads) s_u[i] = uni_r[i];
   }
   __syncthreads();
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
   const bool greedy = greedy_mask[req] != 0;
   const float temp = temperatures[req];
+  const float* sc = staged ? s_sc : src;
+  const int64_t* id = staged ? s_ids : ids_r;
+  const float* un = staged ? s_u : uni_r;
   int prev = 0;
   for (int s = 0; s < slots; ++s) {
     const int64_t row_off = ((int64_t)s * K + prev) * K;
-    const float v = lane < K ? (staged ? s_sc[row_off + lane] : src[row_off + lane]) : 0.f;
-    const float u = uniforms[(int64_t)req * slots + s];
+    const float v = lane < K ? sc[row_off + lane] : 0.f;
     float q;
-    const int idx = walk_decide(v, lane, K, greedy, temp, u, q);
+    const int idx = walk_decide(v, lane, K, greedy, temp, un[s], q);
     const int64_t n = (int64_t)req * slots + s;
     if (lane < K) q_out[n * K + lane] = q;
-    if (lane == 0) tokens[n] = ids[n * K + idx];
+    if (lane == 0) tokens[n] = id[s * K + idx];
+    prev = idx;
+  }
+}
+
+// Lattice + walk for one request in one workgroup, when the request's whole
+// lattice and its staging fit in LDS.  Same per-entry arithmetic as
+// lattice_block (u summed over the projection slices in order, w = A * u,
+// fma chain over k from 0, + unary) and the same walk_decide, so the result
+// is bit-identical to lattice_kernel followed by walk_kernel.
+// LDS layout: pred ids [S][K], cand ids [S][K] (int64), u [S][r], w [S][K][r+1]
+// (fp32), B rows [S][r][KB] (storage dtype, padded to the row width KB),
+// scores [S][K][K] (then q), uniforms [S], chosen index per row [S][K].
+struct LatticeWalkLds {
+  size_t pred, cand, u, w, b, sc, un, bytes;
+};
+// K rounded up to the kernel's row width (4, 8, 16 or 32).
+__host__ __device__ inline int k_bucket(int K) { return K <= 4 ? 4 : K <= 8 ? 8 : K <= 16 ? 16 : 32; }
+
+__host__ __device__ inline LatticeWalkLds lattice_walk_layout(int S, int K, int r, int elem) {
+  LatticeWalkLds L;
+  const int KB = k_bucket(K);
+  size_t o = 0;
+  L.pred = o; o += (size_t)S * K * 8;
+  L.cand = o; o += (size_t)S * K * 8;
+  L.u = o;    o += (size_t)S * r * 4;
+  L.w = o;    o += (size_t)S * K * (r + 1) * 4;
+  o = (o + 15) & ~(size_t)15;
+  L.b = o;    o += ((size_t)S * r * KB * elem + 15) & ~(size_t)15;   // rows padded to KB
+  L.sc = o;   o += (size_t)S * K * K * 4;
+  L.un = o;   o += (size_t)S * 4;
+  o += (size_t)S * K * 4;                                   // chosen index per row
+  L.bytes = o;
+  return L;
+}
+
+template <typename TIO, int KB>   // KB: K rounded up to 4, 8, 16 or 32
+__global__ __launch_bounds__(kThreads) void lattice_walk_kernel(
+    const int64_t* __restrict__ ids, const float* __restrict__ unary, const int64_t* __restrict__ anchor,
+    const TIO* __restrict__ A, const TIO* __restrict__ B, const float* __restrict__ u_parts, int32_t ksplit,
+    int32_t slots, int32_t K, int32_t r, int64_t vocab, int32_t n_rows, const float* __restrict__ uniforms,
+    const float* __restrict__ temperatures, const uint8_t* __restrict__ greedy_mask,
+    float* __restrict__ scores_out, int64_t* __restrict__ tokens, float* __restrict__ q_out) {
+  extern __shared__ __align__(16) unsigned char lw_smem[];
+  const int req = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int S = slots;
+  const LatticeWalkLds L = lattice_walk_layout(S, K, r, (int)sizeof(TIO));
+  int64_t* s_pred = reinterpret_cast<int64_t*>(lw_smem + L.pred);
+  int64_t* s_cand = reinterpret_cast<int64_t*>(lw_smem + L.cand);
+  float* s_u = reinterpret_cast<float*>(lw_smem + L.u);
+  float* s_w = reinterpret_cast<float*>(lw_smem + L.w);
+  TIO* s_b = reinterpret_cast<TIO*>(lw_smem + L.b);
+  float* s_sc = reinterpret_cast<float*>(lw_smem + L.sc);
+  float* s_un = reinterpret_cast<float*>(lw_smem + L.un);
+  const int64_t row0 = (int64_t)req * S;            // first slot row of this request
+  const int wstride = r + 1;
+
+  // ---- ids, u (projection slices summed in order), uniforms -------------
+  for (int i = tid; i < S * K; i += kThreads) {
+    const int s = i / K, j = i % K;
+    s_pred[i] = (s == 0) ? anchor[req] : ids[(row0 + s - 1) * K + j];
+    s_cand[i] = ids[(row0 + s) * K + j];
+  }
+  for (int i = tid; i < S * r; i += kThreads) s_u[i] = sum_proj_slices(u_parts, ksplit, n_rows, r, row0 + i / r, i % r);
+  for (int i = tid; i < S; i += kThreads) s_un[i] = uniforms[row0 + i];
+  __syncthreads();
+
+  // ---- gather: w = A[pred] (.) u (fp32), B[cand] rows ------------------
+  // 16-byte pieces of the table rows (r is a multiple of VEC, rows 16-byte
+  // aligned).  Loads are unconditional (indices clamped into range) so that
+  // every thread issues all of its loads before the first use; out-of-range
+  // ids become NaN afterwards.
+  {
+    constexpr int VEC = Elem<TIO>::kVec;
+    constexpr int kPer = 8;                          // pieces per thread per pass
+    const int pieces_per_row = r / VEC;
+    const int n_pieces = S * K * pieces_per_row;     // per table
+    const int total = 2 * n_pieces;
+    const FastDiv div_ppr(pieces_per_row), div_k(K);
+    for (int base = 0; base < total; base += kThreads * kPer) {
+      uint4 raw[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int i = min(base + q * kThreads + tid, total - 1);
+        const bool is_b = i >= n_pieces;
+        const int ii = is_b ? i - n_pieces : i;
+        const int sj = div_ppr.quot(ii), v = ii - sj * pieces_per_row;
+        const int64_t t = is_b ? s_cand[sj] : s_pred[sj];
+        const int64_t tc = (t >= 0 && t < vocab) ? t : 0;
+        raw[q] = *reinterpret_cast<const uint4*>((is_b ? B : A) + tc * r + v * VEC);
+      }
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int i = base + q * kThreads + tid;
+        if (i >= total) continue;
+        const bool is_b = i >= n_pieces;
+        const int ii = is_b ? i - n_pieces : i;
+        const int sj = div_ppr.quot(ii), v = ii - sj * pieces_per_row;
+        const int s = div_k.quot(sj), j = sj - s * K;
+        const int64_t t = is_b ? s_cand[sj] : s_pred[sj];
+        const bool ok = t >= 0 && t < vocab;
+        const TIO* piece = reinterpret_cast<const TIO*>(&raw[q]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const int k = v * VEC + e;
+          if (is_b) {
+            s_b[((size_t)s * r + k) * KB + j] = ok ? piece[e] : Elem<TIO>::nan_value();
+          } else {
+            const float a = ok ? Elem<TIO>::to_f32(piece[e]) : __builtin_nanf("");
+            s_w[sj * wstride + k] = a * s_u[s * r + k];   // A[p] (.) project(h)
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- every K x K block: a thread evaluates one row (s, j) as KB
+  // independent fma chains over k (each entry the same chain lattice_block
+  // runs); B rows are read as whole padded rows, padding columns discarded --
+  for (int sj = tid; sj < S * K; sj += kThreads) {
+    const int s = sj / K;
+    const float* w = s_w + sj * wstride;
+    const TIO* b = s_b + (size_t)s * r * KB;
+    float acc[KB];
+#pragma unroll
+    for (int c = 0; c < KB; ++c) acc[c] = 0.f;
+#pragma unroll 4
+    for (int k = 0; k < r; ++k) {
+      const float wk = w[k];
+      TIO bv[KB];
+      __builtin_memcpy(bv, __builtin_assume_aligned(b + (size_t)k * KB, sizeof(TIO) * KB >= 16 ? 16 : 8), sizeof(bv));
+#pragma unroll
+      for (int c = 0; c < KB; ++c) acc[c] = fmaf(wk, Elem<TIO>::to_f32(bv[c]), acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < KB; ++c) {
+      if (c < K) {
+        const float v = acc[c] + unary[(row0 + s) * K + c];
+        s_sc[sj * K + c] = v;
+        if (scores_out) scores_out[(row0 * K + sj) * K + c] = v;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- walk: every row's decision is independent of the path, so all S*K
+  // rows are decided in parallel (q written over the row); then one wave
+  // follows the chosen indices from row 0 ------------------------------------
+  const bool greedy = greedy_mask[req] != 0;
+  const float temp = temperatures[req];
+  int* s_next = reinterpret_cast<int*>(s_un + S);
+  for (int sj = tid; sj < S * K; sj += kThreads) {
+    float* row = s_sc + (size_t)sj * K;
+    s_next[sj] = row_decide(row, row, K, greedy, temp, s_un[sj / K]);
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  const int lane = tid;
+  int prev = 0;
+  for (int s = 0; s < S; ++s) {
+    const int sj = s * K + prev;
+    const int64_t n = row0 + s;
+    if (lane < K) q_out[n * K + lane] = s_sc[sj * K + lane];
+    const int idx = s_next[sj];
+    if (lane == 0) tokens[n] = s_cand[s * K + idx];
     prev = idx;
   }
 }
@@ -254,6 +500,7 @@ ProjPlan plan_proj(int32_t n_rows, int32_t rank, int32_t hidden, int32_t dtype) 
     const int max_ks = hidden / 256 > 1 ? hidden / 256 : 1;
     if (ks > max_ks) ks = max_ks;
     if (ks < 1) ks = 1;
+    if (ks > kMaxProjSplit) ks = kMaxProjSplit;
     int slice = (hidden + ks - 1) / ks;
     slice = (slice + 31) / 32 * 32;
     p.kslice = slice;
@@ -318,10 +565,47 @@ hipError_t launch_lattice(const SelectArgs& a, const ProjPlan& p, hipStream_t st
 
 hipError_t launch_walk(const WalkArgs& a, hipStream_t stream) {
   if (a.n_req == 0 || a.slots == 0) return hipSuccess;
-  const int64_t per_req = (int64_t)a.slots * a.top_k * a.top_k;
-  const size_t lds = per_req <= kWalkLdsFloats ? (size_t)per_req * sizeof(float) : 0;
+  const size_t need = (size_t)a.slots * a.top_k * a.top_k * sizeof(float) +
+                      (size_t)a.slots * a.top_k * sizeof(int64_t) + (size_t)a.slots * sizeof(float);
+  const size_t lds = need <= (size_t)kWalkLdsBytes ? need : 0;
   hipLaunchKernelGGL(walk_kernel, dim3(a.n_req), dim3(kThreads), lds, stream, a.scores, a.ids, a.uniforms,
                      a.temperatures, a.greedy, a.slots, a.top_k, a.tokens, a.q);
+  return hipGetLastError();
+}
+
+size_t lattice_walk_lds_bytes(int slots, int K, int r, int dtype) {
+  return lattice_walk_layout(slots, K, r, dtype == DFLASH_BF16 ? 2 : 4).bytes;
+}
+
+bool lattice_walk_fits(const SelectArgs& a) {
+  const int vec = a.dtype == DFLASH_BF16 ? 8 : 4;
+  return lattice_walk_lds_bytes(a.slots, a.top_k, a.rank, a.dtype) <= kLatticeWalkLdsMax && a.rank % vec == 0 &&
+         (reinterpret_cast<uintptr_t>(a.sel_a) & 15) == 0 && (reinterpret_cast<uintptr_t>(a.sel_b) & 15) == 0;
+}
+
+hipError_t launch_lattice_walk(const SelectArgs& a, const ProjPlan& p, const WalkArgs& w, float* scores_out,
+                               hipStream_t stream) {
+  if (a.n_req == 0 || a.slots == 0) return hipSuccess;
+  if (!lattice_walk_fits(a)) return hipErrorInvalidValue;
+  const size_t lds = lattice_walk_lds_bytes(a.slots, a.top_k, a.rank, a.dtype);
+  const int n_rows = a.n_req * a.slots;
+#define DFLASH_LW(TIO, KB)                                                                                    \
+  hipLaunchKernelGGL((lattice_walk_kernel<TIO, KB>), dim3(a.n_req), dim3(kThreads), lds, stream, a.ids, a.unary, \
+                     a.anchor, static_cast<const TIO*>(a.sel_a), static_cast<const TIO*>(a.sel_b), a.u_parts,     \
+                     p.ksplit, a.slots, a.top_k, a.rank, a.vocab, n_rows, w.uniforms, w.temperatures, w.greedy,  \
+                     scores_out, w.tokens, w.q)
+#define DFLASH_LW_K(TIO)                     \
+  if (a.top_k <= 4) DFLASH_LW(TIO, 4);       \
+  else if (a.top_k <= 8) DFLASH_LW(TIO, 8);  \
+  else if (a.top_k <= 16) DFLASH_LW(TIO, 16); \
+  else DFLASH_LW(TIO, 32);
+  if (a.dtype == DFLASH_BF16) {
+    DFLASH_LW_K(uint16_t)
+  } else {
+    DFLASH_LW_K(float)
+  }
+#undef DFLASH_LW_K
+#undef DFLASH_LW
   return hipGetLastError();
 }
 
