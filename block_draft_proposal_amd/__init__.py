@@ -19,5 +19,6 @@ from .binding import (  # noqa: F401
     dflash_lattice,
     dflash_walk,
     dflash_propose_block,
+    ProposeBlock,
     propose_block_workspace_size,
 )

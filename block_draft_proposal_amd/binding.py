@@ -227,46 +227,85 @@ def propose_block_workspace_size(cfg: DraftConfig, n_req: int, valid_vocab: int)
     return lib().dflash_propose_block_workspace_size(ctypes.byref(cfg), n_req, valid_vocab)
 
 
-def dflash_propose_block(cfg: DraftConfig, *, x, conv_base, conv_delta, logits, anchor, sel_a, sel_b, proj,
-                         uniforms, temperatures, greedy_mask, valid_vocab: Optional[int] = None,
-                         vocab: Optional[int] = None, keep_scores: bool = False,
-                         outputs: Optional[Dict[str, torch.Tensor]] = None, workspace=None,
-                         stage_events: Optional[Sequence] = None, stream=None) -> Dict[str, torch.Tensor]:
-    """One draft block.  conv_base [T, H]; conv_delta [N, T, G] (rows may be
-    strided: one side of the packed projection).  Returns a dict with
-    conv_out, ids, unary, tokens, q (and scores when keep_scores)."""
-    B, H, K = cfg.block_size, cfg.hidden_size, cfg.selector_top_k
-    S = B - 1
-    N = x.shape[0]
-    R = N // B
-    vocab = logits.shape[1] if vocab is None else vocab
-    valid_vocab = vocab if valid_vocab is None else valid_vocab
-    dev = x.device
-    _need_inner_contiguous(conv_delta, "conv_delta")
-    if logits.stride(-1) != 1:
-        raise ValueError("logits rows must be contiguous")
-    o = dict(outputs or {})
-    o.setdefault("conv_out", torch.empty_like(x))
-    o.setdefault("ids", torch.empty((R, S, K), dtype=torch.int64, device=dev))
-    o.setdefault("unary", torch.empty((R, S, K), dtype=torch.float32, device=dev))
-    o.setdefault("tokens", torch.empty((R, S), dtype=torch.int64, device=dev))
-    o.setdefault("q", torch.empty((R, S, K), dtype=torch.float32, device=dev))
-    if keep_scores:
-        o.setdefault("scores", torch.empty((R, S, K, K), dtype=torch.float32, device=dev))
-    if workspace is None:
-        nbytes = propose_block_workspace_size(cfg, max(R, 1), valid_vocab)
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    ev_arr = None
-    if stage_events is not None:
-        ev_arr = (ctypes.c_void_p * 8)(*[ctypes.c_void_p(e.cuda_event) for e in stage_events])
-    args = BlockArgs(
-        _p(x), _p(conv_base), _p(conv_delta), conv_delta.stride(0),
-        _p(logits), logits.stride(0), vocab, valid_vocab,
-        _p(anchor), _p(sel_a), _p(sel_b), _p(proj),
-        _p(uniforms), _p(temperatures), _p(greedy_mask),
-        _p(o["conv_out"]), _p(o["ids"]), _p(o["unary"]), _p(o["tokens"]), _p(o["q"]), _p(o.get("scores")),
-        _p(workspace), workspace.numel(),
-        ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None,
-        R, _dtype_code(x))
-    _check(lib().dflash_propose_block(ctypes.byref(cfg), ctypes.byref(args), _stream(stream)))
-    return o
+class ProposeBlock:
+    """Marshalled arguments of dflash_propose_block on one fixed set of
+    buffers: built once, then each call only hands the prepared struct to the
+    library (what a serving loop whose buffers stay put does every step).
+    Inputs as for dflash_propose_block; the outputs dict and the workspace are
+    allocated here unless given, and are rewritten by every call."""
+
+    def __init__(self, cfg: DraftConfig, *, x, conv_base, conv_delta, logits, anchor, sel_a, sel_b, proj,
+                 uniforms, temperatures, greedy_mask, valid_vocab: Optional[int] = None,
+                 vocab: Optional[int] = None, keep_scores: bool = False,
+                 outputs: Optional[Dict[str, torch.Tensor]] = None, workspace=None):
+        B, K = cfg.block_size, cfg.selector_top_k
+        S = B - 1
+        N = x.shape[0]
+        R = N // B
+        vocab = logits.shape[1] if vocab is None else vocab
+        valid_vocab = vocab if valid_vocab is None else valid_vocab
+        dev = x.device
+        _need_inner_contiguous(conv_delta, "conv_delta")
+        if logits.stride(-1) != 1:
+            raise ValueError("logits rows must be contiguous")
+        o = dict(outputs or {})
+        shapes = {"conv_out": (tuple(x.shape), x.dtype), "ids": ((R, S, K), torch.int64),
+                  "unary": ((R, S, K), torch.float32), "tokens": ((R, S), torch.int64),
+                  "q": ((R, S, K), torch.float32)}
+        if keep_scores:
+            shapes["scores"] = ((R, S, K, K), torch.float32)
+        for k, (shape, dt) in shapes.items():
+            if k not in o:
+                o[k] = torch.empty(shape, dtype=dt, device=dev)
+        if workspace is None:
+            nbytes = propose_block_workspace_size(cfg, max(R, 1), valid_vocab)
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        self.outputs = o
+        # the struct holds raw pointers: keep every tensor it names alive
+        self._keep = (x, conv_base, conv_delta, logits, anchor, sel_a, sel_b, proj, uniforms, temperatures,
+                      greedy_mask, workspace)
+        self._ev = None
+        self._cfg = cfg
+        self._args = BlockArgs(
+            _p(x), _p(conv_base), _p(conv_delta), conv_delta.stride(0),
+            _p(logits), logits.stride(0), vocab, valid_vocab,
+            _p(anchor), _p(sel_a), _p(sel_b), _p(proj),
+            _p(uniforms), _p(temperatures), _p(greedy_mask),
+            _p(o["conv_out"]), _p(o["ids"]), _p(o["unary"]), _p(o["tokens"]), _p(o["q"]), _p(o.get("scores")),
+            _p(workspace), workspace.numel(), None, R, _dtype_code(x))
+        self._cfg_ref = ctypes.byref(cfg)
+        self._args_ref = ctypes.byref(self._args)
+        self._fn = lib().dflash_propose_block
+
+    @staticmethod
+    def event_array(stage_events: Sequence):
+        """8 entries (torch.cuda.Event or None: that record is skipped) as the
+        host array dflash_block_args.stage_events points to."""
+        return (ctypes.c_void_p * 8)(*[None if e is None else e.cuda_event for e in stage_events])
+
+    def __call__(self, stream_handle=None, stage_events=None) -> Dict[str, torch.Tensor]:
+        """stream_handle: a raw HIP stream (``torch.cuda.Stream.cuda_stream``)
+        or None for torch's current stream; stage_events: None or an array
+        from ``event_array``."""
+        if stream_handle is None:
+            stream_handle = torch.cuda.current_stream().cuda_stream
+        if stage_events is not self._ev:
+            self._ev = stage_events
+            self._args.stage_events = None if stage_events is None else ctypes.cast(stage_events, ctypes.c_void_p)
+        st = self._fn(self._cfg_ref, self._args_ref, stream_handle)
+        if st != DFLASH_OK:
+            raise DFlashError(st, last_error())
+        return self.outputs
+
+
+def dflash_propose_block(cfg: DraftConfig, *, stage_events: Optional[Sequence] = None, stream=None,
+                         **kw) -> Dict[str, torch.Tensor]:
+    """One draft block.  x [n_req*B, H]; conv_base [T, H]; conv_delta
+    [N, T, G] (rows may be strided: one side of the packed projection);
+    logits [n_req*(B-1), >= vocab]; anchor [n_req]; sel_a, sel_b [V, r];
+    proj [r, H]; uniforms [n_req, B-1]; temperatures, greedy_mask [n_req].
+    Keywords of ProposeBlock besides.  Returns a dict with conv_out, ids,
+    unary, tokens, q (and scores when keep_scores)."""
+    call = ProposeBlock(cfg, **kw)
+    ev = None if stage_events is None else ProposeBlock.event_array(stage_events)
+    return call(None if stream is None else stream.cuda_stream, ev)

@@ -4,15 +4,15 @@
 // excerpt of the grouped conv):
 //   out[i,c] = sum_{t < T, t <= i mod B} (base[t,c] + delta[i,t,c/gs]) * x[i-t,c]
 //
-// HBM-bound stream: each input row is read once, each output row written once.
-// A thread owns one 16-byte channel vector (8 bf16 / 4 fp32 channels) of one
-// run of consecutive tokens inside one block and walks the run in token order,
-// keeping the last T-1 input vectors in registers as the tap history, so that
-// x is fetched from memory once per token (plus a T-1 token halo when a block
-// is split into several runs to give small batches enough threads).  Lanes of
-// a wave hold consecutive channel vectors of the same token, so every load and
-// store of a wave is one contiguous 1 KiB (bf16) segment.  The static kernel
-// base[t, c] is loaded once per thread and reused for the whole run.
+// HBM-bound stream: each input row is read once from HBM, each output row
+// written once.  A thread owns one 16-byte channel vector (8 bf16 / 4 fp32
+// channels) of a short run of consecutive tokens inside one block.  It loads
+// the run's input rows plus a T-1 token halo (cache hits: the neighbouring
+// run's thread reads the same rows), the run's dynamic coefficients and the
+// static kernel rows in one batch, then computes every token of the run from
+// registers.  Lanes of a wave hold consecutive channel vectors of the same
+// token, so every load and store of a wave is one contiguous 1 KiB (bf16)
+// segment.
 #include "dflash.h"
 #include "dflash_internal.h"
 
@@ -20,6 +20,7 @@ namespace dflash {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kRun = 4;   // tokens per thread in the fixed-tap kernels
 
 template <typename TIO>
 __device__ __forceinline__ void load_vec(const TIO* p, float (&o)[Elem<TIO>::kVec]) {
@@ -61,13 +62,21 @@ __device__ __forceinline__ void add_delta(const TIO* drow, int t, int groups, in
   }
 }
 
-// TAPS > 0: compile-time tap count with the register tap history.
+// TAPS <= 8: compile-time tap count.  A thread owns kRun consecutive tokens
+// of one block (fewer at the block's end) for one channel vector.  Every load
+// it needs -- the kRun + TAPS - 1 input rows of its window, the kRun x TAPS
+// dynamic coefficients and the TAPS static rows -- is issued before the first
+// multiply, with addresses clamped into the block, so a thread waits for one
+// memory round trip instead of one per token.  Window rows before the block
+// start or after its last token are loaded from a clamped address and never
+// used: their taps are masked by the block-causal condition t <= i mod B.
 template <typename TIO, int TAPS, bool ONE_GROUP>
 __global__ __launch_bounds__(kThreads) void conv_kernel(const TIO* __restrict__ x,
                                                         const TIO* __restrict__ base,
                                                         const TIO* __restrict__ delta,
                                                         TIO* __restrict__ out, ConvGeom g) {
   constexpr int VEC = Elem<TIO>::kVec;
+  constexpr int W = kRun + TAPS - 1;            // window rows j0-TAPS+1 .. j0+kRun-1
   const int64_t unit = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (unit >= g.units) return;
 
@@ -77,53 +86,52 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const TIO* __restrict__ 
   const int64_t blk = rest / g.runs_per_block;
   const int c0 = v * VEC;
   const int H = g.hidden;
-  const int j0 = run * g.run_len;
-  const int j1 = min(j0 + g.run_len, g.block_size);
+  const int j0 = run * kRun;
+  const int jlast = min(j0 + kRun, g.block_size) - 1;
   const int64_t row0 = blk * g.block_size;
 
-  float bt[TAPS][VEC];
+  uint4 xw[W];
 #pragma unroll
-  for (int t = 0; t < TAPS; ++t) load_vec<TIO>(base + (int64_t)t * H + c0, bt[t]);
-
-  float hist[TAPS > 1 ? TAPS - 1 : 1][VEC];   // hist[t-1] = x[i - t]
+  for (int w = 0; w < W; ++w) {
+    const int jj = min(max(j0 - (TAPS - 1) + w, 0), jlast);
+    xw[w] = *reinterpret_cast<const uint4*>(x + (row0 + jj) * H + c0);
+  }
+  uint4 bw[TAPS];
 #pragma unroll
-  for (int t = 1; t < TAPS; ++t) {
-    const int jj = j0 - t;
-    if (jj >= 0) {
-      load_vec<TIO>(x + (row0 + jj) * H + c0, hist[t - 1]);
-    } else {
+  for (int t = 0; t < TAPS; ++t) bw[t] = *reinterpret_cast<const uint4*>(base + (int64_t)t * H + c0);
+  // One coefficient per (token, tap) when the vector lies in one group;
+  // otherwise the per-channel coefficients are read where they are used.
+  float dv[kRun][TAPS];
+  if (ONE_GROUP) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) hist[t - 1][e] = 0.f;
+    for (int u = 0; u < kRun; ++u) {
+      const TIO* drow = delta + (row0 + min(j0 + u, jlast)) * g.delta_row_stride;
+#pragma unroll
+      for (int t = 0; t < TAPS; ++t) dv[u][t] = Elem<TIO>::load(drow + (int64_t)t * g.groups + c0 / g.group_size);
     }
   }
 
-  for (int j = j0; j < j1; ++j) {
-    const int64_t i = row0 + j;
-    float xc[VEC];
-    load_vec<TIO>(x + i * H + c0, xc);
-    const TIO* drow = delta + i * g.delta_row_stride;
-    float coef[VEC], acc[VEC];
-    add_delta<TIO, ONE_GROUP, VEC>(drow, 0, g.groups, c0, g.group_size, bt[0], coef);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = coef[e] * xc[e];
+  for (int u = 0; u < kRun; ++u) {
+    const int j = j0 + u;
+    if (j > jlast) break;
+    float acc[VEC];
 #pragma unroll
-    for (int t = 1; t < TAPS; ++t) {
-      if (j >= t) {   // taps that reach before the block start are zero
-        add_delta<TIO, ONE_GROUP, VEC>(drow, t, g.groups, c0, g.group_size, bt[t], coef);
+    for (int t = 0; t < TAPS; ++t) {
+      if (t > j) break;                           // taps that reach before the block start are zero
+      float bt[VEC], xv[VEC], coef[VEC];
+      unpack16(bw[t], bt);
+      unpack16(xw[u + TAPS - 1 - t], xv);
+      if (ONE_GROUP) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = fmaf(coef[e], hist[t - 1][e], acc[e]);
+        for (int e = 0; e < VEC; ++e) coef[e] = bt[e] + dv[u][t];
+      } else {
+        add_delta<TIO, false, VEC>(delta + (row0 + j) * g.delta_row_stride, t, g.groups, c0, g.group_size, bt, coef);
       }
-    }
-    store_vec(out + i * H + c0, acc);
 #pragma unroll
-    for (int t = TAPS - 2; t >= 1; --t) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) hist[t][e] = hist[t - 1][e];
+      for (int e = 0; e < VEC; ++e) acc[e] = (t == 0) ? coef[e] * xv[e] : fmaf(coef[e], xv[e], acc[e]);
     }
-    if (TAPS > 1) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) hist[0][e] = xc[e];
-    }
+    store_vec(out + (row0 + j) * H + c0, acc);
   }
 }
 
@@ -210,15 +218,17 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
   g.delta_row_stride = a.delta_row_stride;
   g.nvec = a.hidden / vec;
   const int64_t nblocks = a.n_tokens / a.block_size;
-  // Split blocks into shorter token runs until the launch has enough threads
-  // to cover the chip (each run re-reads a T-1 token halo from cache).
-  int run = a.block_size;
-  const int min_run = a.taps > 2 ? a.taps : 2;
-  while (run > min_run &&
-         nblocks * ((a.block_size + run - 1) / run) * (int64_t)g.nvec < (int64_t)256 * 1024)
-    run = (run + 1) / 2;
-  g.run_len = run;
-  g.runs_per_block = (a.block_size + run - 1) / run;
+  if (a.taps <= 8) {
+    g.run_len = kRun;
+  } else {
+    // Any tap count: split blocks into shorter token runs until the launch
+    // has enough threads to cover the chip.
+    int run = a.block_size;
+    while (run > 2 && nblocks * ((a.block_size + run - 1) / run) * (int64_t)g.nvec < (int64_t)256 * 1024)
+      run = (run + 1) / 2;
+    g.run_len = run;
+  }
+  g.runs_per_block = (a.block_size + g.run_len - 1) / g.run_len;
   g.units = nblocks * g.runs_per_block * g.nvec;
   if (g.units == 0) return hipSuccess;
   return a.dtype == DFLASH_BF16 ? launch_dtype<uint16_t>(a, g, stream)

@@ -182,8 +182,14 @@ int dflash_walk(const float* scores, const int64_t* ids, const float* uniforms,
  *   transform + top-K over the slot logits ->
  *   projection of each slot's hidden = conv-output row r*B + 1 + s (block
  *   position 0 is the verified anchor) -> lattice -> walk,
- * on one stream.  Results equal the chain dflash_conv -> dflash_topk ->
- * dflash_lattice -> dflash_walk on the same inputs bit for bit.
+ * ordered on `stream` as one unit.  The conv and the projection, which do
+ * not depend on the top-K, run beside it on an auxiliary stream of the
+ * library (one per host thread and device, created on the first call with
+ * default priority and kept until the process ends) that waits for the work
+ * already on `stream` and that `stream` waits for before the lattice: the
+ * call's outputs are ready for work enqueued on `stream` after it.  Results
+ * equal the chain dflash_conv -> dflash_topk -> dflash_lattice -> dflash_walk
+ * on the same inputs bit for bit.
  * cfg: conv and selector must both be enabled; cfg->hidden_size = H. */
 typedef struct {
   const void* x;              /* [n_req*B, H] dtype */
@@ -210,8 +216,9 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   /* NULL, or 8 hipEvent_t handles (host array): events[2*k] is recorded before
-   * and events[2*k+1] after stage k on `stream`; stages: 0 conv, 1 top-K,
-   * 2 projection, 3 lattice + walk.  For timing only. */
+   * and events[2*k+1] after stage k on the stream that runs it; stages:
+   * 0 conv and 2 projection (auxiliary stream), 1 top-K and 3 lattice + walk
+   * (`stream`).  A NULL entry skips that record.  For timing only. */
   void* const* stage_events;
   int32_t n_req;
   int32_t dtype;

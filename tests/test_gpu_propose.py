@@ -148,6 +148,30 @@ def test_end_to_end_against_oracle(name, reqs):
     print(f"[e2e] {name}: decisions inside the rounding band: {near}", flush=True)
 
 
+def test_auxiliary_stream_is_ordered_with_the_callers_stream():
+    """The conv and the projection run on the library's auxiliary stream: they
+    must see inputs written on the caller's stream just before the call, and
+    work the caller enqueues on that stream after it must see every output."""
+    require_gpu()
+    w = W.WORKLOADS["bf16_b16_v151936"]
+    inp = W.make_inputs(w, device=DEV)
+    ref = _propose(w, inp)
+    x_late = torch.zeros_like(inp["x"])
+    busy = torch.empty(1 << 28, dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    say("dflash_propose_block on a side stream after a late input write")
+    with torch.cuda.stream(side):
+        for _ in range(4):
+            busy.fill_(1)                 # keeps the side stream busy before the write
+        x_late.copy_(inp["x"])
+        out = _propose(w, dict(inp, x=x_late))
+        got = {k: out[k].clone() for k in ("conv_out", "ids", "scores", "tokens", "q")}
+    torch.cuda.synchronize()
+    for k, v in got.items():
+        assert torch.equal(v, ref[k]), k
+
+
 def test_stage_events_are_recorded():
     require_gpu()
     w = W.WORKLOADS["bf16_b16_v151936"]
@@ -163,6 +187,20 @@ def test_stage_events_are_recorded():
     assert all(t >= 0 for t in times)
     assert times[1] > 0
     assert out["tokens"].shape == (w.n_req, w.slots)
+    # NULL entries are skipped: only the top-K pair, through a prepared call
+    call = D.ProposeBlock(_cfg(w), x=inp["x"], conv_base=inp["base"][0], conv_delta=inp["delta"][:, 0],
+                          logits=inp["logits"], anchor=inp["anchor"], sel_a=inp["sel_a"], sel_b=inp["sel_b"],
+                          proj=inp["proj"], uniforms=inp["uniforms"], temperatures=inp["temperatures"],
+                          greedy_mask=inp["greedy_mask"], valid_vocab=w.valid_vocab)
+    pair = [None, None, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] + [None] * 4
+    for e in pair[2:4]:
+        e.record()
+    torch.cuda.synchronize()
+    got = call(stage_events=D.ProposeBlock.event_array(pair))
+    got = call(stage_events=D.ProposeBlock.event_array(pair))
+    torch.cuda.synchronize()
+    assert pair[2].elapsed_time(pair[3]) > 0
+    assert torch.equal(got["tokens"], out["tokens"]) and torch.equal(got["q"], out["q"])
 
 
 def test_zero_requests_is_a_no_op():
