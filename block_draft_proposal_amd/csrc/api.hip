@@ -180,9 +180,9 @@ int fork_join(ForkJoin** out, const char* who) {
     if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
     if (e != hipSuccess) {
-      if (n.join) hipEventDestroy(n.join);
-      if (n.fork) hipEventDestroy(n.fork);
-      if (n.aux) hipStreamDestroy(n.aux);
+      if (n.join) (void)hipEventDestroy(n.join);   // best effort: the set-up error is the one reported
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.aux) (void)hipStreamDestroy(n.aux);
       return fail(DFLASH_ERR_LAUNCH, "%s: auxiliary stream set-up failed: %s", who, hipGetErrorString(e));
     }
     f = n;

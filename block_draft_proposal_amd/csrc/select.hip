@@ -236,40 +236,6 @@ __device__ __forceinline__ int walk_decide(float v, int lane, int K, bool greedy
   return cnt < K - 1 ? cnt : K - 1;
 }
 
-// The same decision for one lattice row evaluated by a single thread:
-// row[0..K) in, q[0..K) out (q may alias row).  Same operations in the same
-// order as walk_decide, so the two give identical bits.
-__device__ __forceinline__ int row_decide(const float* row, float* q, int K, bool greedy, float temp, float u) {
-  if (greedy) {
-    float best = row[0];
-    int idx = 0;
-    for (int c = 1; c < K; ++c) {
-      const float x = row[c];
-      if (x > best) { best = x; idx = c; }
-    }
-    for (int c = 0; c < K; ++c) q[c] = (c == idx) ? 1.f : 0.f;
-    return idx;
-  }
-  const float t = fmaxf(temp, 1e-5f);
-  float mx = row[0] / t;
-  for (int c = 1; c < K; ++c) mx = fmaxf(mx, row[c] / t);
-  float total = 0.f;
-  for (int c = 0; c < K; ++c) {
-    const float e = (float)exp((double)(row[c] / t - mx));
-    q[c] = e;
-    total += e;                                                   // left to right
-  }
-  float cdf = 0.f;
-  int cnt = 0;
-  for (int c = 0; c < K; ++c) {
-    const float p = q[c] / total;
-    q[c] = p;
-    cdf += p;                                                     // C_c left to right
-    cnt += (u >= cdf) ? 1 : 0;
-  }
-  return cnt < K - 1 ? cnt : K - 1;
-}
-
 constexpr int kWalkLdsBytes = 64 * 1024;   // scores + ids + uniforms of a request, staged when they fit
 
 __device__ __forceinline__ size_t walk_stage_bytes(int slots, int K) {
@@ -321,39 +287,50 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(const float* __restrict_
   }
 }
 
-// Lattice + walk for one request in one workgroup, when the request's whole
-// lattice and its staging fit in LDS.  Same per-entry arithmetic as
-// lattice_block (u summed over the projection slices in order, w = A * u,
-// fma chain over k from 0, + unary) and the same walk_decide, so the result
-// is bit-identical to lattice_kernel followed by walk_kernel.
+// Lattice + walk for one request in one workgroup of 1024 threads, when the
+// request's whole lattice and its staging fit in LDS.  Same per-entry
+// arithmetic as lattice_block (u summed over the projection slices in order,
+// w = A * u, fma chain over k from 0, + unary) and the same decision
+// arithmetic as walk_decide, so the result is bit-identical to lattice_kernel
+// followed by walk_kernel.  Phases, each one round of global loads or pure
+// LDS work:
+//   1. ids of every slot and its predecessor, u, unary, uniforms -> LDS
+//   2. w = A[pred] (.) u (fp32) and the B[cand] rows -> LDS
+//   3. one thread per lattice entry: its fma chain over k
+//   4. every row's decision, which does not depend on the path: row maxima
+//      and sums stay sequential per row, the fp64 exponentials are spread
+//      over the entries
+//   5. one wave follows the chosen indices from row 0.
 // LDS layout: pred ids [S][K], cand ids [S][K] (int64), u [S][r], w [S][K][r+1]
-// (fp32), B rows [S][r][KB] (storage dtype, padded to the row width KB),
-// scores [S][K][K] (then q), uniforms [S], chosen index per row [S][K].
+// (fp32), B rows [S][r][K] (storage dtype), unary [S][K], scores [S][K][K]
+// (then q), exponentials [S][K][K], row maxima [S][K], uniforms [S], chosen
+// index per row [S][K].
+constexpr int kLWThreads = 1024;
+
 struct LatticeWalkLds {
-  size_t pred, cand, u, w, b, sc, un, bytes;
+  size_t pred, cand, u, w, b, unary, sc, e, mx, un, next, bytes;
 };
-// K rounded up to the kernel's row width (4, 8, 16 or 32).
-__host__ __device__ inline int k_bucket(int K) { return K <= 4 ? 4 : K <= 8 ? 8 : K <= 16 ? 16 : 32; }
 
 __host__ __device__ inline LatticeWalkLds lattice_walk_layout(int S, int K, int r, int elem) {
   LatticeWalkLds L;
-  const int KB = k_bucket(K);
   size_t o = 0;
-  L.pred = o; o += (size_t)S * K * 8;
-  L.cand = o; o += (size_t)S * K * 8;
-  L.u = o;    o += (size_t)S * r * 4;
-  L.w = o;    o += (size_t)S * K * (r + 1) * 4;
-  o = (o + 15) & ~(size_t)15;
-  L.b = o;    o += ((size_t)S * r * KB * elem + 15) & ~(size_t)15;   // rows padded to KB
-  L.sc = o;   o += (size_t)S * K * K * 4;
-  L.un = o;   o += (size_t)S * 4;
-  o += (size_t)S * K * 4;                                   // chosen index per row
+  L.pred = o;  o += (size_t)S * K * 8;
+  L.cand = o;  o += (size_t)S * K * 8;
+  L.u = o;     o += (size_t)S * r * 4;
+  L.w = o;     o += (size_t)S * K * (r + 1) * 4;
+  L.b = o;     o += ((size_t)S * r * K * elem + 3) & ~(size_t)3;
+  L.unary = o; o += (size_t)S * K * 4;
+  L.sc = o;    o += (size_t)S * K * K * 4;
+  L.e = o;     o += (size_t)S * K * K * 4;
+  L.mx = o;    o += (size_t)S * K * 4;
+  L.un = o;    o += (size_t)S * 4;
+  L.next = o;  o += (size_t)S * K * 4;
   L.bytes = o;
   return L;
 }
 
-template <typename TIO, int KB>   // KB: K rounded up to 4, 8, 16 or 32
-__global__ __launch_bounds__(kThreads) void lattice_walk_kernel(
+template <typename TIO>
+__global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
     const int64_t* __restrict__ ids, const float* __restrict__ unary, const int64_t* __restrict__ anchor,
     const TIO* __restrict__ A, const TIO* __restrict__ B, const float* __restrict__ u_parts, int32_t ksplit,
     int32_t slots, int32_t K, int32_t r, int64_t vocab, int32_t n_rows, const float* __restrict__ uniforms,
@@ -369,38 +346,47 @@ __global__ __launch_bounds__(kThreads) void lattice_walk_kernel(
   float* s_u = reinterpret_cast<float*>(lw_smem + L.u);
   float* s_w = reinterpret_cast<float*>(lw_smem + L.w);
   TIO* s_b = reinterpret_cast<TIO*>(lw_smem + L.b);
+  float* s_unary = reinterpret_cast<float*>(lw_smem + L.unary);
   float* s_sc = reinterpret_cast<float*>(lw_smem + L.sc);
+  float* s_e = reinterpret_cast<float*>(lw_smem + L.e);
+  float* s_mx = reinterpret_cast<float*>(lw_smem + L.mx);
   float* s_un = reinterpret_cast<float*>(lw_smem + L.un);
+  int* s_next = reinterpret_cast<int*>(lw_smem + L.next);
   const int64_t row0 = (int64_t)req * S;            // first slot row of this request
   const int wstride = r + 1;
+  const FastDiv div_k(K), div_r(r);                 // every index below is < 2^16 (LDS bound)
 
-  // ---- ids, u (projection slices summed in order), uniforms -------------
-  for (int i = tid; i < S * K; i += kThreads) {
-    const int s = i / K, j = i % K;
+  // ---- 1. ids, u (projection slices summed in order), unary, uniforms ----
+  for (int i = tid; i < S * K; i += kLWThreads) {
+    const int s = div_k.quot(i), j = i - s * K;
     s_pred[i] = (s == 0) ? anchor[req] : ids[(row0 + s - 1) * K + j];
-    s_cand[i] = ids[(row0 + s) * K + j];
+    s_cand[i] = ids[row0 * K + i];
+    s_unary[i] = unary[row0 * K + i];
   }
-  for (int i = tid; i < S * r; i += kThreads) s_u[i] = sum_proj_slices(u_parts, ksplit, n_rows, r, row0 + i / r, i % r);
-  for (int i = tid; i < S; i += kThreads) s_un[i] = uniforms[row0 + i];
+  for (int i = tid; i < S * r; i += kLWThreads) {
+    const int s = div_r.quot(i);
+    s_u[i] = sum_proj_slices(u_parts, ksplit, n_rows, r, row0 + s, i - s * r);
+  }
+  for (int i = tid; i < S; i += kLWThreads) s_un[i] = uniforms[row0 + i];
   __syncthreads();
 
-  // ---- gather: w = A[pred] (.) u (fp32), B[cand] rows ------------------
+  // ---- 2. gather: w = A[pred] (.) u (fp32), B[cand] rows ------------------
   // 16-byte pieces of the table rows (r is a multiple of VEC, rows 16-byte
   // aligned).  Loads are unconditional (indices clamped into range) so that
   // every thread issues all of its loads before the first use; out-of-range
   // ids become NaN afterwards.
   {
     constexpr int VEC = Elem<TIO>::kVec;
-    constexpr int kPer = 8;                          // pieces per thread per pass
+    constexpr int kPer = 2;                          // pieces per thread per pass
     const int pieces_per_row = r / VEC;
     const int n_pieces = S * K * pieces_per_row;     // per table
     const int total = 2 * n_pieces;
-    const FastDiv div_ppr(pieces_per_row), div_k(K);
-    for (int base = 0; base < total; base += kThreads * kPer) {
+    const FastDiv div_ppr(pieces_per_row);
+    for (int base = 0; base < total; base += kLWThreads * kPer) {
       uint4 raw[kPer];
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
-        const int i = min(base + q * kThreads + tid, total - 1);
+        const int i = min(base + q * kLWThreads + tid, total - 1);
         const bool is_b = i >= n_pieces;
         const int ii = is_b ? i - n_pieces : i;
         const int sj = div_ppr.quot(ii), v = ii - sj * pieces_per_row;
@@ -410,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void lattice_walk_kernel(
       }
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
-        const int i = base + q * kThreads + tid;
+        const int i = base + q * kLWThreads + tid;
         if (i >= total) continue;
         const bool is_b = i >= n_pieces;
         const int ii = is_b ? i - n_pieces : i;
@@ -423,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void lattice_walk_kernel(
         for (int e = 0; e < VEC; ++e) {
           const int k = v * VEC + e;
           if (is_b) {
-            s_b[((size_t)s * r + k) * KB + j] = ok ? piece[e] : Elem<TIO>::nan_value();
+            s_b[((size_t)s * r + k) * K + j] = ok ? piece[e] : Elem<TIO>::nan_value();
           } else {
             const float a = ok ? Elem<TIO>::to_f32(piece[e]) : __builtin_nanf("");
             s_w[sj * wstride + k] = a * s_u[s * r + k];   // A[p] (.) project(h)
@@ -434,46 +420,70 @@ __global__ __launch_bounds__(kThreads) void lattice_walk_kernel(
   }
   __syncthreads();
 
-  // ---- every K x K block: a thread evaluates one row (s, j) as KB
-  // independent fma chains over k (each entry the same chain lattice_block
-  // runs); B rows are read as whole padded rows, padding columns discarded --
-  for (int sj = tid; sj < S * K; sj += kThreads) {
-    const int s = sj / K;
+  // ---- 3. one thread per entry (s, j, c): fma chain over k from 0 ---------
+  const int n_entries = S * K * K;
+  for (int e = tid; e < n_entries; e += kLWThreads) {
+    const int sj = div_k.quot(e), c = e - sj * K;
+    const int s = div_k.quot(sj);
     const float* w = s_w + sj * wstride;
-    const TIO* b = s_b + (size_t)s * r * KB;
-    float acc[KB];
-#pragma unroll
-    for (int c = 0; c < KB; ++c) acc[c] = 0.f;
-#pragma unroll 4
-    for (int k = 0; k < r; ++k) {
-      const float wk = w[k];
-      TIO bv[KB];
-      __builtin_memcpy(bv, __builtin_assume_aligned(b + (size_t)k * KB, sizeof(TIO) * KB >= 16 ? 16 : 8), sizeof(bv));
-#pragma unroll
-      for (int c = 0; c < KB; ++c) acc[c] = fmaf(wk, Elem<TIO>::to_f32(bv[c]), acc[c]);
-    }
-#pragma unroll
-    for (int c = 0; c < KB; ++c) {
-      if (c < K) {
-        const float v = acc[c] + unary[(row0 + s) * K + c];
-        s_sc[sj * K + c] = v;
-        if (scores_out) scores_out[(row0 * K + sj) * K + c] = v;
+    const TIO* b = s_b + (size_t)s * r * K + c;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int k = 0; k < r; ++k) acc = fmaf(w[k], Elem<TIO>::to_f32(b[k * K]), acc);
+    const float v = acc + s_unary[s * K + c];
+    s_sc[e] = v;
+    if (scores_out) scores_out[row0 * K * K + e] = v;
+  }
+  __syncthreads();
+
+  // ---- 4. every row's decision (q written over the row's scores) ----------
+  const bool greedy = greedy_mask[req] != 0;       // uniform over the workgroup
+  const float temp = temperatures[req];
+  if (greedy) {
+    for (int sj = tid; sj < S * K; sj += kLWThreads) {
+      float* row = s_sc + sj * K;
+      // first maximum in candidate order = lowest index among ties
+      float best = row[0];
+      int idx = 0;
+      for (int c = 1; c < K; ++c) {
+        const float x = row[c];
+        if (x > best) { best = x; idx = c; }
       }
+      for (int c = 0; c < K; ++c) row[c] = (c == idx) ? 1.f : 0.f;
+      s_next[sj] = idx;
+    }
+  } else {
+    const float t = fmaxf(temp, 1e-5f);
+    for (int sj = tid; sj < S * K; sj += kLWThreads) {
+      const float* row = s_sc + sj * K;
+      float mx = row[0] / t;
+      for (int c = 1; c < K; ++c) mx = fmaxf(mx, row[c] / t);
+      s_mx[sj] = mx;
+    }
+    __syncthreads();
+    // exp rounded once to fp32 (from the fp64 exponential)
+    for (int e = tid; e < n_entries; e += kLWThreads) s_e[e] = (float)exp((double)(s_sc[e] / t - s_mx[div_k.quot(e)]));
+    __syncthreads();
+    for (int sj = tid; sj < S * K; sj += kLWThreads) {
+      float* row = s_sc + sj * K;
+      const float* ex = s_e + sj * K;
+      float total = 0.f;
+      for (int c = 0; c < K; ++c) total += ex[c];                   // left to right
+      const float u = s_un[div_k.quot(sj)];
+      float cdf = 0.f;
+      int cnt = 0;
+      for (int c = 0; c < K; ++c) {
+        const float p = ex[c] / total;
+        row[c] = p;
+        cdf += p;                                                   // C_c left to right
+        cnt += (u >= cdf) ? 1 : 0;
+      }
+      s_next[sj] = cnt < K - 1 ? cnt : K - 1;
     }
   }
   __syncthreads();
 
-  // ---- walk: every row's decision is independent of the path, so all S*K
-  // rows are decided in parallel (q written over the row); then one wave
-  // follows the chosen indices from row 0 ------------------------------------
-  const bool greedy = greedy_mask[req] != 0;
-  const float temp = temperatures[req];
-  int* s_next = reinterpret_cast<int*>(s_un + S);
-  for (int sj = tid; sj < S * K; sj += kThreads) {
-    float* row = s_sc + (size_t)sj * K;
-    s_next[sj] = row_decide(row, row, K, greedy, temp, s_un[sj / K]);
-  }
-  __syncthreads();
+  // ---- 5. walk: follow the chosen indices from row 0 ----------------------
   if (tid >= 64) return;
   const int lane = tid;
   int prev = 0;
@@ -589,23 +599,16 @@ hipError_t launch_lattice_walk(const SelectArgs& a, const ProjPlan& p, const Wal
   if (!lattice_walk_fits(a)) return hipErrorInvalidValue;
   const size_t lds = lattice_walk_lds_bytes(a.slots, a.top_k, a.rank, a.dtype);
   const int n_rows = a.n_req * a.slots;
-#define DFLASH_LW(TIO, KB)                                                                                    \
-  hipLaunchKernelGGL((lattice_walk_kernel<TIO, KB>), dim3(a.n_req), dim3(kThreads), lds, stream, a.ids, a.unary, \
-                     a.anchor, static_cast<const TIO*>(a.sel_a), static_cast<const TIO*>(a.sel_b), a.u_parts,     \
-                     p.ksplit, a.slots, a.top_k, a.rank, a.vocab, n_rows, w.uniforms, w.temperatures, w.greedy,  \
-                     scores_out, w.tokens, w.q)
-#define DFLASH_LW_K(TIO)                     \
-  if (a.top_k <= 4) DFLASH_LW(TIO, 4);       \
-  else if (a.top_k <= 8) DFLASH_LW(TIO, 8);  \
-  else if (a.top_k <= 16) DFLASH_LW(TIO, 16); \
-  else DFLASH_LW(TIO, 32);
-  if (a.dtype == DFLASH_BF16) {
-    DFLASH_LW_K(uint16_t)
-  } else {
-    DFLASH_LW_K(float)
-  }
-#undef DFLASH_LW_K
-#undef DFLASH_LW
+  if (a.dtype == DFLASH_BF16)
+    hipLaunchKernelGGL((lattice_walk_kernel<uint16_t>), dim3(a.n_req), dim3(kLWThreads), lds, stream, a.ids, a.unary,
+                       a.anchor, static_cast<const uint16_t*>(a.sel_a), static_cast<const uint16_t*>(a.sel_b),
+                       a.u_parts, p.ksplit, a.slots, a.top_k, a.rank, a.vocab, n_rows, w.uniforms, w.temperatures,
+                       w.greedy, scores_out, w.tokens, w.q);
+  else
+    hipLaunchKernelGGL((lattice_walk_kernel<float>), dim3(a.n_req), dim3(kLWThreads), lds, stream, a.ids, a.unary,
+                       a.anchor, static_cast<const float*>(a.sel_a), static_cast<const float*>(a.sel_b), a.u_parts,
+                       p.ksplit, a.slots, a.top_k, a.rank, a.vocab, n_rows, w.uniforms, w.temperatures, w.greedy,
+                       scores_out, w.tokens, w.q);
   return hipGetLastError();
 }
 

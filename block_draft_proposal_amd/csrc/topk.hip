@@ -17,11 +17,14 @@
 //    and which is unique within a row.
 //  * A workgroup of 4 waves owns a row (or, when rows are very few, a segment
 //    of one; a small second kernel then merges segments).  The row is cut
-//    into wave-chunks of 4096 values dealt round-robin to the waves; every
-//    wave streams its chunks on its own -- 64 values per lane as eight
-//    16-byte loads, each wave load one contiguous 1 KiB, the next chunk's
-//    loads in flight while the current chunk is processed -- and keeps its
-//    own K best in LDS.  No workgroup barrier until the final merge.
+//    into group-chunks of 16384 values; inside one, the waves interleave at
+//    the granularity of one wave load (64 lanes x 16 bytes), so each wave
+//    holds 64 values per lane, as eight 16-byte loads, and the four waves
+//    split every group-chunk -- the row's partial last one included -- into
+//    equal quarters.  Waves stream on their own, the next group-chunk's
+//    loads in flight while the current one is processed, and each keeps its
+//    own K best in LDS.  No workgroup barrier until the final merge.  The
+//    logits are read once, with non-temporal loads.
 //  * Threshold: on a wave's first chunk, the K-th largest of its 64 lane
 //    maxima (found bit by bit with ballot counts; those K lanes hold K
 //    distinct values that reach it); afterwards a value must beat the wave's
@@ -29,7 +32,10 @@
 //  * bf16: while that threshold is a positive value, the filter runs on the
 //    raw bits (a positive bf16 read as int16 orders like its value), one
 //    packed signed max per two values; keys are built only for survivors.
-//    Otherwise (and for fp32) keys are built per value.
+//    Otherwise (and for fp32) keys are built per value.  Either way a lane
+//    first compares the maxima of groups of its registers with the
+//    threshold, and searches register by register only a group that holds
+//    a survivor (after the first chunks, most lanes hold none).
 //  * Survivors are compacted into LDS; the wave's sorted list is updated with
 //    ranks from a binary search in the held list plus a count among the new.
 //  * If a chunk yields more survivors than LDS holds (mass ties), an exact
@@ -47,13 +53,19 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kPerLane = 64;                   // values per lane per wave-chunk
-constexpr int kWaveChunk = 64 * kPerLane;      // 4096 values
+constexpr int kWaveChunk = 64 * kPerLane;      // 4096 values of one wave
+constexpr int kGroupChunk = kWaves * kWaveChunk;  // 16384 values of one workgroup
+// Elements between a lane's consecutive 16-byte vectors inside a group-chunk:
+// the waves interleave at 1 KiB (one wave load), so each wave load of the
+// four waves covers one contiguous 4 KiB (bf16) stretch.
+template <int VEC> constexpr int64_t vec_stride() { return (int64_t)kWaves * 64 * VEC; }
 constexpr int kWaveCap = 256;                  // LDS slots for one chunk's new candidates
 constexpr int kMaxK = DFLASH_MAX_TOP_K;
 constexpr int kMergeThreads = 256;
 constexpr uint32_t kIdMask = 0xffffffu;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, int64_t id) {
   return ((uint64_t)key << 24) | (uint64_t)(kIdMask - (uint32_t)id);
@@ -95,8 +107,9 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One lane's 64 values of a wave-chunk.  Value i (0..63) sits at
-// id = c_start + ((i / VEC) * 64 + lane) * VEC + i % VEC.
+// One lane's 64 values of a group-chunk.  With the lane base
+// lb = c_start + (wave * 64 + lane) * VEC, value i (0..63) sits at
+// id = lb + (i / VEC) * vec_stride<VEC>() + i % VEC.
 template <typename TIO> struct Chunk;
 
 template <> struct Chunk<uint16_t> {
@@ -106,28 +119,26 @@ template <> struct Chunk<uint16_t> {
   // `full` (wave-uniform): the whole wave-chunk lies below the logical vocab
   // end, so every load is unconditional and the key conversion branch-free
   // (keeps the wait for this chunk's loads from draining the prefetch).
-  __device__ void issue(const uint16_t* rowp, int64_t c_start, int64_t valid, int lane, bool full) {
-    if (full) {
-      const uint4* p = reinterpret_cast<const uint4*>(rowp + c_start) + lane;
-#pragma unroll
-      for (int l = 0; l < L; ++l) {
-        const uint4 r = p[l * 64];
-        w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
-      }
-    } else {
-#pragma unroll
-      for (int l = 0; l < L; ++l) {
-        const int64_t e0 = c_start + ((int64_t)l * 64 + lane) * VEC;
-        const uint4 r = (e0 + VEC <= valid) ? *reinterpret_cast<const uint4*>(rowp + e0) : make_uint4(0u, 0u, 0u, 0u);
-        w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
-      }
-    }
-  }
-  __device__ void issue_full(const uint16_t* rowp, int64_t c_start, int lane) {
-    const uint4* p = reinterpret_cast<const uint4*>(rowp + c_start) + lane;
+  // Partial group-chunk: vectors past the logical vocab end read as zero.
+  __device__ void issue(const uint16_t* rowp, int64_t lb, int64_t valid) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
-      const uint4 r = p[l * 64];
+      const int64_t e0 = lb + l * vec_stride<VEC>();
+      const uint4 r = (e0 + VEC <= valid) ? *reinterpret_cast<const uint4*>(rowp + e0) : make_uint4(0u, 0u, 0u, 0u);
+      w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
+    }
+  }
+  // A group-chunk of a row with valid >= VEC, by unconditional loads (so the
+  // wait for them is an exact in-order count): a vector past last_vec, the
+  // last whole vector below the logical end, re-reads that one instead; its
+  // values are replaced in make_keys.  In a whole group-chunk every vector
+  // lies at or below last_vec.
+  __device__ void issue_clamped(const uint16_t* rowp, int32_t lb, int32_t last_vec) {
+#pragma unroll
+    for (int l = 0; l < L; ++l) {
+      const int32_t e0 = min(lb + l * (int32_t)vec_stride<VEC>(), last_vec);
+      const u32x4 rv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowp + e0));   // streamed once
+      const uint4 r = make_uint4(rv.x, rv.y, rv.z, rv.w);
       w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
     }
   }
@@ -135,15 +146,11 @@ template <> struct Chunk<uint16_t> {
 #pragma unroll
     for (int j = 0; j < W; ++j) w[j] = bf16_key2(w[j]);
   }
-  __device__ void make_keys(const uint16_t* rowp, int64_t c_start, int64_t valid, int lane, bool full) {
-    if (full) {
-#pragma unroll
-      for (int j = 0; j < W; ++j) w[j] = bf16_key2(w[j]);
-      return;
-    }
+  // Keys of a partial group-chunk (issue() read the vectors below the end).
+  __device__ void make_keys(const uint16_t* rowp, int64_t lb, int64_t valid) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
-      const int64_t e0 = c_start + ((int64_t)l * 64 + lane) * VEC;
+      const int64_t e0 = lb + l * vec_stride<VEC>();
       if (e0 + VEC <= valid) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) w[l * 4 + q] = bf16_key2(w[l * 4 + q]);
@@ -165,15 +172,32 @@ template <> struct Chunk<uint16_t> {
     return max((uint32_t)m.x, (uint32_t)m.y);
   }
   // Calls f(key, value index) for every key >= tau (1 <= tau < 0x10000).
+  // Survivors are rare: the lane first tests the maxima of four groups of
+  // eight registers, and only a group holding one is searched register by
+  // register.
   template <class F> __device__ void for_each_ge(uint64_t tau, F&& f) const {
     const unsigned short t1 = (unsigned short)(tau - 1);
     const u16x2 t = {t1, t1};
+    u16x2 gm[4];
 #pragma unroll
-    for (int j = 0; j < W; ++j) {
-      const u16x2 d = __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, w[j]), t);
-      if (__builtin_bit_cast(uint32_t, d) != 0u) {
-        if (d.x) f(w[j] & 0xffffu, 2 * j);
-        if (d.y) f(w[j] >> 16, 2 * j + 1);
+    for (int g = 0; g < 4; ++g) {
+      gm[g] = __builtin_bit_cast(u16x2, w[8 * g]);
+#pragma unroll
+      for (int j = 1; j < 8; ++j) gm[g] = __builtin_elementwise_max(gm[g], __builtin_bit_cast(u16x2, w[8 * g + j]));
+    }
+    const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(gm[0], gm[1]),
+                                              __builtin_elementwise_max(gm[2], gm[3]));
+    if (max(m.x, m.y) <= t1) return;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (max(gm[g].x, gm[g].y) <= t1) continue;
+#pragma unroll
+      for (int j = 8 * g; j < 8 * g + 8; ++j) {
+        const u16x2 d = __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, w[j]), t);
+        if (__builtin_bit_cast(uint32_t, d) != 0u) {
+          if (d.x) f(w[j] & 0xffffu, 2 * j);
+          if (d.y) f(w[j] >> 16, 2 * j + 1);
+        }
       }
     }
   }
@@ -192,18 +216,33 @@ template <> struct Chunk<uint16_t> {
   // negative values (int16 < 0) never pass.  One packed signed max tests two
   // values.
   static constexpr bool kHasRawFilter = true;
+  // Same group pre-test as for_each_ge.
   template <class F> __device__ void for_each_raw_ge(uint32_t r, F&& f) const {
     typedef short s16x2 __attribute__((ext_vector_type(2)));
     const short r1 = (short)(r - 1);
     const s16x2 t = {r1, r1};
     const uint32_t t32 = __builtin_bit_cast(uint32_t, t);
+    s16x2 gm[4];
 #pragma unroll
-    for (int j = 0; j < W; ++j) {
-      const s16x2 x = __builtin_bit_cast(s16x2, w[j]);
-      const s16x2 m = __builtin_elementwise_max(x, t);
-      if (__builtin_bit_cast(uint32_t, m) != t32) {
-        if (x.x > r1) f((w[j] & 0xffffu) | 0x8000u, 2 * j);
-        if (x.y > r1) f((w[j] >> 16) | 0x8000u, 2 * j + 1);
+    for (int g = 0; g < 4; ++g) {
+      gm[g] = __builtin_bit_cast(s16x2, w[8 * g]);
+#pragma unroll
+      for (int j = 1; j < 8; ++j) gm[g] = __builtin_elementwise_max(gm[g], __builtin_bit_cast(s16x2, w[8 * g + j]));
+    }
+    const s16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(gm[0], gm[1]),
+                                              __builtin_elementwise_max(gm[2], gm[3]));
+    if (max(m.x, m.y) <= r1) return;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (max(gm[g].x, gm[g].y) <= r1) continue;
+#pragma unroll
+      for (int j = 8 * g; j < 8 * g + 8; ++j) {
+        const s16x2 x = __builtin_bit_cast(s16x2, w[j]);
+        const s16x2 mx = __builtin_elementwise_max(x, t);
+        if (__builtin_bit_cast(uint32_t, mx) != t32) {
+          if (x.x > r1) f((w[j] & 0xffffu) | 0x8000u, 2 * j);
+          if (x.y > r1) f((w[j] >> 16) | 0x8000u, 2 * j + 1);
+        }
       }
     }
   }
@@ -217,20 +256,20 @@ template <> struct Chunk<float> {
   static constexpr int VEC = 4, L = kPerLane / VEC;
   uint32_t w[kPerLane];
 
-  __device__ void issue(const float* rowp, int64_t c_start, int64_t valid, int lane, bool full) {
+  __device__ void issue(const float* rowp, int64_t lb, int64_t valid) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
-      const int64_t e0 = c_start + ((int64_t)l * 64 + lane) * VEC;
-      const uint4 r = (full || e0 + VEC <= valid) ? *reinterpret_cast<const uint4*>(rowp + e0)
-                                                  : make_uint4(0u, 0u, 0u, 0u);
+      const int64_t e0 = lb + l * vec_stride<VEC>();
+      const uint4 r = (e0 + VEC <= valid) ? *reinterpret_cast<const uint4*>(rowp + e0) : make_uint4(0u, 0u, 0u, 0u);
       w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
     }
   }
-  __device__ void issue_full(const float* rowp, int64_t c_start, int lane) {
-    const uint4* p = reinterpret_cast<const uint4*>(rowp + c_start) + lane;
+  __device__ void issue_clamped(const float* rowp, int32_t lb, int32_t last_vec) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
-      const uint4 r = p[l * 64];
+      const int32_t e0 = min(lb + l * (int32_t)vec_stride<VEC>(), last_vec);
+      const u32x4 rv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowp + e0));   // streamed once
+      const uint4 r = make_uint4(rv.x, rv.y, rv.z, rv.w);
       w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
     }
   }
@@ -238,13 +277,13 @@ template <> struct Chunk<float> {
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) w[j] = f32_key(w[j]);
   }
-  __device__ void make_keys(const float* rowp, int64_t c_start, int64_t valid, int lane, bool full) {
+  __device__ void make_keys(const float* rowp, int64_t lb, int64_t valid) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
-      const int64_t e0 = c_start + ((int64_t)l * 64 + lane) * VEC;
+      const int64_t e0 = lb + l * vec_stride<VEC>();
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        w[l * 4 + q] = (full || e0 + VEC <= valid) ? f32_key(w[l * 4 + q])
+        w[l * 4 + q] = (e0 + VEC <= valid) ? f32_key(w[l * 4 + q])
                        : (e0 + q < valid) ? f32_key(__float_as_uint(rowp[e0 + q])) : 0u;
     }
   }
@@ -254,10 +293,26 @@ template <> struct Chunk<float> {
     for (int j = 0; j < kPerLane; ++j) m = max(m, w[j]);
     return m;
   }
+  // Group pre-test as in the bf16 chunk: eight groups of eight keys.
   template <class F> __device__ void for_each_ge(uint64_t tau, F&& f) const {
+    uint32_t gm[8];
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j)
-      if ((uint64_t)w[j] >= tau) f(w[j], j);
+    for (int g = 0; g < 8; ++g) {
+      gm[g] = w[8 * g];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) gm[g] = max(gm[g], w[8 * g + j]);
+    }
+    uint32_t m = gm[0];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) m = max(m, gm[g]);
+    if ((uint64_t)m < tau) return;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      if ((uint64_t)gm[g] < tau) continue;
+#pragma unroll
+      for (int j = 8 * g; j < 8 * g + 8; ++j)
+        if ((uint64_t)w[j] >= tau) f(w[j], j);
+    }
   }
   static constexpr bool kHasRawFilter = false;
   __device__ int raw_max_i16() const { return 0; }
@@ -279,20 +334,21 @@ struct Shared {
   WaveLds wave[kWaves];
 };
 
-__device__ __forceinline__ int64_t value_id(int64_t c_start, int i, int vec, int lane) {
-  return c_start + ((int64_t)(i / vec) * 64 + lane) * vec + (i % vec);
+template <int VEC>
+__device__ __forceinline__ int64_t value_id(int64_t lb, int i) {
+  return lb + (i / VEC) * vec_stride<VEC>() + (i % VEC);
 }
 
 // Counts, over this lane's chunk values re-read from memory, those with
 // key >= lo_key (mode 0), key > key_eq (mode 1), or key == key_eq and
 // id < id_bound (mode 2); then sums over the wave.
 template <typename TIO>
-__device__ uint32_t count_pass(const TIO* rowp, int64_t c_start, int64_t valid, int lane, int mode,
+__device__ uint32_t count_pass(const TIO* rowp, int64_t lb, int64_t valid, int mode,
                                uint64_t lo_key, uint32_t key_eq, int64_t id_bound) {
   constexpr int VEC = Chunk<TIO>::VEC;
   uint32_t c = 0;
   for (int i = 0; i < kPerLane; ++i) {
-    const int64_t id = value_id(c_start, i, VEC, lane);
+    const int64_t id = value_id<VEC>(lb, i);
     if (id >= valid) continue;
     const uint32_t k = Chunk<TIO>::key_at(rowp + id);
     if (mode == 0) c += ((uint64_t)k >= lo_key) ? 1u : 0u;
@@ -306,25 +362,25 @@ __device__ uint32_t count_pass(const TIO* rowp, int64_t c_start, int64_t valid, 
 // replaces the new candidates (pool[nbest, ...)) by exactly the chunk's K
 // best (or all its real values if fewer); returns their number.
 template <typename TIO>
-__device__ __noinline__ uint32_t narrow_exact(const TIO* rowp, int64_t c_start, int64_t valid, int lane, int K,
-                                              int nbest, WaveLds& wl) {
+__device__ __noinline__ uint32_t narrow_exact(const TIO* rowp, int64_t lb, int64_t c_start, int64_t valid, int lane,
+                                              int K, int nbest, WaveLds& wl) {
   constexpr int VEC = Chunk<TIO>::VEC;
-  const uint32_t n_real = count_pass(rowp, c_start, valid, lane, 0, 1, 0, 0);
+  const uint32_t n_real = count_pass(rowp, lb, valid, 0, 1, 0, 0);
   uint32_t kt = 1;                                     // take every real value when there are few
   int64_t id_bound = INT64_MAX;
   if (n_real > (uint32_t)K) {
     uint64_t lo = 1, hi = Chunk<TIO>::kKeyLimit;       // count(>= lo) >= K > count(>= hi)
     while (hi - lo > 1) {
       const uint64_t mid = lo + (hi - lo) / 2;
-      if (count_pass(rowp, c_start, valid, lane, 0, mid, 0, 0) >= (uint32_t)K) lo = mid; else hi = mid;
+      if (count_pass(rowp, lb, valid, 0, mid, 0, 0) >= (uint32_t)K) lo = mid; else hi = mid;
     }
     kt = (uint32_t)lo;
-    const uint32_t c_gt = count_pass(rowp, c_start, valid, lane, 1, 0, kt, 0);
+    const uint32_t c_gt = count_pass(rowp, lb, valid, 1, 0, kt, 0);
     const uint32_t need = (uint32_t)K - c_gt;          // ties at kt to take, lowest ids first
-    int64_t lo_i = c_start, hi_i = c_start + kWaveChunk;  // count(id < lo_i) < need <= count(id < hi_i)
+    int64_t lo_i = c_start, hi_i = c_start + kGroupChunk;  // count(id < lo_i) < need <= count(id < hi_i)
     while (hi_i - lo_i > 1) {
       const int64_t mid = lo_i + (hi_i - lo_i) / 2;
-      if (count_pass(rowp, c_start, valid, lane, 2, 0, kt, mid) >= need) hi_i = mid; else lo_i = mid;
+      if (count_pass(rowp, lb, valid, 2, 0, kt, mid) >= need) hi_i = mid; else lo_i = mid;
     }
     id_bound = hi_i;
   }
@@ -332,7 +388,7 @@ __device__ __noinline__ uint32_t narrow_exact(const TIO* rowp, int64_t c_start, 
   if (lane == 0) wl.count = 0;
   wave_sync();
   for (int i = 0; i < kPerLane; ++i) {
-    const int64_t id = value_id(c_start, i, VEC, lane);
+    const int64_t id = value_id<VEC>(lb, i);
     if (id >= valid) continue;
     const uint32_t k = Chunk<TIO>::key_at(rowp + id);
     if (k > kt || (k == kt && id < id_bound)) {
@@ -420,26 +476,26 @@ __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, i
   int nbest = 0;                                 // held best composites (wave-uniform)
 
   constexpr int VEC = Chunk<TIO>::VEC;
-  // Appends a survivor (key, value index i of chunk c_start) behind the held best.
+  // Appends a survivor (key, value index i of the lane's values) behind the held best.
   auto push = [&](uint32_t k, int i, uint32_t id_base) {
     const uint32_t pos = atomicAdd(&wl.count, 1u);
-    // ids < 2^24: a 32-bit lane base plus the value's compile-time offset
-    const uint32_t id = id_base + (uint32_t)((i / VEC) * 64 * VEC + i % VEC);
+    // ids < 2^24: the 32-bit lane base plus the value's compile-time offset
+    const uint32_t id = id_base + (uint32_t)((i / VEC) * vec_stride<VEC>() + i % VEC);
     if (pos < (uint32_t)kWaveCap) wl.pool[nbest + pos] = ((uint64_t)k << 24) | (uint64_t)(kIdMask - id);
   };
   // After the survivors of one chunk are in the pool: exact narrowing if they
   // overflowed, then keep the wave's K best.
-  auto update = [&](int64_t c_start) {
+  auto update = [&](int64_t lb, int64_t c_start) {
     wave_sync();
     uint32_t n = __builtin_amdgcn_readfirstlane(wl.count);
-    if (n > (uint32_t)kWaveCap) n = narrow_exact<TIO>(rowp, c_start, valid_vocab, lane, K, nbest, wl);
+    if (n > (uint32_t)kWaveCap) n = narrow_exact<TIO>(rowp, lb, c_start, valid_vocab, lane, K, nbest, wl);
     if (n > 0) {
       keep_best(wl, nbest, (int)n, K, lane);
       nbest = min(K, nbest + (int)n);
     }
   };
   // General path: `ch` holds keys.  Threshold, compaction, update.
-  auto process_keys = [&](const Chunk<TIO>& ch, int64_t c_start) {
+  auto process_keys = [&](const Chunk<TIO>& ch, int64_t lb, int64_t c_start) {
     uint64_t tau;
     if (nbest < K) {
       // K-th largest lane maximum: at least K values reach it (key 0 =
@@ -453,14 +509,13 @@ __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, i
     }
     if (lane == 0) wl.count = 0;
     wave_sync();
-    const uint32_t id_base = (uint32_t)c_start + (uint32_t)lane * VEC;
-    if (tau < Chunk<TIO>::kKeyLimit) ch.for_each_ge(tau, [&](uint32_t k, int i) { push(k, i, id_base); });
-    update(c_start);
+    if (tau < Chunk<TIO>::kKeyLimit) ch.for_each_ge(tau, [&](uint32_t k, int i) { push(k, i, (uint32_t)lb); });
+    update(lb, c_start);
   };
   // One full chunk whose raw bits are in `ch`.  bf16: while the threshold is
   // a positive value the filter runs on raw bits (keys are built only for
   // survivors); otherwise the chunk goes through the key path.
-  auto process_full = [&](Chunk<TIO>& ch, int64_t c_start) {
+  auto process_full = [&](Chunk<TIO>& ch, int64_t lb, int64_t c_start) {
     if (Chunk<TIO>::kHasRawFilter) {
       int r = 0;                                                 // raw int16 threshold, >= 1 when usable
       if (nbest == K) {
@@ -475,48 +530,63 @@ __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, i
       if (r >= 1) {
         if (lane == 0) wl.count = 0;
         wave_sync();
-        const uint32_t id_base = (uint32_t)c_start + (uint32_t)lane * VEC;
-        ch.for_each_raw_ge((uint32_t)r, [&](uint32_t k, int i) { push(k, i, id_base); });
-        update(c_start);
+        ch.for_each_raw_ge((uint32_t)r, [&](uint32_t k, int i) { push(k, i, (uint32_t)lb); });
+        update(lb, c_start);
         return;
       }
     }
     ch.keys_full();
-    process_keys(ch, c_start);
+    process_keys(ch, lb, c_start);
   };
 
-  // Wave-chunks below n_full lie entirely inside the logical vocabulary; at
-  // most the row's last chunk is partial.  The loop over full chunks always
-  // issues the next chunk's loads (the last iteration re-reads its own chunk,
-  // a cache hit), so the wait for the current chunk is an exact in-order
-  // count and the next chunk's loads stay in flight while this one is
-  // processed.
-  const int n_full = (int)(valid_vocab / kWaveChunk);
+  // Every wave walks the same group-chunks, each taking its interleaved
+  // quarter.  Group-chunks below n_full lie entirely inside the logical
+  // vocabulary; at most the row's last one is partial.  The loop over whole
+  // group-chunks always issues the next one's loads before processing the
+  // current one -- the partial one after the last whole one, else a re-read
+  // of the current one (a cache hit) -- and every issue is unconditional, so
+  // the wait for the current one is an exact in-order count and the next
+  // one's loads stay in flight meanwhile.  A row too short to hold one whole
+  // vector reads its partial group-chunk with bounds-checked loads instead.
+  const int64_t wave_off = (int64_t)(wave * 64 + lane) * VEC;
+  const int32_t wave_off32 = (int32_t)wave_off;                       // vocab < 2^24
+  const int n_full = (int)(valid_vocab / kGroupChunk);
   const int full_end = min(c_end, n_full);
-  int c = c_begin + wave;
+  const bool clampable = valid_vocab >= VEC;
+  const int32_t last_vec = clampable ? (int32_t)((valid_vocab / VEC - 1) * VEC) : 0;  // last whole vector
+  const int pre_end = (c_end > n_full && clampable) ? full_end + 1 : full_end;       // chunks worth prefetching
+  int c = c_begin;
+  Chunk<TIO> tail;
+  bool tail_loaded = false;
   if (c < full_end) {
     // two buffers, alternating roles, so that no chunk is copied
     Chunk<TIO> a, b;
-    a.issue_full(rowp, (int64_t)c * kWaveChunk, lane);
+    bool in_b = false;                            // where the chunk prefetched past the loop sits
+    a.issue_clamped(rowp, c * kGroupChunk + wave_off32, last_vec);
     while (true) {
-      int c_next = (c + kWaves < full_end) ? c + kWaves : c;
-      b.issue_full(rowp, (int64_t)c_next * kWaveChunk, lane);
-      process_full(a, (int64_t)c * kWaveChunk);
-      c += kWaves;
-      if (c >= full_end) break;
-      c_next = (c + kWaves < full_end) ? c + kWaves : c;
-      a.issue_full(rowp, (int64_t)c_next * kWaveChunk, lane);
-      process_full(b, (int64_t)c * kWaveChunk);
-      c += kWaves;
-      if (c >= full_end) break;
+      int cn = c + 1 < pre_end ? c + 1 : c;
+      b.issue_clamped(rowp, cn * kGroupChunk + wave_off32, last_vec);
+      process_full(a, (int64_t)c * kGroupChunk + wave_off, (int64_t)c * kGroupChunk);
+      if (++c >= full_end) { in_b = true; break; }
+      cn = c + 1 < pre_end ? c + 1 : c;
+      a.issue_clamped(rowp, cn * kGroupChunk + wave_off32, last_vec);
+      process_full(b, (int64_t)c * kGroupChunk + wave_off, (int64_t)c * kGroupChunk);
+      if (++c >= full_end) break;
+    }
+    if (pre_end > full_end) {
+#pragma unroll
+      for (int j = 0; j < (int)(sizeof(tail.w) / sizeof(tail.w[0])); ++j) tail.w[j] = in_b ? b.w[j] : a.w[j];
+      tail_loaded = true;
     }
   }
-  if (c < c_end) {                               // the partial last chunk of the row
-    Chunk<TIO> tail;
-    const int64_t c_start = (int64_t)c * kWaveChunk;
-    tail.issue(rowp, c_start, valid_vocab, lane, false);
-    tail.make_keys(rowp, c_start, valid_vocab, lane, false);
-    process_keys(tail, c_start);
+  if (c < c_end) {                               // the partial last group-chunk of the row
+    const int64_t c_start = (int64_t)c * kGroupChunk;
+    if (!tail_loaded) {
+      if (clampable) tail.issue_clamped(rowp, (int32_t)c_start + wave_off32, last_vec);
+      else tail.issue(rowp, c_start + wave_off, valid_vocab);
+    }
+    tail.make_keys(rowp, c_start + wave_off, valid_vocab);
+    process_keys(tail, c_start + wave_off, c_start);
   }
   if (lane == 0) wl.nbest = (uint32_t)nbest;
   __syncthreads();
@@ -601,7 +671,7 @@ TopkPlan plan_topk(int64_t n_rows, int64_t valid_vocab, int32_t top_k) {
   p.n_rows = n_rows;
   p.valid_vocab = valid_vocab;
   p.top_k = top_k;
-  p.chunks = (int32_t)((valid_vocab + kWaveChunk - 1) / kWaveChunk);   // wave-chunks per row
+  p.chunks = (int32_t)((valid_vocab + kGroupChunk - 1) / kGroupChunk);   // group-chunks per row
   if (p.chunks < 1) p.chunks = 1;
   // One workgroup (4 waves) per row; only when rows are very few are they
   // split into segments (merged by a second kernel), since the merge launch
@@ -609,8 +679,7 @@ TopkPlan plan_topk(int64_t n_rows, int64_t valid_vocab, int32_t top_k) {
   int segs = 1;
   if (n_rows > 0 && n_rows < 128) {
     segs = (int)((512 + n_rows - 1) / n_rows);
-    const int max_by_chunks = (p.chunks + kWaves - 1) / kWaves;         // >= 1 wave-chunk per wave
-    if (segs > max_by_chunks) segs = max_by_chunks;
+    if (segs > p.chunks) segs = p.chunks;                               // >= 1 group-chunk per segment
     if (segs * top_k > kTopkMergeCap) segs = kTopkMergeCap / top_k;
     if (segs < 1) segs = 1;
   }
