@@ -54,8 +54,46 @@ def algorithmic_bytes(w):
     }
 
 
-def cpu_baseline(w, n_req_sample: int):
-    """Time the oracle (as it stands) on a bounded sample of the workload."""
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "topk_traffic.json")
+TOPK_SOURCE = os.path.join(ROOT, "block_draft_proposal_amd", "csrc", "topk.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per top-K launch from the committed counter runs (FETCH_SIZE
+    + WRITE_SIZE, scaled by a copy kernel of known size), or None when they
+    were taken on another workload or on a top-K source other than the one
+    built now."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(TOPK_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != sha or t.get("workload") != workload:
+        return None
+    return t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
+
+
+def copy_calibration(n_bytes: int, reps: int):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = n_bytes // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0").uniform_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_dispatch": n * 4, "bytes_written_per_dispatch": n * 4,
+                                           "dispatches": reps}}), flush=True)
+
+
+def cpu_baseline(w, n_req_sample: int, min_seconds: float = 10.0):
+    """Time the oracle (as it stands) on a bounded sample of the workload:
+    batches of n_req_sample requests (fresh seeds each) until min_seconds of
+    CPU work have been timed."""
     import numpy as np
     import torch
     import workloads as W
@@ -66,17 +104,21 @@ def cpu_baseline(w, n_req_sample: int):
     except Exception:   # pragma: no cover - threadpoolctl is optional
         limiter = None
     ws = w.replace(n_req=n_req_sample)
-    inp = W.make_inputs(ws, device="cpu")
-    host = {k: (v.to(torch.float64).numpy() if v.is_floating_point() else v.numpy()) for k, v in inp.items()}
-    t0 = time.perf_counter()
-    O.propose_block(host, block_size=ws.block_size, group_size=ws.group_size, valid_vocab=ws.valid_vocab,
-                    top_k=ws.top_k, multiplier=ws.multiplier, softcap=ws.softcap, dtype=ws.dtype)
-    dt = time.perf_counter() - t0
+    dt, batches = 0.0, 0
+    while dt < min_seconds:
+        inp = W.make_inputs(ws, device="cpu", seed=W.master_seed(ws) + 7919 * batches)
+        host = {k: (v.to(torch.float64).numpy() if v.is_floating_point() else v.numpy()) for k, v in inp.items()}
+        t0 = time.perf_counter()
+        O.propose_block(host, block_size=ws.block_size, group_size=ws.group_size, valid_vocab=ws.valid_vocab,
+                        top_k=ws.top_k, multiplier=ws.multiplier, softcap=ws.softcap, dtype=ws.dtype)
+        dt += time.perf_counter() - t0
+        batches += 1
     if limiter is not None:
         limiter.unregister() if hasattr(limiter, "unregister") else None
-    return {"value": ws.n_slot_rows / dt, "unit": "draft tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_req_sample} of {w.n_req} requests ({ws.n_slot_rows} draft tokens), full vocab/hidden; "
-                      f"{dt:.2f} s single-threaded numpy float64 (walk in fp32)"}
+    tokens = batches * ws.n_slot_rows
+    return {"value": tokens / dt, "unit": "draft tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{batches} batches of {n_req_sample} of the {w.n_req} requests ({tokens} draft tokens), "
+                      f"full vocab/hidden; {dt:.1f} s single-threaded numpy float64 (walk in fp32)"}
 
 
 def main():
@@ -87,6 +129,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-requests", type=int, default=12)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards requests with no "
@@ -96,6 +140,10 @@ def main():
     import torch
     import block_draft_proposal_amd as D
     import workloads as W
+
+    if args.copy_calibration:
+        copy_calibration(1 << 30, 10)
+        return
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -189,7 +237,7 @@ def main():
                    "top_k": w.top_k, "rank": w.rank, "draft_tokens_per_step": w.n_slot_rows,
                    "input_sets": n_sets},
         "roofline": {"bound": "hbm", "kernel": "topk_kernel", "achieved": topk_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": topk_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": topk_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                      "algorithmic_bytes_per_launch": nbytes["topk"], "avg_launch_us": avg_ms[1] * 1e3},
         "conv_hbm": {"achieved": conv_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": conv_gbs / HBM_PEAK_GBS,
                      "algorithmic_bytes_per_launch": nbytes["conv"], "avg_launch_us": avg_ms[0] * 1e3},
