@@ -16,8 +16,9 @@ model weights.  Inputs are resident in HBM before the timed region starts.
 
 Prints one JSON line: draft tokens/s over the timed steps, the top-K kernel's
 achieved HBM bandwidth against the 8 TB/s peak (timed with HIP events recorded
-by the library around that kernel on its stream), and the CPU oracle timed on
-a bounded sample of the same workload.
+by the library around that kernel on its stream; the events are created for
+timing only, without a system-scope fence), and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -74,6 +75,53 @@ def measured_traffic(workload: str):
     if t.get("source_sha256") != sha or t.get("workload") != workload:
         return None
     return t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
+
+
+class TimingEvent:
+    """A HIP event for timing only: created through the HIP runtime with
+    hipEventDisableSystemFence, so recording it adds no system-scope cache
+    write-back to the stream it times (torch's timing events carry one).
+    Exposes ``cuda_event`` like torch.cuda.Event for the library's stage-event
+    array."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def _lib(cls):
+        import ctypes
+        if cls._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ctypes = ctypes
+        h = ctypes.c_void_p()
+        st = self._lib().hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {st}")
+        self.cuda_event = h.value
+
+    def record(self, stream_handle):
+        st = self._lib().hipEventRecord(self.cuda_event, stream_handle)
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed: {st}")
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        ms = self._ctypes.c_float()
+        st = self._lib().hipEventElapsedTime(self._ctypes.byref(ms), self.cuda_event, end.cuda_event)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {st}")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and getattr(self, "cuda_event", None):
+            self._hip.hipEventDestroy(self.cuda_event)
 
 
 def copy_calibration(n_bytes: int, reps: int):
@@ -188,10 +236,10 @@ def main():
         only the listed stages get events (the library skips NULL entries)."""
         evs = []
         for _ in range(n):
-            row = [torch.cuda.Event(enable_timing=True) if k // 2 in stages else None for k in range(8)]
+            row = [TimingEvent() if k // 2 in stages else None for k in range(8)]
             for e in row:
                 if e is not None:
-                    e.record()
+                    e.record(stream)
             evs.append((row, D.ProposeBlock.event_array(row)))
         torch.cuda.synchronize()
         return evs

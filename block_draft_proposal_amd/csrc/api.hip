@@ -166,6 +166,11 @@ struct ForkJoin {
   hipEvent_t fork, join;
 };
 constexpr int kMaxDevices = 64;
+// The two events only order work between two streams of one device: no
+// timing, and no system-scope fence (nothing on the host waits for them;
+// the device-side ordering and the kernel-boundary cache maintenance still
+// hold).  The system-scope fence would cost a cache write-back per call.
+constexpr unsigned kOrderFlags = hipEventDisableTiming | hipEventDisableSystemFence;
 
 int fork_join(ForkJoin** out, const char* who) {
   thread_local ForkJoin per_device[kMaxDevices] = {};
@@ -177,8 +182,8 @@ int fork_join(ForkJoin** out, const char* who) {
   if (!f.aux) {
     ForkJoin n{};
     e = hipStreamCreateWithFlags(&n.aux, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, kOrderFlags);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, kOrderFlags);
     if (e != hipSuccess) {
       if (n.join) (void)hipEventDestroy(n.join);   // best effort: the set-up error is the one reported
       if (n.fork) (void)hipEventDestroy(n.fork);
