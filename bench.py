@@ -36,6 +36,7 @@ METRIC = "draft tokens/s through conv+topK+lattice walk; conv/topK HBM GB/s % of
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "bf16_b16_v151936"
 MALL_BYTES = 256 * 1024 * 1024
+TIMED_EVERY = 4          # top-K events on every 4th timed step
 
 
 def log(*a):
@@ -244,15 +245,19 @@ def main():
         torch.cuda.synchronize()
         return evs
 
-    # Timed region: every step carries the two events around the top-K (the
-    # dominant kernel), on the stream it runs on.
-    timed = event_sets(args.steps, stages=(1,))
+    # Timed region: every TIMED_EVERY-th step carries the two events around
+    # the top-K (the dominant kernel), on the stream it runs on.  Each event
+    # record adds a few microseconds to the stream, so sampling keeps the
+    # instrumentation from inflating the step time it sits in.
+    sampled = [i for i in range(args.steps) if i % TIMED_EVERY == 0]
+    timed = dict(zip(sampled, event_sets(len(sampled), stages=(1,))))
     t0 = time.perf_counter()
     for i in range(args.steps):
-        calls[(args.warmup + i) % n_sets](stream, timed[i][1])
+        ev = timed.get(i)
+        calls[(args.warmup + i) % n_sets](stream, ev[1] if ev else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    topk_ms = sum(r[2].elapsed_time(r[3]) for r, _ in timed) / args.steps
+    topk_ms = sum(r[2].elapsed_time(r[3]) for r, _ in timed.values()) / len(timed)
 
     # Per-stage breakdown from a shorter pass with all eight events.
     n_stage = min(args.steps, 50)
@@ -290,7 +295,7 @@ def main():
         "conv_hbm": {"achieved": conv_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": conv_gbs / HBM_PEAK_GBS,
                      "algorithmic_bytes_per_launch": nbytes["conv"], "avg_launch_us": avg_ms[0] * 1e3},
         "stage_us": {"conv": avg_ms[0] * 1e3, "topk": avg_ms[1] * 1e3, "proj": avg_ms[2] * 1e3,
-                     "lattice_walk": avg_ms[3] * 1e3, "note": "top-K from the timed steps, the other stages "
+                     "lattice_walk": avg_ms[3] * 1e3, "note": f"top-K from every {TIMED_EVERY}th timed step, the other stages "
                      f"from {n_stage} further steps with all stage events; conv and projection run "
                      "beside the top-K on a second stream"},
         "cpu_baseline": None,

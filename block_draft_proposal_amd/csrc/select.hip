@@ -300,28 +300,36 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(const float* __restrict_
 //   4. every row's decision, which does not depend on the path: row maxima
 //      and sums stay sequential per row, the fp64 exponentials are spread
 //      over the entries
-//   5. one wave follows the chosen indices from row 0.
-// LDS layout: pred ids [S][K], cand ids [S][K] (int64), u [S][r], w [S][K][r+1]
-// (fp32), B rows [S][r][K] (storage dtype), unary [S][K], scores [S][K][K]
-// (then q), exponentials [S][K][K], row maxima [S][K], uniforms [S], chosen
-// index per row [S][K].
+//   5. the walked path by pointer jumping: the index chosen at slot s is the
+//      composition of the slots' choice maps 0..s applied to row 0, an
+//      inclusive scan in ceil(log2 S) rounds; then q rows and tokens are
+//      written in parallel.
+// LDS layout: pred ids [S][K], cand ids [S][K] (int64), w [S][K][r+4] (fp32;
+// rows 16-byte aligned and 4 banks apart), B rows [S][K][r + 16 bytes]
+// (storage dtype, one row per candidate), unary [S][K], scores [S][K][K]
+// (then q), exponentials [S][K][K] (holding u [S][r] during the gather and
+// the scan's second buffer during the walk), row maxima [S][K], uniforms [S],
+// chosen index per row [S][K].
 constexpr int kLWThreads = 1024;
 
 struct LatticeWalkLds {
-  size_t pred, cand, u, w, b, unary, sc, e, mx, un, next, bytes;
+  size_t pred, cand, w, b, unary, sc, e, mx, un, next, bytes;
+  int wstride, bstride;   // row strides of w (floats) and B rows (elements)
 };
 
 __host__ __device__ inline LatticeWalkLds lattice_walk_layout(int S, int K, int r, int elem) {
   LatticeWalkLds L;
+  L.wstride = r + 4;
+  L.bstride = r + 16 / elem;
+  const size_t e_bytes = (size_t)S * K * K * 4, u_bytes = (size_t)S * r * 4, g_bytes = (size_t)S * K * 4;
   size_t o = 0;
   L.pred = o;  o += (size_t)S * K * 8;
   L.cand = o;  o += (size_t)S * K * 8;
-  L.u = o;     o += (size_t)S * r * 4;
-  L.w = o;     o += (size_t)S * K * (r + 1) * 4;
-  L.b = o;     o += ((size_t)S * r * K * elem + 3) & ~(size_t)3;
+  L.w = o;     o += (size_t)S * K * L.wstride * 4;
+  L.b = o;     o += (size_t)S * K * L.bstride * elem;
   L.unary = o; o += (size_t)S * K * 4;
   L.sc = o;    o += (size_t)S * K * K * 4;
-  L.e = o;     o += (size_t)S * K * K * 4;
+  L.e = o;     o += (e_bytes > u_bytes ? (e_bytes > g_bytes ? e_bytes : g_bytes) : (u_bytes > g_bytes ? u_bytes : g_bytes));
   L.mx = o;    o += (size_t)S * K * 4;
   L.un = o;    o += (size_t)S * 4;
   L.next = o;  o += (size_t)S * K * 4;
@@ -343,7 +351,7 @@ __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
   const LatticeWalkLds L = lattice_walk_layout(S, K, r, (int)sizeof(TIO));
   int64_t* s_pred = reinterpret_cast<int64_t*>(lw_smem + L.pred);
   int64_t* s_cand = reinterpret_cast<int64_t*>(lw_smem + L.cand);
-  float* s_u = reinterpret_cast<float*>(lw_smem + L.u);
+  float* s_u = reinterpret_cast<float*>(lw_smem + L.e);      // u lives in the exponentials' space until phase 4
   float* s_w = reinterpret_cast<float*>(lw_smem + L.w);
   TIO* s_b = reinterpret_cast<TIO*>(lw_smem + L.b);
   float* s_unary = reinterpret_cast<float*>(lw_smem + L.unary);
@@ -353,7 +361,7 @@ __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
   float* s_un = reinterpret_cast<float*>(lw_smem + L.un);
   int* s_next = reinterpret_cast<int*>(lw_smem + L.next);
   const int64_t row0 = (int64_t)req * S;            // first slot row of this request
-  const int wstride = r + 1;
+  const int wstride = L.wstride, bstride = L.bstride;
   const FastDiv div_k(K), div_r(r);                 // every index below is < 2^16 (LDS bound)
 
   // ---- 1. ids, u (projection slices summed in order), unary, uniforms ----
@@ -401,19 +409,26 @@ __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
         const bool is_b = i >= n_pieces;
         const int ii = is_b ? i - n_pieces : i;
         const int sj = div_ppr.quot(ii), v = ii - sj * pieces_per_row;
-        const int s = div_k.quot(sj), j = sj - s * K;
+        const int s = div_k.quot(sj);
         const int64_t t = is_b ? s_cand[sj] : s_pred[sj];
         const bool ok = t >= 0 && t < vocab;
-        const TIO* piece = reinterpret_cast<const TIO*>(&raw[q]);
+        if (is_b) {
+          // the candidate's row piece as it is (NaN for an out-of-range id)
+          TIO nanrow[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const int k = v * VEC + e;
-          if (is_b) {
-            s_b[((size_t)s * r + k) * K + j] = ok ? piece[e] : Elem<TIO>::nan_value();
-          } else {
-            const float a = ok ? Elem<TIO>::to_f32(piece[e]) : __builtin_nanf("");
-            s_w[sj * wstride + k] = a * s_u[s * r + k];   // A[p] (.) project(h)
-          }
+          for (int e = 0; e < VEC; ++e) nanrow[e] = Elem<TIO>::nan_value();
+          *reinterpret_cast<uint4*>(s_b + (size_t)sj * bstride + v * VEC) =
+              ok ? raw[q] : *reinterpret_cast<const uint4*>(nanrow);
+        } else {
+          float a[VEC];
+          unpack16(raw[q], a);
+          float wv[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e)
+            wv[e] = (ok ? a[e] : __builtin_nanf("")) * s_u[s * r + v * VEC + e];   // A[p] (.) project(h)
+#pragma unroll
+          for (int e = 0; e < VEC; e += 4)
+            *reinterpret_cast<float4*>(s_w + sj * wstride + v * VEC + e) = make_float4(wv[e], wv[e + 1], wv[e + 2], wv[e + 3]);
         }
       }
     }
@@ -423,13 +438,24 @@ __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
   // ---- 3. one thread per entry (s, j, c): fma chain over k from 0 ---------
   const int n_entries = S * K * K;
   for (int e = tid; e < n_entries; e += kLWThreads) {
+    constexpr int VEC = Elem<TIO>::kVec;
     const int sj = div_k.quot(e), c = e - sj * K;
     const int s = div_k.quot(sj);
     const float* w = s_w + sj * wstride;
-    const TIO* b = s_b + (size_t)s * r * K + c;
+    const TIO* b = s_b + (size_t)(s * K + c) * bstride;
     float acc = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < r; ++k) acc = fmaf(w[k], Elem<TIO>::to_f32(b[k * K]), acc);
+    for (int k0 = 0; k0 < r; k0 += VEC) {
+      float bv[VEC];
+      unpack16(*reinterpret_cast<const uint4*>(b + k0), bv);
+#pragma unroll
+      for (int e4 = 0; e4 < VEC; e4 += 4) {
+        const float4 wv = *reinterpret_cast<const float4*>(w + k0 + e4);
+        acc = fmaf(wv.x, bv[e4 + 0], acc);
+        acc = fmaf(wv.y, bv[e4 + 1], acc);
+        acc = fmaf(wv.z, bv[e4 + 2], acc);
+        acc = fmaf(wv.w, bv[e4 + 3], acc);
+      }
+    }
     const float v = acc + s_unary[s * K + c];
     s_sc[e] = v;
     if (scores_out) scores_out[row0 * K * K + e] = v;
@@ -483,17 +509,25 @@ __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
   }
   __syncthreads();
 
-  // ---- 5. walk: follow the chosen indices from row 0 ----------------------
-  if (tid >= 64) return;
-  const int lane = tid;
-  int prev = 0;
-  for (int s = 0; s < S; ++s) {
-    const int sj = s * K + prev;
+  // ---- 5. walk: g_s = choice maps of slots 0..s composed, by pointer
+  // jumping; the index chosen at slot s is g_s(0), and the row walked there
+  // is the one of the index chosen at slot s - 1 (row 0 at slot 0) --------
+  int* g_cur = s_next;
+  int* g_alt = reinterpret_cast<int*>(lw_smem + L.e);
+  for (int d = 1; d < S; d <<= 1) {
+    for (int i = tid; i < S * K; i += kLWThreads) {
+      const int s = div_k.quot(i);
+      g_alt[i] = (s >= d) ? g_cur[s * K + g_cur[i - d * K]] : g_cur[i];
+    }
+    __syncthreads();
+    int* t = g_cur; g_cur = g_alt; g_alt = t;
+  }
+  for (int i = tid; i < S * K; i += kLWThreads) {
+    const int s = div_k.quot(i), c = i - s * K;
+    const int prev = (s == 0) ? 0 : g_cur[(s - 1) * K];   // row walked at slot s
     const int64_t n = row0 + s;
-    if (lane < K) q_out[n * K + lane] = s_sc[sj * K + lane];
-    const int idx = s_next[sj];
-    if (lane == 0) tokens[n] = s_cand[s * K + idx];
-    prev = idx;
+    q_out[n * K + c] = s_sc[(s * K + prev) * K + c];
+    if (c == 0) tokens[n] = s_cand[s * K + g_cur[s * K]];
   }
 }
 

@@ -62,6 +62,26 @@ def test_fused_equals_chain_and_repeats(name):
     assert torch.equal(a["tokens"], d["tokens"]) and torch.equal(a["q"], d["q"])
 
 
+@pytest.mark.parametrize("modes", ["sampled:2.0", "alt:1.5", "greedy"])
+def test_fused_walk_follows_nonzero_choices(modes):
+    """Lattices that fit the fused kernel, with walks that leave row 0: q of
+    slot s must be the row of the index chosen at slot s - 1, tokens the
+    candidate chosen at slot s -- equal to the chain of entry points."""
+    require_gpu()
+    w = W.WORKLOADS["bf16_b16_v151936"].replace(n_req=8, plant_peak=False, modes=modes, vocab=8192,
+                                               valid_vocab=8192)
+    inp = W.make_inputs(w, device=DEV)
+    say(f"dflash_propose_block fused walk, {modes}")
+    a = _propose(w, inp)
+    c = _chain(w, inp)
+    torch.cuda.synchronize()
+    for k in ("scores", "tokens", "q"):
+        assert torch.equal(a[k], c[k]), k
+    # the walk must have left row 0 somewhere, or this test covers nothing
+    chosen = (a["ids"] == a["tokens"].unsqueeze(-1)).float().argmax(-1)
+    assert int((chosen[:, :-1] != 0).sum()) > 0
+
+
 def _e2e(w: W.Workload, req_sample):
     inp = W.make_inputs(w, device=DEV)
     say(f"dflash_propose_block {w.name} (end to end vs oracle)")
