@@ -139,6 +139,104 @@ def copy_calibration(n_bytes: int, reps: int):
                                            "dispatches": reps}}), flush=True)
 
 
+def call_bytes(w):
+    """Algorithmic bytes of each C-ABI call on workload w (inputs read once,
+    outputs written once; the lattice includes its projection)."""
+    e = w.elem_bytes
+    N, H, T, G = w.n_tokens, w.hidden, w.taps, w.groups
+    Ns, K, r, V, R = w.n_slot_rows, w.top_k, w.rank, w.valid_vocab, w.n_req
+    conv = 2 * N * H * e + N * T * G * e + T * H * e
+    topk = Ns * V * e + 12 * Ns * K
+    proj = Ns * H * e + r * H * e
+    gathers = 2 * Ns * K * r * e
+    lattice = proj + gathers + 12 * Ns * K + 8 * R + 4 * Ns * K * K
+    walk = 4 * Ns * K * K + 8 * Ns * K + 4 * Ns + 5 * R + 8 * Ns + 4 * Ns * K
+    propose = conv + topk + proj + gathers + 8 * R + 4 * Ns + 5 * R + 8 * Ns + 4 * Ns * K
+    return {"dflash_conv": conv, "dflash_topk": topk, "dflash_lattice": lattice, "dflash_walk": walk,
+            "dflash_propose_block": propose}
+
+
+def sweep(iters: int = 50, warm: int = 5):
+    """Per-call GPU time of every C-ABI entry point on every workload: HIP
+    events around each call on one stream, a 1 GiB scratch write before each
+    call (flushes the 256 MB Infinity Cache and keeps the GPU busy while the
+    host enqueues the call), median and p10/p90 over the timed calls."""
+    import torch
+    import block_draft_proposal_amd as D
+    import workloads as W
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        out = []
+        for it in range(warm + iters):
+            scratch.fill_(it & 0xff)
+            a, b = TimingEvent(), TimingEvent()
+            a.record(stream)
+            fn()
+            b.record(stream)
+            out.append((a, b))
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) * 1e3 for a, b in out[warm:])
+        pick = lambda q: t[min(len(t) - 1, int(q * (len(t) - 1) + 0.5))]
+        return pick(0.5), pick(0.1), pick(0.9)
+
+    # copy ceiling: 1 GiB device-to-device (reads 1 GiB, writes 1 GiB)
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    med, _, _ = timed(lambda: dst.copy_(src))
+    copy_gbs = 2 * (1 << 30) / (med * 1e-6) / 1e9
+    del src, dst
+    print(f"copy ceiling: 1 GiB device copy {med:.1f} us -> {copy_gbs:.0f} GB/s (read + write)\n")
+    print("| workload | call | median us | p10 us | p90 us | algorithmic MB | GB/s | % of 8 TB/s | % of copy |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for name, w in W.WORKLOADS.items():
+        cfg = D.make_config(taps=w.taps, group_size=w.group_size, rank=w.rank, top_k=w.top_k,
+                            multiplier=w.multiplier, softcap=w.softcap, block_size=w.block_size, hidden=w.hidden)
+        inp = W.make_inputs(w, device=dev)
+        R, B, S, K, H = w.n_req, w.block_size, w.slots, w.top_k, w.hidden
+        conv_out = torch.empty_like(inp["x"])
+        ids = torch.empty((R * S, K), dtype=torch.int64, device=dev)
+        unary = torch.empty((R * S, K), dtype=torch.float32, device=dev)
+        tk_ws = torch.empty(max(1, D.lib().dflash_topk_workspace_size(R * S, w.valid_vocab, K)), dtype=torch.uint8,
+                            device=dev)
+        D.dflash_conv(inp["x"], inp["base"][0], inp["delta"][:, 0], block_size=B, group_size=w.group_size, out=conv_out)
+        D.dflash_topk(inp["logits"], top_k=K, valid_vocab=w.valid_vocab, multiplier=w.multiplier, softcap=w.softcap,
+                      ids_out=ids, unary_out=unary, workspace=tk_ws)
+        hid = conv_out.view(R, B, H)[:, 1:, :]
+        lat_ws = torch.empty(max(1, D.lib().dflash_lattice_workspace_size(R, S, w.rank, H)), dtype=torch.uint8,
+                             device=dev)
+        scores = torch.empty((R, S, K, K), dtype=torch.float32, device=dev)
+        idv, unv = ids.view(R, S, K), unary.view(R, S, K)
+        tokens = torch.empty((R, S), dtype=torch.int64, device=dev)
+        q = torch.empty((R, S, K), dtype=torch.float32, device=dev)
+        call = D.ProposeBlock(cfg, x=inp["x"], conv_base=inp["base"][0], conv_delta=inp["delta"][:, 0],
+                              logits=inp["logits"], anchor=inp["anchor"], sel_a=inp["sel_a"], sel_b=inp["sel_b"],
+                              proj=inp["proj"], uniforms=inp["uniforms"], temperatures=inp["temperatures"],
+                              greedy_mask=inp["greedy_mask"], valid_vocab=w.valid_vocab)
+        fns = {
+            "dflash_conv": lambda: D.dflash_conv(inp["x"], inp["base"][0], inp["delta"][:, 0], block_size=B,
+                                                 group_size=w.group_size, out=conv_out),
+            "dflash_topk": lambda: D.dflash_topk(inp["logits"], top_k=K, valid_vocab=w.valid_vocab,
+                                                 multiplier=w.multiplier, softcap=w.softcap, ids_out=ids,
+                                                 unary_out=unary, workspace=tk_ws),
+            "dflash_lattice": lambda: D.dflash_lattice(idv, unv, hid, inp["anchor"], inp["sel_a"], inp["sel_b"],
+                                                       inp["proj"], scores_out=scores, workspace=lat_ws),
+            "dflash_walk": lambda: D.dflash_walk(scores, idv, inp["uniforms"], inp["temperatures"],
+                                                 inp["greedy_mask"], tokens_out=tokens, q_out=q),
+            "dflash_propose_block": lambda: call(stream),
+        }
+        nbytes = call_bytes(w)
+        for cname, fn in fns.items():
+            med, p10, p90 = timed(fn)
+            gbs = nbytes[cname] / (med * 1e-6) / 1e9
+            print(f"| {name} | {cname} | {med:.2f} | {p10:.2f} | {p90:.2f} | {nbytes[cname] / 1e6:.2f} | {gbs:.0f} | "
+                  f"{100 * gbs / HBM_PEAK_GBS:.1f} | {100 * gbs / copy_gbs:.1f} |", flush=True)
+        del inp, call, fns
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(w, n_req_sample: int, min_seconds: float = 10.0):
     """Time the oracle (as it stands) on a bounded sample of the workload:
     batches of n_req_sample requests (fresh seeds each) until min_seconds of
@@ -178,6 +276,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-requests", type=int, default=12)
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time every C-ABI call on every workload (markdown table) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters) and exit")
     args = ap.parse_args()
@@ -192,6 +292,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(1 << 30, 10)
+        return
+    if args.sweep:
+        sweep()
         return
 
     if not torch.cuda.is_available():
