@@ -162,7 +162,9 @@ hipError_t launch_walk(const WalkArgs& a, hipStream_t stream);
 // Lattice and walk in one kernel (one workgroup per request) when the
 // request's lattice and its staging fit in LDS; bit-identical to
 // launch_lattice followed by launch_walk.  scores_out may be null.
-constexpr size_t kLatticeWalkLdsMax = 64 * 1024;
+// gfx950 lets one workgroup address 160 KB of LDS
+constexpr size_t kLatticeWalkLdsMax = 160 * 1024;
+constexpr size_t kWalkLdsMax = 160 * 1024;
 size_t lattice_walk_lds_bytes(int slots, int top_k, int rank, int dtype);
 bool lattice_walk_fits(const struct SelectArgs& a);   // LDS size, rank multiple of a vector, 16-byte tables
 hipError_t launch_lattice_walk(const SelectArgs& a, const ProjPlan& p, const WalkArgs& w, float* scores_out,

@@ -194,6 +194,149 @@ __global__ __launch_bounds__(kThreads) void lattice_kernel(const int64_t* __rest
                      s_u, s_w, s_bt, s_ids, s_ids + K, scores + (int64_t)n * K * K);
 }
 
+// The same lattice block for the common case (rank a multiple of the 16-byte
+// vector, 16-byte aligned tables): 16-byte gathers of the A and B rows, B
+// kept one row per candidate in LDS, and each thread evaluates a TJ x TC
+// tile of entries, so that every LDS read feeds TJ or TC chains.  Every
+// entry is still one fma chain over k from 0 with w = A * u, so the result
+// equals lattice_block's bit for bit.
+// LDS: pred, cand [K] (int64), u [r], w [K][r+4] (fp32), B rows [K][r + 16 B].
+struct LatticeTileLds {
+  size_t pred, cand, u, w, b, bytes;
+  int wstride, bstride;
+};
+__host__ __device__ inline LatticeTileLds lattice_tile_layout(int K, int r, int elem) {
+  LatticeTileLds L;
+  L.wstride = r + 4;
+  L.bstride = r + 16 / elem;
+  size_t o = 0;
+  L.pred = o; o += (size_t)K * 8;
+  L.cand = o; o += (size_t)K * 8;
+  L.u = o;    o += (((size_t)r * 4) + 15) & ~(size_t)15;
+  L.w = o;    o += (size_t)K * L.wstride * 4;
+  L.b = o;    o += (size_t)K * L.bstride * elem;
+  L.bytes = o;
+  return L;
+}
+
+template <typename TIO, int TJ, int TC>
+__global__ __launch_bounds__(kThreads) void lattice_tiled_kernel(
+    const int64_t* __restrict__ ids, const float* __restrict__ unary, const int64_t* __restrict__ anchor,
+    const TIO* __restrict__ A, const TIO* __restrict__ B, const float* __restrict__ u_parts, int32_t ksplit,
+    int32_t slots, int32_t K, int32_t r, int64_t vocab, int32_t n_rows, float* __restrict__ scores) {
+  constexpr int VEC = Elem<TIO>::kVec;
+  extern __shared__ __align__(16) unsigned char lt_smem[];
+  const LatticeTileLds L = lattice_tile_layout(K, r, (int)sizeof(TIO));
+  int64_t* s_pred = reinterpret_cast<int64_t*>(lt_smem + L.pred);
+  int64_t* s_cand = reinterpret_cast<int64_t*>(lt_smem + L.cand);
+  float* s_u = reinterpret_cast<float*>(lt_smem + L.u);
+  float* s_w = reinterpret_cast<float*>(lt_smem + L.w);
+  TIO* s_b = reinterpret_cast<TIO*>(lt_smem + L.b);
+  const int tid = threadIdx.x;
+  const int n = blockIdx.x;
+  const int req = n / slots, s = n % slots;
+
+  for (int k = tid; k < r; k += kThreads) s_u[k] = sum_proj_slices(u_parts, ksplit, n_rows, r, n, k);
+  for (int j = tid; j < K; j += kThreads) {
+    s_pred[j] = (s == 0) ? anchor[req] : ids[((int64_t)req * slots + s - 1) * K + j];
+    s_cand[j] = ids[(int64_t)n * K + j];
+  }
+  __syncthreads();
+
+  // gather: 16-byte pieces, unconditional loads (ids clamped into range),
+  // out-of-range ids become NaN afterwards
+  {
+    constexpr int kPer = 4;
+    const int ppr = r / VEC;
+    const int n_pieces = K * ppr;                   // per table
+    const int total = 2 * n_pieces;
+    for (int base = 0; base < total; base += kThreads * kPer) {
+      uint4 raw[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int i = min(base + q * kThreads + tid, total - 1);
+        const bool is_b = i >= n_pieces;
+        const int ii = is_b ? i - n_pieces : i;
+        const int j = ii / ppr, v = ii - j * ppr;
+        const int64_t t = is_b ? s_cand[j] : s_pred[j];
+        const int64_t tc = (t >= 0 && t < vocab) ? t : 0;
+        raw[q] = *reinterpret_cast<const uint4*>((is_b ? B : A) + tc * r + v * VEC);
+      }
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int i = base + q * kThreads + tid;
+        if (i >= total) continue;
+        const bool is_b = i >= n_pieces;
+        const int ii = is_b ? i - n_pieces : i;
+        const int j = ii / ppr, v = ii - j * ppr;
+        const int64_t t = is_b ? s_cand[j] : s_pred[j];
+        const bool ok = t >= 0 && t < vocab;
+        if (is_b) {
+          TIO nanrow[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) nanrow[e] = Elem<TIO>::nan_value();
+          *reinterpret_cast<uint4*>(s_b + (size_t)j * L.bstride + v * VEC) =
+              ok ? raw[q] : *reinterpret_cast<const uint4*>(nanrow);
+        } else {
+          float a[VEC];
+          unpack16(raw[q], a);
+#pragma unroll
+          for (int e = 0; e < VEC; e += 4)
+            *reinterpret_cast<float4*>(s_w + j * L.wstride + v * VEC + e) =
+                make_float4((ok ? a[e] : __builtin_nanf("")) * s_u[v * VEC + e],
+                            (ok ? a[e + 1] : __builtin_nanf("")) * s_u[v * VEC + e + 1],
+                            (ok ? a[e + 2] : __builtin_nanf("")) * s_u[v * VEC + e + 2],
+                            (ok ? a[e + 3] : __builtin_nanf("")) * s_u[v * VEC + e + 3]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // TJ x TC tiles of the K x K block; rows and columns past K are clamped
+  // (computed, not stored)
+  const int ntc = (K + TC - 1) / TC, ntiles = ((K + TJ - 1) / TJ) * ntc;
+  for (int t = tid; t < ntiles; t += kThreads) {
+    const int j0 = (t / ntc) * TJ, c0 = (t % ntc) * TC;
+    const float* w[TJ];
+    const TIO* b[TC];
+#pragma unroll
+    for (int a = 0; a < TJ; ++a) w[a] = s_w + min(j0 + a, K - 1) * L.wstride;
+#pragma unroll
+    for (int c = 0; c < TC; ++c) b[c] = s_b + (size_t)min(c0 + c, K - 1) * L.bstride;
+    float acc[TJ][TC];
+#pragma unroll
+    for (int a = 0; a < TJ; ++a)
+#pragma unroll
+      for (int c = 0; c < TC; ++c) acc[a][c] = 0.f;
+    for (int k0 = 0; k0 < r; k0 += VEC) {
+      float bv[TC][VEC];
+#pragma unroll
+      for (int c = 0; c < TC; ++c) unpack16(*reinterpret_cast<const uint4*>(b[c] + k0), bv[c]);
+#pragma unroll
+      for (int a = 0; a < TJ; ++a) {
+#pragma unroll
+        for (int e4 = 0; e4 < VEC; e4 += 4) {
+          const float4 wv = *reinterpret_cast<const float4*>(w[a] + k0 + e4);
+#pragma unroll
+          for (int c = 0; c < TC; ++c) {
+            acc[a][c] = fmaf(wv.x, bv[c][e4 + 0], acc[a][c]);
+            acc[a][c] = fmaf(wv.y, bv[c][e4 + 1], acc[a][c]);
+            acc[a][c] = fmaf(wv.z, bv[c][e4 + 2], acc[a][c]);
+            acc[a][c] = fmaf(wv.w, bv[c][e4 + 3], acc[a][c]);
+          }
+        }
+      }
+    }
+    float* dst = scores + (int64_t)n * K * K;
+#pragma unroll
+    for (int a = 0; a < TJ; ++a)
+#pragma unroll
+      for (int c = 0; c < TC; ++c)
+        if (j0 + a < K && c0 + c < K) dst[(j0 + a) * K + c0 + c] = acc[a][c] + unary[(int64_t)n * K + c0 + c];
+  }
+}
+
 // Lane j's value of v, as a wave-uniform value.
 __device__ __forceinline__ float lane_value(float v, int j) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
@@ -287,6 +430,142 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(const float* __restrict_
   }
 }
 
+// Every row's walk decision, then the walked path, for one request whose
+// S x K x K scores sit in LDS (sc, overwritten: exponentials, then q).  A
+// row's decision does not depend on the path, so all S*K rows are decided in
+// parallel (row maxima, sums and CDFs sequential per row, as walk_decide
+// runs them; the fp64 exponentials spread over entries, in place).  The
+// path is then found by pointer jumping: with f_s the choice map of slot s
+// (row j -> index chosen in row (s, j)), the index chosen at slot s is
+// (f_s o ... o f_0)(0), an inclusive scan in ceil(log2 S) rounds; the row
+// walked at slot s is the index chosen at slot s - 1 (row 0 at slot 0).
+// Row sj of sc starts at sc + sj * (K + 1): the odd stride keeps the per-row
+// threads, which walk their rows in step, on distinct LDS banks.
+// mx, nxt, galt: [S*K] LDS scratch; un: the request's uniforms (LDS);
+// cand: the request's candidate ids [S][K] (LDS or global).  Every thread of
+// the workgroup calls; ends with the outputs written.
+template <int NT>
+__device__ void decide_and_walk(float* sc, float* mx, int* nxt, int* galt, const float* un, int S, int K,
+                                bool greedy, float temp, const FastDiv& div_k, int64_t row0,
+                                const int64_t* cand, int64_t* __restrict__ tokens, float* __restrict__ q_out) {
+  const int tid = threadIdx.x;
+  const int n_entries = S * K * K;
+  const int ks = K + 1;
+  if (greedy) {
+    for (int sj = tid; sj < S * K; sj += NT) {
+      float* row = sc + sj * ks;
+      // first maximum in candidate order = lowest index among ties
+      float best = row[0];
+      int idx = 0;
+      for (int c = 1; c < K; ++c) {
+        const float x = row[c];
+        if (x > best) { best = x; idx = c; }
+      }
+      for (int c = 0; c < K; ++c) row[c] = (c == idx) ? 1.f : 0.f;
+      nxt[sj] = idx;
+    }
+  } else {
+    const float t = fmaxf(temp, 1e-5f);
+    for (int sj = tid; sj < S * K; sj += NT) {
+      const float* row = sc + sj * ks;
+      float m = row[0] / t;
+      for (int c = 1; c < K; ++c) m = fmaxf(m, row[c] / t);
+      mx[sj] = m;
+    }
+    __syncthreads();
+    // exp rounded once to fp32 (from the fp64 exponential), over the score
+    for (int e = tid; e < n_entries; e += NT) {
+      const int sj = div_k.quot(e);
+      float* x = sc + sj * ks + (e - sj * K);
+      *x = (float)exp((double)(*x / t - mx[sj]));
+    }
+    __syncthreads();
+    for (int sj = tid; sj < S * K; sj += NT) {
+      float* row = sc + sj * ks;
+      float total = 0.f;
+      for (int c = 0; c < K; ++c) total += row[c];                 // left to right
+      const float u = un[div_k.quot(sj)];
+      float cdf = 0.f;
+      int cnt = 0;
+      for (int c = 0; c < K; ++c) {
+        const float p = row[c] / total;
+        row[c] = p;
+        cdf += p;                                                   // C_c left to right
+        cnt += (u >= cdf) ? 1 : 0;
+      }
+      nxt[sj] = cnt < K - 1 ? cnt : K - 1;
+    }
+  }
+  __syncthreads();
+  int* g_cur = nxt;
+  int* g_alt = galt;
+  for (int d = 1; d < S; d <<= 1) {
+    for (int i = tid; i < S * K; i += NT) {
+      const int s = div_k.quot(i);
+      g_alt[i] = (s >= d) ? g_cur[s * K + g_cur[i - d * K]] : g_cur[i];
+    }
+    __syncthreads();
+    int* tmp = g_cur; g_cur = g_alt; g_alt = tmp;
+  }
+  for (int i = tid; i < S * K; i += NT) {
+    const int s = div_k.quot(i), c = i - s * K;
+    const int prev = (s == 0) ? 0 : g_cur[(s - 1) * K];   // row walked at slot s
+    const int64_t n = row0 + s;
+    q_out[n * K + c] = sc[(s * K + prev) * ks + c];
+    if (c == 0) tokens[n] = cand[s * K + g_cur[s * K]];
+  }
+}
+
+// Walk for one request in one workgroup of 1024 threads when its scores fit
+// in LDS: the scores, staged with batched coalesced loads, then
+// decide_and_walk.  Same arithmetic as walk_kernel (bit-identical tokens and
+// q).  LDS: scores [S][K][K+1], row maxima, choice maps, scan buffer [S][K],
+// uniforms [S].
+constexpr int kWalkThreads = 1024;
+__host__ __device__ inline size_t walk_lds_bytes(int S, int K) {
+  return (size_t)S * K * (K + 1) * 4 + 3 * (size_t)S * K * 4 + (size_t)S * 4;
+}
+
+__global__ __launch_bounds__(kWalkThreads) void walk_lds_kernel(const float* __restrict__ scores,
+                                                                const int64_t* __restrict__ ids,
+                                                                const float* __restrict__ uniforms,
+                                                                const float* __restrict__ temperatures,
+                                                                const uint8_t* __restrict__ greedy_mask,
+                                                                int32_t slots, int32_t K,
+                                                                int64_t* __restrict__ tokens,
+                                                                float* __restrict__ q_out) {
+  extern __shared__ __align__(16) float wk_smem[];
+  const int S = slots;
+  const int req = blockIdx.x, tid = threadIdx.x;
+  float* sc = wk_smem;
+  float* mx = sc + S * K * (K + 1);
+  int* nxt = reinterpret_cast<int*>(mx + S * K);
+  int* galt = nxt + S * K;
+  float* un = reinterpret_cast<float*>(galt + S * K);
+  const int64_t row0 = (int64_t)req * S;
+  const int n_e = S * K * K;
+  const float* src = scores + row0 * K * K;
+  const FastDiv div_k(K);                           // indices < S*K*K <= 40960 (LDS bound)
+  constexpr int kBatch = 16;                        // loads issued before the first store
+  for (int base = 0; base < n_e; base += kWalkThreads * kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) v[q] = src[min(base + q * kWalkThreads + tid, n_e - 1)];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int i = base + q * kWalkThreads + tid;
+      if (i < n_e) {
+        const int sj = div_k.quot(i);
+        sc[sj * (K + 1) + i - sj * K] = v[q];
+      }
+    }
+  }
+  for (int i = tid; i < S; i += kWalkThreads) un[i] = uniforms[row0 + i];
+  __syncthreads();
+  decide_and_walk<kWalkThreads>(sc, mx, nxt, galt, un, S, K, greedy_mask[req] != 0, temperatures[req], div_k,
+                                row0, ids + row0 * K, tokens, q_out);
+}
+
 // Lattice + walk for one request in one workgroup of 1024 threads, when the
 // request's whole lattice and its staging fit in LDS.  Same per-entry
 // arithmetic as lattice_block (u summed over the projection slices in order,
@@ -297,19 +576,14 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(const float* __restrict_
 //   1. ids of every slot and its predecessor, u, unary, uniforms -> LDS
 //   2. w = A[pred] (.) u (fp32) and the B[cand] rows -> LDS
 //   3. one thread per lattice entry: its fma chain over k
-//   4. every row's decision, which does not depend on the path: row maxima
-//      and sums stay sequential per row, the fp64 exponentials are spread
-//      over the entries
-//   5. the walked path by pointer jumping: the index chosen at slot s is the
-//      composition of the slots' choice maps 0..s applied to row 0, an
-//      inclusive scan in ceil(log2 S) rounds; then q rows and tokens are
-//      written in parallel.
+//   4, 5. decide_and_walk: every row's decision in parallel, then the walked
+//      path by pointer jumping, q rows and tokens written in parallel.
 // LDS layout: pred ids [S][K], cand ids [S][K] (int64), w [S][K][r+4] (fp32;
 // rows 16-byte aligned and 4 banks apart), B rows [S][K][r + 16 bytes]
-// (storage dtype, one row per candidate), unary [S][K], scores [S][K][K]
-// (then q), exponentials [S][K][K] (holding u [S][r] during the gather and
-// the scan's second buffer during the walk), row maxima [S][K], uniforms [S],
-// chosen index per row [S][K].
+// (storage dtype, one row per candidate), unary [S][K], scores [S][K][K+1]
+// (then exponentials, then q), u [S][r] during the gather (the scan's
+// second buffer during the walk), row maxima [S][K], uniforms [S], chosen
+// index per row [S][K].
 constexpr int kLWThreads = 1024;
 
 struct LatticeWalkLds {
@@ -321,15 +595,15 @@ __host__ __device__ inline LatticeWalkLds lattice_walk_layout(int S, int K, int 
   LatticeWalkLds L;
   L.wstride = r + 4;
   L.bstride = r + 16 / elem;
-  const size_t e_bytes = (size_t)S * K * K * 4, u_bytes = (size_t)S * r * 4, g_bytes = (size_t)S * K * 4;
+  const size_t u_bytes = (size_t)S * r * 4, g_bytes = (size_t)S * K * 4;
   size_t o = 0;
   L.pred = o;  o += (size_t)S * K * 8;
   L.cand = o;  o += (size_t)S * K * 8;
   L.w = o;     o += (size_t)S * K * L.wstride * 4;
   L.b = o;     o += (size_t)S * K * L.bstride * elem;
   L.unary = o; o += (size_t)S * K * 4;
-  L.sc = o;    o += (size_t)S * K * K * 4;
-  L.e = o;     o += (e_bytes > u_bytes ? (e_bytes > g_bytes ? e_bytes : g_bytes) : (u_bytes > g_bytes ? u_bytes : g_bytes));
+  L.sc = o;    o += (size_t)S * K * (K + 1) * 4;
+  L.e = o;     o += u_bytes > g_bytes ? u_bytes : g_bytes;
   L.mx = o;    o += (size_t)S * K * 4;
   L.un = o;    o += (size_t)S * 4;
   L.next = o;  o += (size_t)S * K * 4;
@@ -351,12 +625,11 @@ __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
   const LatticeWalkLds L = lattice_walk_layout(S, K, r, (int)sizeof(TIO));
   int64_t* s_pred = reinterpret_cast<int64_t*>(lw_smem + L.pred);
   int64_t* s_cand = reinterpret_cast<int64_t*>(lw_smem + L.cand);
-  float* s_u = reinterpret_cast<float*>(lw_smem + L.e);      // u lives in the exponentials' space until phase 4
+  float* s_u = reinterpret_cast<float*>(lw_smem + L.e);      // u during the gather, the scan buffer afterwards
   float* s_w = reinterpret_cast<float*>(lw_smem + L.w);
   TIO* s_b = reinterpret_cast<TIO*>(lw_smem + L.b);
   float* s_unary = reinterpret_cast<float*>(lw_smem + L.unary);
   float* s_sc = reinterpret_cast<float*>(lw_smem + L.sc);
-  float* s_e = reinterpret_cast<float*>(lw_smem + L.e);
   float* s_mx = reinterpret_cast<float*>(lw_smem + L.mx);
   float* s_un = reinterpret_cast<float*>(lw_smem + L.un);
   int* s_next = reinterpret_cast<int*>(lw_smem + L.next);
@@ -457,78 +730,14 @@ __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
       }
     }
     const float v = acc + s_unary[s * K + c];
-    s_sc[e] = v;
+    s_sc[sj * (K + 1) + c] = v;
     if (scores_out) scores_out[row0 * K * K + e] = v;
   }
   __syncthreads();
 
-  // ---- 4. every row's decision (q written over the row's scores) ----------
-  const bool greedy = greedy_mask[req] != 0;       // uniform over the workgroup
-  const float temp = temperatures[req];
-  if (greedy) {
-    for (int sj = tid; sj < S * K; sj += kLWThreads) {
-      float* row = s_sc + sj * K;
-      // first maximum in candidate order = lowest index among ties
-      float best = row[0];
-      int idx = 0;
-      for (int c = 1; c < K; ++c) {
-        const float x = row[c];
-        if (x > best) { best = x; idx = c; }
-      }
-      for (int c = 0; c < K; ++c) row[c] = (c == idx) ? 1.f : 0.f;
-      s_next[sj] = idx;
-    }
-  } else {
-    const float t = fmaxf(temp, 1e-5f);
-    for (int sj = tid; sj < S * K; sj += kLWThreads) {
-      const float* row = s_sc + sj * K;
-      float mx = row[0] / t;
-      for (int c = 1; c < K; ++c) mx = fmaxf(mx, row[c] / t);
-      s_mx[sj] = mx;
-    }
-    __syncthreads();
-    // exp rounded once to fp32 (from the fp64 exponential)
-    for (int e = tid; e < n_entries; e += kLWThreads) s_e[e] = (float)exp((double)(s_sc[e] / t - s_mx[div_k.quot(e)]));
-    __syncthreads();
-    for (int sj = tid; sj < S * K; sj += kLWThreads) {
-      float* row = s_sc + sj * K;
-      const float* ex = s_e + sj * K;
-      float total = 0.f;
-      for (int c = 0; c < K; ++c) total += ex[c];                   // left to right
-      const float u = s_un[div_k.quot(sj)];
-      float cdf = 0.f;
-      int cnt = 0;
-      for (int c = 0; c < K; ++c) {
-        const float p = ex[c] / total;
-        row[c] = p;
-        cdf += p;                                                   // C_c left to right
-        cnt += (u >= cdf) ? 1 : 0;
-      }
-      s_next[sj] = cnt < K - 1 ? cnt : K - 1;
-    }
-  }
-  __syncthreads();
-
-  // ---- 5. walk: g_s = choice maps of slots 0..s composed, by pointer
-  // jumping; the index chosen at slot s is g_s(0), and the row walked there
-  // is the one of the index chosen at slot s - 1 (row 0 at slot 0) --------
-  int* g_cur = s_next;
-  int* g_alt = reinterpret_cast<int*>(lw_smem + L.e);
-  for (int d = 1; d < S; d <<= 1) {
-    for (int i = tid; i < S * K; i += kLWThreads) {
-      const int s = div_k.quot(i);
-      g_alt[i] = (s >= d) ? g_cur[s * K + g_cur[i - d * K]] : g_cur[i];
-    }
-    __syncthreads();
-    int* t = g_cur; g_cur = g_alt; g_alt = t;
-  }
-  for (int i = tid; i < S * K; i += kLWThreads) {
-    const int s = div_k.quot(i), c = i - s * K;
-    const int prev = (s == 0) ? 0 : g_cur[(s - 1) * K];   // row walked at slot s
-    const int64_t n = row0 + s;
-    q_out[n * K + c] = s_sc[(s * K + prev) * K + c];
-    if (c == 0) tokens[n] = s_cand[s * K + g_cur[s * K]];
-  }
+  // ---- 4, 5. every row's decision, then the walked path --------------------
+  decide_and_walk<kLWThreads>(s_sc, s_mx, s_next, reinterpret_cast<int*>(lw_smem + L.e), s_un, S, K,
+                              greedy_mask[req] != 0, temperatures[req], div_k, row0, s_cand, tokens, q_out);
 }
 
 }  // namespace
@@ -595,6 +804,24 @@ size_t lattice_lds_bytes(int K, int r) {
 hipError_t launch_lattice(const SelectArgs& a, const ProjPlan& p, hipStream_t stream) {
   const int n_rows = a.n_req * a.slots;
   if (n_rows == 0) return hipSuccess;
+  const int vec = a.dtype == DFLASH_BF16 ? 8 : 4;
+  if (a.rank % vec == 0 && (reinterpret_cast<uintptr_t>(a.sel_a) & 15) == 0 &&
+      (reinterpret_cast<uintptr_t>(a.sel_b) & 15) == 0) {
+    const size_t lds = lattice_tile_layout(a.top_k, a.rank, a.dtype == DFLASH_BF16 ? 2 : 4).bytes;
+    // 2 x 2 tiles once the block has enough entries to keep the threads busy
+    const bool big = a.top_k >= 16;
+#define DFLASH_LT(TIO, TJ, TC)                                                                                    \
+  hipLaunchKernelGGL((lattice_tiled_kernel<TIO, TJ, TC>), dim3(n_rows), dim3(kThreads), lds, stream, a.ids, a.unary, \
+                     a.anchor, static_cast<const TIO*>(a.sel_a), static_cast<const TIO*>(a.sel_b), a.u_parts,       \
+                     p.ksplit, a.slots, a.top_k, a.rank, a.vocab, n_rows, a.scores)
+    if (a.dtype == DFLASH_BF16) {
+      if (big) DFLASH_LT(uint16_t, 2, 2); else DFLASH_LT(uint16_t, 1, 1);
+    } else {
+      if (big) DFLASH_LT(float, 2, 2); else DFLASH_LT(float, 1, 1);
+    }
+#undef DFLASH_LT
+    return hipGetLastError();
+  }
   const size_t lds = lattice_lds_bytes(a.top_k, a.rank);
   if (a.dtype == DFLASH_BF16)
     hipLaunchKernelGGL(lattice_kernel<uint16_t>, dim3(n_rows), dim3(kThreads), lds, stream, a.ids, a.unary,
@@ -609,6 +836,12 @@ hipError_t launch_lattice(const SelectArgs& a, const ProjPlan& p, hipStream_t st
 
 hipError_t launch_walk(const WalkArgs& a, hipStream_t stream) {
   if (a.n_req == 0 || a.slots == 0) return hipSuccess;
+  const size_t wl = walk_lds_bytes(a.slots, a.top_k);
+  if (wl <= kWalkLdsMax) {
+    hipLaunchKernelGGL(walk_lds_kernel, dim3(a.n_req), dim3(kWalkThreads), wl, stream, a.scores, a.ids, a.uniforms,
+                       a.temperatures, a.greedy, a.slots, a.top_k, a.tokens, a.q);
+    return hipGetLastError();
+  }
   const size_t need = (size_t)a.slots * a.top_k * a.top_k * sizeof(float) +
                       (size_t)a.slots * a.top_k * sizeof(int64_t) + (size_t)a.slots * sizeof(float);
   const size_t lds = need <= (size_t)kWalkLdsBytes ? need : 0;

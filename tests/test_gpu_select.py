@@ -172,14 +172,17 @@ def test_walk_greedy_rows_are_deterministic_in_a_mixed_batch():
         assert torch.equal(t2[0], t0[r]) and torch.equal(q2[0], q0[r])
 
 
-def test_walk_large_lattice_beyond_lds_staging():
-    # S * K * K above the 16384 floats staged in LDS: rows are read from memory.
+@pytest.mark.parametrize("S", [20, 45])
+def test_walk_large_lattice_beyond_lds_staging(S):
+    # K = 32: S = 20 stages 80 KB of scores in the 1024-thread walk (beyond
+    # the 64 KB of earlier parts, within gfx950's 160 KB per workgroup);
+    # S = 45 (180 KB) is beyond it, and the serial walk reads rows from memory.
     require_gpu()
-    g = torch.Generator(device=DEV).manual_seed(9)
-    R, S, K = 5, 20, 32
+    g = torch.Generator(device=DEV).manual_seed(9 + S)
+    R, K = 5, 32
     scores = torch.randn((R, S, K, K), generator=g, device=DEV) * 2
     ids = torch.randint(0, 1000, (R, S, K), generator=g, device=DEV)
     uni = torch.rand((R, S), generator=g, device=DEV)
     temps = torch.full((R,), 0.9, device=DEV)
     greedy = torch.tensor([True, False, False, True, False], device=DEV)
-    _walk_check(scores, ids, uni, temps, greedy, "unstaged")
+    _walk_check(scores, ids, uni, temps, greedy, f"S={S}")
