@@ -156,7 +156,7 @@ def call_bytes(w):
             "dflash_propose_block": propose}
 
 
-def sweep(iters: int = 50, warm: int = 5):
+def sweep(iters: int = 50, warm: int = 5, only=None):
     """Per-call GPU time of every C-ABI entry point on every workload: HIP
     events around each call on one stream, a 1 GiB scratch write before each
     call (flushes the 256 MB Infinity Cache and keeps the GPU busy while the
@@ -192,6 +192,8 @@ def sweep(iters: int = 50, warm: int = 5):
     print("| workload | call | median us | p10 us | p90 us | algorithmic MB | GB/s | % of 8 TB/s | % of copy |")
     print("|---|---|---|---|---|---|---|---|---|")
     for name, w in W.WORKLOADS.items():
+        if only and name not in only:
+            continue
         cfg = D.make_config(taps=w.taps, group_size=w.group_size, rank=w.rank, top_k=w.top_k,
                             multiplier=w.multiplier, softcap=w.softcap, block_size=w.block_size, hidden=w.hidden)
         inp = W.make_inputs(w, device=dev)
@@ -278,6 +280,8 @@ def main():
     ap.add_argument("--cpu-sample-requests", type=int, default=12)
     ap.add_argument("--sweep", action="store_true",
                     help="only time every C-ABI call on every workload (markdown table) and exit")
+    ap.add_argument("--sweep-only", nargs="*", default=None, metavar="WORKLOAD",
+                    help="with --sweep: only these workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling rocprofv3 byte counters) and exit")
     args = ap.parse_args()
@@ -294,7 +298,7 @@ def main():
         copy_calibration(1 << 30, 10)
         return
     if args.sweep:
-        sweep()
+        sweep(only=args.sweep_only)
         return
 
     if not torch.cuda.is_available():

@@ -125,6 +125,7 @@ constexpr int kMaxProjSplit = 32;
 struct ProjPlan {
   int32_t n_rows, rank, hidden;
   int32_t row_tiles, ksplit, kslice;   // split of the contraction over workgroups
+  int32_t frags;                       // row fragments of 16 per wave (bf16)
   size_t bytes;                        // fp32 partials [ksplit][n_rows][rank]
 };
 ProjPlan plan_proj(int32_t n_rows, int32_t rank, int32_t hidden, int32_t dtype);

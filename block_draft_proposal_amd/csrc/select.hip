@@ -35,6 +35,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kRowsPerWG = 64;       // 4 waves x 16 rows
+constexpr int kProjUnroll = 4;       // projection k-steps whose loads are issued together
 
 // Exact n / d for 0 <= n, d < 2^16 (d >= 1) by one multiply-high:
 // q = (n * ceil(2^32 / d)) >> 32.  The error n * (M d - 2^32) / (d 2^32) is
@@ -52,40 +53,69 @@ __device__ __forceinline__ const void* hidden_row(const void* hidden, int64_t re
   return static_cast<const char*>(hidden) + ((int64_t)req * req_stride + (int64_t)s * slot_stride) * elem_bytes;
 }
 
-// RT = column tiles of 16 per wave (rank <= 16 * RT).
-template <int RT>
+// RT = column tiles of 16 per wave (rank <= 16 * RT); FR = row fragments of
+// 16 per wave, so that each wave reuses every P fragment it loads for FR
+// MFMAs (P is read from cache once per 16 * FR rows instead of per 16).  A
+// workgroup covers 64 * FR rows, all rank columns and one slice of H.
+template <int RT, int FR>
 __global__ __launch_bounds__(kThreads) void proj_mfma_kernel(const uint16_t* __restrict__ hidden,
                                                              int64_t req_stride, int64_t slot_stride,
                                                              int32_t slots, const uint16_t* __restrict__ P,
                                                              int32_t n_rows, int32_t rank, int32_t H,
                                                              int32_t kslice, float* __restrict__ u_parts) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row_base = blockIdx.x * kRowsPerWG + wave * 16;
+  const int row_base = (blockIdx.x * 4 + wave) * 16 * FR;
   const int split = blockIdx.y;
   const int k0 = split * kslice;
   const int k1 = min(H, k0 + kslice);
-  const int arow = row_base + (lane & 15);
-  const bool arow_ok = arow < n_rows;
-  const uint16_t* hrow = arow_ok ? static_cast<const uint16_t*>(hidden_row(hidden, req_stride, slot_stride,
-                                                                         slots, arow, 2))
-                                 : hidden;
   const int kofs = 8 * (lane >> 4);
-  f32x4_t acc[RT];
+  const uint16_t* hrow[FR];
+  bool arow_ok[FR];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int kk = k0; kk < k1; kk += 32) {
-    const int k = kk + kofs;
-    const bool k_ok = k < k1;
-    uint4 av = make_uint4(0u, 0u, 0u, 0u);
-    if (arow_ok && k_ok) av = *reinterpret_cast<const uint4*>(hrow + k);
-    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+  for (int f = 0; f < FR; ++f) {
+    const int arow = row_base + 16 * f + (lane & 15);
+    arow_ok[f] = arow < n_rows;
+    hrow[f] = arow_ok[f] ? static_cast<const uint16_t*>(hidden_row(hidden, req_stride, slot_stride, slots, arow, 2))
+                         : hidden;
+  }
+  f32x4_t acc[FR][RT];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int col = t * 16 + (lane & 15);
-      uint4 bv = make_uint4(0u, 0u, 0u, 0u);
-      if (col < rank && k_ok) bv = *reinterpret_cast<const uint4*>(P + (int64_t)col * H + k);
-      const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bv);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[t], 0, 0, 0);
+  for (int f = 0; f < FR; ++f)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[f][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // kProjUnroll k-steps per round: every load of the round is issued (at an
+  // address clamped into the slice and the table) before the first MFMA;
+  // operands past the slice, the rows or the rank are zeroed afterwards, so
+  // each output is the same MFMA chain over the slice's k-steps in order,
+  // whatever FR is.
+  constexpr int U = FR > 1 ? 2 : kProjUnroll;
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  for (int kk = k0; kk < k1; kk += 32 * U) {
+    uint4 av[U][FR], bv[U][RT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kc = min(kk + 32 * u + kofs, k1 - 8);
+#pragma unroll
+      for (int f = 0; f < FR; ++f) av[u][f] = *reinterpret_cast<const uint4*>(hrow[f] + kc);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int col = min(t * 16 + (lane & 15), rank - 1);
+        bv[u][t] = *reinterpret_cast<const uint4*>(P + (int64_t)col * H + kc);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool k_ok = kk + 32 * u + kofs < k1;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const bool c_ok = t * 16 + (lane & 15) < rank;
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, (c_ok && k_ok) ? bv[u][t] : zero);
+#pragma unroll
+        for (int f = 0; f < FR; ++f) {
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (arow_ok[f] && k_ok) ? av[u][f] : zero);
+          acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[f][t], 0, 0, 0);
+        }
+      }
     }
   }
   // D layout: lane holds column (lane & 15), rows 4 * (lane >> 4) + v.
@@ -94,10 +124,12 @@ __global__ __launch_bounds__(kThreads) void proj_mfma_kernel(const uint16_t* __r
     const int col = t * 16 + (lane & 15);
     if (col >= rank) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = row_base + 4 * (lane >> 4) + v;
-      if (row < n_rows) u_parts[((int64_t)split * n_rows + row) * rank + col] = acc[t][v];
-    }
+    for (int f = 0; f < FR; ++f)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = row_base + 16 * f + 4 * (lane >> 4) + v;
+        if (row < n_rows) u_parts[((int64_t)split * n_rows + row) * rank + col] = acc[f][t][v];
+      }
   }
 }
 
@@ -748,7 +780,9 @@ ProjPlan plan_proj(int32_t n_rows, int32_t rank, int32_t hidden, int32_t dtype) 
   p.rank = rank;
   p.hidden = hidden;
   if (dtype == DFLASH_BF16) {
-    p.row_tiles = (n_rows + kRowsPerWG - 1) / kRowsPerWG;
+    // four row fragments per wave once there are rows enough to fill the chip
+    p.frags = n_rows >= 4096 ? 4 : 1;
+    p.row_tiles = (n_rows + kRowsPerWG * p.frags - 1) / (kRowsPerWG * p.frags);
     int ks = p.row_tiles > 0 ? (512 + p.row_tiles - 1) / p.row_tiles : 1;
     const int max_ks = hidden / 256 > 1 ? hidden / 256 : 1;
     if (ks > max_ks) ks = max_ks;
@@ -776,15 +810,22 @@ hipError_t launch_proj(const SelectArgs& a, const ProjPlan& p, hipStream_t strea
     const uint16_t* h = static_cast<const uint16_t*>(a.hidden);
     const uint16_t* P = static_cast<const uint16_t*>(a.proj);
     const int tiles = (a.rank + 15) / 16;
-#define DFLASH_PROJ(RT)                                                                        \
-  hipLaunchKernelGGL(proj_mfma_kernel<RT>, grid, dim3(kThreads), 0, stream, h, a.hidden_req_stride, \
-                     a.hidden_slot_stride, a.slots, P, n_rows, a.rank, a.hidden_size, p.kslice,    \
+#define DFLASH_PROJ(RT, FR)                                                                        \
+  hipLaunchKernelGGL((proj_mfma_kernel<RT, FR>), grid, dim3(kThreads), 0, stream, h, a.hidden_req_stride, \
+                     a.hidden_slot_stride, a.slots, P, n_rows, a.rank, a.hidden_size, p.kslice,          \
                      a.u_parts)
-    if (tiles <= 1) DFLASH_PROJ(1);
-    else if (tiles <= 2) DFLASH_PROJ(2);
-    else if (tiles <= 4) DFLASH_PROJ(4);
-    else if (tiles <= 8) DFLASH_PROJ(8);
-    else return hipErrorInvalidValue;   // rank > 128 is rejected by the API layer
+#define DFLASH_PROJ_RT(FR)                  \
+  if (tiles <= 1) DFLASH_PROJ(1, FR);       \
+  else if (tiles <= 2) DFLASH_PROJ(2, FR);  \
+  else if (tiles <= 4) DFLASH_PROJ(4, FR);  \
+  else if (tiles <= 8) DFLASH_PROJ(8, FR);  \
+  else return hipErrorInvalidValue;   /* rank > 128 is rejected by the API layer */
+    if (p.frags == 4) {
+      DFLASH_PROJ_RT(4)
+    } else {
+      DFLASH_PROJ_RT(1)
+    }
+#undef DFLASH_PROJ_RT
 #undef DFLASH_PROJ
   } else {
     const int64_t n = (int64_t)n_rows * a.rank;
