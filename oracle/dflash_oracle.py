@@ -31,6 +31,8 @@ Readings where the pages are silent (each listed again in the design doc):
     at or beyond the logical vocab are never selected.
   * lattice: A and B are [V, r] per-token tables, project(h) = P h with
     P [r, H]; slot 0's predecessor is the anchor.
+  * candidates from hidden states: the dense head's logits are the exact
+    sums rounded once to the storage dtype, and the top-k ranks them.
 """
 from __future__ import annotations
 
@@ -175,6 +177,41 @@ def topk(logits: np.ndarray, valid_vocab: int, top_k: int, multiplier: float,
         out_ids[n] = order[:top_k]
     unary = transform(np.take_along_axis(z, out_ids, axis=1), multiplier, softcap)
     return out_ids, unary
+
+
+# ---------------------------------------------------------------------------
+# Candidates straight from the slot hidden states  [DF2] implementation
+# breakdown and risk notes: compute_candidates multiplies the hidden rows by
+# the target lm_head weight taken as a dense matrix, then applies the unary
+# transform and the deterministic top-k.
+# Reading: the dense head's product is returned in the model's storage dtype
+# (a bf16 matmul returns bf16), so the logits are the exact sums rounded once
+# to that dtype, and the top-k ranks those rounded values.
+# ---------------------------------------------------------------------------
+
+def lm_head_logits(h: np.ndarray, weight: np.ndarray, dtype: str) -> np.ndarray:
+    """h [rows, H], weight [V, H] -> logits [rows, V]: every product summed
+    exactly enough in float64 (each bf16 x bf16 product is exact, and float64
+    holds the sum of H of them to far below the bf16 step), then rounded once
+    to the storage dtype."""
+    z = np.asarray(h, np.float64) @ np.asarray(weight, np.float64).T
+    return round_to_dtype(z, dtype)
+
+
+def lm_head_sum_bound(h: np.ndarray, weight: np.ndarray) -> np.ndarray:
+    """Per logit, a bound on how far an fp32 accumulation of the H exact
+    products (in any order) can land from the exact sum: H * 2^-24 *
+    sum_k |h_k| |w_k| (the classic n*u bound for a sum of n terms)."""
+    a = np.abs(np.asarray(h, np.float64))
+    b = np.abs(np.asarray(weight, np.float64))
+    return a.shape[1] * 2.0 ** -24 * (a @ b.T)
+
+
+def compute_candidates(h: np.ndarray, weight: np.ndarray, valid_vocab: int, top_k: int,
+                       multiplier: float, softcap: float, dtype: str):
+    """h [rows, H] -> (ids [rows, K], unary [rows, K]): the top-k of the
+    rounded head logits, as topk() ranks any logits."""
+    return topk(lm_head_logits(h, weight, dtype), valid_vocab, top_k, multiplier, softcap)
 
 
 # ---------------------------------------------------------------------------
