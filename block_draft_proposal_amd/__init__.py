@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     dflash_topk,
     dflash_lattice,
     dflash_walk,
+    dflash_lm_head,
     dflash_propose_block,
     ProposeBlock,
     propose_block_workspace_size,

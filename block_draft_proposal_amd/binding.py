@@ -70,6 +70,7 @@ _SIGNATURES = {
     "dflash_lattice": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32,
                                 _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_vp, _c_vp, _c_size, _c_vp]),
     "dflash_walk": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp]),
+    "dflash_lm_head": (_c_i32, [_c_vp, _c_i64, _c_vp, _c_i64, _c_i32, _c_i64, _c_vp, _c_i64, _c_i32, _c_vp]),
     "dflash_propose_block_workspace_size": (_c_size, [ctypes.POINTER(DraftConfig), _c_i32, _c_i64]),
     "dflash_propose_block": (_c_i32, [ctypes.POINTER(DraftConfig), ctypes.POINTER(BlockArgs), _c_vp]),
 }
@@ -221,6 +222,21 @@ def dflash_walk(scores: torch.Tensor, ids: torch.Tensor, uniforms: torch.Tensor,
     _check(lib().dflash_walk(_p(scores), _p(ids), _p(uniforms), _p(temperatures), _p(greedy_mask), R, S, K,
                              _p(tokens_out), _p(q_out), _stream(stream)))
     return tokens_out, q_out
+
+
+def dflash_lm_head(hidden: torch.Tensor, weight: torch.Tensor, *, vocab: Optional[int] = None,
+                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """hidden [rows, H] bf16 (rows may be strided); weight [V, H] bf16.
+    Returns logits [rows, V] bf16 = hidden @ weight.T rounded once."""
+    if hidden.dim() != 2 or hidden.stride(1) != 1 or not weight.is_contiguous():
+        raise ValueError("hidden rows and weight must be contiguous")
+    rows, H = hidden.shape
+    V = weight.shape[0] if vocab is None else vocab
+    if out is None:
+        out = torch.empty((rows, V), dtype=hidden.dtype, device=hidden.device)
+    _check(lib().dflash_lm_head(_p(hidden), hidden.stride(0) if rows else H, _p(weight), rows, H, V, _p(out),
+                                out.stride(0) if rows else V, _dtype_code(hidden), _stream(stream)))
+    return out
 
 
 def propose_block_workspace_size(cfg: DraftConfig, n_req: int, valid_vocab: int) -> int:

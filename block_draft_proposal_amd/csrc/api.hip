@@ -329,6 +329,34 @@ int dflash_walk(const float* scores, const int64_t* ids, const float* uniforms, 
   return st == DFLASH_OK ? ok() : st;
 }
 
+int dflash_lm_head(const void* hidden, int64_t hidden_row_stride, const void* weight, int64_t n_rows,
+                   int32_t hidden_size, int64_t vocab, void* logits_out, int64_t logits_row_stride, int32_t dtype,
+                   dflash_stream_t stream) {
+  const char* who = "dflash_lm_head";
+  if (!dtype_ok(dtype)) return fail(DFLASH_ERR_INVALID_ARG, "%s: unknown dtype %d", who, dtype);
+  if (dtype != DFLASH_BF16) return fail(DFLASH_ERR_UNSUPPORTED, "%s: bf16 only", who);
+  if (n_rows < 0 || vocab < 0) return fail(DFLASH_ERR_INVALID_ARG, "%s: n_rows and vocab must be >= 0", who);
+  if (n_rows >= ((int64_t)1 << 31) || vocab >= ((int64_t)1 << 31))
+    return fail(DFLASH_ERR_UNSUPPORTED, "%s: n_rows and vocab must be < 2^31", who);
+  if (hidden_size < 8 || hidden_size % 8)
+    return fail(DFLASH_ERR_UNSUPPORTED, "%s: hidden_size must be a positive multiple of 8", who);
+  if (hidden_row_stride < hidden_size || logits_row_stride < vocab)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: row strides shorter than the rows", who);
+  if (hidden_row_stride % 8 || logits_row_stride % 8)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: row strides must be multiples of 8 elements", who);
+  if (n_rows == 0 || vocab == 0) return ok();
+  if (!hidden || !weight || !logits_out) return fail(DFLASH_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!aligned16(hidden) || !aligned16(weight) || !aligned16(logits_out))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: hidden, weight and logits_out must be 16-byte aligned", who);
+  const size_t lb = ((size_t)(n_rows - 1) * logits_row_stride + vocab) * 2;
+  if (overlaps(logits_out, lb, hidden, ((size_t)(n_rows - 1) * hidden_row_stride + hidden_size) * 2) ||
+      overlaps(logits_out, lb, weight, (size_t)vocab * hidden_size * 2))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: logits_out overlaps an input", who);
+  dflash::LmHeadArgs a{hidden, hidden_row_stride, weight, n_rows, hidden_size, vocab, logits_out, logits_row_stride};
+  const int st = launch_status(dflash::launch_lm_head(a, as_hip(stream)), who);
+  return st == DFLASH_OK ? ok() : st;
+}
+
 size_t dflash_propose_block_workspace_size(const dflash_draft_config* cfg, int32_t n_req, int64_t valid_vocab) {
   if (!cfg || n_req <= 0 || valid_vocab <= 0 || cfg->block_size < 2 || cfg->selector_top_k <= 0 ||
       cfg->selector_rank <= 0 || cfg->hidden_size <= 0)

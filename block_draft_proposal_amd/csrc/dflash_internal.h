@@ -37,6 +37,25 @@ template <> struct Elem<float> {
   __device__ static float nan_value() { return __builtin_nanf(""); }
 };
 
+// 16 bytes as a native 4 x u32 vector.  Register arrays of it, and selects
+// between two of them, stay in registers (the HIP uint4 struct can be
+// demoted to scratch memory by such a select).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ void unpack16(u32x4 v, float (&o)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(v[i] << 16);
+    o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack16(u32x4 v, float (&o)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(v[i]);
+}
+
 // Unpack one 16-byte vector into fp32 values.
 __device__ __forceinline__ void unpack16(const uint4& v, float (&o)[8]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -159,6 +178,19 @@ struct WalkArgs {
   float* q;
 };
 hipError_t launch_walk(const WalkArgs& a, hipStream_t stream);
+
+// Dense head: logits[n, v] = round_bf16(sum_k hidden[n, k] W[v, k]) (bf16).
+struct LmHeadArgs {
+  const void* hidden;
+  int64_t hidden_row_stride;   // elements
+  const void* weight;          // [vocab, hidden_size], rows contiguous
+  int64_t n_rows;
+  int32_t hidden_size;
+  int64_t vocab;
+  void* logits;
+  int64_t logits_row_stride;   // elements
+};
+hipError_t launch_lm_head(const LmHeadArgs& a, hipStream_t stream);
 
 // Lattice and walk in one kernel (one workgroup per request) when the
 // request's lattice and its staging fit in LDS; bit-identical to

@@ -89,18 +89,18 @@ __global__ __launch_bounds__(kThreads) void proj_mfma_kernel(const uint16_t* __r
   // each output is the same MFMA chain over the slice's k-steps in order,
   // whatever FR is.
   constexpr int U = FR > 1 ? 2 : kProjUnroll;
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int kk = k0; kk < k1; kk += 32 * U) {
-    uint4 av[U][FR], bv[U][RT];
+    u32x4 av[U][FR], bv[U][RT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kc = min(kk + 32 * u + kofs, k1 - 8);
 #pragma unroll
-      for (int f = 0; f < FR; ++f) av[u][f] = *reinterpret_cast<const uint4*>(hrow[f] + kc);
+      for (int f = 0; f < FR; ++f) av[u][f] = ld16(hrow[f] + kc);
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         const int col = min(t * 16 + (lane & 15), rank - 1);
-        bv[u][t] = *reinterpret_cast<const uint4*>(P + (int64_t)col * H + kc);
+        bv[u][t] = ld16(P + (int64_t)col * H + kc);
       }
     }
 #pragma unroll
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void lattice_tiled_kernel(
     const int n_pieces = K * ppr;                   // per table
     const int total = 2 * n_pieces;
     for (int base = 0; base < total; base += kThreads * kPer) {
-      uint4 raw[kPer];
+      u32x4 raw[kPer];
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
         const int i = min(base + q * kThreads + tid, total - 1);
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void lattice_tiled_kernel(
         const int j = ii / ppr, v = ii - j * ppr;
         const int64_t t = is_b ? s_cand[j] : s_pred[j];
         const int64_t tc = (t >= 0 && t < vocab) ? t : 0;
-        raw[q] = *reinterpret_cast<const uint4*>((is_b ? B : A) + tc * r + v * VEC);
+        raw[q] = ld16((is_b ? B : A) + tc * r + v * VEC);
       }
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
@@ -307,8 +307,7 @@ __global__ __launch_bounds__(kThreads) void lattice_tiled_kernel(
           TIO nanrow[VEC];
 #pragma unroll
           for (int e = 0; e < VEC; ++e) nanrow[e] = Elem<TIO>::nan_value();
-          *reinterpret_cast<uint4*>(s_b + (size_t)j * L.bstride + v * VEC) =
-              ok ? raw[q] : *reinterpret_cast<const uint4*>(nanrow);
+          st16(s_b + (size_t)j * L.bstride + v * VEC, ok ? raw[q] : ld16(nanrow));
         } else {
           float a[VEC];
           unpack16(raw[q], a);
@@ -344,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void lattice_tiled_kernel(
     for (int k0 = 0; k0 < r; k0 += VEC) {
       float bv[TC][VEC];
 #pragma unroll
-      for (int c = 0; c < TC; ++c) unpack16(*reinterpret_cast<const uint4*>(b[c] + k0), bv[c]);
+      for (int c = 0; c < TC; ++c) unpack16(ld16(b[c] + k0), bv[c]);
 #pragma unroll
       for (int a = 0; a < TJ; ++a) {
 #pragma unroll
@@ -696,7 +695,7 @@ __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
     const int total = 2 * n_pieces;
     const FastDiv div_ppr(pieces_per_row);
     for (int base = 0; base < total; base += kLWThreads * kPer) {
-      uint4 raw[kPer];
+      u32x4 raw[kPer];
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
         const int i = min(base + q * kLWThreads + tid, total - 1);
@@ -705,7 +704,7 @@ __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
         const int sj = div_ppr.quot(ii), v = ii - sj * pieces_per_row;
         const int64_t t = is_b ? s_cand[sj] : s_pred[sj];
         const int64_t tc = (t >= 0 && t < vocab) ? t : 0;
-        raw[q] = *reinterpret_cast<const uint4*>((is_b ? B : A) + tc * r + v * VEC);
+        raw[q] = ld16((is_b ? B : A) + tc * r + v * VEC);
       }
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
@@ -722,8 +721,7 @@ __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
           TIO nanrow[VEC];
 #pragma unroll
           for (int e = 0; e < VEC; ++e) nanrow[e] = Elem<TIO>::nan_value();
-          *reinterpret_cast<uint4*>(s_b + (size_t)sj * bstride + v * VEC) =
-              ok ? raw[q] : *reinterpret_cast<const uint4*>(nanrow);
+          st16(s_b + (size_t)sj * bstride + v * VEC, ok ? raw[q] : ld16(nanrow));
         } else {
           float a[VEC];
           unpack16(raw[q], a);
@@ -751,7 +749,7 @@ __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
     float acc = 0.f;
     for (int k0 = 0; k0 < r; k0 += VEC) {
       float bv[VEC];
-      unpack16(*reinterpret_cast<const uint4*>(b + k0), bv);
+      unpack16(ld16(b + k0), bv);
 #pragma unroll
       for (int e4 = 0; e4 < VEC; e4 += 4) {
         const float4 wv = *reinterpret_cast<const float4*>(w + k0 + e4);

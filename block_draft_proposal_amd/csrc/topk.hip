@@ -65,7 +65,6 @@ constexpr int kMergeThreads = 256;
 constexpr uint32_t kIdMask = 0xffffffu;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, int64_t id) {
   return ((uint64_t)key << 24) | (uint64_t)(kIdMask - (uint32_t)id);

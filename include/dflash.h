@@ -177,6 +177,24 @@ int dflash_walk(const float* scores, const int64_t* ids, const float* uniforms,
                 dflash_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * dflash_lm_head -- the dense head of compute_candidates ("[Spec] DFlash2",
+ * implementation breakdown and risk notes: the slot hidden rows times the
+ * target lm_head weight taken as a dense matrix; the product comes back in
+ * the model's dtype):
+ *   logits[n, v] = round_bf16( sum_k hidden[n, k] * weight[v, k] )
+ *   hidden       row n at hidden + n*hidden_row_stride, hidden_size elements
+ *   weight       [vocab, hidden_size], rows contiguous (the head's layout)
+ *   logits_out   row n at logits_out + n*logits_row_stride, vocab elements
+ * bf16 only (DFLASH_ERR_UNSUPPORTED otherwise).  The products are exact in
+ * fp32 and summed in fp32 on the matrix cores; each sum is rounded once to
+ * bf16 (nearest, ties to even).  hidden_size must be a multiple of 8;
+ * hidden, weight, logits_out and both row strides 16-byte aligned;
+ * logits_out must not overlap the inputs; n_rows and vocab below 2^31. */
+int dflash_lm_head(const void* hidden, int64_t hidden_row_stride, const void* weight, int64_t n_rows,
+                   int32_t hidden_size, int64_t vocab, void* logits_out, int64_t logits_row_stride,
+                   int32_t dtype, dflash_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * dflash_propose_block -- one whole draft block (draft-sampler excerpt):
  *   conv (side given by the caller's base/delta pointers) ->
  *   transform + top-K over the slot logits ->

@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_entry_point():
     names = _declared_functions()
-    assert "dflash_propose_block" in names and len(names) == 11
+    assert "dflash_propose_block" in names and len(names) == 12
     lib = D.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -175,6 +175,24 @@ def test_propose_block_validation():
     bad = _cfg(block_size=1)
     assert L.dflash_propose_block(ctypes.byref(bad), ctypes.byref(args), None) == -1
     assert L.dflash_propose_block_workspace_size(ctypes.byref(cfg), 32, 151936) > 0
+
+
+def test_lm_head_validation():
+    L = Bd.lib()
+    V8 = ctypes.c_void_p(16)
+    call = lambda **kw: L.dflash_lm_head(*[kw.get(k, d) for k, d in (
+        ("h", V8), ("hs", 64), ("w", V8), ("n", 4), ("H", 64), ("V", 128), ("o", ctypes.c_void_p(1 << 40)),
+        ("os", 128), ("dt", 1), ("st", None))])
+    assert call(dt=0) == Bd.DFLASH_ERR_UNSUPPORTED            # fp32
+    assert call(dt=7) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(H=60, hs=64) == Bd.DFLASH_ERR_UNSUPPORTED      # hidden_size not a multiple of 8
+    assert call(hs=32) == Bd.DFLASH_ERR_INVALID_ARG            # stride shorter than a row
+    assert call(os=130) == Bd.DFLASH_ERR_INVALID_ARG           # stride not a multiple of 8
+    assert call(n=-1) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(V=1 << 31, os=1 << 31) == Bd.DFLASH_ERR_UNSUPPORTED
+    assert call(h=ctypes.c_void_p(18)) == Bd.DFLASH_ERR_INVALID_ARG   # misaligned
+    assert call(o=ctypes.c_void_p(16)) == Bd.DFLASH_ERR_INVALID_ARG   # overlaps the inputs
+    assert call(n=0) == Bd.DFLASH_OK and call(V=0, os=0) == Bd.DFLASH_OK   # nothing to do
 
 
 def test_error_message_is_per_call():

@@ -1,0 +1,99 @@
+"""GPU parity of the dense head of compute_candidates ("[Spec] DFlash2",
+implementation breakdown and risk notes): dflash_lm_head against the
+oracle's exact sums rounded once to bf16.
+
+Rule: a GPU logit equals the oracle's rounding of the exact sum, except
+where the exact sum lies within the fp32 accumulation bound
+(O.lm_head_sum_bound) of a bf16 rounding midpoint; there either neighbour is
+correct, and both candidates are checked.  Such cases are counted.  The top-K
+of the GPU logits (dflash_topk) equals the oracle's top-K of those logits
+bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import block_draft_proposal_amd as D
+import workloads as W
+from gpu_helpers import DEV, f64, require_gpu, sample_indices, say
+from oracle import dflash_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_logits(got: np.ndarray, h: np.ndarray, w: np.ndarray) -> int:
+    """got [rows, cols] (float64 copies of bf16) vs the exact sums of h @ w.T."""
+    exact = h @ w.T
+    ref = O.round_to_bf16(exact)
+    bound = O.lm_head_sum_bound(h, w)
+    lo, hi = O.round_to_bf16(exact - bound), O.round_to_bf16(exact + bound)
+    off = got != ref
+    assert np.all(~off | ((got >= lo) & (got <= hi))), float(np.max(np.abs(got - ref)))
+    return int(off.sum())
+
+
+def _head(w: W.Workload, rows=None, seed=None):
+    d = W.make_head_inputs(w, device=DEV, seed=seed, n_rows=rows)
+    return d["hidden"], d["weight"]
+
+
+@pytest.mark.parametrize("M,H,V", [(70, 96, 1000), (130, 200, 392), (1, 8, 8), (257, 64, 136), (128, 4096, 1024)])
+def test_lm_head_small_shapes_match_the_exact_sums(M, H, V):
+    # ragged row blocks (70, 130, 257 rows), a hidden size that is not a
+    # multiple of the 64-wide stage (96, 200), a vocabulary that ends inside a
+    # 128-column tile (1000, 392, 136) and the smallest case
+    require_gpu()
+    w = W.WORKLOADS["bf16_b16_v151936"].replace(hidden=H, vocab=V, valid_vocab=V, n_req=1)
+    hid, wt = _head(w, rows=M, seed=M * 7919 + H)
+    say(f"dflash_lm_head M={M} H={H} V={V}")
+    out = D.dflash_lm_head(hid, wt)
+    torch.cuda.synchronize()
+    near = _check_logits(f64(out), f64(hid), f64(wt))
+    print(f"[lm_head] {M}x{H}x{V}: {near} logits on the rounding band", flush=True)
+
+
+def test_lm_head_strided_rows_and_output_stride():
+    require_gpu()
+    w = W.WORKLOADS["bf16_b16_v151936"].replace(hidden=256, vocab=520, valid_vocab=520, n_req=1)
+    hid, wt = _head(w, rows=40, seed=5)
+    wide = torch.zeros((40, 256 + 64), dtype=hid.dtype, device=DEV)
+    wide[:, 16:16 + 256] = hid
+    view = wide[:, 16:16 + 256]                          # row stride 320, 32-byte offset
+    out_wide = torch.full((40, 600), 7.0, dtype=hid.dtype, device=DEV)
+    say("dflash_lm_head strided")
+    D.dflash_lm_head(view, wt, out=out_wide[:, :520])
+    torch.cuda.synchronize()
+    _check_logits(f64(out_wide[:, :520]), f64(hid), f64(wt))
+    assert torch.all(out_wide[:, 520:] == 7.0)            # nothing written past the vocab
+
+
+def test_lm_head_full_bench_shape_sampled_rows_then_topk():
+    # 480 slot rows x 4096 x 151936: sampled rows checked over every column,
+    # and the chain head -> dflash_topk equal to the oracle's top-K of the
+    # GPU logits
+    require_gpu()
+    w = W.WORKLOADS["bf16_b16_v151936"]
+    hid, wt = _head(w)
+    say("dflash_lm_head 480x4096x151936")
+    out = D.dflash_lm_head(hid, wt)
+    ids, unary = D.dflash_topk(out, top_k=w.top_k, valid_vocab=w.valid_vocab, multiplier=w.multiplier,
+                               softcap=w.softcap)
+    torch.cuda.synchronize()
+    rows = sample_indices(w.n_slot_rows, 6, seed=11)
+    wt64 = f64(wt)
+    got = f64(out[torch.from_numpy(rows).to(DEV)])
+    near = _check_logits(got, f64(hid)[rows], wt64)
+    print(f"[lm_head] bench shape, {len(rows)} rows: {near} logits on the rounding band", flush=True)
+    ref_ids, ref_unary = O.topk(got, w.valid_vocab, w.top_k, w.multiplier, w.softcap)
+    np.testing.assert_array_equal(ids.cpu().numpy()[rows], ref_ids)
+    assert np.all(np.abs(f64(unary)[rows] - ref_unary) <= 1e-5 * (1 + np.abs(ref_unary)))
+
+
+def test_lm_head_rejects_fp32_and_empty_is_a_no_op():
+    require_gpu()
+    h = torch.zeros((4, 16), dtype=torch.float32, device=DEV)
+    wt = torch.zeros((8, 16), dtype=torch.float32, device=DEV)
+    with pytest.raises(D.DFlashError):
+        D.dflash_lm_head(h, wt)
+    e = D.dflash_lm_head(torch.zeros((0, 16), dtype=torch.bfloat16, device=DEV),
+                         torch.zeros((8, 16), dtype=torch.bfloat16, device=DEV))
+    assert e.shape == (0, 8)

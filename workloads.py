@@ -28,6 +28,7 @@ from __future__ import annotations
 
 import dataclasses
 import hashlib
+import math
 from typing import Dict, Optional, Tuple
 
 import torch
@@ -234,3 +235,18 @@ def sha256_of(t: torch.Tensor) -> str:
     """SHA-256 of a tensor's bytes (host copy), for logging input identity."""
     b = t.detach().contiguous().cpu().view(torch.uint8).numpy().tobytes()
     return hashlib.sha256(b).hexdigest()
+
+
+def make_head_inputs(w: Workload, device="cpu", seed: Optional[int] = None, n_rows: Optional[int] = None
+                     ) -> Dict[str, torch.Tensor]:
+    """Inputs of the candidates-from-hidden step for workload ``w``:
+      hidden [N_s, H]  slot hidden rows, N(0, 1), storage dtype
+      weight [V, H]    dense head, N(0, (logit_sigma / sqrt(H))^2), so the
+                       logits spread like the workload's logits
+    The padded tail of a physical vocabulary gets the same draws (its ids are
+    excluded by valid_vocab, as on the pages)."""
+    m = master_seed(w) if seed is None else int(seed)
+    dev = torch.device(device)
+    rows = w.n_slot_rows if n_rows is None else int(n_rows)
+    return {"hidden": normal((rows, w.hidden), 1.0, w.dtype, m, "head_hidden", dev),
+            "weight": normal((w.vocab, w.hidden), w.logit_sigma / math.sqrt(w.hidden), w.dtype, m, "head_weight", dev)}
