@@ -71,6 +71,9 @@ _SIGNATURES = {
                                 _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_vp, _c_vp, _c_size, _c_vp]),
     "dflash_walk": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp]),
     "dflash_lm_head": (_c_i32, [_c_vp, _c_i64, _c_vp, _c_i64, _c_i32, _c_i64, _c_vp, _c_i64, _c_i32, _c_vp]),
+    "dflash_lm_head_topk_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i32]),
+    "dflash_lm_head_topk": (_c_i32, [_c_vp, _c_i64, _c_vp, _c_i64, _c_i32, _c_i64, _c_i64, _c_i32, _c_f32, _c_f32,
+                                     _c_i32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "dflash_propose_block_workspace_size": (_c_size, [ctypes.POINTER(DraftConfig), _c_i32, _c_i64]),
     "dflash_propose_block": (_c_i32, [ctypes.POINTER(DraftConfig), ctypes.POINTER(BlockArgs), _c_vp]),
 }
@@ -237,6 +240,29 @@ def dflash_lm_head(hidden: torch.Tensor, weight: torch.Tensor, *, vocab: Optiona
     _check(lib().dflash_lm_head(_p(hidden), hidden.stride(0) if rows else H, _p(weight), rows, H, V, _p(out),
                                 out.stride(0) if rows else V, _dtype_code(hidden), _stream(stream)))
     return out
+
+
+def dflash_lm_head_topk(hidden: torch.Tensor, weight: torch.Tensor, *, top_k: int,
+                        valid_vocab: Optional[int] = None, multiplier: float = 1.0, softcap: float = 0.0,
+                        ids_out=None, unary_out=None, workspace=None, stream=None):
+    """hidden [rows, H] bf16 (rows may be strided); weight [V, H] bf16.
+    Returns (ids int64 [rows, K], unary fp32 [rows, K]) of the head's
+    logits, without materialising them."""
+    if hidden.dim() != 2 or hidden.stride(1) != 1 or not weight.is_contiguous():
+        raise ValueError("hidden rows and weight must be contiguous")
+    rows, H = hidden.shape
+    V = weight.shape[0]
+    valid_vocab = V if valid_vocab is None else valid_vocab
+    dev = hidden.device
+    ids_out = torch.empty((rows, top_k), dtype=torch.int64, device=dev) if ids_out is None else ids_out
+    unary_out = torch.empty((rows, top_k), dtype=torch.float32, device=dev) if unary_out is None else unary_out
+    if workspace is None:
+        nbytes = lib().dflash_lm_head_topk_workspace_size(rows, V, top_k)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib().dflash_lm_head_topk(_p(hidden), hidden.stride(0) if rows else H, _p(weight), rows, H, V,
+                                     valid_vocab, top_k, multiplier, softcap, _dtype_code(hidden), _p(ids_out),
+                                     _p(unary_out), _p(workspace), workspace.numel(), _stream(stream)))
+    return ids_out, unary_out
 
 
 def propose_block_workspace_size(cfg: DraftConfig, n_req: int, valid_vocab: int) -> int:

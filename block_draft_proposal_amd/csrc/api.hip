@@ -357,6 +357,49 @@ int dflash_lm_head(const void* hidden, int64_t hidden_row_stride, const void* we
   return st == DFLASH_OK ? ok() : st;
 }
 
+size_t dflash_lm_head_topk_workspace_size(int64_t n_rows, int64_t vocab, int32_t top_k) {
+  if (n_rows <= 0 || vocab <= 0 || top_k <= 0 || top_k > DFLASH_MAX_TOP_K) return 0;
+  return dflash::plan_lm_head_topk(n_rows, vocab, top_k).bytes;
+}
+
+int dflash_lm_head_topk(const void* hidden, int64_t hidden_row_stride, const void* weight, int64_t n_rows,
+                        int32_t hidden_size, int64_t vocab, int64_t valid_vocab, int32_t top_k,
+                        float output_multiplier, float final_logit_softcapping, int32_t dtype, int64_t* ids_out,
+                        float* unary_out, void* workspace, size_t workspace_bytes, dflash_stream_t stream) {
+  const char* who = "dflash_lm_head_topk";
+  if (!dtype_ok(dtype)) return fail(DFLASH_ERR_INVALID_ARG, "%s: unknown dtype %d", who, dtype);
+  if (dtype != DFLASH_BF16) return fail(DFLASH_ERR_UNSUPPORTED, "%s: bf16 only", who);
+  if (n_rows < 0 || vocab < 1) return fail(DFLASH_ERR_INVALID_ARG, "%s: n_rows >= 0 and vocab >= 1 needed", who);
+  if (n_rows >= ((int64_t)1 << 31) || vocab >= kMaxVocab)
+    return fail(DFLASH_ERR_UNSUPPORTED, "%s: n_rows < 2^31 and vocab < 2^24 needed", who);
+  if (valid_vocab < 1 || valid_vocab > vocab)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: need 1 <= valid_vocab <= vocab", who);
+  if (top_k < 1 || top_k > valid_vocab) return fail(DFLASH_ERR_INVALID_ARG, "%s: need 1 <= top_k <= valid_vocab", who);
+  if (top_k > DFLASH_MAX_TOP_K) return fail(DFLASH_ERR_UNSUPPORTED, "%s: top_k > %d", who, DFLASH_MAX_TOP_K);
+  if (!std::isfinite(output_multiplier) || output_multiplier <= 0.f || !std::isfinite(final_logit_softcapping) ||
+      final_logit_softcapping < 0.f)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: multiplier must be finite and > 0, softcap finite and >= 0", who);
+  if (hidden_size < 8 || hidden_size % 8)
+    return fail(DFLASH_ERR_UNSUPPORTED, "%s: hidden_size must be a positive multiple of 8", who);
+  if (hidden_row_stride < hidden_size || hidden_row_stride % 8)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: hidden_row_stride must be >= hidden_size and a multiple of 8", who);
+  if (n_rows == 0) return ok();
+  if (!hidden || !weight || !ids_out || !unary_out) return fail(DFLASH_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!aligned16(hidden) || !aligned16(weight))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: hidden and weight must be 16-byte aligned", who);
+  const dflash::LmTopkPlan p = dflash::plan_lm_head_topk(n_rows, vocab, top_k);
+  if (workspace_bytes < p.bytes || !workspace)
+    return fail(DFLASH_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu needed", who, workspace_bytes, p.bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", who);
+  dflash::LmHeadArgs a{hidden, hidden_row_stride, weight, n_rows, hidden_size, vocab, nullptr, 0};
+  const int st = launch_status(dflash::launch_lm_head_topk(a, p, valid_vocab, top_k, output_multiplier,
+                                                           final_logit_softcapping, ids_out, unary_out, workspace,
+                                                           as_hip(stream)),
+                               who);
+  return st == DFLASH_OK ? ok() : st;
+}
+
 size_t dflash_propose_block_workspace_size(const dflash_draft_config* cfg, int32_t n_req, int64_t valid_vocab) {
   if (!cfg || n_req <= 0 || valid_vocab <= 0 || cfg->block_size < 2 || cfg->selector_top_k <= 0 ||
       cfg->selector_rank <= 0 || cfg->hidden_size <= 0)

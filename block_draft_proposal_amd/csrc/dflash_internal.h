@@ -73,6 +73,47 @@ __device__ __forceinline__ void unpack16(const uint4& v, float (&o)[4]) {
 }
 
 // ---------------------------------------------------------------------------
+// Top-K keys (shared by the streaming top-K and the fused head epilogue)
+// ---------------------------------------------------------------------------
+// Every value has an order-preserving unsigned key; every (key, id) pair a
+// 56-bit composite key << 24 | (2^24 - 1 - id) whose order is exactly
+// (value descending, id ascending) and which is unique within a row
+// (ids < 2^24).  Composite 0 is below every real one.
+constexpr uint32_t kIdMask = 0xffffffu;
+__device__ __forceinline__ uint64_t composite(uint32_t key, int64_t id) {
+  return ((uint64_t)key << 24) | (uint64_t)(kIdMask - (uint32_t)id);
+}
+__device__ __forceinline__ uint32_t composite_key(uint64_t c) { return (uint32_t)(c >> 24); }
+__device__ __forceinline__ int64_t composite_id(uint64_t c) {
+  return (int64_t)(kIdMask - (uint32_t)(c & kIdMask));
+}
+// bf16 bits -> key in [1, 0xffff]: negatives map to 0x10000 - bits (so -0
+// joins +0 at 0x8000), non-negatives to bits | 0x8000.
+__device__ __forceinline__ uint32_t bf16_key(uint32_t b) {
+  return (b & 0x8000u) ? ((0x10000u - b) & 0xffffu) : (b | 0x8000u);
+}
+__device__ __forceinline__ float bf16_key_value(uint32_t k) {
+  const uint32_t b = (k & 0x8000u) ? (k & 0x7fffu) : ((0x10000u - k) & 0xffffu);
+  return __uint_as_float(b << 16);
+}
+// The unary transform of a selected logit: m z, then cap tanh(. / cap) when
+// cap > 0; a masked (-inf) entry stays -inf.
+__device__ __forceinline__ float unary_transform(float z, float mult, float cap) {
+  float y = mult * z;
+  if (cap > 0.f) y = cap * tanhf(y / cap);
+  return (z == -INFINITY) ? -INFINITY : y;     // masked entries stay masked
+}
+// Number of entries of the sorted (descending) list l[0, n) greater than c.
+__device__ __forceinline__ int count_greater(const uint64_t* l, int n, uint64_t c) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (l[mid] > c) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
 // Wave (64-lane) reductions
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max_f32(float v) {
@@ -191,6 +232,18 @@ struct LmHeadArgs {
   int64_t logits_row_stride;   // elements
 };
 hipError_t launch_lm_head(const LmHeadArgs& a, hipStream_t stream);
+
+// Fused head + top-K: per-row K best of each group of column tiles (sorted
+// composites in the workspace [n_rows][n_grp][K]), then a merge per row.
+constexpr int kLmMergeCap = 8192;   // composites of one row the merge stages in LDS
+struct LmTopkPlan {
+  int32_t n_mb, n_nb, tiles_per_group, n_grp;
+  size_t bytes;
+};
+LmTopkPlan plan_lm_head_topk(int64_t n_rows, int64_t vocab, int32_t top_k);
+hipError_t launch_lm_head_topk(const LmHeadArgs& a, const LmTopkPlan& p, int64_t valid_vocab, int32_t top_k,
+                               float mult, float cap, int64_t* ids_out, float* unary_out, void* workspace,
+                               hipStream_t stream);
 
 // Lattice and walk in one kernel (one workgroup per request) when the
 // request's lattice and its staging fit in LDS; bit-identical to

@@ -19,6 +19,17 @@
 // that share one head tile on the same XCD, so each head tile is fetched from
 // HBM about once and re-read from that XCD's L2.  The fp32 tile is rounded
 // to bf16 (nearest, ties to even) and written through LDS as 16-byte rows.
+//
+// Fused head + top-K (compute_candidates without the logits reaching HBM):
+// a workgroup walks T column tiles of its row block with the same tile
+// product; each rounded tile is put in LDS and one thread per row folds the
+// row's values into a sorted register list of its K best composites
+// (value descending, id ascending; ids grow along the walk, so one strict
+// comparison with the K-th decides).  The lists of all column groups are
+// merged per row by a second kernel, which ranks every candidate by binary-
+// searched counts in the other sorted lists.  Both paths rank the same bf16
+// logits, so the fused result equals the head followed by the streaming
+// top-K bit for bit.
 #include "dflash.h"
 #include "dflash_internal.h"
 
@@ -122,6 +133,20 @@ __device__ __forceinline__ void tile_product(const uint16_t* __restrict__ h, int
   }
 }
 
+// Rounds the wave's accumulators to bf16 into the output tile in LDS.
+__device__ __forceinline__ void tile_to_lds(const f32x4_t (&acc)[4][4], uint16_t* cs) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        cs[(wm + 16 * i + 4 * (lane >> 4) + v) * kCPad + wn + 16 * j + (lane & 15)] =
+            (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+}
+
 __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const uint16_t* __restrict__ h, int64_t h_stride,
                                                              const uint16_t* __restrict__ W, int32_t M, int32_t H,
                                                              int32_t V, uint16_t* __restrict__ logits,
@@ -136,17 +161,9 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const uint16_t* __r
   tile_product(h, h_stride, W, M, H, V, m0, n0, sm, acc);
 
   // round to bf16 into LDS, then write whole 16-byte row pieces
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int tid = threadIdx.x;
   uint16_t* cs = sm.a[0];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        cs[(wm + 16 * i + 4 * (lane >> 4) + v) * kCPad + wn + 16 * j + (lane & 15)] =
-            (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+  tile_to_lds(acc, cs);
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < (kBM * kBN / 8) / kLmThreads; ++q) {
@@ -163,7 +180,139 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const uint16_t* __r
   }
 }
 
+// KB: list slots (K rounded up to 8, 16 or 32).  The list holds KB - K
+// sentinels (all ones, above every composite) ahead of the K real entries,
+// so the threshold is always the last slot and no index depends on K.
+template <int KB>
+__global__ __launch_bounds__(kLmThreads) void lm_head_topk_kernel(
+    const uint16_t* __restrict__ h, int64_t h_stride, const uint16_t* __restrict__ W, int32_t M, int32_t H,
+    int32_t V, int32_t valid, int32_t K, int32_t n_mb, int32_t n_nb, int32_t tiles_per_group, int32_t n_grp,
+    uint64_t* __restrict__ parts) {
+  extern __shared__ __align__(16) unsigned char lm_smem[];
+  LmSmem& sm = *reinterpret_cast<LmSmem*>(lm_smem);
+  int mb, grp;
+  tile_of(blockIdx.x, n_mb, mb, grp);
+  if (grp >= n_grp) return;
+  const int m0 = mb * kBM, tid = threadIdx.x;
+  uint64_t best[KB];
+#pragma unroll
+  for (int i = 0; i < KB; ++i) best[i] = (i < KB - K) ? ~0ull : 0ull;
+  const int nb0 = grp * tiles_per_group, nb1 = min(n_nb, nb0 + tiles_per_group);
+  uint16_t* cs = sm.a[0];
+  for (int nb = nb0; nb < nb1; ++nb) {
+    const int n0 = nb * kBN;
+    f32x4_t acc[4][4];
+    tile_product(h, h_stride, W, M, H, V, m0, n0, sm, acc);   // ends with a barrier
+    tile_to_lds(acc, cs);
+    __syncthreads();
+    if (tid < kBM && m0 + tid < M) {
+      const uint16_t* rowp = cs + tid * kCPad;
+      for (int c8 = 0; c8 < kBN && n0 + c8 < valid; c8 += 8) {
+        const u32x4 v = ld16(rowp + c8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int col = n0 + c8 + e;
+          const uint32_t bits = (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu);
+          uint64_t c = composite(bf16_key(bits), col);
+          if (col < valid && c > best[KB - 1]) {
+#pragma unroll
+            for (int i = 0; i < KB; ++i) {     // insert, keeping the list sorted
+              if (c > best[i]) { const uint64_t t = best[i]; best[i] = c; c = t; }
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();                           // the tile's LDS is reused by the next stage
+  }
+  if (tid < kBM && m0 + tid < M) {
+    uint64_t* dst = parts + ((int64_t)(m0 + tid) * n_grp + grp) * K;
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+      if (i >= KB - K) dst[i - (KB - K)] = best[i];
+  }
+}
+
+// Per row: the K best of n_grp sorted lists of K composites (0 = empty
+// slot).  Only candidates at or above the K-th largest list head can rank
+// below K (K heads are at least that large); each of those is ranked by its
+// position in its list plus binary-searched counts in the other lists.
+constexpr int kMergeThreadsLm = 256;
+__global__ __launch_bounds__(kMergeThreadsLm) void merge_lists_kernel(const uint64_t* __restrict__ parts,
+                                                                    int32_t n_grp, int32_t K, float mult, float cap,
+                                                                    int64_t* __restrict__ ids_out,
+                                                                    float* __restrict__ unary_out) {
+  extern __shared__ __align__(16) uint64_t ml_smem[];
+  uint64_t* L = ml_smem;                                  // [n_grp][K]
+  __shared__ uint64_t s_floor;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, m = n_grp * K;
+  const uint64_t* src = parts + row * (int64_t)m;
+  for (int i = tid; i < m; i += kMergeThreadsLm) L[i] = src[i];
+  if (tid == 0) s_floor = 0;
+  __syncthreads();
+  // K-th largest list head (0 when fewer than K lists hold anything)
+  for (int g = tid; g < n_grp; g += kMergeThreadsLm) {
+    const uint64_t hg = L[g * K];
+    int above = 0;
+    for (int o = 0; o < n_grp; ++o) above += (L[o * K] > hg) ? 1 : 0;
+    if (hg != 0 && above == K - 1) s_floor = hg;         // unique: composites are distinct
+  }
+  __syncthreads();
+  const uint64_t floor = s_floor;
+  for (int i = tid; i < m; i += kMergeThreadsLm) {
+    const uint64_t c = L[i];
+    if (c == 0 || c < floor) continue;
+    const int g = i / K;
+    int rank = i - g * K;
+    for (int o = 0; o < n_grp && rank < K; ++o)
+      if (o != g) rank += count_greater(L + o * K, K, c);
+    if (rank < K) {
+      ids_out[row * K + rank] = composite_id(c);
+      unary_out[row * K + rank] = unary_transform(bf16_key_value(composite_key(c)), mult, cap);
+    }
+  }
+}
+
 }  // namespace
+
+LmTopkPlan plan_lm_head_topk(int64_t n_rows, int64_t vocab, int32_t top_k) {
+  LmTopkPlan p{};
+  p.n_mb = (int32_t)((n_rows + kBM - 1) / kBM);
+  p.n_nb = (int32_t)((vocab + kBN - 1) / kBN);
+  int t = 4;
+  while ((int64_t)((p.n_nb + t - 1) / t) * top_k > kLmMergeCap) t *= 2;
+  p.tiles_per_group = t;
+  p.n_grp = (p.n_nb + t - 1) / t;
+  p.bytes = (size_t)n_rows * p.n_grp * top_k * sizeof(uint64_t);
+  p.bytes = (p.bytes + 255) & ~(size_t)255;
+  return p;
+}
+
+hipError_t launch_lm_head_topk(const LmHeadArgs& a, const LmTopkPlan& p, int64_t valid_vocab, int32_t top_k,
+                               float mult, float cap, int64_t* ids_out, float* unary_out, void* workspace,
+                               hipStream_t stream) {
+  if (a.n_rows == 0) return hipSuccess;
+  uint64_t* parts = static_cast<uint64_t*>(workspace);
+  const int64_t slots = (int64_t)((p.n_grp + 7) / 8) * p.n_mb;
+  const dim3 grid((unsigned)(slots * 8));
+#define DFLASH_LMTK(KB)                                                                                    \
+  hipLaunchKernelGGL((lm_head_topk_kernel<KB>), grid, dim3(kLmThreads), sizeof(LmSmem), stream,                \
+                     static_cast<const uint16_t*>(a.hidden), a.hidden_row_stride,                          \
+                     static_cast<const uint16_t*>(a.weight), (int32_t)a.n_rows, a.hidden_size,             \
+                     (int32_t)a.vocab, (int32_t)valid_vocab, top_k, p.n_mb, p.n_nb, p.tiles_per_group,     \
+                     p.n_grp, parts)
+  if (top_k <= 8) DFLASH_LMTK(8);
+  else if (top_k <= 16) DFLASH_LMTK(16);
+  else DFLASH_LMTK(32);
+#undef DFLASH_LMTK
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(merge_lists_kernel, dim3((unsigned)a.n_rows), dim3(kMergeThreadsLm),
+                     (size_t)p.n_grp * top_k * sizeof(uint64_t), stream, parts, p.n_grp, top_k, mult, cap, ids_out,
+                     unary_out);
+  return hipGetLastError();
+}
 
 hipError_t launch_lm_head(const LmHeadArgs& a, hipStream_t stream) {
   if (a.n_rows == 0 || a.vocab == 0) return hipSuccess;

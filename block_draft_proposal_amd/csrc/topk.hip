@@ -62,27 +62,9 @@ template <int VEC> constexpr int64_t vec_stride() { return (int64_t)kWaves * 64 
 constexpr int kWaveCap = 256;                  // LDS slots for one chunk's new candidates
 constexpr int kMaxK = DFLASH_MAX_TOP_K;
 constexpr int kMergeThreads = 256;
-constexpr uint32_t kIdMask = 0xffffffu;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint64_t composite(uint32_t key, int64_t id) {
-  return ((uint64_t)key << 24) | (uint64_t)(kIdMask - (uint32_t)id);
-}
-__device__ __forceinline__ uint32_t composite_key(uint64_t c) { return (uint32_t)(c >> 24); }
-__device__ __forceinline__ int64_t composite_id(uint64_t c) {
-  return (int64_t)(kIdMask - (uint32_t)(c & kIdMask));
-}
-
-// bf16 bits -> key in [1, 0xffff]: negatives map to 0x10000 - bits (so -0
-// joins +0 at 0x8000), non-negatives to bits | 0x8000.
-__device__ __forceinline__ uint32_t bf16_key(uint32_t b) {
-  return (b & 0x8000u) ? ((0x10000u - b) & 0xffffu) : (b | 0x8000u);
-}
-__device__ __forceinline__ float bf16_key_value(uint32_t k) {
-  const uint32_t b = (k & 0x8000u) ? (k & 0x7fffu) : ((0x10000u - k) & 0xffffu);
-  return __uint_as_float(b << 16);
-}
 // Two packed bf16 -> two packed keys.  Per half: negative -> ~b + 1
 // (never carries: ~b <= 0x7fff), non-negative -> b ^ 0x8000.
 __device__ __forceinline__ uint32_t bf16_key2(uint32_t w) {
@@ -399,15 +381,6 @@ __device__ __noinline__ uint32_t narrow_exact(const TIO* rowp, int64_t lb, int64
   return __builtin_amdgcn_readfirstlane(wl.count);
 }
 
-// Number of entries of the sorted (descending) list l[0, n) greater than c.
-__device__ __forceinline__ int count_greater(const uint64_t* l, int n, uint64_t c) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (l[mid] > c) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
 
 // Merge n new candidates pool[nb, nb + n) into the held sorted list
 // pool[0, nb) and keep the best min(nb + n, K), sorted, in pool[0, ...).
@@ -435,11 +408,6 @@ __device__ void keep_best(WaveLds& wl, int nb, int n, int K, int lane) {
   wave_sync();
 }
 
-__device__ __forceinline__ float unary_transform(float z, float mult, float cap) {
-  float y = mult * z;
-  if (cap > 0.f) y = cap * tanhf(y / cap);
-  return (z == -INFINITY) ? -INFINITY : y;     // masked entries stay masked
-}
 
 // K-th largest of the 64 lane values m (unsigned, below 2^bits): the largest
 // t with #{lanes : m >= t} >= K, found bit by bit with ballot counts.  Those

@@ -195,6 +195,24 @@ int dflash_lm_head(const void* hidden, int64_t hidden_row_stride, const void* we
                    int32_t dtype, dflash_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * dflash_lm_head_topk -- compute_candidates from the hidden rows ("[Spec]
+ * DFlash2", implementation breakdown: the dense head, the unary transform
+ * and the deterministic top-k) without the logits reaching memory:
+ *   ids_out[n, 0..K)   = dflash_topk over the rows of dflash_lm_head(hidden)
+ *   unary_out[n, 0..K) = their transformed logits
+ * bit for bit equal to dflash_lm_head followed by dflash_topk with the same
+ * arguments.  Arguments as for those two calls (bf16 only; valid_vocab <=
+ * vocab; 1 <= top_k <= DFLASH_MAX_TOP_K, top_k <= valid_vocab).  Scratch:
+ * dflash_lm_head_topk_workspace_size(n_rows, vocab, top_k) bytes, 256-byte
+ * aligned (per row, the K best of every group of 128-column tiles). */
+size_t dflash_lm_head_topk_workspace_size(int64_t n_rows, int64_t vocab, int32_t top_k);
+int dflash_lm_head_topk(const void* hidden, int64_t hidden_row_stride, const void* weight, int64_t n_rows,
+                        int32_t hidden_size, int64_t vocab, int64_t valid_vocab, int32_t top_k,
+                        float output_multiplier, float final_logit_softcapping, int32_t dtype,
+                        int64_t* ids_out, float* unary_out, void* workspace, size_t workspace_bytes,
+                        dflash_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * dflash_propose_block -- one whole draft block (draft-sampler excerpt):
  *   conv (side given by the caller's base/delta pointers) ->
  *   transform + top-K over the slot logits ->

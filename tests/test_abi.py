@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_entry_point():
     names = _declared_functions()
-    assert "dflash_propose_block" in names and len(names) == 12
+    assert "dflash_propose_block" in names and len(names) == 14
     lib = D.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -193,6 +193,26 @@ def test_lm_head_validation():
     assert call(h=ctypes.c_void_p(18)) == Bd.DFLASH_ERR_INVALID_ARG   # misaligned
     assert call(o=ctypes.c_void_p(16)) == Bd.DFLASH_ERR_INVALID_ARG   # overlaps the inputs
     assert call(n=0) == Bd.DFLASH_OK and call(V=0, os=0) == Bd.DFLASH_OK   # nothing to do
+
+
+def test_lm_head_topk_validation():
+    L = Bd.lib()
+    V8 = ctypes.c_void_p(16)
+    ws_need = L.dflash_lm_head_topk_workspace_size(4, 1000, 8)
+    assert ws_need > 0 and L.dflash_lm_head_topk_workspace_size(0, 1000, 8) == 0
+    call = lambda **kw: L.dflash_lm_head_topk(*[kw.get(k, d) for k, d in (
+        ("h", V8), ("hs", 64), ("w", V8), ("n", 4), ("H", 64), ("V", 1000), ("vv", 1000), ("K", 8), ("m", 1.0),
+        ("cap", 0.0), ("dt", 1), ("ids", V8), ("un", V8), ("ws", ctypes.c_void_p(256)), ("wsb", ws_need),
+        ("st", None))])
+    assert call(dt=0) == Bd.DFLASH_ERR_UNSUPPORTED
+    assert call(vv=1001) == Bd.DFLASH_ERR_INVALID_ARG          # valid_vocab > vocab
+    assert call(K=0) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(K=33, vv=1000) == Bd.DFLASH_ERR_UNSUPPORTED
+    assert call(m=0.0) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(cap=-1.0) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(wsb=ws_need - 1) == Bd.DFLASH_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(128)) == Bd.DFLASH_ERR_INVALID_ARG   # not 256-byte aligned
+    assert call(n=0) == Bd.DFLASH_OK
 
 
 def test_error_message_is_per_call():

@@ -97,3 +97,54 @@ def test_lm_head_rejects_fp32_and_empty_is_a_no_op():
     e = D.dflash_lm_head(torch.zeros((0, 16), dtype=torch.bfloat16, device=DEV),
                          torch.zeros((8, 16), dtype=torch.bfloat16, device=DEV))
     assert e.shape == (0, 8)
+
+
+@pytest.mark.parametrize("M,H,V,valid,K,m,cap", [
+    (70, 96, 1000, 1000, 8, 1.0, 30.0),       # ragged rows, hidden and vocabulary
+    (130, 64, 2056, 2000, 16, 0.5, 30.0),     # logical vocab inside the last tile
+    (257, 200, 392, 392, 1, 1.0, 0.0),        # K = 1
+    (40, 128, 4096, 4093, 32, 1.0, 30.0),     # K = 32, valid not a multiple of 8
+    (5, 64, 136, 40, 40 // 2, 1.0, 0.0),      # few valid ids
+])
+def test_fused_head_topk_equals_head_then_topk(M, H, V, valid, K, m, cap):
+    require_gpu()
+    w = W.WORKLOADS["bf16_b16_v151936"].replace(hidden=H, vocab=V, valid_vocab=valid, n_req=1)
+    hid, wt = _head(w, rows=M, seed=M * 31 + V)
+    say(f"dflash_lm_head_topk M={M} H={H} V={V} valid={valid} K={K}")
+    ids, unary = D.dflash_lm_head_topk(hid, wt, top_k=K, valid_vocab=valid, multiplier=m, softcap=cap)
+    logits = D.dflash_lm_head(hid, wt)
+    ids2, unary2 = D.dflash_topk(logits, top_k=K, valid_vocab=valid, multiplier=m, softcap=cap)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(unary, unary2)
+    ref_ids, _ = O.topk(f64(logits), valid, K, m, cap)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+
+
+def test_fused_head_topk_ties_go_to_the_lower_id():
+    # identical head rows give equal logits in every row: the lower id first
+    require_gpu()
+    w = W.WORKLOADS["bf16_b16_v151936"].replace(hidden=64, vocab=512, valid_vocab=512, n_req=1)
+    hid, wt = _head(w, rows=33, seed=77)
+    wt = wt.clone()
+    wt[300] = hid[0] * 2                  # a clear winner in row 0 ...
+    wt[301] = wt[300]                     # ... and its twin with a larger id
+    wt[40:48] = wt[7]                     # a block of equal rows
+    say("dflash_lm_head_topk ties")
+    ids, _ = D.dflash_lm_head_topk(hid, wt, top_k=12)
+    torch.cuda.synchronize()
+    assert ids[0, 0].item() == 300 and ids[0, 1].item() == 301
+    ref, _ = O.topk(f64(D.dflash_lm_head(hid, wt)), 512, 12, 1.0, 0.0)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref)
+
+
+def test_fused_head_topk_bench_shape_equals_chain():
+    require_gpu()
+    w = W.WORKLOADS["bf16_b16_v151936"]
+    hid, wt = _head(w)
+    say("dflash_lm_head_topk 480x4096x151936")
+    ids, unary = D.dflash_lm_head_topk(hid, wt, top_k=w.top_k, valid_vocab=w.valid_vocab, multiplier=w.multiplier,
+                                       softcap=w.softcap)
+    ids2, unary2 = D.dflash_topk(D.dflash_lm_head(hid, wt), top_k=w.top_k, valid_vocab=w.valid_vocab,
+                                 multiplier=w.multiplier, softcap=w.softcap)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(unary, unary2)
