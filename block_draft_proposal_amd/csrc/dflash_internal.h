@@ -235,7 +235,7 @@ hipError_t launch_lm_head(const LmHeadArgs& a, hipStream_t stream);
 
 // Fused head + top-K: per-row K best of each group of column tiles (sorted
 // composites in the workspace [n_rows][n_grp][K]), then a merge per row.
-constexpr int kLmMergeCap = 8192;   // composites of one row the merge stages in LDS
+constexpr int kLmMergeCand = 3072;  // merge candidates of one row held in LDS (24 KB)
 struct LmTopkPlan {
   int32_t n_mb, n_nb, tiles_per_group, n_grp;
   size_t bytes;

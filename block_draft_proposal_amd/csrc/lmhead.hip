@@ -21,13 +21,15 @@
 // to bf16 (nearest, ties to even) and written through LDS as 16-byte rows.
 //
 // Fused head + top-K (compute_candidates without the logits reaching HBM):
-// a workgroup walks T column tiles of its row block with the same tile
-// product; each rounded tile is put in LDS and one thread per row folds the
-// row's values into a sorted register list of its K best composites
-// (value descending, id ascending; ids grow along the walk, so one strict
-// comparison with the K-th decides).  The lists of all column groups are
-// merged per row by a second kernel, which ranks every candidate by binary-
-// searched counts in the other sorted lists.  Both paths rank the same bf16
+// a workgroup computes one column tile of its row block (a few when a row's
+// lists would not fit the merge) with the same tile product; each rounded
+// tile is put in LDS and two threads per row fold the row's values into
+// sorted register lists of the K best composites (value descending, id
+// ascending; ids grow along each thread's walk, so one strict comparison
+// with the K-th decides), merged pairwise at the end.  The lists of all
+// column groups are merged per row by a second kernel, which ranks the
+// candidates that can still place by binary-searched counts in the other
+// sorted lists.  Both paths rank the same bf16
 // logits, so the fused result equals the head followed by the streaming
 // top-K bit for bit.
 #include "dflash.h"
@@ -184,6 +186,19 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const uint16_t* __r
 // sentinels (all ones, above every composite) ahead of the K real entries,
 // so the threshold is always the last slot and no index depends on K.
 template <int KB>
+__device__ __forceinline__ void list_insert(uint64_t (&best)[KB], uint64_t c) {
+#pragma unroll
+  for (int i = 0; i < KB; ++i) {                 // keeps the list sorted descending
+    if (c > best[i]) { const uint64_t t = best[i]; best[i] = c; c = t; }
+  }
+}
+
+static_assert(sizeof(uint64_t) * kBM * 32 <= sizeof(LmSmem), "pair exchange fits the stage buffers");
+
+// Two threads per row: thread t takes row t / 2 and the 64 columns of half
+// t % 2 of every tile of its group, keeping its own sorted list; at the end
+// the pair's lists meet in LDS and the even thread writes their merge.
+template <int KB>
 __global__ __launch_bounds__(kLmThreads) void lm_head_topk_kernel(
     const uint16_t* __restrict__ h, int64_t h_stride, const uint16_t* __restrict__ W, int32_t M, int32_t H,
     int32_t V, int32_t valid, int32_t K, int32_t n_mb, int32_t n_nb, int32_t tiles_per_group, int32_t n_grp,
@@ -194,6 +209,8 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_topk_kernel(
   tile_of(blockIdx.x, n_mb, mb, grp);
   if (grp >= n_grp) return;
   const int m0 = mb * kBM, tid = threadIdx.x;
+  const int row = tid >> 1, half = tid & 1;
+  const bool row_ok = m0 + row < M;
   uint64_t best[KB];
 #pragma unroll
   for (int i = 0; i < KB; ++i) best[i] = (i < KB - K) ? ~0ull : 0ull;
@@ -205,28 +222,38 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_topk_kernel(
     tile_product(h, h_stride, W, M, H, V, m0, n0, sm, acc);   // ends with a barrier
     tile_to_lds(acc, cs);
     __syncthreads();
-    if (tid < kBM && m0 + tid < M) {
-      const uint16_t* rowp = cs + tid * kCPad;
-      for (int c8 = 0; c8 < kBN && n0 + c8 < valid; c8 += 8) {
+    if (row_ok) {
+      const uint16_t* rowp = cs + row * kCPad + 64 * half;
+      const int c_lo = n0 + 64 * half;
+#pragma unroll 2
+      for (int c8 = 0; c8 < 64; c8 += 8) {
+        if (c_lo + c8 >= valid) break;
         const u32x4 v = ld16(rowp + c8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int col = n0 + c8 + e;
+          const int col = c_lo + c8 + e;
           const uint32_t bits = (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu);
-          uint64_t c = composite(bf16_key(bits), col);
-          if (col < valid && c > best[KB - 1]) {
-#pragma unroll
-            for (int i = 0; i < KB; ++i) {     // insert, keeping the list sorted
-              if (c > best[i]) { const uint64_t t = best[i]; best[i] = c; c = t; }
-            }
-          }
+          const uint64_t c = composite(bf16_key(bits), col);
+          if (col < valid && c > best[KB - 1]) list_insert(best, c);
         }
       }
     }
     __syncthreads();                           // the tile's LDS is reused by the next stage
   }
-  if (tid < kBM && m0 + tid < M) {
-    uint64_t* dst = parts + ((int64_t)(m0 + tid) * n_grp + grp) * K;
+  // pair merge: the odd thread's list to LDS, the even thread folds it in
+  uint64_t* xch = reinterpret_cast<uint64_t*>(lm_smem);      // [128 rows][KB], after the last barrier
+  if (half == 1) {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) xch[row * KB + i] = best[i];
+  }
+  __syncthreads();
+  if (half == 0 && row_ok) {
+#pragma unroll
+    for (int i = KB - 1; i >= 0; --i) {
+      const uint64_t c = xch[row * KB + i];
+      if (c != ~0ull && c > best[KB - 1]) list_insert(best, c);
+    }
+    uint64_t* dst = parts + ((int64_t)(m0 + row) * n_grp + grp) * K;
 #pragma unroll
     for (int i = 0; i < KB; ++i)
       if (i >= KB - K) dst[i - (KB - K)] = best[i];
@@ -234,39 +261,51 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_topk_kernel(
 }
 
 // Per row: the K best of n_grp sorted lists of K composites (0 = empty
-// slot).  Only candidates at or above the K-th largest list head can rank
-// below K (K heads are at least that large); each of those is ranked by its
-// position in its list plus binary-searched counts in the other lists.
+// slot), all distinct.  Thread t takes lists t, t + 256, ... and the largest
+// head among them; the K-th largest of these thread maxima (the floor) has K
+// list heads at or above it, so nothing below it can place.  Only the K
+// threads at or above the floor hold entries at or above it, at most
+// ceil(n_grp / 256) lists of K each, so the candidates fit kLmMergeCand;
+// every entry above a candidate is a candidate too, so its rank among the
+// candidates is its rank in the row.
 constexpr int kMergeThreadsLm = 256;
 __global__ __launch_bounds__(kMergeThreadsLm) void merge_lists_kernel(const uint64_t* __restrict__ parts,
                                                                     int32_t n_grp, int32_t K, float mult, float cap,
                                                                     int64_t* __restrict__ ids_out,
                                                                     float* __restrict__ unary_out) {
-  extern __shared__ __align__(16) uint64_t ml_smem[];
-  uint64_t* L = ml_smem;                                  // [n_grp][K]
+  __shared__ uint64_t s_max[kMergeThreadsLm];
+  __shared__ uint64_t s_cand[kLmMergeCand];
   __shared__ uint64_t s_floor;
+  __shared__ int s_n;
   const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x, m = n_grp * K;
-  const uint64_t* src = parts + row * (int64_t)m;
-  for (int i = tid; i < m; i += kMergeThreadsLm) L[i] = src[i];
-  if (tid == 0) s_floor = 0;
+  const int tid = threadIdx.x;
+  const uint64_t* src = parts + row * (int64_t)n_grp * K;
+  uint64_t mx = 0;
+  for (int g = tid; g < n_grp; g += kMergeThreadsLm) mx = max(mx, src[(int64_t)g * K]);
+  s_max[tid] = mx;
+  if (tid == 0) { s_floor = 0; s_n = 0; }
   __syncthreads();
-  // K-th largest list head (0 when fewer than K lists hold anything)
-  for (int g = tid; g < n_grp; g += kMergeThreadsLm) {
-    const uint64_t hg = L[g * K];
-    int above = 0;
-    for (int o = 0; o < n_grp; ++o) above += (L[o * K] > hg) ? 1 : 0;
-    if (hg != 0 && above == K - 1) s_floor = hg;         // unique: composites are distinct
-  }
+  int above = 0;
+  for (int o = 0; o < kMergeThreadsLm; ++o) above += (s_max[o] > mx) ? 1 : 0;
+  if (mx != 0 && above == K - 1) s_floor = mx;   // exactly one thread: the maxima are distinct
   __syncthreads();
   const uint64_t floor = s_floor;
-  for (int i = tid; i < m; i += kMergeThreadsLm) {
-    const uint64_t c = L[i];
-    if (c == 0 || c < floor) continue;
-    const int g = i / K;
-    int rank = i - g * K;
-    for (int o = 0; o < n_grp && rank < K; ++o)
-      if (o != g) rank += count_greater(L + o * K, K, c);
+  if (mx != 0 && mx >= floor) {
+    for (int g = tid; g < n_grp; g += kMergeThreadsLm) {
+      const uint64_t* list = src + (int64_t)g * K;
+      for (int j = 0; j < K; ++j) {             // descending: stop at the first miss
+        const uint64_t c = list[j];
+        if (c == 0 || c < floor) break;
+        s_cand[atomicAdd(&s_n, 1)] = c;
+      }
+    }
+  }
+  __syncthreads();
+  const int n = s_n;
+  for (int i = tid; i < n; i += kMergeThreadsLm) {
+    const uint64_t c = s_cand[i];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) rank += (s_cand[j] > c) ? 1 : 0;
     if (rank < K) {
       ids_out[row * K + rank] = composite_id(c);
       unary_out[row * K + rank] = unary_transform(bf16_key_value(composite_key(c)), mult, cap);
@@ -280,8 +319,10 @@ LmTopkPlan plan_lm_head_topk(int64_t n_rows, int64_t vocab, int32_t top_k) {
   LmTopkPlan p{};
   p.n_mb = (int32_t)((n_rows + kBM - 1) / kBM);
   p.n_nb = (int32_t)((vocab + kBN - 1) / kBN);
-  int t = 4;
-  while ((int64_t)((p.n_nb + t - 1) / t) * top_k > kLmMergeCap) t *= 2;
+  // one tile per workgroup unless a row's merge candidates could overflow
+  // (K threads of the merge, ceil(n_grp / 256) lists of K each)
+  int t = 1;
+  while ((int64_t)top_k * top_k * (((p.n_nb + t - 1) / t + 255) / 256) > kLmMergeCand) ++t;
   p.tiles_per_group = t;
   p.n_grp = (p.n_nb + t - 1) / t;
   p.bytes = (size_t)n_rows * p.n_grp * top_k * sizeof(uint64_t);
@@ -308,8 +349,7 @@ hipError_t launch_lm_head_topk(const LmHeadArgs& a, const LmTopkPlan& p, int64_t
 #undef DFLASH_LMTK
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_lists_kernel, dim3((unsigned)a.n_rows), dim3(kMergeThreadsLm),
-                     (size_t)p.n_grp * top_k * sizeof(uint64_t), stream, parts, p.n_grp, top_k, mult, cap, ids_out,
+  hipLaunchKernelGGL(merge_lists_kernel, dim3((unsigned)a.n_rows), dim3(kMergeThreadsLm), 0, stream, parts, p.n_grp, top_k, mult, cap, ids_out,
                      unary_out);
   return hipGetLastError();
 }
