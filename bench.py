@@ -57,20 +57,29 @@ def algorithmic_bytes(w):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "topk_traffic.json")
-TOPK_SOURCE = os.path.join(ROOT, "block_draft_proposal_amd", "csrc", "topk.hip")
+# the top-K kernel's sources: its own file and the device helpers it inlines
+TOPK_SOURCES = tuple(os.path.join(ROOT, "block_draft_proposal_amd", "csrc", f)
+                     for f in ("topk.hip", "device_common.h"))
+
+
+def sources_sha256(paths) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):
     """HBM bytes per top-K launch from the committed counter runs (FETCH_SIZE
     + WRITE_SIZE, scaled by a copy kernel of known size), or None when they
-    were taken on another workload or on a top-K source other than the one
+    were taken on another workload or on top-K sources other than the ones
     built now."""
-    import hashlib
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        with open(TOPK_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = sources_sha256(TOPK_SOURCES)
     except (OSError, ValueError):
         return None
     if t.get("source_sha256") != sha or t.get("workload") != workload:
