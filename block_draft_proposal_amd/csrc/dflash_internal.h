@@ -111,7 +111,8 @@ hipError_t launch_lm_head(const LmHeadArgs& a, hipStream_t stream);
 constexpr int kLmMergeCand = 3072;  // merge candidates of one row held in LDS (24 KB)
 struct LmTopkPlan {
   int32_t n_mb, n_nb, tiles_per_group, n_grp;
-  size_t bytes;
+  size_t bound_offset;      // byte offset of the per-row key bounds (uint32 [n_rows])
+  size_t bytes;             // total workspace bytes: group lists, then the bounds
 };
 LmTopkPlan plan_lm_head_topk(int64_t n_rows, int64_t vocab, int32_t top_k);
 hipError_t launch_lm_head_topk(const LmHeadArgs& a, const LmTopkPlan& p, int64_t valid_vocab, int32_t top_k,

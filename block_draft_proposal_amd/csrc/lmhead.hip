@@ -41,16 +41,45 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kLmThreads = 256;
-constexpr int kRowPad = kBK + 8;            // bf16 elements per LDS row of a stage
-constexpr int kCPad = kBN + 8;              // bf16 elements per LDS row of the output tile
+// Each wave computes a (16 kFragM) x (16 kFragN) block of the tile with
+// kFragM x kFragN MFMAs of 16 x 16 x 32; the waves tile it kWavesM x kWavesN.
+// The LDS bytes each MFMA needs fall as the wave's block grows.
+constexpr int kFragM = 8, kFragN = 4;
+constexpr int kWavesM = 2, kWavesN = 4;
+constexpr int kWM = 16 * kFragM, kWN = 16 * kFragN;
+constexpr int kBM = kWM * kWavesM, kBN = kWN * kWavesN;
+constexpr int kBK = 64;                     // contraction depth of one stage (32 or 64)
+constexpr int kChunks = kBK / 8;            // 16-byte chunks per stage row
+constexpr int kRowBytes = kBK * 2;
+constexpr int kBlockRows = 1024 / kRowBytes;   // rows per 1 KB block of direct loads
+constexpr int kSwzShift = kBK == 64 ? 1 : 2;   // log2 of the rows sharing a 256-byte bank window
+constexpr int kWaves = kWavesM * kWavesN;
+constexpr int kLmThreads = 64 * kWaves;
+constexpr int kStages = 2;                  // LDS ring depth: loads run kStages - 1 stages ahead
+constexpr int kStageBytes = (kBM + kBN) * kBK * 2;   // one stage of A and B
+constexpr int kLoadsPerStage = (kBM + kBN) / kBlockRows / kWaves;   // direct loads per thread per stage
+// The rounded output tile goes through LDS in passes of kOutCols columns.
+constexpr int kOutCols = kBN < 128 ? kBN : 128;
+constexpr int kOutPasses = kBN / kOutCols;
+constexpr int kCPad = kOutCols + 8;         // bf16 elements per LDS row of one pass
+static_assert(kBK == 32 || kBK == 64, "stage depth");
+static_assert(kBM % (kBlockRows * kWaves) == 0 && kBN % (kBlockRows * kWaves) == 0,
+              "stage rows split evenly over the waves");
+static_assert(kStages >= 2 && kStages <= 5, "wait counts below cover up to three stages ahead");
+static_assert(kOutCols % kWN == 0 && kBN % kOutCols == 0, "a wave's columns lie in one output pass");
 
+// The LDS of one workgroup: a ring of kStages stages, each the A tile
+// [kBM rows][kBK k] then the B tile [kBN rows][kBK k], rows of kRowBytes
+// without padding.  Within a row the 16-byte k chunks are stored
+// XOR-swizzled: chunk c of row r sits in slot c ^ swz(r), so the 16 rows one
+// MFMA fragment reads, and the two chunks of neighbouring lane groups, fall
+// on distinct banks.
 struct LmSmem {
-  uint16_t a[2][kBM * kRowPad];
-  uint16_t b[2][kBN * kRowPad];
+  unsigned char stage[kStages][kStageBytes];
 };
-static_assert(sizeof(uint16_t) * kBM * kCPad <= sizeof(uint16_t) * 2 * kBM * kRowPad, "output tile fits in A");
+static_assert(sizeof(uint16_t) * kBM * kCPad <= sizeof(LmSmem), "output tile fits in the ring");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Workgroup -> (row block, column block).  Consecutive workgroups go to
 // consecutive XCDs; the n_mb row blocks of one column block get ids that
@@ -61,92 +90,158 @@ __device__ __forceinline__ void tile_of(int id, int n_mb, int& mb, int& nb) {
   mb = slot % n_mb;
 }
 
-// Stage loads: rows [r0, r0 + 128) x k [k0, k0 + 64) of a [rows, H] matrix,
-// as 1024 16-byte chunks, 4 per thread (chunk c: row c / 8, k offset 8 (c % 8)).
-// Loads are unconditional at clamped addresses; chunks outside the matrix
-// become zero afterwards.
-__device__ __forceinline__ void load_stage(const uint16_t* __restrict__ base, int64_t stride, int rows, int H,
-                                           int r0, int k0, int tid, u32x4 (&v)[4]) {
+__device__ __forceinline__ int swz(int row) { return (row >> kSwzShift) & (kChunks - 1); }
+
+// Issues the direct global -> LDS loads of one stage: rows [r0, r0 + ROWS)
+// x k [k0, k0 + kBK) of a [rows, H] matrix, in 1 KB blocks of kBlockRows
+// rows dealt round the waves; lane l of a block fills slot l % kChunks of
+// row l / kChunks with the chunk the swizzle puts there.  Addresses are
+// clamped into the matrix: rows past the end repeat the last row (their
+// results are never used) and k past H is zeroed by zero_tail before use.
+template <int ROWS>
+__device__ __forceinline__ void issue_stage(const uint16_t* __restrict__ base, int64_t stride, int rows, int H,
+                                            int r0, int k0, unsigned char* dst) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < ROWS / kBlockRows / kWaves; ++q) {
+    const int blk = q * kWaves + wave, r = blk * kBlockRows + lane / kChunks;
+    const int k = k0 + 8 * ((lane % kChunks) ^ swz(r));
+    const uint16_t* src = base + (int64_t)min(r0 + r, rows - 1) * stride + min(k, H - 8);
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(dst + blk * 1024), 16, 0, 0);
+  }
+}
+
+// After the stage has landed: zeroes this thread's chunks of it whose k is
+// at or past H (only the last stage of a hidden size that is not a multiple
+// of kBK has any).
+template <int ROWS>
+__device__ __forceinline__ void zero_tail(int H, int k0, unsigned char* dst) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c = tid + kLmThreads * q;
-    const int row = r0 + (c >> 3), k = k0 + 8 * (c & 7);
-    const u32x4 x = ld16(base + (int64_t)min(row, rows - 1) * stride + min(k, H - 8));
-    v[q] = (row < rows && k < H) ? x : zero;
+  for (int q = 0; q < ROWS / kBlockRows / kWaves; ++q) {
+    const int blk = q * kWaves + wave, r = blk * kBlockRows + lane / kChunks;
+    if (k0 + 8 * ((lane % kChunks) ^ swz(r)) >= H) st16(dst + blk * 1024 + lane * 16, zero);
   }
 }
 
-__device__ __forceinline__ void store_stage(uint16_t* __restrict__ s, int tid, const u32x4 (&v)[4]) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c = tid + kLmThreads * q;
-    st16(s + (c >> 3) * kRowPad + 8 * (c & 7), v[q]);
-  }
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// The 128 x 128 fp32 tile of (mb, nb), in the wave's 4 x 4 accumulators.
-// D layout of one 16 x 16 MFMA: lane l holds column l % 16 and rows
-// 4 (l / 16) + v, v = 0..3.
+// Workgroup barrier for the stage ring.  __syncthreads() would also fence,
+// which waits for every outstanding direct load, prefetched stages included;
+// here each thread has already waited for its own loads of the stage about to
+// be read (wait_vm) and for its own LDS accesses (lgkmcnt 0), and the empty
+// asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));   // lgkmcnt(0) only
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The kBM x kBN fp32 tile of (mb, nb); each wave holds its kWM x kWN block
+// in kFragM x kFragN accumulators.  D layout of one 16 x 16 MFMA: lane l holds column
+// l % 16 and rows 4 (l / 16) + v, v = 0..3.  Stage t of the contraction
+// lives in ring slot t % kStages; each iteration waits for its own stage,
+// passes one barrier (after which the slot computed last iteration is free)
+// and refills that slot with stage t + kStages - 1 before computing.  Ends
+// with a barrier, so the ring may be reused.
 __device__ __forceinline__ void tile_product(const uint16_t* __restrict__ h, int64_t h_stride,
                                              const uint16_t* __restrict__ W, int M, int H, int V, int m0, int n0,
-                                             LmSmem& sm, f32x4_t (&acc)[4][4]) {
+                                             LmSmem& sm, f32x4_t (&acc)[kFragM][kFragN]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave / kWavesN) * kWM, wn = (wave % kWavesN) * kWN;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kFragM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kFragN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int nk = (H + kBK - 1) / kBK;
-  u32x4 ra[4], rb[4];
-  load_stage(h, h_stride, M, H, m0, 0, tid, ra);
-  load_stage(W, H, V, H, n0, 0, tid, rb);
-  store_stage(sm.a[0], tid, ra);
-  store_stage(sm.b[0], tid, rb);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      load_stage(h, h_stride, M, H, m0, (kt + 1) * kBK, tid, ra);
-      load_stage(W, H, V, H, n0, (kt + 1) * kBK, tid, rb);
+  const bool ragged = (H % kBK) != 0;
+  constexpr int kBOff = kBM * kRowBytes;        // the B tile within a stage
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t) {
+    if (t < nk) {
+      issue_stage<kBM>(h, h_stride, M, H, m0, t * kBK, sm.stage[t]);
+      issue_stage<kBN>(W, H, V, H, n0, t * kBK, sm.stage[t] + kBOff);
     }
-    const uint16_t* sa = sm.a[cur];
-    const uint16_t* sb = sm.b[cur];
-#pragma unroll
-    for (int ks = 0; ks < kBK; ks += 32) {
-      bf16x8_t af[4], bfrag[4];
-      const int kofs = ks + 8 * (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = __builtin_bit_cast(bf16x8_t, ld16(sa + (wm + 16 * i + (lane & 15)) * kRowPad + kofs));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfrag[j] = __builtin_bit_cast(bf16x8_t, ld16(sb + (wn + 16 * j + (lane & 15)) * kRowPad + kofs));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfrag[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      store_stage(sm.a[cur ^ 1], tid, ra);
-      store_stage(sm.b[cur ^ 1], tid, rb);
-    }
-    __syncthreads();
   }
+  // fragment reads: row (lane & 15) of a 16-row group, chunk (lane >> 4) of a
+  // 32-wide k slice (16-row groups start at multiples of 16, so the swizzle
+  // of the row is that of lane & 15)
+  const int frow = lane & 15, fsw = swz(frow);
+  for (int kt = 0; kt < nk; ++kt) {
+    unsigned char* cur = sm.stage[kt % kStages];
+    // this thread's loads of stage kt are done once at most the loads of
+    // the later stages already issued are outstanding
+    const int ahead = min(kStages - 2, nk - 1 - kt);
+    if (ahead >= 3) wait_vm<3 * kLoadsPerStage>();
+    else if (ahead == 2) wait_vm<2 * kLoadsPerStage>();
+    else if (ahead == 1) wait_vm<kLoadsPerStage>();
+    else wait_vm<0>();
+    if (ragged && kt == nk - 1) {
+      zero_tail<kBM>(H, kt * kBK, cur);
+      zero_tail<kBN>(H, kt * kBK, cur + kBOff);
+    }
+    ring_barrier();
+    if (kt + kStages - 1 < nk) {
+      unsigned char* nxt = sm.stage[(kt + kStages - 1) % kStages];
+      issue_stage<kBM>(h, h_stride, M, H, m0, (kt + kStages - 1) * kBK, nxt);
+      issue_stage<kBN>(W, H, V, H, n0, (kt + kStages - 1) * kBK, nxt + kBOff);
+    }
+    const unsigned char* sa = cur;
+    const unsigned char* sb = cur + kBOff;
+#pragma unroll
+    for (int ks = 0; ks < kChunks; ks += 4) {        // 32-wide k slices: chunks ks .. ks + 3
+      const int slot = ((ks + (lane >> 4)) ^ fsw) * 16;
+      bf16x8_t af[kFragM], bfrag[kFragN];
+#pragma unroll
+      for (int i = 0; i < kFragM; ++i)
+        af[i] = __builtin_bit_cast(bf16x8_t, ld16(sa + (wm + 16 * i + frow) * kRowBytes + slot));
+#pragma unroll
+      for (int j = 0; j < kFragN; ++j)
+        bfrag[j] = __builtin_bit_cast(bf16x8_t, ld16(sb + (wn + 16 * j + frow) * kRowBytes + slot));
+#pragma unroll
+      for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfrag[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  __syncthreads();
 }
 
-// Rounds the wave's accumulators to bf16 into the output tile in LDS.
-__device__ __forceinline__ void tile_to_lds(const f32x4_t (&acc)[4][4], uint16_t* cs) {
+// The wave's accumulators rounded to bf16 (nearest, ties to even), two per
+// register: pk[i][j][0] holds rows 4 (l / 16) + 0, 1 and pk[i][j][1] rows
+// + 2, 3 of fragment (i, j), low half first.  Rounding once here frees the
+// fp32 accumulators before the epilogue.
+__device__ __forceinline__ void pack_tile(const f32x4_t (&acc)[kFragM][kFragN], uint32_t (&pk)[kFragM][kFragN][2]) {
+#pragma unroll
+  for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+    for (int j = 0; j < kFragN; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        pk[i][j][h] = f32_to_bf16_rne(acc[i][j][2 * h]) | (f32_to_bf16_rne(acc[i][j][2 * h + 1]) << 16);
+}
+
+// Writes into LDS the rounded values of the waves whose columns lie in
+// output pass `pass` (tile columns [pass kOutCols, (pass + 1) kOutCols)).
+__device__ __forceinline__ void tile_to_lds(const uint32_t (&pk)[kFragM][kFragN][2], uint16_t* cs, int pass) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave / kWavesN) * kWM, wn = (wave % kWavesN) * kWN - pass * kOutCols;
+  if (wn < 0 || wn >= kOutCols) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kFragM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kFragN; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         cs[(wm + 16 * i + 4 * (lane >> 4) + v) * kCPad + wn + 16 * j + (lane & 15)] =
-            (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+            (uint16_t)((v & 1) ? (pk[i][j][v >> 1] >> 16) : (pk[i][j][v >> 1] & 0xffffu));
 }
 
 __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const uint16_t* __restrict__ h, int64_t h_stride,
@@ -159,32 +254,40 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const uint16_t* __r
   tile_of(blockIdx.x, n_mb, mb, nb);
   if (nb >= n_nb) return;
   const int m0 = mb * kBM, n0 = nb * kBN;
-  f32x4_t acc[4][4];
-  tile_product(h, h_stride, W, M, H, V, m0, n0, sm, acc);
+  uint32_t pk[kFragM][kFragN][2];
+  {
+    f32x4_t acc[kFragM][kFragN];
+    tile_product(h, h_stride, W, M, H, V, m0, n0, sm, acc);
+    pack_tile(acc, pk);
+  }
 
-  // round to bf16 into LDS, then write whole 16-byte row pieces
+  // per pass: the rounded values into LDS, then whole 16-byte row pieces out
   const int tid = threadIdx.x;
-  uint16_t* cs = sm.a[0];
-  tile_to_lds(acc, cs);
-  __syncthreads();
+  uint16_t* cs = reinterpret_cast<uint16_t*>(sm.stage[0]);
+  for (int pass = 0; pass < kOutPasses; ++pass) {
+    tile_to_lds(pk, cs, pass);
+    __syncthreads();
+    const int c0 = n0 + pass * kOutCols;
 #pragma unroll
-  for (int q = 0; q < (kBM * kBN / 8) / kLmThreads; ++q) {
-    const int c = tid + kLmThreads * q;
-    const int row = c >> 4, col = 8 * (c & 15);
-    if (m0 + row >= M) continue;
-    uint16_t* dst = logits + (int64_t)(m0 + row) * l_stride + n0 + col;
-    const uint16_t* src = cs + row * kCPad + col;
-    if (n0 + col + 8 <= V) {
-      st16(dst, ld16(src));
-    } else {
-      for (int e = 0; e < 8 && n0 + col + e < V; ++e) dst[e] = src[e];
+    for (int q = 0; q < (kBM * kOutCols / 8) / kLmThreads; ++q) {
+      const int c = tid + kLmThreads * q;
+      const int row = c / (kOutCols / 8), col = 8 * (c % (kOutCols / 8));
+      if (m0 + row >= M) continue;
+      uint16_t* dst = logits + (int64_t)(m0 + row) * l_stride + c0 + col;
+      const uint16_t* src = cs + row * kCPad + col;
+      if (c0 + col + 8 <= V) {
+        st16(dst, ld16(src));
+      } else {
+        for (int e = 0; e < 8 && c0 + col + e < V; ++e) dst[e] = src[e];
+      }
     }
+    __syncthreads();
   }
 }
 
 // KB: list slots (K rounded up to 8, 16 or 32).  The list holds KB - K
-// sentinels (all ones, above every composite) ahead of the K real entries,
-// so the threshold is always the last slot and no index depends on K.
+// sentinels (all ones, above every entry) ahead of the K real entries, so
+// the threshold is always the last slot and no index depends on K.
 template <int KB>
 __device__ __forceinline__ void list_insert(uint64_t (&best)[KB], uint64_t c) {
 #pragma unroll
@@ -192,72 +295,143 @@ __device__ __forceinline__ void list_insert(uint64_t (&best)[KB], uint64_t c) {
     if (c > best[i]) { const uint64_t t = best[i]; best[i] = c; c = t; }
   }
 }
+template <int KB>
+__device__ __forceinline__ void list_insert(uint32_t (&best)[KB], uint32_t c) {
+#pragma unroll
+  for (int i = 0; i < KB; ++i) {                 // keeps the list sorted descending
+    const uint32_t hi = max(best[i], c);
+    c = min(best[i], c);
+    best[i] = hi;
+  }
+}
 
-static_assert(sizeof(uint64_t) * kBM * 32 <= sizeof(LmSmem), "pair exchange fits the stage buffers");
+// Within one tile a value's order is carried by a 32-bit key: its 16-bit
+// value key above 255 - (column within the tile), so larger is better and
+// equal values rank by column; 0 marks an empty slot.
+static_assert(kBN <= 256, "tile columns fit the 8-bit column field");
+__device__ __forceinline__ uint32_t tile_key(uint32_t key, int col_in_tile) {
+  return (key << 8) | (uint32_t)(255 - col_in_tile);
+}
+__device__ __forceinline__ uint64_t tile_key_composite(uint32_t tk, int n0) {
+  return composite(tk >> 8, n0 + 255 - (int)(tk & 255u));
+}
 
-// Two threads per row: thread t takes row t / 2 and the 64 columns of half
-// t % 2 of every tile of its group, keeping its own sorted list; at the end
-// the pair's lists meet in LDS and the even thread writes their merge.
+constexpr int kRowThreads = kLmThreads / kBM;   // scan threads per tile row
+constexpr int kScanCols = kOutCols / kRowThreads;   // columns each of them folds in per output pass
+static_assert(kLmThreads % kBM == 0 && kScanCols % 8 == 0, "scan threads split the rows evenly");
+static_assert(sizeof(uint32_t) * kBM * (kRowThreads - 1) * 32 <= sizeof(LmSmem), "list exchange fits the ring");
+
+// kRowThreads threads per row: thread t takes row t / kRowThreads and, of
+// every output pass of a tile, the kScanCols columns from p kScanCols on,
+// p = t % kRowThreads, folding them into a sorted list of its own.  After
+// the tile the lists of a row meet in LDS and the row's p = 0 thread merges
+// them, with the group's list so far (from the workspace, for the second
+// tile of a group on), and stores the group's list.  No list is live across
+// a tile product.
+//
+// bound[r] is a lower bound on the key of row r's K-th best value: once a
+// merged list holds K values the bound is raised (atomic max) to the key of
+// its K-th, since K values of the row have at least that key.  Values with a
+// smaller key cannot place and are skipped before any list work; the bound
+// only grows, so a stale read filters less but never wrongly.
 template <int KB>
 __global__ __launch_bounds__(kLmThreads) void lm_head_topk_kernel(
     const uint16_t* __restrict__ h, int64_t h_stride, const uint16_t* __restrict__ W, int32_t M, int32_t H,
     int32_t V, int32_t valid, int32_t K, int32_t n_mb, int32_t n_nb, int32_t tiles_per_group, int32_t n_grp,
-    uint64_t* __restrict__ parts) {
+    uint64_t* __restrict__ parts, uint32_t* __restrict__ bound) {
   extern __shared__ __align__(16) unsigned char lm_smem[];
   LmSmem& sm = *reinterpret_cast<LmSmem*>(lm_smem);
   int mb, grp;
   tile_of(blockIdx.x, n_mb, mb, grp);
   if (grp >= n_grp) return;
   const int m0 = mb * kBM, tid = threadIdx.x;
-  const int row = tid >> 1, half = tid & 1;
+  const int row = tid / kRowThreads, part = tid % kRowThreads;
   const bool row_ok = m0 + row < M;
-  uint64_t best[KB];
-#pragma unroll
-  for (int i = 0; i < KB; ++i) best[i] = (i < KB - K) ? ~0ull : 0ull;
   const int nb0 = grp * tiles_per_group, nb1 = min(n_nb, nb0 + tiles_per_group);
-  uint16_t* cs = sm.a[0];
+  uint16_t* cs = reinterpret_cast<uint16_t*>(sm.stage[0]);
+  uint64_t* dst = parts + ((int64_t)(m0 + row) * n_grp + grp) * K;
   for (int nb = nb0; nb < nb1; ++nb) {
     const int n0 = nb * kBN;
-    f32x4_t acc[4][4];
-    tile_product(h, h_stride, W, M, H, V, m0, n0, sm, acc);   // ends with a barrier
-    tile_to_lds(acc, cs);
-    __syncthreads();
-    if (row_ok) {
-      const uint16_t* rowp = cs + row * kCPad + 64 * half;
-      const int c_lo = n0 + 64 * half;
-#pragma unroll 2
-      for (int c8 = 0; c8 < 64; c8 += 8) {
-        if (c_lo + c8 >= valid) break;
-        const u32x4 v = ld16(rowp + c8);
+    uint32_t pk[kFragM][kFragN][2];
+    {
+      f32x4_t acc[kFragM][kFragN];
+      tile_product(h, h_stride, W, M, H, V, m0, n0, sm, acc);   // ends with a barrier
+      pack_tile(acc, pk);
+    }
+    uint32_t lo = 0;
+    if (row_ok) lo = __hip_atomic_load(bound + m0 + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t tl[KB];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int col = c_lo + c8 + e;
-          const uint32_t bits = (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu);
-          const uint64_t c = composite(bf16_key(bits), col);
-          if (col < valid && c > best[KB - 1]) list_insert(best, c);
+    for (int i = 0; i < KB; ++i) tl[i] = (i < KB - K) ? ~0u : 0u;
+    for (int pass = 0; pass < kOutPasses; ++pass) {
+      tile_to_lds(pk, cs, pass);
+      __syncthreads();
+      const int t_lo = pass * kOutCols + kScanCols * part;   // first column within the tile
+      if (row_ok && n0 + t_lo < valid) {
+        const uint16_t* rowp = cs + row * kCPad + kScanCols * part;
+#pragma unroll 2
+        for (int c8 = 0; c8 < kScanCols; c8 += 8) {
+          if (n0 + t_lo + c8 >= valid) break;
+          const u32x4 v = ld16(rowp + c8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int tc = t_lo + c8 + e;
+            const uint32_t key = bf16_key((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu));
+            if (key >= lo && n0 + tc < valid) {
+              const uint32_t c = tile_key(key, tc);
+              if (c > tl[KB - 1]) list_insert(tl, c);
+            }
+          }
         }
       }
+      __syncthreads();                         // the pass's LDS is reused next
     }
-    __syncthreads();                           // the tile's LDS is reused by the next stage
-  }
-  // pair merge: the odd thread's list to LDS, the even thread folds it in
-  uint64_t* xch = reinterpret_cast<uint64_t*>(lm_smem);      // [128 rows][KB], after the last barrier
-  if (half == 1) {
+    // row merge: the other threads' lists to LDS, the p = 0 thread folds them
+    // in, widens its list to composites and adds the group's earlier tiles
+    uint32_t* xch = reinterpret_cast<uint32_t*>(lm_smem);   // [kBM][kRowThreads - 1][KB]
+    if (part > 0) {
 #pragma unroll
-    for (int i = 0; i < KB; ++i) xch[row * KB + i] = best[i];
-  }
-  __syncthreads();
-  if (half == 0 && row_ok) {
-#pragma unroll
-    for (int i = KB - 1; i >= 0; --i) {
-      const uint64_t c = xch[row * KB + i];
-      if (c != ~0ull && c > best[KB - 1]) list_insert(best, c);
+      for (int i = 0; i < KB; ++i) xch[(row * (kRowThreads - 1) + part - 1) * KB + i] = tl[i];
     }
-    uint64_t* dst = parts + ((int64_t)(m0 + row) * n_grp + grp) * K;
+    __syncthreads();
+    if (part == 0 && row_ok) {
+      for (int o = 0; o < kRowThreads - 1; ++o) {
 #pragma unroll
-    for (int i = 0; i < KB; ++i)
-      if (i >= KB - K) dst[i - (KB - K)] = best[i];
+        for (int i = KB - 1; i >= 0; --i) {
+          const uint32_t c = xch[(row * (kRowThreads - 1) + o) * KB + i];
+          if (c != ~0u && c > tl[KB - 1]) list_insert(tl, c);
+        }
+      }
+      uint64_t kth;                            // the group list's K-th entry
+      if (nb == nb0) {
+#pragma unroll
+        for (int i = 0; i < KB; ++i)
+          if (i >= KB - K) dst[i - (KB - K)] = tl[i] == 0u ? 0ull : tile_key_composite(tl[i], n0);
+        kth = tl[KB - 1] == 0u ? 0ull : tile_key_composite(tl[KB - 1], n0);
+      } else {                                 // with the group's earlier tiles (stored by this thread)
+        uint64_t best[KB];
+#pragma unroll
+        for (int i = 0; i < KB; ++i)
+          best[i] = (i < KB - K) ? ~0ull : (tl[i] == 0u ? 0ull : tile_key_composite(tl[i], n0));
+        for (int i = K - 1; i >= 0; --i) {
+          const uint64_t c = dst[i];
+          if (c > best[KB - 1]) list_insert(best, c);
+        }
+#pragma unroll
+        for (int i = 0; i < KB; ++i)
+          if (i >= KB - K) dst[i - (KB - K)] = best[i];
+        kth = best[KB - 1];
+      }
+      if (kth != 0 && composite_key(kth) > lo)
+        __hip_atomic_fetch_max(bound + m0 + row, composite_key(kth), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();                           // xch lies in the ring the next tile refills
   }
+}
+
+__global__ void clear_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 // Per row: the K best of n_grp sorted lists of K composites (0 = empty
@@ -325,8 +499,9 @@ LmTopkPlan plan_lm_head_topk(int64_t n_rows, int64_t vocab, int32_t top_k) {
   while ((int64_t)top_k * top_k * (((p.n_nb + t - 1) / t + 255) / 256) > kLmMergeCand) ++t;
   p.tiles_per_group = t;
   p.n_grp = (p.n_nb + t - 1) / t;
-  p.bytes = (size_t)n_rows * p.n_grp * top_k * sizeof(uint64_t);
-  p.bytes = (p.bytes + 255) & ~(size_t)255;
+  const size_t lists = (size_t)n_rows * p.n_grp * top_k * sizeof(uint64_t);
+  p.bound_offset = (lists + 255) & ~(size_t)255;
+  p.bytes = (p.bound_offset + (size_t)n_rows * sizeof(uint32_t) + 255) & ~(size_t)255;
   return p;
 }
 
@@ -335,6 +510,9 @@ hipError_t launch_lm_head_topk(const LmHeadArgs& a, const LmTopkPlan& p, int64_t
                                hipStream_t stream) {
   if (a.n_rows == 0) return hipSuccess;
   uint64_t* parts = static_cast<uint64_t*>(workspace);
+  uint32_t* bound = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) + p.bound_offset);
+  hipLaunchKernelGGL(clear_u32_kernel, dim3((unsigned)((a.n_rows + 255) / 256)), dim3(256), 0, stream, bound,
+                     a.n_rows);
   const int64_t slots = (int64_t)((p.n_grp + 7) / 8) * p.n_mb;
   const dim3 grid((unsigned)(slots * 8));
 #define DFLASH_LMTK(KB)                                                                                    \
@@ -342,7 +520,7 @@ hipError_t launch_lm_head_topk(const LmHeadArgs& a, const LmTopkPlan& p, int64_t
                      static_cast<const uint16_t*>(a.hidden), a.hidden_row_stride,                          \
                      static_cast<const uint16_t*>(a.weight), (int32_t)a.n_rows, a.hidden_size,             \
                      (int32_t)a.vocab, (int32_t)valid_vocab, top_k, p.n_mb, p.n_nb, p.tiles_per_group,     \
-                     p.n_grp, parts)
+                     p.n_grp, parts, bound)
   if (top_k <= 8) DFLASH_LMTK(8);
   else if (top_k <= 16) DFLASH_LMTK(16);
   else DFLASH_LMTK(32);
