@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 
 METRIC = "draft tokens/s through conv+topK+lattice walk; conv/topK HBM GB/s % of peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFS = 2500.0      # MI355X dense bf16 matrix peak, TFLOP/s
 DEFAULT_WORKLOAD = "bf16_b16_v151936"
 MALL_BYTES = 256 * 1024 * 1024
 TIMED_EVERY = 4          # top-K events on every 4th timed step
@@ -245,6 +246,35 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
             print(f"| {name} | {cname} | {med:.2f} | {p10:.2f} | {p90:.2f} | {nbytes[cname] / 1e6:.2f} | {gbs:.0f} | "
                   f"{100 * gbs / HBM_PEAK_GBS:.1f} | {100 * gbs / copy_gbs:.1f} |", flush=True)
         del inp, call, fns
+        torch.cuda.empty_cache()
+
+    # the dense head in front of the top-K (bf16 workloads): plain, and fused with the top-K
+    print("\n| workload | call | rows x hidden x vocab | median us | p10 us | p90 us | GFLOP | TFLOP/s | "
+          "% of 2.5 PFLOP/s |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for name, w in W.WORKLOADS.items():
+        if (only and name not in only) or w.dtype != "bf16":
+            continue
+        d = W.make_head_inputs(w, device=dev)
+        hid, wt = d["hidden"], d["weight"]
+        M, H, V, K = hid.shape[0], hid.shape[1], wt.shape[0], w.top_k
+        logits = torch.empty((M, V), dtype=hid.dtype, device=dev)
+        ids = torch.empty((M, K), dtype=torch.int64, device=dev)
+        unary = torch.empty((M, K), dtype=torch.float32, device=dev)
+        ws = torch.empty(D.lib().dflash_lm_head_topk_workspace_size(M, V, K), dtype=torch.uint8, device=dev)
+        fns = {
+            "dflash_lm_head": lambda: D.dflash_lm_head(hid, wt, out=logits),
+            "dflash_lm_head_topk": lambda: D.dflash_lm_head_topk(hid, wt, top_k=K, valid_vocab=w.valid_vocab,
+                                                                 multiplier=w.multiplier, softcap=w.softcap,
+                                                                 ids_out=ids, unary_out=unary, workspace=ws),
+        }
+        flop = 2.0 * M * H * V
+        for cname, fn in fns.items():
+            med, p10, p90 = timed(fn)
+            tfs = flop / (med * 1e-6) / 1e12
+            print(f"| {name} | {cname} | {M} x {H} x {V} | {med:.1f} | {p10:.1f} | {p90:.1f} | {flop / 1e9:.1f} | "
+                  f"{tfs:.0f} | {100 * tfs / MFMA_PEAK_TFS:.1f} |", flush=True)
+        del d, hid, wt, logits, ids, unary, ws, fns
         torch.cuda.empty_cache()
 
 
