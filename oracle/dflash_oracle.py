@@ -33,6 +33,9 @@ Readings where the pages are silent (each listed again in the design doc):
     P [r, H]; slot 0's predecessor is the anchor.
   * candidates from hidden states: the dense head's logits are the exact
     sums rounded once to the storage dtype, and the top-k ranks them.
+  * conv module: the kernel projection's output (both sides' coefficients)
+    is the exact sums rounded once to the storage dtype; its 2*T*G outputs
+    per token are ordered (side, tap, group).
 """
 from __future__ import annotations
 
@@ -134,6 +137,42 @@ def conv(x: np.ndarray, base: np.ndarray, delta: np.ndarray, block_size: int,
                 coeff = base[t] + np.repeat(delta[i, t], group_size)   # channel c uses group c // gs
                 out[i] += coeff * x[i - t]
     return out
+
+
+# ---------------------------------------------------------------------------
+# Step 1b: the conv module's kernel projection and its two sides
+# [DF2] code excerpt of the grouped conv module: the base kernel is laid out
+# [input/output side, tap, channel] and starts as the identity (tap 0 = 1);
+# one bias-free linear map of a token's input gives 2 * T * G coefficients,
+# read as [2, T, G]; prepare convolves the input with side 0 and hands side
+# 1's coefficients on, and finish convolves the sublayer output with side 1.
+# ---------------------------------------------------------------------------
+
+def conv_projection(x: np.ndarray, weight: np.ndarray, dtype: str) -> np.ndarray:
+    """x [N, H], weight [2*T*G, H] (the linear map's [out, in] layout) ->
+    coefficients [N, 2*T*G]: each the exact sum of its H products, rounded
+    once to the storage dtype (the map's output dtype)."""
+    z = np.asarray(x, np.float64) @ np.asarray(weight, np.float64).T
+    return round_to_dtype(z, dtype)
+
+
+def conv_prepare(x: np.ndarray, weight: np.ndarray, base2: np.ndarray, block_size: int,
+                 group_size: int, dtype: str):
+    """x [N, H], weight [2*T*G, H], base2 [2, T, H] -> (out [N, H] float64,
+    unrounded; coefficients [N, 2, T, G] in dtype).  out convolves x with
+    side 0; side 1's coefficients, coefficients[:, 1], are what finish uses."""
+    N, H = np.asarray(x).shape
+    T = np.asarray(base2).shape[1]
+    G = H // group_size
+    coeff = conv_projection(x, weight, dtype).reshape(N, 2, T, G)
+    return conv(x, np.asarray(base2)[0], coeff[:, 0], block_size, group_size), coeff
+
+
+def conv_finish(y: np.ndarray, coeff: np.ndarray, base2: np.ndarray, block_size: int,
+                group_size: int) -> np.ndarray:
+    """y [N, H] (the sublayer output), coeff [N, 2, T, G] from conv_prepare ->
+    y convolved with side 1 (float64, unrounded)."""
+    return conv(y, np.asarray(base2)[1], np.asarray(coeff)[:, 1], block_size, group_size)
 
 
 # ---------------------------------------------------------------------------
