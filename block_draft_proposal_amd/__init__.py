@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     make_config,
     dflash_validate_config,
     dflash_conv,
+    dflash_conv_prepare,
     dflash_topk,
     dflash_lattice,
     dflash_walk,

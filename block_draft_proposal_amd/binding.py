@@ -63,6 +63,9 @@ _SIGNATURES = {
     "dflash_validate_config": (_c_i32, [ctypes.POINTER(DraftConfig)]),
     "dflash_last_error": (ctypes.c_char_p, []),
     "dflash_conv": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i64, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp]),
+    "dflash_conv_prepare_workspace_size": (_c_size, [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "dflash_conv_prepare": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
+                                     _c_i32, _c_vp, _c_size, _c_vp]),
     "dflash_topk_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i32]),
     "dflash_topk": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_f32, _c_f32, _c_i32, _c_vp, _c_vp,
                              _c_vp, _c_size, _c_vp]),
@@ -157,6 +160,29 @@ def dflash_conv(x: torch.Tensor, base: torch.Tensor, delta: torch.Tensor, *, blo
     _check(lib().dflash_conv(_p(x), _p(base), _p(delta), delta.stride(0) if N else T * (H // group_size), _p(out),
                              N, H, group_size, T, block_size, _dtype_code(x), _stream(stream)))
     return out
+
+
+def dflash_conv_prepare(x: torch.Tensor, proj_weight: torch.Tensor, base2: torch.Tensor, *, block_size: int,
+                        group_size: int, out: Optional[torch.Tensor] = None, coeff_out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None):
+    """x [N, H]; proj_weight [2*T*G, H]; base2 [2, T, H].  Returns (out [N, H]:
+    x convolved with side 0, coeff [N, 2, T, G]: both sides' coefficients).
+    finish is dflash_conv(y, base2[1], coeff[:, 1], ...)."""
+    if not (x.is_contiguous() and proj_weight.is_contiguous() and base2.is_contiguous()):
+        raise ValueError("x, proj_weight and base2 must be contiguous")
+    N, H = x.shape
+    T = base2.shape[1]
+    G = H // group_size
+    if out is None:
+        out = torch.empty_like(x)
+    if coeff_out is None:
+        coeff_out = torch.empty((N, 2, T, G), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        nbytes = lib().dflash_conv_prepare_workspace_size(N, H, group_size, T, _dtype_code(x))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().dflash_conv_prepare(_p(x), _p(proj_weight), _p(base2), _p(out), _p(coeff_out), N, H, group_size, T,
+                                     block_size, _dtype_code(x), _p(workspace), workspace.numel(), _stream(stream)))
+    return out, coeff_out
 
 
 def dflash_topk(logits: torch.Tensor, *, top_k: int, valid_vocab: Optional[int] = None,

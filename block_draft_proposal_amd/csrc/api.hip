@@ -265,6 +265,47 @@ int dflash_conv(const void* x, const void* base, const void* delta, int64_t delt
   return st == DFLASH_OK ? ok() : st;
 }
 
+size_t dflash_conv_prepare_workspace_size(int64_t n_tokens, int32_t hidden, int32_t group_size, int32_t taps,
+                                          int32_t dtype) {
+  if (n_tokens <= 0 || hidden <= 0 || group_size <= 0 || taps <= 0 || hidden % group_size) return 0;
+  const int64_t outputs = 2LL * taps * (hidden / group_size);
+  if (outputs > INT32_MAX) return 0;
+  return dflash::plan_conv_prepare(n_tokens, hidden, (int32_t)outputs, dtype).bytes;
+}
+
+int dflash_conv_prepare(const void* x, const void* proj_weight, const void* base2, void* out, void* coeff_out,
+                        int64_t n_tokens, int32_t hidden, int32_t group_size, int32_t taps, int32_t block_size,
+                        int32_t dtype, void* workspace, size_t workspace_bytes, dflash_stream_t stream) {
+  if (hidden > 0 && group_size > 0 && taps > 0 && hidden % group_size == 0 &&
+      2LL * taps * (hidden / group_size) > INT32_MAX)
+    return fail(DFLASH_ERR_UNSUPPORTED, "dflash_conv_prepare: 2*taps*groups too large");
+  const int64_t P = (hidden > 0 && group_size > 0) ? 2LL * (taps > 0 ? taps : 1) * (hidden / group_size) : 1;
+  int st = check_conv(x, base2, coeff_out, P, out, n_tokens, hidden, group_size, taps, block_size, dtype);
+  if (st != DFLASH_OK) return st;
+  if (n_tokens == 0) return ok();
+  if (!proj_weight) return fail(DFLASH_ERR_INVALID_ARG, "dflash_conv_prepare: null proj_weight");
+  if (!aligned16(proj_weight) || !aligned16(coeff_out))
+    return fail(DFLASH_ERR_INVALID_ARG, "dflash_conv_prepare: proj_weight and coeff_out must be 16-byte aligned");
+  const size_t e = elem_bytes(dtype);
+  const size_t xb = (size_t)n_tokens * hidden * e, cb = (size_t)n_tokens * P * e;
+  if (overlaps(coeff_out, cb, x, xb) || overlaps(coeff_out, cb, out, xb) ||
+      overlaps(coeff_out, cb, proj_weight, (size_t)P * hidden * e) ||
+      overlaps(coeff_out, cb, base2, 2 * (size_t)taps * hidden * e) ||
+      overlaps(out, xb, proj_weight, (size_t)P * hidden * e) || overlaps(out, xb, base2, 2 * (size_t)taps * hidden * e))
+    return fail(DFLASH_ERR_INVALID_ARG, "dflash_conv_prepare: an output overlaps another buffer");
+  const dflash::ConvPrepPlan plan = dflash::plan_conv_prepare(n_tokens, hidden, (int32_t)P, dtype);
+  if (plan.bytes > 0) {
+    if (!workspace || workspace_bytes < plan.bytes)
+      return fail(DFLASH_ERR_WORKSPACE, "dflash_conv_prepare: workspace needs %zu bytes", plan.bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+      return fail(DFLASH_ERR_INVALID_ARG, "dflash_conv_prepare: workspace must be 256-byte aligned");
+  }
+  dflash::ConvPrepArgs a{x, proj_weight, base2, out, coeff_out, n_tokens, hidden, group_size, taps, block_size,
+                         dtype, workspace};
+  st = launch_status(dflash::launch_conv_prepare(a, plan, as_hip(stream)), "dflash_conv_prepare");
+  return st == DFLASH_OK ? ok() : st;
+}
+
 size_t dflash_topk_workspace_size(int64_t n_rows, int64_t valid_vocab, int32_t top_k) {
   if (n_rows <= 0 || valid_vocab <= 0 || top_k <= 0) return 0;
   return dflash::plan_topk(n_rows, valid_vocab, top_k).bytes;

@@ -119,6 +119,28 @@ hipError_t launch_lm_head_topk(const LmHeadArgs& a, const LmTopkPlan& p, int64_t
                                float mult, float cap, int64_t* ids_out, float* unary_out, void* workspace,
                                hipStream_t stream);
 
+// The conv module's prepare side: kernel projection of x (all 2 * T * G
+// coefficients of each token, in the storage dtype), then the conv of x with
+// side 0.
+struct ConvPrepArgs {
+  const void* x;            // [n_tokens, hidden]
+  const void* proj_weight;  // [2 * taps * G, hidden]
+  const void* base2;        // [2, taps, hidden]; side 0 is used
+  void* out;                // [n_tokens, hidden]
+  void* coeff_out;          // [n_tokens, 2, taps, G]
+  int64_t n_tokens;
+  int32_t hidden, group_size, taps, block_size;
+  int32_t dtype;
+  void* workspace;          // fp32 partial sums when the contraction is split
+};
+struct ConvPrepPlan {
+  int32_t n_mb, n_nb;       // 128 x 128 tiles over (tokens, coefficients)
+  int32_t slices, kb_per_slice;   // split of the contraction (bf16); slices == 1: none
+  size_t bytes;             // workspace bytes (0 without a split)
+};
+ConvPrepPlan plan_conv_prepare(int64_t n_tokens, int32_t hidden, int32_t outputs, int32_t dtype);
+hipError_t launch_conv_prepare(const ConvPrepArgs& a, const ConvPrepPlan& p, hipStream_t stream);
+
 // Lattice and walk in one kernel (one workgroup per request) when the
 // request's lattice and its staging fit in LDS; bit-identical to
 // launch_lattice followed by launch_walk.  scores_out may be null.

@@ -113,6 +113,32 @@ int dflash_conv(const void* x, const void* base, const void* delta, int64_t delt
                 int32_t block_size, int32_t dtype, dflash_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * dflash_conv_prepare -- the prepare side of the grouped conv module ("[Spec]
+ * DFlash2", code excerpt of the conv module: one bias-free projection of the
+ * input gives both sides' coefficients, read as [2, taps, G]; prepare
+ * convolves the input with side 0 and returns side 1's coefficients):
+ *   coeff[n, p] = round( sum_k x[n, k] * proj_weight[p, k] ),  p < 2*taps*G,
+ *                 p = side*taps*G + tap*G + group
+ *   out         = dflash_conv(x, base2[0], delta = coeff (row stride 2*taps*G))
+ *   x           [n_tokens, hidden]            dtype; 16-byte aligned
+ *   proj_weight [2*taps*G, hidden]            dtype; 16-byte aligned (the
+ *                                             linear map's [out, in] layout)
+ *   base2       [2, taps, hidden]             dtype; 16-byte aligned
+ *   out         [n_tokens, hidden]            dtype; 16-byte aligned
+ *   coeff_out   [n_tokens, 2, taps, G]        dtype; 16-byte aligned; both
+ *                                             sides, rounded once (bf16: to
+ *                                             nearest even; fp32 sums in fp32)
+ * finish is dflash_conv(y, base2 + taps*hidden, coeff_out + taps*G,
+ * 2*taps*G, ...).  Conv requirements as for dflash_conv.  bf16 needs
+ * dflash_conv_prepare_workspace_size() bytes of scratch (256-byte aligned;
+ * may be 0), fp32 none.  n_tokens == 0 is a no-op. */
+size_t dflash_conv_prepare_workspace_size(int64_t n_tokens, int32_t hidden, int32_t group_size, int32_t taps,
+                                          int32_t dtype);
+int dflash_conv_prepare(const void* x, const void* proj_weight, const void* base2, void* out, void* coeff_out,
+                        int64_t n_tokens, int32_t hidden, int32_t group_size, int32_t taps, int32_t block_size,
+                        int32_t dtype, void* workspace, size_t workspace_bytes, dflash_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * dflash_topk -- per-row top-K over transformed unary logits.
  * For each row n: the K ids v < valid_vocab with the largest transformed
  * value y = T(z[n,v]), ordered by (y descending, id ascending).  T(z) = m*z,

@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_entry_point():
     names = _declared_functions()
-    assert "dflash_propose_block" in names and len(names) == 14
+    assert "dflash_propose_block" in names and len(names) == 16
     lib = D.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -212,6 +212,31 @@ def test_lm_head_topk_validation():
     assert call(cap=-1.0) == Bd.DFLASH_ERR_INVALID_ARG
     assert call(wsb=ws_need - 1) == Bd.DFLASH_ERR_WORKSPACE
     assert call(ws=ctypes.c_void_p(128)) == Bd.DFLASH_ERR_INVALID_ARG   # not 256-byte aligned
+    assert call(n=0) == Bd.DFLASH_OK
+
+
+def test_conv_prepare_validation():
+    L = Bd.lib()
+    A = ctypes.c_void_p
+    N, H, gs, T, B = 32, 64, 8, 3, 4
+    ws_need = L.dflash_conv_prepare_workspace_size(N, H, gs, T, 1)
+    assert L.dflash_conv_prepare_workspace_size(N, H, gs, T, 0) == 0          # fp32 needs none
+    assert L.dflash_conv_prepare_workspace_size(0, H, gs, T, 1) == 0
+    # disjoint fake device addresses: x, weight, base2, out, coeff, workspace
+    x, w, b2, o, c, ws = A(1 << 20), A(2 << 20), A(3 << 20), A(4 << 20), A(5 << 20), A(6 << 20)
+    call = lambda **kw: L.dflash_conv_prepare(*[kw.get(k, d) for k, d in (
+        ("x", x), ("w", w), ("b2", b2), ("o", o), ("c", c), ("n", N), ("H", H), ("gs", gs), ("T", T), ("B", B),
+        ("dt", 1), ("ws", ws), ("wsb", ws_need), ("st", None))])
+    assert call(dt=7) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(gs=12) == Bd.DFLASH_ERR_INVALID_ARG              # does not divide hidden
+    assert call(n=30) == Bd.DFLASH_ERR_INVALID_ARG               # not whole blocks
+    assert call(H=60, gs=4) == Bd.DFLASH_ERR_UNSUPPORTED         # bf16 hidden not a multiple of 8
+    assert call(w=None) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(w=A((2 << 20) + 8)) == Bd.DFLASH_ERR_INVALID_ARG  # misaligned weight
+    assert call(c=A((1 << 20) + 64)) == Bd.DFLASH_ERR_INVALID_ARG   # coefficients overlap x
+    if ws_need:
+        assert call(wsb=ws_need - 1) == Bd.DFLASH_ERR_WORKSPACE
+        assert call(ws=A((6 << 20) + 128)) == Bd.DFLASH_ERR_INVALID_ARG   # not 256-byte aligned
     assert call(n=0) == Bd.DFLASH_OK
 
 

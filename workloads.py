@@ -250,3 +250,22 @@ def make_head_inputs(w: Workload, device="cpu", seed: Optional[int] = None, n_ro
     rows = w.n_slot_rows if n_rows is None else int(n_rows)
     return {"hidden": normal((rows, w.hidden), 1.0, w.dtype, m, "head_hidden", dev),
             "weight": normal((w.vocab, w.hidden), w.logit_sigma / math.sqrt(w.hidden), w.dtype, m, "head_weight", dev)}
+
+
+def make_conv_module_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
+                            n_tokens: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Inputs of the conv module's prepare / finish for workload ``w``:
+      x           [N, H]          module input, N(0, 1), storage dtype
+      y           [N, H]          a sublayer output for finish, N(0, 1)
+      proj_weight [2*T*G, H]      kernel projection, N(0, (delta_sigma / sqrt(H))^2),
+                                  so the coefficients spread like the workload's delta
+      base2       [2, T, H]       base kernel, both sides, N(0, base_sigma^2)
+    N defaults to the workload's token count (whole blocks)."""
+    m = master_seed(w) if seed is None else int(seed)
+    dev = torch.device(device)
+    N = w.n_tokens if n_tokens is None else int(n_tokens)
+    H, T, G = w.hidden, w.taps, w.hidden // w.group_size
+    return {"x": normal((N, H), 1.0, w.dtype, m, "module_x", dev),
+            "y": normal((N, H), 1.0, w.dtype, m, "module_y", dev),
+            "proj_weight": normal((2 * T * G, H), w.delta_sigma / math.sqrt(H), w.dtype, m, "module_proj", dev),
+            "base2": normal((2, T, H), w.base_sigma, w.dtype, m, "module_base", dev)}
