@@ -162,8 +162,10 @@ def call_bytes(w):
     lattice = proj + gathers + 12 * Ns * K + 8 * R + 4 * Ns * K * K
     walk = 4 * Ns * K * K + 8 * Ns * K + 4 * Ns + 5 * R + 8 * Ns + 4 * Ns * K
     propose = conv + topk + proj + gathers + 8 * R + 4 * Ns + 5 * R + 8 * Ns + 4 * Ns * K
-    return {"dflash_conv": conv, "dflash_topk": topk, "dflash_lattice": lattice, "dflash_walk": walk,
-            "dflash_propose_block": propose}
+    # x and the projection weight in, side-0 base in, out and both sides' coefficients written
+    prepare = 2 * N * H * e + 2 * T * G * H * e + T * H * e + 2 * N * T * G * e
+    return {"dflash_conv": conv, "dflash_conv_prepare": prepare, "dflash_topk": topk, "dflash_lattice": lattice,
+            "dflash_walk": walk, "dflash_propose_block": propose}
 
 
 def sweep(iters: int = 50, warm: int = 5, only=None):
@@ -227,9 +229,16 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
                               logits=inp["logits"], anchor=inp["anchor"], sel_a=inp["sel_a"], sel_b=inp["sel_b"],
                               proj=inp["proj"], uniforms=inp["uniforms"], temperatures=inp["temperatures"],
                               greedy_mask=inp["greedy_mask"], valid_vocab=w.valid_vocab)
+        mod = W.make_conv_module_inputs(w, device=dev)
+        coeff = torch.empty((w.n_tokens, 2, w.taps, w.groups), dtype=inp["x"].dtype, device=dev)
+        prep_ws = torch.empty(max(1, D.lib().dflash_conv_prepare_workspace_size(
+            w.n_tokens, H, w.group_size, w.taps, 1 if w.dtype == "bf16" else 0)), dtype=torch.uint8, device=dev)
         fns = {
             "dflash_conv": lambda: D.dflash_conv(inp["x"], inp["base"][0], inp["delta"][:, 0], block_size=B,
                                                  group_size=w.group_size, out=conv_out),
+            "dflash_conv_prepare": lambda: D.dflash_conv_prepare(mod["x"], mod["proj_weight"], mod["base2"],
+                                                                 block_size=B, group_size=w.group_size,
+                                                                 out=conv_out, coeff_out=coeff, workspace=prep_ws),
             "dflash_topk": lambda: D.dflash_topk(inp["logits"], top_k=K, valid_vocab=w.valid_vocab,
                                                  multiplier=w.multiplier, softcap=w.softcap, ids_out=ids,
                                                  unary_out=unary, workspace=tk_ws),
@@ -245,7 +254,7 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
             gbs = nbytes[cname] / (med * 1e-6) / 1e9
             print(f"| {name} | {cname} | {med:.2f} | {p10:.2f} | {p90:.2f} | {nbytes[cname] / 1e6:.2f} | {gbs:.0f} | "
                   f"{100 * gbs / HBM_PEAK_GBS:.1f} | {100 * gbs / copy_gbs:.1f} |", flush=True)
-        del inp, call, fns
+        del inp, call, fns, mod, coeff, prep_ws
         torch.cuda.empty_cache()
 
     # the dense head in front of the top-K (bf16 workloads): plain, and fused with the top-K

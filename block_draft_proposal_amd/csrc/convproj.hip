@@ -11,7 +11,8 @@
 // rounded once to the storage dtype (the linear map's output dtype).
 //
 // Design (bf16): the tile product of gemm_tile.h with 128 x 128 tiles over 4
-// waves and two 64-deep stages (64 KB of LDS, two workgroups per CU).  The
+// waves and two 64-deep stages (64 KB of LDS, two workgroups per CU), or
+// 64 x 64 tiles when there are too few of those to fill the chip.  The
 // projection is skinny (a few hundred to a few thousand outputs), so when the
 // tiles alone would leave the chip idle the contraction is split into slices
 // of k blocks, one workgroup per (tile, slice), each writing fp32 partial
@@ -28,34 +29,39 @@
 namespace dflash {
 namespace {
 
+// Large problems: 128 x 128 tiles over 4 waves of 64 x 64; small ones (too
+// few 128 x 128 tiles to fill the chip): 64 x 64 tiles over 4 waves of
+// 32 x 32, so fewer slices (less partial traffic) fill it.  Two 64-deep
+// stages either way, three for the small tile (48 KB).
 using ProjCfg = TileCfg<4, 4, 2, 2, 64, 2>;
+using ProjCfgSmall = TileCfg<2, 2, 2, 2, 64, 3>;
 constexpr int kProjTargetGroups = 256;   // workgroups the split aims for (one per CU at least)
-constexpr int kProjMinBlocks = 4;        // k blocks per slice at least (the ring's pipeline depth)
+constexpr int kProjMinBlocks = 8;        // k blocks per slice at least
 
 // One (tile, slice) of the projection.  SPLIT: fp32 partial sums of slice
 // blockIdx.y into parts[slice][n][p]; otherwise the whole contraction,
 // rounded to bf16 into coeff[n][p].
-template <bool SPLIT>
-__global__ __launch_bounds__(ProjCfg::kThreads) void conv_proj_kernel(
+template <class Cfg, bool SPLIT>
+__global__ __launch_bounds__(Cfg::kThreads) void conv_proj_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int32_t N, int32_t H, int32_t P, int32_t n_mb,
     int32_t n_nb, int32_t kb_per_slice, float* __restrict__ parts, uint16_t* __restrict__ coeff) {
   extern __shared__ __align__(16) unsigned char cp_smem[];
   int mb, nb;
   tile_of(blockIdx.x, n_mb, mb, nb);
   if (nb >= n_nb) return;
-  const int m0 = mb * ProjCfg::kBM, n0 = nb * ProjCfg::kBN;
-  const int nk = (H + ProjCfg::kBK - 1) / ProjCfg::kBK;
+  const int m0 = mb * Cfg::kBM, n0 = nb * Cfg::kBN;
+  const int nk = (H + Cfg::kBK - 1) / Cfg::kBK;
   const int kb0 = (int)blockIdx.y * kb_per_slice;
   const int nkb = min(kb_per_slice, nk - kb0);
-  f32x4_t acc[ProjCfg::kFragM][ProjCfg::kFragN];
-  tile_product<ProjCfg>(x, H, w, H, N, P, H, m0, n0, kb0, nkb, cp_smem, acc);
+  f32x4_t acc[Cfg::kFragM][Cfg::kFragN];
+  tile_product<Cfg>(x, H, w, H, N, P, H, m0, n0, kb0, nkb, cp_smem, acc);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = (wave / ProjCfg::kWavesN) * ProjCfg::kWM, wn = (wave % ProjCfg::kWavesN) * ProjCfg::kWN;
+  const int wm = (wave / Cfg::kWavesN) * Cfg::kWM, wn = (wave % Cfg::kWavesN) * Cfg::kWN;
   float* part = parts + (int64_t)blockIdx.y * N * P;
 #pragma unroll
-  for (int i = 0; i < ProjCfg::kFragM; ++i)
+  for (int i = 0; i < Cfg::kFragM; ++i)
 #pragma unroll
-    for (int j = 0; j < ProjCfg::kFragN; ++j) {
+    for (int j = 0; j < Cfg::kFragN; ++j) {
       const int col = n0 + wn + 16 * j + (lane & 15);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -96,8 +102,12 @@ __global__ void conv_proj_f32_kernel(const float* __restrict__ x, const float* _
 ConvPrepPlan plan_conv_prepare(int64_t n_tokens, int32_t hidden, int32_t outputs, int32_t dtype) {
   ConvPrepPlan p{};
   if (dtype != DFLASH_BF16 || n_tokens <= 0 || outputs <= 0) return p;
-  p.n_mb = (int32_t)((n_tokens + ProjCfg::kBM - 1) / ProjCfg::kBM);
-  p.n_nb = (outputs + ProjCfg::kBN - 1) / ProjCfg::kBN;
+  const int64_t big_tiles = ((n_tokens + ProjCfg::kBM - 1) / ProjCfg::kBM) *
+                            ((outputs + ProjCfg::kBN - 1) / ProjCfg::kBN);
+  p.small = big_tiles < kProjTargetGroups / 2;
+  const int bm = p.small ? ProjCfgSmall::kBM : ProjCfg::kBM, bn = p.small ? ProjCfgSmall::kBN : ProjCfg::kBN;
+  p.n_mb = (int32_t)((n_tokens + bm - 1) / bm);
+  p.n_nb = (outputs + bn - 1) / bn;
   const int nk = (hidden + ProjCfg::kBK - 1) / ProjCfg::kBK;
   const int64_t tiles = (int64_t)p.n_mb * p.n_nb;
   int slices = (int)((kProjTargetGroups + tiles - 1) / tiles);
@@ -121,17 +131,24 @@ hipError_t launch_conv_prepare(const ConvPrepArgs& a, const ConvPrepPlan& p, hip
     const uint16_t* w = static_cast<const uint16_t*>(a.proj_weight);
     uint16_t* coeff = static_cast<uint16_t*>(a.coeff_out);
     float* parts = static_cast<float*>(a.workspace);
-    if (p.slices > 1) {
-      hipLaunchKernelGGL((conv_proj_kernel<true>), grid, dim3(ProjCfg::kThreads), ProjCfg::kSmemBytes, stream, x, w,
-                         (int32_t)a.n_tokens, a.hidden, P, p.n_mb, p.n_nb, p.kb_per_slice, parts, coeff);
+    const bool split = p.slices > 1;
+#define DFLASH_PROJ_TILE(CFG, SPLIT)                                                                        \
+  hipLaunchKernelGGL((conv_proj_kernel<CFG, SPLIT>), grid, dim3(CFG::kThreads), CFG::kSmemBytes, stream, x, w, \
+                     (int32_t)a.n_tokens, a.hidden, P, p.n_mb, p.n_nb, p.kb_per_slice, parts, coeff)
+    if (p.small) {
+      if (split) DFLASH_PROJ_TILE(ProjCfgSmall, true);
+      else DFLASH_PROJ_TILE(ProjCfgSmall, false);
+    } else {
+      if (split) DFLASH_PROJ_TILE(ProjCfg, true);
+      else DFLASH_PROJ_TILE(ProjCfg, false);
+    }
+#undef DFLASH_PROJ_TILE
+    if (split) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       const int64_t count = a.n_tokens * P;
       hipLaunchKernelGGL(conv_proj_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream,
                          parts, p.slices, count, coeff);
-    } else {
-      hipLaunchKernelGGL((conv_proj_kernel<false>), grid, dim3(ProjCfg::kThreads), ProjCfg::kSmemBytes, stream, x,
-                         w, (int32_t)a.n_tokens, a.hidden, P, p.n_mb, p.n_nb, p.kb_per_slice, parts, coeff);
     }
   } else {
     const int64_t count = a.n_tokens * P;

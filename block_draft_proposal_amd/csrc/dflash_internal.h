@@ -134,7 +134,8 @@ struct ConvPrepArgs {
   void* workspace;          // fp32 partial sums when the contraction is split
 };
 struct ConvPrepPlan {
-  int32_t n_mb, n_nb;       // 128 x 128 tiles over (tokens, coefficients)
+  bool small;               // 64 x 64 tiles instead of 128 x 128
+  int32_t n_mb, n_nb;       // tiles over (tokens, coefficients)
   int32_t slices, kb_per_slice;   // split of the contraction (bf16); slices == 1: none
   size_t bytes;             // workspace bytes (0 without a split)
 };

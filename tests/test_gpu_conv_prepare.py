@@ -78,12 +78,13 @@ def test_prepare_full_size_sampled_blocks(name):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("R,B,T,gs,H", [(3, 10, 3, 8, 200), (13, 10, 5, 16, 64), (1, 4, 2, 4, 40),
-                                        (40, 4, 4, 8, 512), (2, 16, 1, 64, 64), (9, 7, 9, 4, 96)])
+                                        (40, 4, 4, 8, 1024), (2, 16, 1, 64, 64), (9, 7, 9, 4, 96)])
 def test_prepare_edge_shapes(dtype, R, B, T, gs, H):
     # token counts that end inside a 128-row tile, coefficient counts that end
-    # inside a 128-column tile (2 T G = 150, 40, 20, 2, 432), hidden sizes
+    # inside a tile (2 T G = 150, 40, 20, 1024, 2, 432), hidden sizes
     # that are not a multiple of the 64-deep stage (200, 40, 96), T = 1,
-    # T = 9 (the generic conv), a split contraction (H = 512 with 160 tokens)
+    # T = 9 (the generic conv), a split contraction (H = 1024 with 160 tokens)
+    # and the 64 x 64 tile
     require_gpu()
     if H % (8 if dtype == "bf16" else 4):
         pytest.skip("hidden not a whole number of 16-byte vectors")
