@@ -415,3 +415,79 @@ def propose_block(inp: Dict[str, np.ndarray], *, block_size: int, group_size: in
                                    inp["greedy_mask"], return_margins=True)
     return dict(conv_out=out, conv_out_q=out_q, h=h, ids=ids, unary=unary, u=u, scores=scores,
                 tokens=tokens, q=q, idx=idx, margins=margins)
+
+
+# ---------------------------------------------------------------------------
+# Verify and commit  [DF2] executive summary and walk-kernel excerpt: verify
+# is lossless because the proposal distribution it checks against is the one
+# the walk actually drew from (a point mass on greedy rows, the softmax the
+# token was sampled from otherwise); the worker then commits the accepted
+# block with the bonus token placed after it.  The pages do not print the
+# verify itself; this is the standard rejection rule of speculative sampling
+# (accept a drafted token x with probability min(1, p(x) / q(x)); on the
+# first rejection draw from max(0, p - q) renormalised; after S acceptances
+# draw a bonus token from the next position's p).
+# ---------------------------------------------------------------------------
+
+def target_distribution(z: np.ndarray, valid_vocab: int, temperature: float, greedy: bool) -> np.ndarray:
+    """z [V] target logits -> p [V] (float64): the point mass at the lowest-id
+    maximum for a greedy request, softmax(z / T) with T clamped to >= 1e-5
+    otherwise; ids at or past valid_vocab (and -inf logits) get 0."""
+    z = np.asarray(z, np.float64)[:valid_vocab]
+    p = np.zeros(valid_vocab)
+    if greedy:
+        p[int(np.argmax(z))] = 1.0                   # argmax returns the first (lowest) id of the max
+        return p
+    y = z / max(float(temperature), 1e-5)
+    e = np.exp(y - np.max(y))
+    return e / np.sum(e)
+
+
+def inverse_cdf(weights: np.ndarray, u: float) -> int:
+    """The first index whose running sum (in index order) exceeds u times the
+    total: #{v : C_v <= u * C_last}, capped at the last positive entry."""
+    c = np.cumsum(np.asarray(weights, np.float64))
+    v = int(np.sum(c <= u * c[-1]))
+    last = int(np.flatnonzero(np.asarray(weights) > 0)[-1])
+    return min(v, last)
+
+
+def verify(target_logits: np.ndarray, valid_vocab: int, cand_ids: np.ndarray, q: np.ndarray,
+           tokens: np.ndarray, u_accept: np.ndarray, u_residual: np.ndarray, temperatures: np.ndarray,
+           greedy_mask: np.ndarray):
+    """target_logits [R, S+1, V] (row s: the target's logits for the token at
+    slot s given the block before it; row S: after the whole block);
+    cand_ids [R, S, K], q [R, S, K] (the walk's candidates and the
+    distribution each token was drawn from), tokens [R, S];
+    u_accept [R, S], u_residual [R] uniforms in [0, 1).
+    Returns (accepted [R]: drafted tokens kept, committed [R, S+1]: those
+    tokens then the correction or bonus token, -1 after)."""
+    R, S = np.asarray(tokens).shape
+    accepted = np.zeros(R, np.int64)
+    committed = np.full((R, S + 1), -1, np.int64)
+    for r in range(R):
+        greedy = bool(greedy_mask[r])
+        n = 0
+        while n < S:
+            x = int(tokens[r, n])
+            p = target_distribution(target_logits[r, n], valid_vocab, temperatures[r], greedy)
+            j = int(np.flatnonzero(np.asarray(cand_ids[r, n]) == x)[0])
+            qx = float(q[r, n, j])
+            px = float(p[x]) if x < valid_vocab else 0.0
+            if not (float(u_accept[r, n]) * qx < px):         # rejected: draw from max(0, p - q)
+                residual = p.copy()
+                for jj, v in enumerate(np.asarray(cand_ids[r, n])):
+                    if v < valid_vocab:
+                        residual[v] = max(0.0, residual[v] - float(q[r, n, jj]))
+                if not np.any(residual > 0):
+                    residual = p
+                committed[r, :n] = tokens[r, :n]
+                committed[r, n] = inverse_cdf(residual, float(u_residual[r]))
+                break
+            n += 1
+        if n == S:                                            # every drafted token kept: bonus token
+            p = target_distribution(target_logits[r, S], valid_vocab, temperatures[r], greedy)
+            committed[r, :S] = tokens[r]
+            committed[r, S] = inverse_cdf(p, float(u_residual[r]))
+        accepted[r] = n
+    return accepted, committed
