@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     dflash_topk,
     dflash_lattice,
     dflash_walk,
+    dflash_verify,
     dflash_lm_head,
     dflash_lm_head_topk,
     dflash_propose_block,

@@ -66,6 +66,9 @@ _SIGNATURES = {
     "dflash_conv_prepare_workspace_size": (_c_size, [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32]),
     "dflash_conv_prepare": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_vp, _c_size, _c_vp]),
+    "dflash_verify_workspace_size": (_c_size, [_c_i32, _c_i32]),
+    "dflash_verify": (_c_i32, [_c_vp, _c_i64, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp,
+                               _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "dflash_topk_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i32]),
     "dflash_topk": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_f32, _c_f32, _c_i32, _c_vp, _c_vp,
                              _c_vp, _c_size, _c_vp]),
@@ -183,6 +186,36 @@ def dflash_conv_prepare(x: torch.Tensor, proj_weight: torch.Tensor, base2: torch
     _check(lib().dflash_conv_prepare(_p(x), _p(proj_weight), _p(base2), _p(out), _p(coeff_out), N, H, group_size, T,
                                      block_size, _dtype_code(x), _p(workspace), workspace.numel(), _stream(stream)))
     return out, coeff_out
+
+
+def dflash_verify(target_logits: torch.Tensor, cand_ids: torch.Tensor, q: torch.Tensor, tokens: torch.Tensor,
+                  u_accept: torch.Tensor, u_residual: torch.Tensor, temperatures: torch.Tensor,
+                  greedy_mask: torch.Tensor, *, valid_vocab: Optional[int] = None, accepted_out=None,
+                  committed_out=None, workspace=None, stream=None):
+    """target_logits [R, S+1, V] (rows contiguous); cand_ids / q [R, S, K];
+    tokens / u_accept [R, S]; u_residual, temperatures, greedy_mask [R].
+    Returns (accepted int32 [R], committed int64 [R, S+1])."""
+    R, S1, V = target_logits.shape
+    S = S1 - 1
+    K = cand_ids.shape[-1] if cand_ids.numel() else 1
+    if target_logits.dim() != 3 or target_logits.stride(2) != 1 or \
+            (R and S1 > 1 and target_logits.stride(0) != S1 * target_logits.stride(1)):
+        raise ValueError("target_logits must be [R, S+1, V] rows of one row stride")
+    valid_vocab = V if valid_vocab is None else valid_vocab
+    dev = target_logits.device
+    accepted_out = torch.empty(R, dtype=torch.int32, device=dev) if accepted_out is None else accepted_out
+    committed_out = torch.empty((R, S1), dtype=torch.int64, device=dev) if committed_out is None else committed_out
+    if workspace is None:
+        workspace = torch.empty(max(1, lib().dflash_verify_workspace_size(R, S)), dtype=torch.uint8, device=dev)
+    for t, name in ((cand_ids, "cand_ids"), (q, "q"), (tokens, "tokens"), (u_accept, "u_accept"),
+                    (u_residual, "u_residual"), (temperatures, "temperatures"), (greedy_mask, "greedy_mask")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _check(lib().dflash_verify(_p(target_logits), target_logits.stride(1) if R else V, R, S, V, valid_vocab, K,
+                               _p(cand_ids), _p(q), _p(tokens), _p(u_accept), _p(u_residual), _p(temperatures),
+                               _p(greedy_mask), _dtype_code(target_logits), _p(accepted_out), _p(committed_out),
+                               _p(workspace), workspace.numel(), _stream(stream)))
+    return accepted_out, committed_out
 
 
 def dflash_topk(logits: torch.Tensor, *, top_k: int, valid_vocab: Optional[int] = None,

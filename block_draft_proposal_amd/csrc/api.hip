@@ -306,6 +306,40 @@ int dflash_conv_prepare(const void* x, const void* proj_weight, const void* base
   return st == DFLASH_OK ? ok() : st;
 }
 
+size_t dflash_verify_workspace_size(int32_t n_req, int32_t slots) {
+  if (n_req <= 0 || slots < 0) return 0;
+  return (size_t)n_req * (slots + 1) * sizeof(dflash::VerifyRowStats);
+}
+
+int dflash_verify(const void* target_logits, int64_t row_stride, int32_t n_req, int32_t slots, int64_t vocab,
+                  int64_t valid_vocab, int32_t top_k, const int64_t* cand_ids, const float* q, const int64_t* tokens,
+                  const float* u_accept, const float* u_residual, const float* temperatures,
+                  const uint8_t* greedy_mask, int32_t dtype, int32_t* accepted_out, int64_t* committed_out,
+                  void* workspace, size_t workspace_bytes, dflash_stream_t stream) {
+  const char* who = "dflash_verify";
+  if (!dtype_ok(dtype)) return fail(DFLASH_ERR_INVALID_ARG, "%s: unknown dtype %d", who, dtype);
+  if (n_req < 0 || slots < 0) return fail(DFLASH_ERR_INVALID_ARG, "%s: n_req and slots must be >= 0", who);
+  if (top_k < 1) return fail(DFLASH_ERR_INVALID_ARG, "%s: top_k must be >= 1", who);
+  if (top_k > DFLASH_MAX_TOP_K) return fail(DFLASH_ERR_UNSUPPORTED, "%s: top_k > %d", who, DFLASH_MAX_TOP_K);
+  if (!(valid_vocab >= 1 && valid_vocab <= vocab && vocab <= row_stride))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: need 1 <= valid_vocab <= vocab <= row_stride", who);
+  if (n_req == 0) return ok();
+  if (!target_logits || !u_residual || !temperatures || !greedy_mask || !accepted_out || !committed_out ||
+      (slots > 0 && (!cand_ids || !q || !tokens || !u_accept)))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (reinterpret_cast<uintptr_t>(target_logits) % elem_bytes(dtype))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: target_logits misaligned", who);
+  const size_t need = dflash_verify_workspace_size(n_req, slots);
+  if (!workspace || workspace_bytes < need)
+    return fail(DFLASH_ERR_WORKSPACE, "%s: workspace needs %zu bytes", who, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 8)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: workspace must be 8-byte aligned", who);
+  dflash::VerifyArgs a{target_logits, row_stride, vocab, valid_vocab, n_req, slots, top_k, cand_ids, q, tokens,
+                       u_accept, u_residual, temperatures, greedy_mask, dtype, accepted_out, committed_out, workspace};
+  const int st = launch_status(dflash::launch_verify(a, as_hip(stream)), who);
+  return st == DFLASH_OK ? ok() : st;
+}
+
 size_t dflash_topk_workspace_size(int64_t n_rows, int64_t valid_vocab, int32_t top_k) {
   if (n_rows <= 0 || valid_vocab <= 0 || top_k <= 0) return 0;
   return dflash::plan_topk(n_rows, valid_vocab, top_k).bytes;

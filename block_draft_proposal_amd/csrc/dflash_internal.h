@@ -142,6 +142,30 @@ struct ConvPrepPlan {
 ConvPrepPlan plan_conv_prepare(int64_t n_tokens, int32_t hidden, int32_t outputs, int32_t dtype);
 hipError_t launch_conv_prepare(const ConvPrepArgs& a, const ConvPrepPlan& p, hipStream_t stream);
 
+// Verify and commit of a drafted block.
+struct VerifyRowStats {
+  double m;                 // maximum logit of the row (valid ids), -inf if none is finite
+  double s;                 // sum_v exp((z_v - m) / T) (sampled requests)
+  int64_t arg;              // lowest id of the maximum
+};
+struct VerifyArgs {
+  const void* logits;       // [n_req * (slots + 1)] rows of row_stride elements
+  int64_t row_stride, vocab, valid_vocab;
+  int32_t n_req, slots, top_k;
+  const int64_t* cand_ids;  // [n_req, slots, top_k]
+  const float* q;           // [n_req, slots, top_k]
+  const int64_t* tokens;    // [n_req, slots]
+  const float* u_accept;    // [n_req, slots]
+  const float* u_residual;  // [n_req]
+  const float* temperatures;
+  const uint8_t* greedy_mask;
+  int32_t dtype;
+  int32_t* accepted_out;    // [n_req]
+  int64_t* committed_out;   // [n_req, slots + 1]
+  void* workspace;          // VerifyRowStats [n_req * (slots + 1)]
+};
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+
 // Lattice and walk in one kernel (one workgroup per request) when the
 // request's lattice and its staging fit in LDS; bit-identical to
 // launch_lattice followed by launch_walk.  scores_out may be null.

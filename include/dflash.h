@@ -239,6 +239,39 @@ int dflash_lm_head_topk(const void* hidden, int64_t hidden_row_stride, const voi
                         dflash_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * dflash_verify -- verify and commit of a drafted block ("[Spec] DFlash2",
+ * executive summary and walk-kernel excerpt: verify checks the drafted tokens
+ * against the distribution the walk drew them from -- a point mass on greedy
+ * rows -- which is what keeps the draft lossless; the worker then commits the
+ * kept tokens and places the bonus token after them).  Rule (the standard
+ * rejection rule of speculative sampling):
+ *   for s = 0 .. slots-1: keep tokens[r,s] = x while u_accept[r,s]*q(x) < p_s(x),
+ *     q(x) = q[r,s,j] for cand_ids[r,s,j] == x (0 if x is not a candidate);
+ *   at the first rejection commit a draw from max(0, p_s - q_s) renormalised,
+ *   after slots kept tokens commit a draw from p_slots.
+ * p_s = softmax(z_s / max(T, 1e-5)) over ids < valid_vocab, or the point mass
+ * on the lowest-id maximum for a greedy request; draws are inverse CDFs in id
+ * order with u_residual[r] (fp64 sums).
+ *   target_logits  rows r*(slots+1) + s, s = 0..slots, row_stride elements
+ *                  (row s: the target's logits for slot s given the block
+ *                  before it; row slots: after the whole block); dtype
+ *   cand_ids, q    [n_req, slots, top_k] int64 / fp32 (the walk's candidates
+ *                  and q); tokens [n_req, slots] int64
+ *   u_accept       [n_req, slots] fp32 in [0,1); u_residual [n_req] fp32
+ *   temperatures   [n_req] fp32; greedy_mask [n_req] u8
+ *   accepted_out   [n_req] int32: drafted tokens kept
+ *   committed_out  [n_req, slots+1] int64: the kept tokens, then the
+ *                  correction or bonus token, then -1
+ * Scratch: dflash_verify_workspace_size(n_req, slots) bytes, 8-byte aligned.
+ * n_req == 0 is a no-op. */
+size_t dflash_verify_workspace_size(int32_t n_req, int32_t slots);
+int dflash_verify(const void* target_logits, int64_t row_stride, int32_t n_req, int32_t slots, int64_t vocab,
+                  int64_t valid_vocab, int32_t top_k, const int64_t* cand_ids, const float* q, const int64_t* tokens,
+                  const float* u_accept, const float* u_residual, const float* temperatures,
+                  const uint8_t* greedy_mask, int32_t dtype, int32_t* accepted_out, int64_t* committed_out,
+                  void* workspace, size_t workspace_bytes, dflash_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * dflash_propose_block -- one whole draft block (draft-sampler excerpt):
  *   conv (side given by the caller's base/delta pointers) ->
  *   transform + top-K over the slot logits ->

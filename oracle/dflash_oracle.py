@@ -471,8 +471,8 @@ def verify(target_logits: np.ndarray, valid_vocab: int, cand_ids: np.ndarray, q:
         while n < S:
             x = int(tokens[r, n])
             p = target_distribution(target_logits[r, n], valid_vocab, temperatures[r], greedy)
-            j = int(np.flatnonzero(np.asarray(cand_ids[r, n]) == x)[0])
-            qx = float(q[r, n, j])
+            hits = np.flatnonzero(np.asarray(cand_ids[r, n]) == x)
+            qx = float(q[r, n, hits[0]]) if len(hits) else 0.0   # a token outside the candidates has q = 0
             px = float(p[x]) if x < valid_vocab else 0.0
             if not (float(u_accept[r, n]) * qx < px):         # rejected: draw from max(0, p - q)
                 residual = p.copy()

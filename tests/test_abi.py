@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_entry_point():
     names = _declared_functions()
-    assert "dflash_propose_block" in names and len(names) == 16
+    assert "dflash_propose_block" in names and len(names) == 18
     lib = D.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -238,6 +238,30 @@ def test_conv_prepare_validation():
         assert call(wsb=ws_need - 1) == Bd.DFLASH_ERR_WORKSPACE
         assert call(ws=A((6 << 20) + 128)) == Bd.DFLASH_ERR_INVALID_ARG   # not 256-byte aligned
     assert call(n=0) == Bd.DFLASH_OK
+
+
+def test_verify_validation():
+    L = Bd.lib()
+    A = ctypes.c_void_p
+    R, S, V, K = 4, 3, 100, 8
+    need = L.dflash_verify_workspace_size(R, S)
+    assert need == R * (S + 1) * 24 and L.dflash_verify_workspace_size(0, S) == 0
+    call = lambda **kw: L.dflash_verify(*[kw.get(k, d) for k, d in (
+        ("z", A(1 << 20)), ("rs", V), ("R", R), ("S", S), ("V", V), ("vv", V), ("K", K), ("ids", A(2 << 20)),
+        ("q", A(3 << 20)), ("tok", A(4 << 20)), ("ua", A(5 << 20)), ("ur", A(6 << 20)), ("t", A(7 << 20)),
+        ("g", A(8 << 20)), ("dt", 1), ("acc", A(9 << 20)), ("com", A(10 << 20)), ("ws", A(11 << 20)),
+        ("wsb", need), ("st", None))])
+    assert call(dt=5) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(K=0) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(K=33) == Bd.DFLASH_ERR_UNSUPPORTED
+    assert call(vv=101) == Bd.DFLASH_ERR_INVALID_ARG           # valid_vocab > vocab
+    assert call(rs=99) == Bd.DFLASH_ERR_INVALID_ARG            # row stride < vocab
+    assert call(S=-1) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(q=None) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(z=A((1 << 20) + 1)) == Bd.DFLASH_ERR_INVALID_ARG   # not element aligned
+    assert call(wsb=need - 1) == Bd.DFLASH_ERR_WORKSPACE
+    assert call(ws=A((11 << 20) + 4)) == Bd.DFLASH_ERR_INVALID_ARG   # not 8-byte aligned
+    assert call(R=0) == Bd.DFLASH_OK
 
 
 def test_error_message_is_per_call():

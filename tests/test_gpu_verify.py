@@ -1,0 +1,137 @@
+"""GPU parity of dflash_verify (verify and commit of a drafted block, "[Spec]
+DFlash2" executive summary and walk-kernel excerpt; the rule is the standard
+rejection rule of speculative sampling) against the oracle.
+
+Bar: accepted counts and committed tokens equal the oracle's exactly.  Both
+sides decide in fp64; a decision may differ only where the two fp64
+evaluations straddle it (|u q(x) - p(x)| or the inverse-CDF crossing within
+1e-9 relative), and such a case must show that margin when it occurs.
+Greedy requests are also checked structurally: the committed tokens are the
+target's own argmax decoding."""
+import numpy as np
+import pytest
+import torch
+
+import block_draft_proposal_amd as D
+from gpu_helpers import DEV, f64, require_gpu, say
+from oracle import dflash_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(R, S, V, K, seed, dtype=torch.bfloat16, valid=None, greedy_frac=0.5, match_frac=0.7):
+    """Target logits and a drafted block whose tokens often agree with the
+    target (so blocks run past the first slots): candidates are distinct ids
+    holding the target's argmax with probability match_frac, q a softmax over
+    them, tokens drawn from q."""
+    g = torch.Generator().manual_seed(seed)
+    valid = V if valid is None else valid
+    z = (torch.randn((R, S + 1, V), generator=g) * 3.0).to(dtype)
+    if valid < V:
+        z[:, :, valid:] = 60.0                      # padded ids: large but excluded
+    zf = z.float()
+    cand = torch.zeros((R, S, K), dtype=torch.int64)
+    q = torch.zeros((R, S, K), dtype=torch.float32)
+    tok = torch.zeros((R, S), dtype=torch.int64)
+    greedy = (torch.rand(R, generator=g) < greedy_frac).to(torch.uint8)
+    for r in range(R):
+        for s in range(S):
+            top = int(torch.argmax(zf[r, s, :valid]))
+            ids = torch.randperm(valid, generator=g)[:K]
+            if float(torch.rand(1, generator=g)) < match_frac and not bool((ids == top).any()):
+                ids[0] = top
+            cand[r, s] = ids
+            w = torch.softmax(zf[r, s, ids] + torch.randn(K, generator=g), dim=0)
+            if greedy[r]:
+                j = int(torch.argmax(w))
+                q[r, s] = 0.0
+                q[r, s, j] = 1.0
+            else:
+                q[r, s] = w
+                j = int(torch.multinomial(w, 1, generator=g))
+            tok[r, s] = ids[j]
+    ua = torch.rand((R, S), generator=g)
+    ur = torch.rand(R, generator=g)
+    temps = 0.5 + torch.rand(R, generator=g)
+    return dict(z=z, cand=cand, q=q, tok=tok, ua=ua, ur=ur, temps=temps, greedy=greedy, valid=valid)
+
+
+def _margins_ok(d, r, got_n):
+    """True when request r's differing outcome sits on an fp64 decision edge."""
+    z = f64(d["z"][r])
+    greedy = bool(d["greedy"][r])
+    T = float(d["temps"][r])
+    for s in range(z.shape[0]):
+        p = O.target_distribution(z[s], d["valid"], T, greedy)
+        if s < z.shape[0] - 1:
+            x = int(d["tok"][r, s])
+            hits = np.flatnonzero(d["cand"][r, s].numpy() == x)
+            qx = float(d["q"][r, s, hits[0]]) if len(hits) else 0.0
+            px = p[x] if x < d["valid"] else 0.0
+            if abs(float(d["ua"][r, s]) * qx - px) <= 1e-9 * max(px, 1e-300):
+                return True
+        c = np.cumsum(p)
+        if np.min(np.abs(c - float(d["ur"][r]) * c[-1])) <= 1e-9 * c[-1]:
+            return True
+    return False
+
+
+def _run(R, S, V, K, seed, **kw):
+    require_gpu()
+    d = _inputs(R, S, V, K, seed, **kw)
+    say(f"dflash_verify R={R} S={S} V={V} K={K} valid={d['valid']} seed={seed}")
+    acc, com = D.dflash_verify(d["z"].to(DEV), d["cand"].to(DEV), d["q"].to(DEV), d["tok"].to(DEV),
+                               d["ua"].to(DEV), d["ur"].to(DEV), d["temps"].to(DEV), d["greedy"].to(DEV),
+                               valid_vocab=d["valid"])
+    torch.cuda.synchronize()
+    acc, com = acc.cpu().numpy(), com.cpu().numpy()
+    ra, rc = O.verify(f64(d["z"]), d["valid"], d["cand"].numpy(), d["q"].double().numpy(), d["tok"].numpy(),
+                      d["ua"].double().numpy(), d["ur"].double().numpy(), d["temps"].double().numpy(),
+                      d["greedy"].numpy())
+    edge = 0
+    for r in range(R):
+        if acc[r] != ra[r] or not np.array_equal(com[r], rc[r]):
+            assert _margins_ok(d, r, acc[r]), (r, acc[r], ra[r], com[r], rc[r])
+            edge += 1
+    # greedy requests: the committed tokens are the target's argmax decoding
+    zf = d["z"].float()
+    for r in np.flatnonzero(d["greedy"].numpy()):
+        n = int(acc[r])
+        want = [int(torch.argmax(zf[r, s, :d["valid"]])) for s in range(n + 1)]
+        assert list(com[r, :n + 1]) == want
+    for r in range(R):                            # kept tokens, one committed draw, then -1
+        n = int(acc[r])
+        assert 0 <= n <= S and 0 <= com[r, n] < d["valid"] and np.all(com[r, n + 1:] == -1)
+    print(f"[verify] R={R} S={S} V={V}: mean accepted {acc.mean():.2f}, {edge} decisions on an fp64 edge", flush=True)
+    return acc, com
+
+
+@pytest.mark.parametrize("R,S,V,K,seed", [(16, 5, 1000, 8, 1), (8, 3, 37, 4, 2), (5, 1, 300, 1, 3),
+                                          (12, 15, 5003, 32, 4), (4, 0, 64, 2, 5)])
+def test_verify_matches_the_oracle(R, S, V, K, seed):
+    _run(R, S, V, K, seed)
+
+
+def test_verify_fp32_logits_and_padded_vocab():
+    _run(10, 4, 700, 8, 6, dtype=torch.float32, valid=650)
+
+
+def test_verify_bench_shape():
+    # 32 requests x 15 slots over the 151936-id vocabulary, K = 8
+    _run(32, 15, 151936, 8, 7)
+
+
+def test_verify_all_greedy_and_all_sampled():
+    a, _ = _run(16, 7, 2000, 8, 8, greedy_frac=1.0, match_frac=1.0)
+    assert np.all(a == 7)                         # every drafted token is the target's argmax: all kept
+    _run(16, 7, 2000, 8, 9, greedy_frac=0.0)
+
+
+def test_verify_empty_is_a_no_op():
+    require_gpu()
+    e = torch.zeros((0, 3, 16), dtype=torch.bfloat16, device=DEV)
+    acc, com = D.dflash_verify(e, torch.zeros((0, 2, 4), dtype=torch.int64, device=DEV),
+                               torch.zeros((0, 2, 4), device=DEV), torch.zeros((0, 2), dtype=torch.int64, device=DEV),
+                               torch.zeros((0, 2), device=DEV), torch.zeros(0, device=DEV), torch.zeros(0, device=DEV),
+                               torch.zeros(0, dtype=torch.uint8, device=DEV))
+    assert acc.shape == (0,) and com.shape == (0, 3)
