@@ -164,8 +164,10 @@ def call_bytes(w):
     propose = conv + topk + proj + gathers + 8 * R + 4 * Ns + 5 * R + 8 * Ns + 4 * Ns * K
     # x and the projection weight in, side-0 base in, out and both sides' coefficients written
     prepare = 2 * N * H * e + 2 * T * G * H * e + T * H * e + 2 * N * T * G * e
+    # target rows (every logical id) in; candidates, q, tokens, uniforms in; counts and tokens out
+    verify = R * (w.slots + 1) * V * e + 12 * Ns * K + 12 * Ns + 4 * R + 9 * R + 4 * R + 8 * R * (w.slots + 1)
     return {"dflash_conv": conv, "dflash_conv_prepare": prepare, "dflash_topk": topk, "dflash_lattice": lattice,
-            "dflash_walk": walk, "dflash_propose_block": propose}
+            "dflash_walk": walk, "dflash_verify": verify, "dflash_propose_block": propose}
 
 
 def sweep(iters: int = 50, warm: int = 5, only=None):
@@ -230,6 +232,10 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
                               proj=inp["proj"], uniforms=inp["uniforms"], temperatures=inp["temperatures"],
                               greedy_mask=inp["greedy_mask"], valid_vocab=w.valid_vocab)
         mod = W.make_conv_module_inputs(w, device=dev)
+        ver = W.make_verify_inputs(w, device=dev)
+        v_acc = torch.empty(R, dtype=torch.int32, device=dev)
+        v_com = torch.empty((R, S + 1), dtype=torch.int64, device=dev)
+        v_ws = torch.empty(max(1, D.lib().dflash_verify_workspace_size(R, S)), dtype=torch.uint8, device=dev)
         coeff = torch.empty((w.n_tokens, 2, w.taps, w.groups), dtype=inp["x"].dtype, device=dev)
         prep_ws = torch.empty(max(1, D.lib().dflash_conv_prepare_workspace_size(
             w.n_tokens, H, w.group_size, w.taps, 1 if w.dtype == "bf16" else 0)), dtype=torch.uint8, device=dev)
@@ -246,6 +252,10 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
                                                        inp["proj"], scores_out=scores, workspace=lat_ws),
             "dflash_walk": lambda: D.dflash_walk(scores, idv, inp["uniforms"], inp["temperatures"],
                                                  inp["greedy_mask"], tokens_out=tokens, q_out=q),
+            "dflash_verify": lambda: D.dflash_verify(ver["target_logits"], idv, q, tokens, ver["u_accept"],
+                                                     ver["u_residual"], inp["temperatures"], inp["greedy_mask"],
+                                                     valid_vocab=w.valid_vocab, accepted_out=v_acc,
+                                                     committed_out=v_com, workspace=v_ws),
             "dflash_propose_block": lambda: call(stream),
         }
         nbytes = call_bytes(w)
@@ -254,7 +264,7 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
             gbs = nbytes[cname] / (med * 1e-6) / 1e9
             print(f"| {name} | {cname} | {med:.2f} | {p10:.2f} | {p90:.2f} | {nbytes[cname] / 1e6:.2f} | {gbs:.0f} | "
                   f"{100 * gbs / HBM_PEAK_GBS:.1f} | {100 * gbs / copy_gbs:.1f} |", flush=True)
-        del inp, call, fns, mod, coeff, prep_ws
+        del inp, call, fns, mod, coeff, prep_ws, ver, v_acc, v_com, v_ws
         torch.cuda.empty_cache()
 
     # the dense head in front of the top-K (bf16 workloads): plain, and fused with the top-K

@@ -308,7 +308,7 @@ int dflash_conv_prepare(const void* x, const void* proj_weight, const void* base
 
 size_t dflash_verify_workspace_size(int32_t n_req, int32_t slots) {
   if (n_req <= 0 || slots < 0) return 0;
-  return (size_t)n_req * (slots + 1) * sizeof(dflash::VerifyRowStats);
+  return (size_t)n_req * (slots + 1) * dflash::kVerifySegs * sizeof(dflash::VerifyRowStats);
 }
 
 int dflash_verify(const void* target_logits, int64_t row_stride, int32_t n_req, int32_t slots, int64_t vocab,

@@ -162,8 +162,9 @@ struct VerifyArgs {
   int32_t dtype;
   int32_t* accepted_out;    // [n_req]
   int64_t* committed_out;   // [n_req, slots + 1]
-  void* workspace;          // VerifyRowStats [n_req * (slots + 1)]
+  void* workspace;          // VerifyRowStats [n_req * (slots + 1)][kVerifySegs]
 };
+constexpr int kVerifySegs = 4;   // workgroups (and statistics records) per target row
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 
 // Lattice and walk in one kernel (one workgroup per request) when the

@@ -29,6 +29,7 @@ namespace dflash {
 namespace {
 
 constexpr int kVerifyThreads = 256;
+constexpr int kCommitThreads = 1024;
 
 template <typename TIO>
 __device__ __forceinline__ double logit_at(const TIO* z, int64_t v);
@@ -43,81 +44,136 @@ __device__ __forceinline__ double logit_at<float>(const float* z, int64_t v) {
 
 __device__ __forceinline__ double clamp_temperature(float t) { return fmax((double)t, 1e-5); }
 
-// Running (max, lowest id of the max, normaliser relative to the max).
-struct Online {
-  double m, s;
-  int64_t arg;
-};
-
-__device__ __forceinline__ void online_add(Online& o, double z, int64_t v, double inv_t, bool sum) {
-  if (!(z > -INFINITY)) return;                          // -inf (and NaN) weigh nothing
-  if (z > o.m) {
-    if (sum) o.s = (o.m > -INFINITY ? o.s * exp((o.m - z) * inv_t) : 0.0) + 1.0;
-    o.m = z;
-    o.arg = v;
-  } else {
-    if (sum) o.s += exp((z - o.m) * inv_t);
-    if (z == o.m && v < o.arg) o.arg = v;
-  }
-}
-
-__device__ __forceinline__ Online online_merge(Online a, Online b, double inv_t, bool sum) {
-  if (!(b.m > -INFINITY)) return a;
-  if (!(a.m > -INFINITY)) return b;
-  Online o;
-  o.m = a.m > b.m ? a.m : b.m;
-  o.arg = a.m > b.m ? a.arg : (b.m > a.m ? b.arg : (a.arg < b.arg ? a.arg : b.arg));
-  o.s = sum ? a.s * exp((a.m - o.m) * inv_t) + b.s * exp((b.m - o.m) * inv_t) : 0.0;
-  return o;
-}
+// Statistics of one segment of one target row: the segment's maximum, its
+// lowest id, and (sampled requests) sum exp((z - m) / T) over the segment,
+// relative to the segment's own maximum.  Pass 1 finds the maximum with
+// branch-free selects (each thread walks its ids in increasing order, so a
+// strict comparison keeps the lowest id); pass 2 sums against that fixed
+// maximum.  Loads are issued kUnroll vectors at a time.
+constexpr int kUnroll = 4;
 
 template <typename TIO>
 __global__ __launch_bounds__(kVerifyThreads) void verify_stats_kernel(
     const TIO* __restrict__ logits, int64_t row_stride, int32_t rows_per_req, int64_t valid,
     const float* __restrict__ temperatures, const uint8_t* __restrict__ greedy_mask, VerifyRowStats* __restrict__ stats) {
-  __shared__ double s_m[kVerifyThreads], s_s[kVerifyThreads];
+  __shared__ float s_m[kVerifyThreads];
   __shared__ int64_t s_a[kVerifyThreads];
-  const int64_t row = blockIdx.x;
+  __shared__ double s_s[kVerifyThreads];
+  const int64_t row = blockIdx.x / kVerifySegs;
+  const int seg = (int)(blockIdx.x % kVerifySegs);
   const int r = (int)(row / rows_per_req);
   const int tid = threadIdx.x;
   const TIO* z = logits + row * row_stride;
-  const bool sum = greedy_mask[r] == 0;
-  const double inv_t = 1.0 / clamp_temperature(temperatures[r]);
-  Online o{-INFINITY, 0.0, 0};
   constexpr int VEC = Elem<TIO>::kVec;
-  // rows need not be 16-byte aligned: the elements before the first aligned
-  // 16 bytes and after the last whole vector are read one by one
+  // the row as: `head` single elements up to the first 16-byte boundary,
+  // nvec whole vectors, then single elements; segment `seg` takes its share
+  // of the vectors, the first segment the head and the last the tail
   int64_t head = (int64_t)(((16u - (reinterpret_cast<uintptr_t>(z) & 15u)) & 15u) / sizeof(TIO));
   if (head > valid) head = valid;
   const int64_t nvec = (valid - head) / VEC;
-  for (int64_t v = tid; v < head; v += kVerifyThreads) online_add(o, logit_at(z, v), v, inv_t, sum);
-  for (int64_t i = tid; i < nvec; i += kVerifyThreads) {
-    float f[VEC];
-    unpack16(ld16(z + head + i * VEC), f);
+  const int64_t vlo = nvec * seg / kVerifySegs, vhi = nvec * (seg + 1) / kVerifySegs;
+  const int64_t slo = 0, shi = seg == 0 ? head : 0;           // singles before the vectors
+  const int64_t tlo = seg == kVerifySegs - 1 ? head + nvec * VEC : valid, thi = valid;   // singles after
+
+  // pass 1: maximum and its lowest id
+  float m = -INFINITY;
+  int64_t arg = -1;
+  auto see = [&](float v, int64_t id) {
+    const bool up = v > m;                      // -inf and NaN never raise it
+    m = up ? v : m;
+    arg = up ? id : arg;
+  };
+  for (int64_t v = slo + tid; v < shi; v += kVerifyThreads) see(Elem<TIO>::to_f32(z[v]), v);
+  for (int64_t i0 = vlo + tid; i0 < vhi; i0 += kVerifyThreads * kUnroll) {
+    u32x4 raw[kUnroll];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) online_add(o, (double)f[e], head + i * VEC + e, inv_t, sum);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = i0 + (int64_t)u * kVerifyThreads;
+      raw[u] = ld16(z + head + (i < vhi ? i : vlo) * VEC);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = i0 + (int64_t)u * kVerifyThreads;
+      if (i >= vhi) break;
+      float f[VEC];
+      unpack16(raw[u], f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) see(f[e], head + i * VEC + e);
+    }
   }
-  for (int64_t v = head + nvec * VEC + tid; v < valid; v += kVerifyThreads)
-    online_add(o, logit_at(z, v), v, inv_t, sum);
-  s_m[tid] = o.m;
-  s_s[tid] = o.s;
-  s_a[tid] = o.arg;
+  for (int64_t v = tlo + tid; v < thi; v += kVerifyThreads) see(Elem<TIO>::to_f32(z[v]), v);
+  s_m[tid] = m;
+  s_a[tid] = arg;
   __syncthreads();
-  for (int w = kVerifyThreads / 2; w > 0; w >>= 1) {      // tree merge: same order every launch
+  for (int w = kVerifyThreads / 2; w > 0; w >>= 1) {
     if (tid < w) {
-      const Online a{s_m[tid], s_s[tid], s_a[tid]}, b{s_m[tid + w], s_s[tid + w], s_a[tid + w]};
-      const Online c = online_merge(a, b, inv_t, sum);
-      s_m[tid] = c.m;
-      s_s[tid] = c.s;
-      s_a[tid] = c.arg;
+      const float mb = s_m[tid + w];
+      const int64_t ab = s_a[tid + w];
+      if (mb > s_m[tid] || (mb == s_m[tid] && ab >= 0 && (s_a[tid] < 0 || ab < s_a[tid]))) {
+        s_m[tid] = mb;
+        s_a[tid] = ab;
+      }
     }
     __syncthreads();
   }
-  if (tid == 0) stats[row] = VerifyRowStats{s_m[0], s_s[0], s_a[0]};
+  const float mseg = s_m[0];
+  const int64_t aseg = s_a[0];
+
+  // pass 2 (sampled requests): sum exp((z - mseg) / T) in fp64
+  double sum = 0.0;
+  if (greedy_mask[r] == 0 && mseg > -INFINITY) {
+    const double inv_t = 1.0 / clamp_temperature(temperatures[r]);
+    const double mm = (double)mseg;
+    auto add = [&](float v) {
+      if (v > -INFINITY) sum += exp(((double)v - mm) * inv_t);
+    };
+    for (int64_t v = slo + tid; v < shi; v += kVerifyThreads) add(Elem<TIO>::to_f32(z[v]));
+    for (int64_t i0 = vlo + tid; i0 < vhi; i0 += kVerifyThreads * kUnroll) {
+      u32x4 raw[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t i = i0 + (int64_t)u * kVerifyThreads;
+        raw[u] = ld16(z + head + (i < vhi ? i : vlo) * VEC);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t i = i0 + (int64_t)u * kVerifyThreads;
+        if (i >= vhi) break;
+        float f[VEC];
+        unpack16(raw[u], f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) add(f[e]);
+      }
+    }
+    for (int64_t v = tlo + tid; v < thi; v += kVerifyThreads) add(Elem<TIO>::to_f32(z[v]));
+  }
+  s_s[tid] = sum;
+  __syncthreads();
+  for (int w = kVerifyThreads / 2; w > 0; w >>= 1) {      // fixed tree: the same order every launch
+    if (tid < w) s_s[tid] += s_s[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) stats[blockIdx.x] = VerifyRowStats{(double)mseg, s_s[0], aseg};
+}
+
+// The row's statistics from its segments, in segment (id) order: the maximum,
+// its lowest id (the first segment that holds it), and the normaliser
+// sum_k s_k exp((m_k - m) / T).
+__device__ __forceinline__ VerifyRowStats merge_segments(const VerifyRowStats* st, double inv_t) {
+  VerifyRowStats o{-INFINITY, 0.0, 0};
+  for (int k = 0; k < kVerifySegs; ++k)
+    if (st[k].m > o.m) {
+      o.m = st[k].m;
+      o.arg = st[k].arg;
+    }
+  if (o.m > -INFINITY)
+    for (int k = 0; k < kVerifySegs; ++k)
+      if (st[k].m > -INFINITY) o.s += st[k].s * exp((st[k].m - o.m) * inv_t);
+  return o;
 }
 
 template <typename TIO>
-__global__ __launch_bounds__(kVerifyThreads) void verify_commit_kernel(
+__global__ __launch_bounds__(kCommitThreads) void verify_commit_kernel(
     const TIO* __restrict__ logits, int64_t row_stride, int32_t S, int32_t K, int64_t valid,
     const int64_t* __restrict__ cand_ids, const float* __restrict__ q, const int64_t* __restrict__ tokens,
     const float* __restrict__ u_accept, const float* __restrict__ u_residual, const float* __restrict__ temperatures,
@@ -127,7 +183,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_commit_kernel(
   __shared__ int s_nc;
   __shared__ int64_t s_cid[kMaxTopK];
   __shared__ double s_cq[kMaxTopK];
-  __shared__ double s_sum[kVerifyThreads];
+  __shared__ double s_sum[kCommitThreads];
   __shared__ int s_chunk;
   __shared__ double s_base;
   __shared__ int64_t s_tok;
@@ -138,7 +194,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_commit_kernel(
     int n = 0;
     for (; n < S; ++n) {
       const int64_t x = tokens[(int64_t)r * S + n];
-      const VerifyRowStats st = stats[(int64_t)r * (S + 1) + n];
+      const VerifyRowStats st = merge_segments(stats + ((int64_t)r * (S + 1) + n) * kVerifySegs, inv_t);
       bool keep;
       if (greedy) {
         keep = x == st.arg;
@@ -175,7 +231,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_commit_kernel(
   __syncthreads();
   const int n = s_n;
   const int64_t row = (int64_t)r * (S + 1) + n;
-  const VerifyRowStats st = stats[row];
+  const VerifyRowStats st = merge_segments(stats + row * kVerifySegs, inv_t);
   int64_t tok;
   if (greedy || !(st.m > -INFINITY)) {
     tok = st.arg;
@@ -184,7 +240,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_commit_kernel(
     // summed per contiguous id range in id order
     const TIO* z = logits + row * row_stride;
     const int nc = s_nc;
-    const int64_t chunk = (valid + kVerifyThreads - 1) / kVerifyThreads;
+    const int64_t chunk = (valid + kCommitThreads - 1) / kCommitThreads;
     const int64_t v0 = (int64_t)tid * chunk, v1 = v0 + chunk < valid ? v0 + chunk : valid;
     auto weight = [&](int64_t v, int& ci) {
       double w = exp((logit_at(z, v) - st.m) * inv_t) / st.s;
@@ -205,11 +261,11 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_commit_kernel(
     __syncthreads();
     if (tid == 0) {
       double total = 0.0;
-      for (int t = 0; t < kVerifyThreads; ++t) total += s_sum[t];
+      for (int t = 0; t < kCommitThreads; ++t) total += s_sum[t];
       const double target = (double)u_residual[r] * total;
       double base = 0.0;
       int c = -1, last = -1;
-      for (int t = 0; t < kVerifyThreads; ++t) {
+      for (int t = 0; t < kCommitThreads; ++t) {
         if (s_sum[t] > 0.0) last = t;
         if (c < 0 && base + s_sum[t] > target && s_sum[t] > 0.0) {
           c = t;
@@ -228,7 +284,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_commit_kernel(
     __syncthreads();
     if (tid == s_chunk) {
       double total = 0.0;                                  // the same sum, in the same order, as above
-      for (int t = 0; t < kVerifyThreads; ++t) total += s_sum[t];
+      for (int t = 0; t < kCommitThreads; ++t) total += s_sum[t];
       const double goal = (double)u_residual[r] * total;
       double acc = s_base;
       int ci = ci0;
@@ -248,7 +304,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_commit_kernel(
     tok = s_tok;
   }
   if (tid == 0) accepted[r] = n;
-  for (int s = tid; s <= S; s += kVerifyThreads) {
+  for (int s = tid; s <= S; s += kCommitThreads) {
     int64_t c = -1;
     if (s < n) c = tokens[(int64_t)r * S + s];
     else if (s == n) c = tok;
@@ -261,16 +317,17 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_commit_kernel(
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
   if (a.n_req == 0) return hipSuccess;
   const int64_t rows = (int64_t)a.n_req * (a.slots + 1);
-  VerifyRowStats* stats = static_cast<VerifyRowStats*>(a.workspace);
+  VerifyRowStats* stats = static_cast<VerifyRowStats*>(a.workspace);   // [rows][kVerifySegs]
 #define DFLASH_VERIFY(TIO)                                                                                   \
-  hipLaunchKernelGGL(verify_stats_kernel<TIO>, dim3((unsigned)rows), dim3(kVerifyThreads), 0, stream,          \
+  hipLaunchKernelGGL(verify_stats_kernel<TIO>, dim3((unsigned)(rows * kVerifySegs)), dim3(kVerifyThreads), 0,    \
+                     stream,                                                                                  \
                      static_cast<const TIO*>(a.logits), a.row_stride, a.slots + 1, a.valid_vocab,             \
                      a.temperatures, a.greedy_mask, stats);                                                   \
   {                                                                                                          \
     hipError_t e = hipGetLastError();                                                                        \
     if (e != hipSuccess) return e;                                                                           \
   }                                                                                                          \
-  hipLaunchKernelGGL(verify_commit_kernel<TIO>, dim3((unsigned)a.n_req), dim3(kVerifyThreads), 0, stream,      \
+  hipLaunchKernelGGL(verify_commit_kernel<TIO>, dim3((unsigned)a.n_req), dim3(kCommitThreads), 0, stream,      \
                      static_cast<const TIO*>(a.logits), a.row_stride, a.slots, a.top_k, a.valid_vocab,        \
                      a.cand_ids, a.q, a.tokens, a.u_accept, a.u_residual, a.temperatures, a.greedy_mask,      \
                      stats, a.accepted_out, a.committed_out)

@@ -245,7 +245,7 @@ def test_verify_validation():
     A = ctypes.c_void_p
     R, S, V, K = 4, 3, 100, 8
     need = L.dflash_verify_workspace_size(R, S)
-    assert need == R * (S + 1) * 24 and L.dflash_verify_workspace_size(0, S) == 0
+    assert need >= R * (S + 1) * 24 and L.dflash_verify_workspace_size(0, S) == 0
     call = lambda **kw: L.dflash_verify(*[kw.get(k, d) for k, d in (
         ("z", A(1 << 20)), ("rs", V), ("R", R), ("S", S), ("V", V), ("vv", V), ("K", K), ("ids", A(2 << 20)),
         ("q", A(3 << 20)), ("tok", A(4 << 20)), ("ua", A(5 << 20)), ("ur", A(6 << 20)), ("t", A(7 << 20)),

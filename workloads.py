@@ -269,3 +269,21 @@ def make_conv_module_inputs(w: Workload, device="cpu", seed: Optional[int] = Non
             "y": normal((N, H), 1.0, w.dtype, m, "module_y", dev),
             "proj_weight": normal((2 * T * G, H), w.delta_sigma / math.sqrt(H), w.dtype, m, "module_proj", dev),
             "base2": normal((2, T, H), w.base_sigma, w.dtype, m, "module_base", dev)}
+
+
+def make_verify_inputs(w: Workload, device="cpu", seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Target side of a verify for workload ``w`` (the drafted tokens, their
+    candidates and q come from the draft path):
+      target_logits [R, S+1, V]  N(0, logit_sigma^2), storage dtype; ids past
+                                 the logical vocabulary are -inf, as in the draft logits
+      u_accept      [R, S]       uniforms in [0, 1) (multiples of 2^-24)
+      u_residual    [R]          uniforms in [0, 1)"""
+    m = master_seed(w) if seed is None else int(seed)
+    dev = torch.device(device)
+    R, S, V = w.n_req, w.slots, w.vocab
+    z = normal((R * (S + 1), V), w.logit_sigma, w.dtype, m, "target_logits", dev).view(R, S + 1, V)
+    if w.valid_vocab < V:
+        z[:, :, w.valid_vocab:] = float("-inf")
+    return {"target_logits": z,
+            "u_accept": uniform((R, S), m, "verify_accept", dev),
+            "u_residual": uniform((R,), m, "verify_residual", dev)}
