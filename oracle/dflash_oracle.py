@@ -491,3 +491,47 @@ def verify(target_logits: np.ndarray, valid_vocab: int, cand_ids: np.ndarray, q:
             committed[r, S] = inverse_cdf(p, float(u_residual[r]))
         accepted[r] = n
     return accepted, committed
+
+
+# ---------------------------------------------------------------------------
+# Counter-based uniforms for a captured step  [DF2] worker excerpt: the
+# sampler draws its uniforms inside the captured graph with a counter-based
+# generator (Philox), so every replay can draw fresh numbers without host
+# work.  Philox-4x32-10 as published by Salmon, Moraes, Dror and Shaw
+# ("Parallel random numbers: as easy as 1, 2, 3", SC 2011): ten rounds of
+# two 32x32 -> 64-bit multiplications with the Weyl-sequence key schedule.
+# ---------------------------------------------------------------------------
+
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)
+_MASK32 = 0xFFFFFFFF
+
+
+def philox4x32_10(counter, key):
+    """counter: 4 words, key: 2 words (unsigned 32-bit) -> 4 output words."""
+    x0, x1, x2, x3 = (int(c) & _MASK32 for c in counter)
+    k0, k1 = (int(k) & _MASK32 for k in key)
+    for rnd in range(10):
+        p0 = _PHILOX_M[0] * x0
+        p1 = _PHILOX_M[1] * x2
+        x0, x1, x2, x3 = ((p1 >> 32) ^ x1 ^ k0, p1 & _MASK32, (p0 >> 32) ^ x3 ^ k1, p0 & _MASK32)
+        k0 = (k0 + _PHILOX_W[0]) & _MASK32
+        k1 = (k1 + _PHILOX_W[1]) & _MASK32
+    return (x0, x1, x2, x3)
+
+
+def philox_uniforms(seed: int, offset: int, n: int) -> np.ndarray:
+    """n uniforms in [0, 1) (float32 values, multiples of 2^-24): element i is
+    word i % 4 of block offset + i // 4 (64-bit counter in the first two
+    counter words, the others zero; key = the seed's two 32-bit halves),
+    keeping its top 24 bits."""
+    out = np.empty(n, np.float64)
+    key = (seed & _MASK32, (seed >> 32) & _MASK32)
+    for b in range((n + 3) // 4):
+        c = (offset + b) & 0xFFFFFFFFFFFFFFFF
+        words = philox4x32_10((c & _MASK32, c >> 32, 0, 0), key)
+        for j in range(4):
+            i = 4 * b + j
+            if i < n:
+                out[i] = (words[j] >> 8) * 2.0 ** -24
+    return out
