@@ -167,7 +167,8 @@ def call_bytes(w):
     # target rows (every logical id) in; candidates, q, tokens, uniforms in; counts and tokens out
     verify = R * (w.slots + 1) * V * e + 12 * Ns * K + 12 * Ns + 4 * R + 9 * R + 4 * R + 8 * R * (w.slots + 1)
     return {"dflash_conv": conv, "dflash_conv_prepare": prepare, "dflash_topk": topk, "dflash_lattice": lattice,
-            "dflash_walk": walk, "dflash_verify": verify, "dflash_propose_block": propose}
+            "dflash_walk": walk, "dflash_verify": verify, "dflash_propose_block": propose,
+            "ProposeGraph.replay": propose + 4 * Ns + 5 * R + 16}
 
 
 def sweep(iters: int = 50, warm: int = 5, only=None):
@@ -233,6 +234,10 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
                               greedy_mask=inp["greedy_mask"], valid_vocab=w.valid_vocab)
         mod = W.make_conv_module_inputs(w, device=dev)
         ver = W.make_verify_inputs(w, device=dev)
+        graph = D.ProposeGraph(cfg, x=inp["x"], conv_base=inp["base"][0], conv_delta=inp["delta"][:, 0],
+                               logits=inp["logits"], anchor=inp["anchor"], sel_a=inp["sel_a"], sel_b=inp["sel_b"],
+                               proj=inp["proj"], valid_vocab=w.valid_vocab)
+        g_temps, g_mask = inp["temperatures"].cpu(), inp["greedy_mask"].cpu()
         v_acc = torch.empty(R, dtype=torch.int32, device=dev)
         v_com = torch.empty((R, S + 1), dtype=torch.int64, device=dev)
         v_ws = torch.empty(max(1, D.lib().dflash_verify_workspace_size(R, S)), dtype=torch.uint8, device=dev)
@@ -257,6 +262,7 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
                                                      valid_vocab=w.valid_vocab, accepted_out=v_acc,
                                                      committed_out=v_com, workspace=v_ws),
             "dflash_propose_block": lambda: call(stream),
+            "ProposeGraph.replay": lambda: graph.replay(g_temps, g_mask, 1234, 0),
         }
         nbytes = call_bytes(w)
         for cname, fn in fns.items():
@@ -264,7 +270,7 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
             gbs = nbytes[cname] / (med * 1e-6) / 1e9
             print(f"| {name} | {cname} | {med:.2f} | {p10:.2f} | {p90:.2f} | {nbytes[cname] / 1e6:.2f} | {gbs:.0f} | "
                   f"{100 * gbs / HBM_PEAK_GBS:.1f} | {100 * gbs / copy_gbs:.1f} |", flush=True)
-        del inp, call, fns, mod, coeff, prep_ws, ver, v_acc, v_com, v_ws
+        del inp, call, fns, mod, coeff, prep_ws, ver, v_acc, v_com, v_ws, graph
         torch.cuda.empty_cache()
 
     # the dense head in front of the top-K (bf16 workloads): plain, and fused with the top-K

@@ -24,5 +24,7 @@ from .binding import (  # noqa: F401
     dflash_lm_head_topk,
     dflash_propose_block,
     ProposeBlock,
+    ProposeGraph,
+    dflash_philox_uniforms,
     propose_block_workspace_size,
 )

@@ -12,6 +12,7 @@ import ctypes
 import os
 from typing import Dict, Optional, Sequence
 
+import numpy as np
 import torch
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +67,7 @@ _SIGNATURES = {
     "dflash_conv_prepare_workspace_size": (_c_size, [_c_i64, _c_i32, _c_i32, _c_i32, _c_i32]),
     "dflash_conv_prepare": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_vp, _c_size, _c_vp]),
+    "dflash_philox_uniforms": (_c_i32, [_c_vp, _c_i64, _c_vp, _c_vp]),
     "dflash_verify_workspace_size": (_c_size, [_c_i32, _c_i32]),
     "dflash_verify": (_c_i32, [_c_vp, _c_i64, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp,
                                _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
@@ -397,6 +399,122 @@ class ProposeBlock:
         if st != DFLASH_OK:
             raise DFlashError(st, last_error())
         return self.outputs
+
+
+def dflash_philox_uniforms(seed_offset: torch.Tensor, n: int, *, out: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """seed_offset: device int64 [2] = {seed, offset} (read as unsigned by the
+    kernel).  Returns out fp32 [n]: Philox-4x32-10 uniforms in [0, 1)."""
+    if seed_offset.numel() != 2 or seed_offset.dtype != torch.int64 or not seed_offset.is_contiguous():
+        raise ValueError("seed_offset must be a contiguous int64 tensor of 2 elements")
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=seed_offset.device)
+    _check(lib().dflash_philox_uniforms(_p(seed_offset), n, _p(out), _stream(stream)))
+    return out
+
+
+_hip_rt = None
+
+
+def _hip():
+    """The HIP runtime (for the staging copy and its event in ProposeGraph)."""
+    global _hip_rt
+    if _hip_rt is None:
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipMemcpyAsync.argtypes = [_c_vp, _c_vp, _c_size, ctypes.c_int, _c_vp]
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(_c_vp), ctypes.c_uint]
+        h.hipEventRecord.argtypes = [_c_vp, _c_vp]
+        h.hipEventSynchronize.argtypes = [_c_vp]
+        _hip_rt = h
+    return _hip_rt
+
+
+def _as_i64(v: int) -> int:
+    """An unsigned 64-bit value as the int64 with the same bits."""
+    v &= (1 << 64) - 1
+    return v - (1 << 64) if v >= 1 << 63 else v
+
+
+class ProposeGraph:
+    """One draft step captured as a HIP graph: the walk's uniforms drawn in the
+    graph by dflash_philox_uniforms from a staged {seed, offset}, then
+    dflash_propose_block (its auxiliary-stream branch captured through the
+    library's fork/join events).  Temperatures, the greedy mask and {seed,
+    offset} live in device buffers the graph reads; replay() stages new host
+    values into them on the stream (outside the graph) and replays, so one
+    graph serves greedy and sampled requests alike.  The other inputs are
+    fixed buffers (as for ProposeBlock); the outputs are rewritten by every
+    replay."""
+
+    def __init__(self, cfg: DraftConfig, *, x, conv_base, conv_delta, logits, anchor, sel_a, sel_b, proj,
+                 valid_vocab: Optional[int] = None, vocab: Optional[int] = None):
+        B = cfg.block_size
+        R, S = x.shape[0] // B, B - 1
+        dev = x.device
+        self.n = R * S
+        self.uniforms = torch.empty((R, S), dtype=torch.float32, device=dev)
+        # everything staged per replay in one buffer (one copy): {seed, offset}
+        # (16 bytes), temperatures (4 R), greedy mask (R)
+        nbytes = 16 + 4 * R + R
+        self._stage_dev = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        self._stage_host = torch.zeros(nbytes, dtype=torch.uint8).pin_memory()
+        self.seed_offset = self._stage_dev[:16].view(torch.int64)
+        self.temperatures = self._stage_dev[16:16 + 4 * R].view(torch.float32)
+        self.greedy_mask = self._stage_dev[16 + 4 * R:]
+        host = self._stage_host.numpy()             # shares the pinned memory
+        self._h_so = host[:16].view(np.uint64)
+        self._h_temp = host[16:16 + 4 * R].view(np.float32)
+        self._h_mask = host[16 + 4 * R:]
+        self.temperatures.fill_(1.0)
+        self.greedy_mask.fill_(1)
+        # the staging copy is ordered by a plain HIP event (no timing, no
+        # system-scope fence): the next replay's host writes wait for it
+        hip = _hip()
+        ev = _c_vp()
+        if hip.hipEventCreateWithFlags(ctypes.byref(ev), 0x2 | 0x20000000) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self._staged = ev
+        self._stage_args = (_c_vp(self._stage_dev.data_ptr()), _c_vp(self._stage_host.data_ptr()), nbytes)
+        self.call = ProposeBlock(cfg, x=x, conv_base=conv_base, conv_delta=conv_delta, logits=logits, anchor=anchor,
+                                 sel_a=sel_a, sel_b=sel_b, proj=proj, uniforms=self.uniforms,
+                                 temperatures=self.temperatures, greedy_mask=self.greedy_mask,
+                                 valid_vocab=valid_vocab, vocab=vocab)
+        self._philox = lib().dflash_philox_uniforms
+        # one eager step first: the library creates its auxiliary stream and
+        # events on first use, which must not happen inside the capture
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self._step(side.cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self._step(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+
+    def _step(self, stream_handle) -> None:
+        st = self._philox(_p(self.seed_offset), self.n, _p(self.uniforms), stream_handle)
+        if st != DFLASH_OK:
+            raise DFlashError(st, last_error())
+        self.call(stream_handle)
+
+    def replay(self, temperatures, greedy_mask, seed: int, offset: int) -> Dict[str, torch.Tensor]:
+        """Stage the sampling parameters and {seed, offset} (host values), then
+        replay on torch's current stream.  Returns the outputs dict."""
+        hip = _hip()
+        stream = torch.cuda.current_stream().cuda_stream
+        if hip.hipEventSynchronize(self._staged) != 0:     # the previous staging copy has read the pinned buffer
+            raise RuntimeError("hipEventSynchronize failed")
+        self._h_temp[:] = np.asarray(temperatures, dtype=np.float32)
+        self._h_mask[:] = np.asarray(greedy_mask, dtype=np.uint8)
+        self._h_so[0] = seed & ((1 << 64) - 1)
+        self._h_so[1] = offset & ((1 << 64) - 1)
+        dst, src, nbytes = self._stage_args
+        if hip.hipMemcpyAsync(dst, src, nbytes, 1, stream) != 0 or hip.hipEventRecord(self._staged, stream) != 0:
+            raise RuntimeError("staging copy failed")
+        self.graph.replay()
+        return self.call.outputs
 
 
 def dflash_propose_block(cfg: DraftConfig, *, stage_events: Optional[Sequence] = None, stream=None,

@@ -306,6 +306,19 @@ int dflash_conv_prepare(const void* x, const void* proj_weight, const void* base
   return st == DFLASH_OK ? ok() : st;
 }
 
+int dflash_philox_uniforms(const uint64_t* seed_offset, int64_t n, float* out, dflash_stream_t stream) {
+  const char* who = "dflash_philox_uniforms";
+  if (n < 0) return fail(DFLASH_ERR_INVALID_ARG, "%s: n < 0", who);
+  if (n == 0) return ok();
+  if (!seed_offset || !out) return fail(DFLASH_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (reinterpret_cast<uintptr_t>(seed_offset) % 8 || reinterpret_cast<uintptr_t>(out) % 4)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: misaligned pointer", who);
+  if (overlaps(seed_offset, 16, out, (size_t)n * 4))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: out overlaps seed_offset", who);
+  const int st = launch_status(dflash::launch_philox_uniforms(seed_offset, n, out, as_hip(stream)), who);
+  return st == DFLASH_OK ? ok() : st;
+}
+
 size_t dflash_verify_workspace_size(int32_t n_req, int32_t slots) {
   if (n_req <= 0 || slots < 0) return 0;
   return (size_t)n_req * (slots + 1) * dflash::kVerifySegs * sizeof(dflash::VerifyRowStats);

@@ -142,6 +142,9 @@ struct ConvPrepPlan {
 ConvPrepPlan plan_conv_prepare(int64_t n_tokens, int32_t hidden, int32_t outputs, int32_t dtype);
 hipError_t launch_conv_prepare(const ConvPrepArgs& a, const ConvPrepPlan& p, hipStream_t stream);
 
+// Philox-4x32-10 uniforms: seed_offset = {seed, offset} in device memory.
+hipError_t launch_philox_uniforms(const uint64_t* seed_offset, int64_t n, float* out, hipStream_t stream);
+
 // Verify and commit of a drafted block.
 struct VerifyRowStats {
   double m;                 // maximum logit of the row (valid ids), -inf if none is finite

@@ -239,6 +239,20 @@ int dflash_lm_head_topk(const void* hidden, int64_t hidden_row_stride, const voi
                         dflash_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * dflash_philox_uniforms -- counter-based uniforms for a captured draft step
+ * ("[Spec] DFlash2", worker excerpt: the sampler draws its uniforms inside
+ * the captured graph).  Philox-4x32-10 (Salmon et al., "Parallel random
+ * numbers: as easy as 1, 2, 3", SC 2011):
+ *   out[i] = (word i%4 of Philox(counter = {lo, hi of offset + i/4, 0, 0},
+ *             key = {lo, hi of seed})) >> 8, times 2^-24      in [0, 1)
+ *   seed_offset  device uint64 [2] = {seed, offset}, 8-byte aligned; read by
+ *                the kernel, so a captured launch uses what the host staged
+ *                before the replay (advance offset by ceil(n/4) per draw)
+ *   out          device fp32 [n], 4-byte aligned
+ * n == 0 is a no-op. */
+int dflash_philox_uniforms(const uint64_t* seed_offset, int64_t n, float* out, dflash_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * dflash_verify -- verify and commit of a drafted block ("[Spec] DFlash2",
  * executive summary and walk-kernel excerpt: verify checks the drafted tokens
  * against the distribution the walk drew them from -- a point mass on greedy
