@@ -53,13 +53,19 @@ hipError_t launch_topk(const TopkArgs& a, const TopkPlan& p, hipStream_t stream)
 constexpr int kMaxTopK = 32;   // DFLASH_MAX_TOP_K
 
 // Most slices the projection's contraction is split into (their partial
-// sums are added by the consumer, in slice order).
-constexpr int kMaxProjSplit = 32;
+// sums are added by the consumer, in slice order).  Few: the consumer loads
+// and adds every slice of each value it needs, and the projection runs beside
+// the top-K, off the critical path, so more workgroups would not pay.
+constexpr int kMaxProjSplit = 8;
+// The partials are stored slice-minor, [n_rows][rank][kstride]: the slices of
+// one output sit together, kstride = ksplit rounded up to a multiple of 4
+// (one 16-byte vector per 4 slices; the padding is never read as a value).
+__host__ __device__ inline int proj_slice_stride(int ksplit) { return (ksplit + 3) & ~3; }
 struct ProjPlan {
   int32_t n_rows, rank, hidden;
   int32_t row_tiles, ksplit, kslice;   // split of the contraction over workgroups
   int32_t frags;                       // row fragments of 16 per wave (bf16)
-  size_t bytes;                        // fp32 partials [ksplit][n_rows][rank]
+  size_t bytes;                        // fp32 partials [n_rows][rank][proj_slice_stride(ksplit)]
 };
 ProjPlan plan_proj(int32_t n_rows, int32_t rank, int32_t hidden, int32_t dtype);
 

@@ -41,8 +41,8 @@ constexpr int kProjUnroll = 4;       // projection k-steps whose loads are issue
 // q = (n * ceil(2^32 / d)) >> 32.  The error n * (M d - 2^32) / (d 2^32) is
 // below 1/d, so the floor is exact.
 struct FastDiv {
-  uint64_t m;
-  __device__ explicit FastDiv(int d) : m(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d) {}
+  uint64_t m;   // ceil(2^32 / d) = floor((2^32 - 1) / d) + 1, by a 32-bit division
+  __device__ explicit FastDiv(int d) : m((uint64_t)(0xFFFFFFFFu / (uint32_t)d) + 1) {}
   __device__ int quot(int n) const { return (int)(((uint64_t)(uint32_t)n * m) >> 32); }
 };
 
@@ -64,6 +64,7 @@ __global__ __launch_bounds__(kThreads) void proj_mfma_kernel(const uint16_t* __r
                                                              int32_t n_rows, int32_t rank, int32_t H,
                                                              int32_t kslice, float* __restrict__ u_parts) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kstride = proj_slice_stride((int)gridDim.y);   // gridDim.y = ksplit
   const int row_base = (blockIdx.x * 4 + wave) * 16 * FR;
   const int split = blockIdx.y;
   const int k0 = split * kslice;
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void proj_mfma_kernel(const uint16_t* __r
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = row_base + 16 * f + 4 * (lane >> 4) + v;
-        if (row < n_rows) u_parts[((int64_t)split * n_rows + row) * rank + col] = acc[f][t][v];
+        if (row < n_rows) u_parts[((int64_t)row * rank + col) * kstride + split] = acc[f][t][v];
       }
   }
 }
@@ -145,23 +146,39 @@ __global__ __launch_bounds__(kThreads) void proj_f32_kernel(const float* __restr
   const float* p = P + (int64_t)col * H;
   float acc = 0.f;
   for (int k = 0; k < H; ++k) acc = fmaf(h[k], p[k], acc);
-  u_parts[t] = acc;
+  u_parts[t * proj_slice_stride(1)] = acc;   // one slice, slice-minor layout
 }
 
-// u[n][k] = sum over the projection slices sp = 0..ksplit-1 of
-// u_parts[sp][n][k], added in slice order.  All slice loads are issued before
-// the first add (ksplit <= kMaxProjSplit).
-__device__ __forceinline__ float sum_proj_slices(const float* __restrict__ u_parts, int ksplit, int64_t n_rows,
-                                                 int r, int64_t n, int k) {
-  float v[kMaxProjSplit];
-#pragma unroll
-  for (int sp = 0; sp < kMaxProjSplit; ++sp)
-    if (sp < ksplit) v[sp] = u_parts[((int64_t)sp * n_rows + n) * r + k];
+// u[n][k] = sum over the projection slices sp = 0..ksplit-1 of the partial
+// u_parts[n][k][sp] (slice-minor, stride proj_slice_stride(ksplit)), added in
+// slice order.  load_proj_slices issues every load of the value (16-byte
+// vectors of 4 slices) before add_proj_slices uses the first, so callers can
+// put other loads between the two and pay one memory round trip for all.
+__device__ __forceinline__ void load_proj_slices(const float* __restrict__ u_parts, int ksplit, int r, int64_t n,
+                                                 int k, float (&v)[kMaxProjSplit]) {
+  static_assert(kMaxProjSplit == 8, "two 16-byte vectors of slices at most");
+  const float4* base = reinterpret_cast<const float4*>(u_parts + (n * r + k) * (int64_t)proj_slice_stride(ksplit));
+  // both loads unconditional (the second re-reads the first vector when there
+  // are 4 slices or fewer), so neither waits for the other
+  const float4 a = base[0];
+  const float4 b = base[ksplit > 4 ? 1 : 0];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ float add_proj_slices(const float (&v)[kMaxProjSplit], int ksplit) {
   float u = v[0];
 #pragma unroll
   for (int sp = 1; sp < kMaxProjSplit; ++sp)
     if (sp < ksplit) u += v[sp];
   return u;
+}
+
+__device__ __forceinline__ float sum_proj_slices(const float* __restrict__ u_parts, int ksplit, int r, int64_t n,
+                                                 int k) {
+  float v[kMaxProjSplit];
+  load_proj_slices(u_parts, ksplit, r, n, k, v);
+  return add_proj_slices(v, ksplit);
 }
 
 template <typename TIO>
@@ -179,7 +196,7 @@ __device__ void lattice_block(const int64_t* __restrict__ ids, const float* __re
   const int tid = threadIdx.x;
   const int n = req * slots + s;
   const int wstride = r + 1;                         // padded row of w (LDS banks)
-  for (int k = tid; k < r; k += kThreads) s_u[k] = sum_proj_slices(u_parts, ksplit, n_rows, r, n, k);
+  for (int k = tid; k < r; k += kThreads) s_u[k] = sum_proj_slices(u_parts, ksplit, r, n, k);
   for (int j = tid; j < K; j += kThreads) {
     s_pred[j] = (s == 0) ? anchor[req] : ids[((int64_t)req * slots + s - 1) * K + j];
     s_cand[j] = ids[(int64_t)n * K + j];
@@ -268,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void lattice_tiled_kernel(
   const int n = blockIdx.x;
   const int req = n / slots, s = n % slots;
 
-  for (int k = tid; k < r; k += kThreads) s_u[k] = sum_proj_slices(u_parts, ksplit, n_rows, r, n, k);
+  for (int k = tid; k < r; k += kThreads) s_u[k] = sum_proj_slices(u_parts, ksplit, r, n, k);
   for (int j = tid; j < K; j += kThreads) {
     s_pred[j] = (s == 0) ? anchor[req] : ids[((int64_t)req * slots + s - 1) * K + j];
     s_cand[j] = ids[(int64_t)n * K + j];
@@ -669,17 +686,40 @@ __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
   const FastDiv div_k(K), div_r(r);                 // every index below is < 2^16 (LDS bound)
 
   // ---- 1. ids, u (projection slices summed in order), unary, uniforms ----
-  for (int i = tid; i < S * K; i += kLWThreads) {
-    const int s = div_k.quot(i), j = i - s * K;
-    s_pred[i] = (s == 0) ? anchor[req] : ids[(row0 + s - 1) * K + j];
-    s_cand[i] = ids[row0 * K + i];
-    s_unary[i] = unary[row0 * K + i];
+  // Each pass issues every load of its items (uniform, ids, unary, all u
+  // slices) before the first LDS write or add, so the phase costs one memory
+  // round trip per pass (one pass whenever S * max(K, r) <= 1024).
+  {
+    const int n_e = S * K, n_u = S * r;
+    const int n_all = max(max(n_e, n_u), S);
+    for (int i = tid; i < n_all; i += kLWThreads) {
+      const bool has_e = i < n_e, has_u = i < n_u, has_s = i < S;
+      float uni = 0.f, un = 0.f;
+      int64_t pred = 0, cand = 0;
+      float v[kMaxProjSplit];
+      if (has_s) uni = uniforms[row0 + i];
+      if (has_e) {
+        const int s = div_k.quot(i), j = i - s * K;
+        pred = (s == 0) ? anchor[req] : ids[(row0 + s - 1) * K + j];
+        cand = ids[row0 * K + i];
+        un = unary[row0 * K + i];
+      }
+      if (has_u) {
+        const int s = div_r.quot(i);
+        load_proj_slices(u_parts, ksplit, r, row0 + s, i - s * r, v);
+      }
+      // keep the compiler from sinking the slice loads below the LDS writes
+      // (which would start a second round trip after the first one drained)
+      asm volatile("" ::: "memory");
+      if (has_s) s_un[i] = uni;
+      if (has_e) {
+        s_pred[i] = pred;
+        s_cand[i] = cand;
+        s_unary[i] = un;
+      }
+      if (has_u) s_u[i] = add_proj_slices(v, ksplit);
+    }
   }
-  for (int i = tid; i < S * r; i += kLWThreads) {
-    const int s = div_r.quot(i);
-    s_u[i] = sum_proj_slices(u_parts, ksplit, n_rows, r, row0 + s, i - s * r);
-  }
-  for (int i = tid; i < S; i += kLWThreads) s_un[i] = uniforms[row0 + i];
   __syncthreads();
 
   // ---- 2. gather: w = A[pred] (.) u (fp32), B[cand] rows ------------------
@@ -795,7 +835,7 @@ ProjPlan plan_proj(int32_t n_rows, int32_t rank, int32_t hidden, int32_t dtype) 
     p.kslice = hidden;
     p.ksplit = 1;
   }
-  p.bytes = (size_t)p.ksplit * n_rows * rank * sizeof(float);
+  p.bytes = (size_t)proj_slice_stride(p.ksplit) * n_rows * rank * sizeof(float);
   p.bytes = (p.bytes + 255) & ~(size_t)255;
   return p;
 }
