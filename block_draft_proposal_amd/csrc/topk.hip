@@ -101,7 +101,7 @@ template <> struct Chunk<uint16_t> {
   // end, so every load is unconditional and the key conversion branch-free
   // (keeps the wait for this chunk's loads from draining the prefetch).
   // Partial group-chunk: vectors past the logical vocab end read as zero.
-  __device__ void issue(const uint16_t* rowp, int64_t lb, int64_t valid) {
+  __device__ __forceinline__ void issue(const uint16_t* rowp, int64_t lb, int64_t valid) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
       const int64_t e0 = lb + l * vec_stride<VEC>();
@@ -114,7 +114,7 @@ template <> struct Chunk<uint16_t> {
   // last whole vector below the logical end, re-reads that one instead; its
   // values are replaced in make_keys.  In a whole group-chunk every vector
   // lies at or below last_vec.
-  __device__ void issue_clamped(const uint16_t* rowp, int32_t lb, int32_t last_vec) {
+  __device__ __forceinline__ void issue_clamped(const uint16_t* rowp, int32_t lb, int32_t last_vec) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
       const int32_t e0 = min(lb + l * (int32_t)vec_stride<VEC>(), last_vec);
@@ -123,12 +123,12 @@ template <> struct Chunk<uint16_t> {
       w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
     }
   }
-  __device__ void keys_full() {
+  __device__ __forceinline__ void keys_full() {
 #pragma unroll
     for (int j = 0; j < W; ++j) w[j] = bf16_key2(w[j]);
   }
   // Keys of a partial group-chunk (issue() read the vectors below the end).
-  __device__ void make_keys(const uint16_t* rowp, int64_t lb, int64_t valid) {
+  __device__ __forceinline__ void make_keys(const uint16_t* rowp, int64_t lb, int64_t valid) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
       const int64_t e0 = lb + l * vec_stride<VEC>();
@@ -152,36 +152,6 @@ template <> struct Chunk<uint16_t> {
     for (int j = 1; j < W; ++j) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[j]));
     return max((uint32_t)m.x, (uint32_t)m.y);
   }
-  // Calls f(key, value index) for every key >= tau (1 <= tau < 0x10000).
-  // Survivors are rare: the lane first tests the maxima of four groups of
-  // eight registers, and only a group holding one is searched register by
-  // register.
-  template <class F> __device__ void for_each_ge(uint64_t tau, F&& f) const {
-    const unsigned short t1 = (unsigned short)(tau - 1);
-    const u16x2 t = {t1, t1};
-    u16x2 gm[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      gm[g] = __builtin_bit_cast(u16x2, w[8 * g]);
-#pragma unroll
-      for (int j = 1; j < 8; ++j) gm[g] = __builtin_elementwise_max(gm[g], __builtin_bit_cast(u16x2, w[8 * g + j]));
-    }
-    const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(gm[0], gm[1]),
-                                              __builtin_elementwise_max(gm[2], gm[3]));
-    if (max(m.x, m.y) <= t1) return;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (max(gm[g].x, gm[g].y) <= t1) continue;
-#pragma unroll
-      for (int j = 8 * g; j < 8 * g + 8; ++j) {
-        const u16x2 d = __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, w[j]), t);
-        if (__builtin_bit_cast(uint32_t, d) != 0u) {
-          if (d.x) f(w[j] & 0xffffu, 2 * j);
-          if (d.y) f(w[j] >> 16, 2 * j + 1);
-        }
-      }
-    }
-  }
   // On raw bits: the largest lane value read as int16 (the largest positive
   // value, when the lane has one).
   __device__ int raw_max_i16() const {
@@ -191,18 +161,39 @@ template <> struct Chunk<uint16_t> {
     for (int j = 1; j < W; ++j) m = __builtin_elementwise_max(m, __builtin_bit_cast(s16x2, w[j]));
     return max((int)m.x, (int)m.y);
   }
-  // On raw bits (before make_keys): calls f(key, value index) for every
-  // positive value whose bits, read as int16, are >= r (1 <= r <= 0x7fff).
-  // A positive value's key is bits | 0x8000, so this selects key >= r + 0x8000;
-  // negative values (int16 < 0) never pass.  One packed signed max tests two
-  // values.
   static constexpr bool kHasRawFilter = true;
-  // Same group pre-test as for_each_ge.
-  template <class F> __device__ void for_each_raw_ge(uint32_t r, F&& f) const {
+  // Wave-uniform scans.  The group pre-test is taken for the whole wave (a
+  // ballot), and f(pass, key, value index) is called by every lane for every
+  // value of a group where some lane holds a survivor, so f may use ballots.
+  // scan_ge: keys >= tau (1 <= tau < 0x10000).  scan_raw_ge (before
+  // make_keys): positive values whose bits, read as int16, are >= r
+  // (1 <= r <= 0x7fff), i.e. key >= r + 0x8000; negative values never pass.
+  template <class F> __device__ void scan_ge(uint64_t tau, F&& f) const {
+    const uint32_t t1 = (uint32_t)(tau - 1);
+    u16x2 gm[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      gm[g] = __builtin_bit_cast(u16x2, w[8 * g]);
+#pragma unroll
+      for (int j = 1; j < 8; ++j) gm[g] = __builtin_elementwise_max(gm[g], __builtin_bit_cast(u16x2, w[8 * g + j]));
+    }
+    const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(gm[0], gm[1]),
+                                              __builtin_elementwise_max(gm[2], gm[3]));
+    if (__ballot(max((uint32_t)m.x, (uint32_t)m.y) > t1) == 0) return;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (__ballot(max((uint32_t)gm[g].x, (uint32_t)gm[g].y) > t1) == 0) continue;
+#pragma unroll
+      for (int j = 8 * g; j < 8 * g + 8; ++j) {
+        const uint32_t lo = w[j] & 0xffffu, hi = w[j] >> 16;
+        f(lo > t1, lo, 2 * j);
+        f(hi > t1, hi, 2 * j + 1);
+      }
+    }
+  }
+  template <class F> __device__ void scan_raw_ge(uint32_t r, F&& f) const {
     typedef short s16x2 __attribute__((ext_vector_type(2)));
     const short r1 = (short)(r - 1);
-    const s16x2 t = {r1, r1};
-    const uint32_t t32 = __builtin_bit_cast(uint32_t, t);
     s16x2 gm[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -212,18 +203,15 @@ template <> struct Chunk<uint16_t> {
     }
     const s16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(gm[0], gm[1]),
                                               __builtin_elementwise_max(gm[2], gm[3]));
-    if (max(m.x, m.y) <= r1) return;
+    if (__ballot(max(m.x, m.y) > r1) == 0) return;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      if (max(gm[g].x, gm[g].y) <= r1) continue;
+      if (__ballot(max(gm[g].x, gm[g].y) > r1) == 0) continue;
 #pragma unroll
       for (int j = 8 * g; j < 8 * g + 8; ++j) {
         const s16x2 x = __builtin_bit_cast(s16x2, w[j]);
-        const s16x2 mx = __builtin_elementwise_max(x, t);
-        if (__builtin_bit_cast(uint32_t, mx) != t32) {
-          if (x.x > r1) f((w[j] & 0xffffu) | 0x8000u, 2 * j);
-          if (x.y > r1) f((w[j] >> 16) | 0x8000u, 2 * j + 1);
-        }
+        f(x.x > r1, (w[j] & 0xffffu) | 0x8000u, 2 * j);
+        f(x.y > r1, (w[j] >> 16) | 0x8000u, 2 * j + 1);
       }
     }
   }
@@ -237,7 +225,7 @@ template <> struct Chunk<float> {
   static constexpr int VEC = 4, L = kPerLane / VEC;
   uint32_t w[kPerLane];
 
-  __device__ void issue(const float* rowp, int64_t lb, int64_t valid) {
+  __device__ __forceinline__ void issue(const float* rowp, int64_t lb, int64_t valid) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
       const int64_t e0 = lb + l * vec_stride<VEC>();
@@ -245,7 +233,7 @@ template <> struct Chunk<float> {
       w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
     }
   }
-  __device__ void issue_clamped(const float* rowp, int32_t lb, int32_t last_vec) {
+  __device__ __forceinline__ void issue_clamped(const float* rowp, int32_t lb, int32_t last_vec) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
       const int32_t e0 = min(lb + l * (int32_t)vec_stride<VEC>(), last_vec);
@@ -254,11 +242,11 @@ template <> struct Chunk<float> {
       w[l * 4 + 0] = r.x; w[l * 4 + 1] = r.y; w[l * 4 + 2] = r.z; w[l * 4 + 3] = r.w;
     }
   }
-  __device__ void keys_full() {
+  __device__ __forceinline__ void keys_full() {
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) w[j] = f32_key(w[j]);
   }
-  __device__ void make_keys(const float* rowp, int64_t lb, int64_t valid) {
+  __device__ __forceinline__ void make_keys(const float* rowp, int64_t lb, int64_t valid) {
 #pragma unroll
     for (int l = 0; l < L; ++l) {
       const int64_t e0 = lb + l * vec_stride<VEC>();
@@ -274,8 +262,11 @@ template <> struct Chunk<float> {
     for (int j = 0; j < kPerLane; ++j) m = max(m, w[j]);
     return m;
   }
-  // Group pre-test as in the bf16 chunk: eight groups of eight keys.
-  template <class F> __device__ void for_each_ge(uint64_t tau, F&& f) const {
+  static constexpr bool kHasRawFilter = false;
+  __device__ int raw_max_i16() const { return 0; }
+  // Wave-uniform scan as in the bf16 chunk: keys >= tau (eight groups of
+  // eight keys).  There is no raw scan for fp32.
+  template <class F> __device__ void scan_ge(uint64_t tau, F&& f) const {
     uint32_t gm[8];
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
@@ -286,18 +277,15 @@ template <> struct Chunk<float> {
     uint32_t m = gm[0];
 #pragma unroll
     for (int g = 1; g < 8; ++g) m = max(m, gm[g]);
-    if ((uint64_t)m < tau) return;
+    if (__ballot((uint64_t)m >= tau) == 0) return;
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      if ((uint64_t)gm[g] < tau) continue;
+      if (__ballot((uint64_t)gm[g] >= tau) == 0) continue;
 #pragma unroll
-      for (int j = 8 * g; j < 8 * g + 8; ++j)
-        if ((uint64_t)w[j] >= tau) f(w[j], j);
+      for (int j = 8 * g; j < 8 * g + 8; ++j) f((uint64_t)w[j] >= tau, w[j], j);
     }
   }
-  static constexpr bool kHasRawFilter = false;
-  __device__ int raw_max_i16() const { return 0; }
-  template <class F> __device__ void for_each_raw_ge(uint32_t, F&&) const {}
+  template <class F> __device__ void scan_raw_ge(uint32_t, F&&) const {}
   static constexpr uint64_t kKeyLimit = 0x100000000ull;
   static constexpr int kKeyBits = 32;
   __device__ static uint32_t key_at(const float* p) { return f32_key(__float_as_uint(*p)); }
@@ -305,7 +293,7 @@ template <> struct Chunk<float> {
 };
 
 struct WaveLds {
-  uint64_t pool[kMaxK + kWaveCap];   // [0, nbest): held best (sorted); then new candidates
+  uint64_t pool[kMaxK + kWaveCap];   // a chunk's survivors; at the end the sorted best
   uint64_t tmp[kMaxK];
   uint32_t count;
   uint32_t nbest;
@@ -313,6 +301,10 @@ struct WaveLds {
 
 struct Shared {
   WaveLds wave[kWaves];
+  // Largest K-th held key of any wave of the workgroup: K values of the row
+  // reach it, so every wave may drop values below it (not ties: another
+  // wave's values can have smaller ids).
+  uint32_t bound;
 };
 
 template <int VEC>
@@ -382,33 +374,6 @@ __device__ __noinline__ uint32_t narrow_exact(const TIO* rowp, int64_t lb, int64
 }
 
 
-// Merge n new candidates pool[nb, nb + n) into the held sorted list
-// pool[0, nb) and keep the best min(nb + n, K), sorted, in pool[0, ...).
-// A held entry's new rank is its index plus the new candidates above it; a
-// new candidate's rank is a binary search in the held list plus the new
-// candidates above it (composites are unique, so ranks are distinct).
-__device__ void keep_best(WaveLds& wl, int nb, int n, int K, int lane) {
-  const uint64_t* held = wl.pool;
-  const uint64_t* fresh = wl.pool + nb;
-  for (int i = lane; i < nb; i += 64) {
-    const uint64_t c = held[i];
-    int rank = i;
-    for (int j = 0; j < n; ++j) rank += (fresh[j] > c) ? 1 : 0;
-    if (rank < K) wl.tmp[rank] = c;
-  }
-  for (int i = lane; i < n; i += 64) {
-    const uint64_t c = fresh[i];
-    int rank = count_greater(held, nb, c);
-    for (int j = 0; j < n; ++j) rank += (fresh[j] > c) ? 1 : 0;
-    if (rank < K) wl.tmp[rank] = c;
-  }
-  wave_sync();
-  const int m = nb + n < K ? nb + n : K;
-  for (int i = lane; i < m; i += 64) wl.pool[i] = wl.tmp[i];
-  wave_sync();
-}
-
-
 // K-th largest of the 64 lane values m (unsigned, below 2^bits): the largest
 // t with #{lanes : m >= t} >= K, found bit by bit with ballot counts.  Those
 // K lanes each hold a distinct value >= t.  Returns 0 when fewer than K
@@ -422,7 +387,7 @@ __device__ __forceinline__ uint32_t kth_largest_lane(uint32_t m, int K, int bits
   return t;
 }
 
-template <typename TIO>
+template <typename TIO, int NBUF>
 __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, int64_t row_stride,
                                                int64_t valid_vocab, int32_t K, int32_t wchunks, int32_t segs,
                                                int32_t wchunks_per_seg, float mult, float cap,
@@ -440,29 +405,79 @@ __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, i
   const int c_end = min(wchunks, c_begin + wchunks_per_seg);
   const TIO* rowp = logits + row * row_stride;
 
-  int nbest = 0;                                 // held best composites (wave-uniform)
+  // The wave's sorted best composites live in registers: lane i < nbest holds
+  // the i-th (hv); nbest and the K-th key are wave-uniform.
+  int nbest = 0;
+  uint64_t hv = 0;
+  uint32_t kth_key = 0;                          // key of the K-th held one once nbest == K
+  int n_new = 0;                                 // this chunk's survivors in wl.pool[0, n_new) (wave-uniform)
+  if (threadIdx.x == 0) sh.bound = 0;
+  __syncthreads();
+  // The workgroup's shared bound (a key; 0 = none yet), read without ordering:
+  // any value another wave has published is valid.
+  auto shared_bound = [&]() -> uint32_t {
+    return __builtin_amdgcn_readfirstlane(__hip_atomic_load(&sh.bound, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_WORKGROUP));
+  };
+  // (readlane returns a signed int: widen each half through uint32_t)
+  auto readlane64 = [](uint64_t v, int j) -> uint64_t {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), j) << 32) |
+           (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, j);
+  };
 
   constexpr int VEC = Chunk<TIO>::VEC;
-  // Appends a survivor (key, value index i of the lane's values) behind the held best.
-  auto push = [&](uint32_t k, int i, uint32_t id_base) {
-    const uint32_t pos = atomicAdd(&wl.count, 1u);
-    // ids < 2^24: the 32-bit lane base plus the value's compile-time offset
-    const uint32_t id = id_base + (uint32_t)((i / VEC) * vec_stride<VEC>() + i % VEC);
-    if (pos < (uint32_t)kWaveCap) wl.pool[nbest + pos] = ((uint64_t)k << 24) | (uint64_t)(kIdMask - id);
+  // Called by every lane (uniform control flow) for one value index i of the
+  // lane's values: the lanes where it passes append its composite to
+  // wl.pool[n_new, ...) in lane order (slots from a ballot count, no atomics).
+  auto push = [&](bool pass, uint32_t k, int i, uint32_t id_base) {
+    const uint64_t m = __ballot(pass);
+    if (m == 0) return;
+    if (pass) {
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint32_t pos = (uint32_t)n_new + below;
+      // ids < 2^24: the 32-bit lane base plus the value's compile-time offset
+      const uint32_t id = id_base + (uint32_t)((i / VEC) * vec_stride<VEC>() + i % VEC);
+      if (pos < (uint32_t)kWaveCap) wl.pool[pos] = ((uint64_t)k << 24) | (uint64_t)(kIdMask - id);
+    }
+    n_new += (int)__popcll(m);
   };
   // After the survivors of one chunk are in the pool: exact narrowing if they
-  // overflowed, then keep the wave's K best.
+  // overflowed, then merge them into the held list, 64 at a time (one per
+  // lane).  Ranks: a held entry's is its index plus the new ones above it; a
+  // new one's is the held ones above it plus the new ones above it (counted
+  // with readlane over the lanes, no LDS reads); composites are unique, so
+  // ranks are distinct.  The K best are reordered through LDS.  A chunk
+  // without survivors costs nothing here.
   auto update = [&](int64_t lb, int64_t c_start) {
+    if (n_new == 0) return;
+    if (n_new > kWaveCap) n_new = (int)narrow_exact<TIO>(rowp, lb, c_start, valid_vocab, lane, K, 0, wl);
     wave_sync();
-    uint32_t n = __builtin_amdgcn_readfirstlane(wl.count);
-    if (n > (uint32_t)kWaveCap) n = narrow_exact<TIO>(rowp, lb, c_start, valid_vocab, lane, K, nbest, wl);
-    if (n > 0) {
-      keep_best(wl, nbest, (int)n, K, lane);
-      nbest = min(K, nbest + (int)n);
+    for (int b0 = 0; b0 < n_new; b0 += 64) {
+      const int m = min(64, n_new - b0);
+      const uint64_t cv = lane < m ? wl.pool[b0 + lane] : 0ull;
+      int rank_h = lane, rank_c = 0;
+      for (int j = 0; j < m; ++j) {
+        const uint64_t cj = readlane64(cv, j);
+        rank_h += cj > hv ? 1 : 0;
+        rank_c += cj > cv ? 1 : 0;
+      }
+      for (int j = 0; j < nbest; ++j) rank_c += readlane64(hv, j) > cv ? 1 : 0;
+      if (lane < nbest && rank_h < K) wl.tmp[rank_h] = hv;
+      if (lane < m && rank_c < K) wl.tmp[rank_c] = cv;
+      wave_sync();
+      nbest = min(K, nbest + m);
+      hv = lane < nbest ? wl.tmp[lane] : 0ull;
+      wave_sync();
+    }
+    n_new = 0;
+    if (nbest == K) {
+      kth_key = composite_key(readlane64(hv, K - 1));
+      if (lane == 0) atomicMax(&sh.bound, kth_key);
     }
   };
   // General path: `ch` holds keys.  Threshold, compaction, update.
   auto process_keys = [&](const Chunk<TIO>& ch, int64_t lb, int64_t c_start) {
+    const uint32_t sb = shared_bound();
     uint64_t tau;
     if (nbest < K) {
       // K-th largest lane maximum: at least K values reach it (key 0 =
@@ -472,11 +487,11 @@ __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, i
     } else {
       // a later value has a larger id than every held one: it must beat the
       // K-th key strictly
-      tau = (uint64_t)composite_key(wl.pool[K - 1]) + 1;
+      tau = (uint64_t)kth_key + 1;
     }
-    if (lane == 0) wl.count = 0;
-    wave_sync();
-    if (tau < Chunk<TIO>::kKeyLimit) ch.for_each_ge(tau, [&](uint32_t k, int i) { push(k, i, (uint32_t)lb); });
+    if ((uint64_t)sb > tau) tau = sb;
+    if (tau < Chunk<TIO>::kKeyLimit)
+      ch.scan_ge(tau, [&](bool pass, uint32_t k, int i) { push(pass, k, i, (uint32_t)lb); });
     update(lb, c_start);
   };
   // One full chunk whose raw bits are in `ch`.  bf16: while the threshold is
@@ -484,20 +499,21 @@ __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, i
   // survivors); otherwise the chunk goes through the key path.
   auto process_full = [&](Chunk<TIO>& ch, int64_t lb, int64_t c_start) {
     if (Chunk<TIO>::kHasRawFilter) {
+      // key bound (values below it are dropped): the workgroup's, or the
+      // wave's own K-th key + 1 (strict, as above) when that is higher
+      uint32_t tau = shared_bound();
+      if (nbest == K && kth_key + 1 > tau) tau = kth_key + 1;
       int r = 0;                                                 // raw int16 threshold, >= 1 when usable
-      if (nbest == K) {
-        const uint32_t tau = composite_key(wl.pool[K - 1]) + 1;   // strict, as above
-        if (tau > 0x8000u && tau < 0x10000u) r = (int)(tau - 0x8000u);
-      } else if (nbest == 0) {
+      if (tau > 0x8000u && tau < 0x10000u) {
+        r = (int)(tau - 0x8000u);
+      } else if (nbest == 0 && tau <= 0x8000u) {
         // first chunk: K-th largest positive raw lane maximum (a positive
         // int16 orders like its value); 0 when fewer than K lanes hold a
         // positive value
         r = (int)kth_largest_lane((uint32_t)max(ch.raw_max_i16(), 0), K, 15);
       }
       if (r >= 1) {
-        if (lane == 0) wl.count = 0;
-        wave_sync();
-        ch.for_each_raw_ge((uint32_t)r, [&](uint32_t k, int i) { push(k, i, (uint32_t)lb); });
+        ch.scan_raw_ge((uint32_t)r, [&](bool pass, uint32_t k, int i) { push(pass, k, i, (uint32_t)lb); });
         update(lb, c_start);
         return;
       }
@@ -526,24 +542,48 @@ __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, i
   Chunk<TIO> tail;
   bool tail_loaded = false;
   if (c < full_end) {
-    // two buffers, alternating roles, so that no chunk is copied
-    Chunk<TIO> a, b;
-    bool in_b = false;                            // where the chunk prefetched past the loop sits
-    a.issue_clamped(rowp, c * kGroupChunk + wave_off32, last_vec);
-    while (true) {
-      int cn = c + 1 < pre_end ? c + 1 : c;
-      b.issue_clamped(rowp, cn * kGroupChunk + wave_off32, last_vec);
-      process_full(a, (int64_t)c * kGroupChunk + wave_off, (int64_t)c * kGroupChunk);
-      if (++c >= full_end) { in_b = true; break; }
-      cn = c + 1 < pre_end ? c + 1 : c;
-      a.issue_clamped(rowp, cn * kGroupChunk + wave_off32, last_vec);
-      process_full(b, (int64_t)c * kGroupChunk + wave_off, (int64_t)c * kGroupChunk);
-      if (++c >= full_end) break;
-    }
-    if (pre_end > full_end) {
+    // NBUF register buffers in a ring, roles rotating so that no chunk is
+    // copied: while one chunk is processed, the next NBUF - 1 are in flight.
+    // Chunk indices past the prefetch end re-read its last one (a cache hit).
+    auto idx = [&](int k) { return k < pre_end ? k : pre_end - 1; };
+    int tail_in = 0;                              // the buffer holding the prefetched partial chunk
+    if constexpr (NBUF == 3) {
+      Chunk<TIO> a, b, d;
+      a.issue_clamped(rowp, c * kGroupChunk + wave_off32, last_vec);
+      b.issue_clamped(rowp, idx(c + 1) * kGroupChunk + wave_off32, last_vec);
+      while (true) {
+        d.issue_clamped(rowp, idx(c + 2) * kGroupChunk + wave_off32, last_vec);
+        process_full(a, (int64_t)c * kGroupChunk + wave_off, (int64_t)c * kGroupChunk);
+        if (++c >= full_end) { tail_in = 1; break; }
+        a.issue_clamped(rowp, idx(c + 2) * kGroupChunk + wave_off32, last_vec);
+        process_full(b, (int64_t)c * kGroupChunk + wave_off, (int64_t)c * kGroupChunk);
+        if (++c >= full_end) { tail_in = 2; break; }
+        b.issue_clamped(rowp, idx(c + 2) * kGroupChunk + wave_off32, last_vec);
+        process_full(d, (int64_t)c * kGroupChunk + wave_off, (int64_t)c * kGroupChunk);
+        if (++c >= full_end) { tail_in = 0; break; }
+      }
+      if (pre_end > full_end) {
 #pragma unroll
-      for (int j = 0; j < (int)(sizeof(tail.w) / sizeof(tail.w[0])); ++j) tail.w[j] = in_b ? b.w[j] : a.w[j];
-      tail_loaded = true;
+        for (int j = 0; j < (int)(sizeof(tail.w) / sizeof(tail.w[0])); ++j)
+          tail.w[j] = tail_in == 0 ? a.w[j] : tail_in == 1 ? b.w[j] : d.w[j];
+        tail_loaded = true;
+      }
+    } else {
+      Chunk<TIO> a, b;
+      a.issue_clamped(rowp, c * kGroupChunk + wave_off32, last_vec);
+      while (true) {
+        b.issue_clamped(rowp, idx(c + 1) * kGroupChunk + wave_off32, last_vec);
+        process_full(a, (int64_t)c * kGroupChunk + wave_off, (int64_t)c * kGroupChunk);
+        if (++c >= full_end) { tail_in = 1; break; }
+        a.issue_clamped(rowp, idx(c + 1) * kGroupChunk + wave_off32, last_vec);
+        process_full(b, (int64_t)c * kGroupChunk + wave_off, (int64_t)c * kGroupChunk);
+        if (++c >= full_end) { tail_in = 0; break; }
+      }
+      if (pre_end > full_end) {
+#pragma unroll
+        for (int j = 0; j < (int)(sizeof(tail.w) / sizeof(tail.w[0])); ++j) tail.w[j] = tail_in == 1 ? b.w[j] : a.w[j];
+        tail_loaded = true;
+      }
     }
   }
   if (c < c_end) {                               // the partial last group-chunk of the row
@@ -555,6 +595,7 @@ __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, i
     tail.make_keys(rowp, c_start + wave_off, valid_vocab);
     process_keys(tail, c_start + wave_off, c_start);
   }
+  if (lane < nbest) wl.pool[lane] = hv;         // the sorted list, for the merge below
   if (lane == 0) wl.nbest = (uint32_t)nbest;
   __syncthreads();
 
@@ -592,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 4) void topk_rows_bf16(const uint16_t* __
                                                             float cap, uint64_t* __restrict__ parts,
                                                             int64_t* __restrict__ ids_out,
                                                             float* __restrict__ unary_out) {
-  topk_rows_body<uint16_t>(logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap, parts,
+  topk_rows_body<uint16_t, 2>(logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap, parts,
                            ids_out, unary_out);
 }
 __global__ __launch_bounds__(kThreads) void topk_rows_f32(const float* __restrict__ logits, int64_t row_stride,
@@ -601,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_f32(const float* __restric
                                                           float cap, uint64_t* __restrict__ parts,
                                                           int64_t* __restrict__ ids_out,
                                                           float* __restrict__ unary_out) {
-  topk_rows_body<float>(logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap, parts,
+  topk_rows_body<float, 2>(logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap, parts,
                         ids_out, unary_out);
 }
 
