@@ -56,7 +56,7 @@ constexpr int kMaxTopK = 32;   // DFLASH_MAX_TOP_K
 // sums are added by the consumer, in slice order).  Few: the consumer loads
 // and adds every slice of each value it needs, and the projection runs beside
 // the top-K, off the critical path, so more workgroups would not pay.
-constexpr int kMaxProjSplit = 8;
+constexpr int kMaxProjSplit = 16;
 // The partials are stored slice-minor, [n_rows][rank][kstride]: the slices of
 // one output sit together, kstride = ksplit rounded up to a multiple of 4
 // (one 16-byte vector per 4 slices; the padding is never read as a value).

@@ -156,14 +156,19 @@ __global__ __launch_bounds__(kThreads) void proj_f32_kernel(const float* __restr
 // put other loads between the two and pay one memory round trip for all.
 __device__ __forceinline__ void load_proj_slices(const float* __restrict__ u_parts, int ksplit, int r, int64_t n,
                                                  int k, float (&v)[kMaxProjSplit]) {
-  static_assert(kMaxProjSplit == 8, "two 16-byte vectors of slices at most");
-  const float4* base = reinterpret_cast<const float4*>(u_parts + (n * r + k) * (int64_t)proj_slice_stride(ksplit));
-  // both loads unconditional (the second re-reads the first vector when there
-  // are 4 slices or fewer), so neither waits for the other
-  const float4 a = base[0];
-  const float4 b = base[ksplit > 4 ? 1 : 0];
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  constexpr int NV = kMaxProjSplit / 4;
+  const int nv = proj_slice_stride(ksplit) / 4;   // 16-byte vectors holding slices
+  const float4* base = reinterpret_cast<const float4*>(u_parts + (n * r + k) * (int64_t)(4 * nv));
+  // every load unconditional (a vector past the last re-reads it), so none
+  // waits for another
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    const float4 a = base[q < nv ? q : nv - 1];
+    v[4 * q] = a.x;
+    v[4 * q + 1] = a.y;
+    v[4 * q + 2] = a.z;
+    v[4 * q + 3] = a.w;
+  }
 }
 
 __device__ __forceinline__ float add_proj_slices(const float (&v)[kMaxProjSplit], int ksplit) {
