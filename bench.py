@@ -58,9 +58,19 @@ def algorithmic_bytes(w):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "topk_traffic.json")
-# the top-K kernel's sources: its own file and the device helpers it inlines
+# the first-stage kernel's sources: the top-K file and the device code it
+# inlines (the conv + slot projection workgroups share its launch)
 TOPK_SOURCES = tuple(os.path.join(ROOT, "block_draft_proposal_amd", "csrc", f)
-                     for f in ("topk.hip", "device_common.h"))
+                     for f in ("topk.hip", "device_common.h", "conv_slot_proj.h", "conv_core.h", "gemm_tile.h"))
+
+
+def single_launch_stage1(w) -> bool:
+    """Whether dflash_propose_block runs the conv and the slot projection as
+    workgroups of the top-K's launch (bf16, blocks of 16 tokens, <= 8 taps,
+    one group per 16-byte vector, rank <= 128, fewer than 4096 slot rows);
+    otherwise they run beside it on a second stream."""
+    return (w.dtype == "bf16" and w.block_size == 16 and 1 <= w.taps <= 8 and w.group_size % 8 == 0
+            and w.rank <= 128 and w.n_slot_rows < 4096)
 
 
 def sources_sha256(paths) -> str:
@@ -440,8 +450,17 @@ def main():
     avg_ms = [sum(x[k] for x in stage_ms) / n_stage for k in range(4)]
     avg_ms[1] = topk_ms
     nbytes = algorithmic_bytes(w)
-    topk_gbs = nbytes["topk"] / (avg_ms[1] * 1e-3) / 1e9
-    conv_gbs = nbytes["conv"] / (avg_ms[0] * 1e-3) / 1e9
+    fused = single_launch_stage1(w)
+    # the dominant kernel: the first stage (top-K, plus conv and slot
+    # projection when they share its launch: x, base, delta and P read,
+    # conv_out and u written)
+    if fused:
+        stage1_bytes = (nbytes["topk"] + nbytes["conv"] + w.rank * w.hidden * w.elem_bytes
+                        + 4 * w.n_slot_rows * w.rank)
+        stage1_name = "topk_conv_proj_bf16 (top-K + conv + slot projection)"
+    else:
+        stage1_bytes, stage1_name = nbytes["topk"], "topk_rows"
+    topk_gbs = stage1_bytes / (avg_ms[1] * 1e-3) / 1e9
     tokens = w.n_slot_rows * args.steps
     line = {
         "metric": METRIC,
@@ -460,15 +479,15 @@ def main():
                    "groups": w.groups, "taps": w.taps, "vocab": w.vocab, "valid_vocab": w.valid_vocab,
                    "top_k": w.top_k, "rank": w.rank, "draft_tokens_per_step": w.n_slot_rows,
                    "input_sets": n_sets},
-        "roofline": {"bound": "hbm", "kernel": "topk_kernel", "achieved": topk_gbs, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": stage1_name, "achieved": topk_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": topk_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
-                     "algorithmic_bytes_per_launch": nbytes["topk"], "avg_launch_us": avg_ms[1] * 1e3},
-        "conv_hbm": {"achieved": conv_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": conv_gbs / HBM_PEAK_GBS,
-                     "algorithmic_bytes_per_launch": nbytes["conv"], "avg_launch_us": avg_ms[0] * 1e3},
+                     "algorithmic_bytes_per_launch": stage1_bytes, "avg_launch_us": avg_ms[1] * 1e3},
         "stage_us": {"conv": avg_ms[0] * 1e3, "topk": avg_ms[1] * 1e3, "proj": avg_ms[2] * 1e3,
                      "lattice_walk": avg_ms[3] * 1e3, "note": f"top-K from every {TIMED_EVERY}th timed step, the other stages "
-                     f"from {n_stage} further steps with all stage events; conv and projection run "
-                     "beside the top-K on a second stream"},
+                     f"from {n_stage} further steps with all stage events; "
+                     + ("conv and projection are workgroups of the top-K's launch (their events bracket it; "
+                        "the projection stage is empty)" if fused else
+                        "conv and projection run beside the top-K on a second stream")},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -528,40 +528,51 @@ int dflash_propose_block(const dflash_draft_config* cfg, const dflash_block_args
     return fail(DFLASH_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", who);
 
   hipStream_t s = as_hip(stream);
-  ForkJoin* fj = nullptr;
-  if ((st = fork_join(&fj, who)) != DFLASH_OK) return st;
-  hipStream_t aux = fj->aux;
   char* ws = static_cast<char*>(a->workspace);
   float* scores = a->scores_out ? a->scores_out : reinterpret_cast<float*>(ws + L.scores_off);
   void* const* ev = a->stage_events;
-
-  // fork: the auxiliary stream starts after the work already on `stream`
-  if ((st = stream_op(hipEventRecord(fj->fork, s), who)) != DFLASH_OK) return st;
-  // stage 1 on `stream`: transform + top-K
-  if ((st = record(ev, 2, s)) != DFLASH_OK) return st;
   dflash::TopkArgs ta{a->logits, a->logits_row_stride, rows, a->vocab, a->valid_vocab, K, cfg->output_multiplier,
                       cfg->final_logit_softcapping, a->dtype, a->ids_out, a->unary_out, a->workspace};
-  if ((st = launch_status(dflash::launch_topk(ta, L.topk, s), who)) != DFLASH_OK) return st;
-  if ((st = record(ev, 3, s)) != DFLASH_OK) return st;
-  // stages 0 and 2 on the auxiliary stream: conv, then the projection of the
-  // slot rows of its output
-  if ((st = stream_op(hipStreamWaitEvent(aux, fj->fork, 0), who)) != DFLASH_OK) return st;
-  if ((st = record(ev, 0, aux)) != DFLASH_OK) return st;
   dflash::ConvArgs ca{a->x, a->conv_base, a->conv_delta, a->delta_row_stride, a->conv_out, N, H, gs, T, B,
                       a->dtype};
-  if ((st = launch_status(dflash::launch_conv(ca, aux), who)) != DFLASH_OK) return st;
-  if ((st = record(ev, 1, aux)) != DFLASH_OK) return st;
   const dflash::ProjPlan pp = dflash::plan_proj((int32_t)rows, r, H, a->dtype);
   const void* hidden = static_cast<const char*>(a->conv_out) + (size_t)H * (a->dtype == DFLASH_BF16 ? 2 : 4);
   dflash::SelectArgs sa{a->ids_out, a->unary_out, hidden, (int64_t)B * H, (int64_t)H, a->anchor_ids, a->sel_a,
                         a->sel_b, a->proj, a->n_req, S, K, H, r, a->vocab, a->dtype,
                         reinterpret_cast<float*>(ws + L.proj_off), scores};
-  if ((st = record(ev, 4, aux)) != DFLASH_OK) return st;
-  if ((st = launch_status(dflash::launch_proj(sa, pp, aux), who)) != DFLASH_OK) return st;
-  if ((st = record(ev, 5, aux)) != DFLASH_OK) return st;
-  // join: `stream` waits for the auxiliary chain
-  if ((st = stream_op(hipEventRecord(fj->join, aux), who)) != DFLASH_OK) return st;
-  if ((st = stream_op(hipStreamWaitEvent(s, fj->join, 0), who)) != DFLASH_OK) return st;
+  if (dflash::conv_slot_proj_fits(ca, sa, pp)) {
+    // stages 0-2 in one launch on `stream`: the conv and the slot projection
+    // as workgroups beside the top-K's (their stage events bracket it)
+    if ((st = record(ev, 0, s)) != DFLASH_OK) return st;
+    if ((st = record(ev, 2, s)) != DFLASH_OK) return st;
+    if ((st = launch_status(dflash::launch_topk_conv_proj(ta, L.topk, ca, sa, pp, s), who)) != DFLASH_OK) return st;
+    if ((st = record(ev, 1, s)) != DFLASH_OK) return st;
+    if ((st = record(ev, 3, s)) != DFLASH_OK) return st;
+    if ((st = record(ev, 4, s)) != DFLASH_OK) return st;
+    if ((st = record(ev, 5, s)) != DFLASH_OK) return st;
+  } else {
+    ForkJoin* fj = nullptr;
+    if ((st = fork_join(&fj, who)) != DFLASH_OK) return st;
+    hipStream_t aux = fj->aux;
+    // fork: the auxiliary stream starts after the work already on `stream`
+    if ((st = stream_op(hipEventRecord(fj->fork, s), who)) != DFLASH_OK) return st;
+    // stage 1 on `stream`: transform + top-K
+    if ((st = record(ev, 2, s)) != DFLASH_OK) return st;
+    if ((st = launch_status(dflash::launch_topk(ta, L.topk, s), who)) != DFLASH_OK) return st;
+    if ((st = record(ev, 3, s)) != DFLASH_OK) return st;
+    // stages 0 and 2 on the auxiliary stream: conv, then the projection of
+    // the slot rows of its output
+    if ((st = stream_op(hipStreamWaitEvent(aux, fj->fork, 0), who)) != DFLASH_OK) return st;
+    if ((st = record(ev, 0, aux)) != DFLASH_OK) return st;
+    if ((st = launch_status(dflash::launch_conv(ca, aux), who)) != DFLASH_OK) return st;
+    if ((st = record(ev, 1, aux)) != DFLASH_OK) return st;
+    if ((st = record(ev, 4, aux)) != DFLASH_OK) return st;
+    if ((st = launch_status(dflash::launch_proj(sa, pp, aux), who)) != DFLASH_OK) return st;
+    if ((st = record(ev, 5, aux)) != DFLASH_OK) return st;
+    // join: `stream` waits for the auxiliary chain
+    if ((st = stream_op(hipEventRecord(fj->join, aux), who)) != DFLASH_OK) return st;
+    if ((st = stream_op(hipStreamWaitEvent(s, fj->join, 0), who)) != DFLASH_OK) return st;
+  }
   // stage 3 on `stream`: lattice + walk (one kernel when a request's lattice fits in LDS)
   if ((st = record(ev, 6, s)) != DFLASH_OK) return st;
   dflash::WalkArgs wa{scores, a->ids_out, a->uniforms, a->temperatures, a->greedy_mask, a->n_req, S, K,

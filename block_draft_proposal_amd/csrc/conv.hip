@@ -13,6 +13,7 @@
 // registers.  Lanes of a wave hold consecutive channel vectors of the same
 // token, so every load and store of a wave is one contiguous 1 KiB (bf16)
 // segment.
+#include "conv_core.h"
 #include "dflash.h"
 #include "dflash_internal.h"
 
@@ -29,12 +30,7 @@ __device__ __forceinline__ void load_vec(const TIO* p, float (&o)[Elem<TIO>::kVe
 }
 
 __device__ __forceinline__ void store_vec(uint16_t* p, const float (&a)[8]) {
-  uint4 v;
-  v.x = f32_to_bf16_rne(a[0]) | (f32_to_bf16_rne(a[1]) << 16);
-  v.y = f32_to_bf16_rne(a[2]) | (f32_to_bf16_rne(a[3]) << 16);
-  v.z = f32_to_bf16_rne(a[4]) | (f32_to_bf16_rne(a[5]) << 16);
-  v.w = f32_to_bf16_rne(a[6]) | (f32_to_bf16_rne(a[7]) << 16);
-  *reinterpret_cast<uint4*>(p) = v;
+  *reinterpret_cast<uint4*>(p) = pack_bf16x8(a);
 }
 __device__ __forceinline__ void store_vec(float* p, const float (&a)[4]) {
   *reinterpret_cast<float4*>(p) = make_float4(a[0], a[1], a[2], a[3]);
@@ -116,21 +112,17 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const TIO* __restrict__ 
     const int j = j0 + u;
     if (j > jlast) break;
     float acc[VEC];
-#pragma unroll
-    for (int t = 0; t < TAPS; ++t) {
-      if (t > j) break;                           // taps that reach before the block start are zero
-      float bt[VEC], xv[VEC], coef[VEC];
-      unpack16(bw[t], bt);
-      unpack16(xw[u + TAPS - 1 - t], xv);
-      if (ONE_GROUP) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) coef[e] = bt[e] + dv[u][t];
-      } else {
-        add_delta<TIO, false, VEC>(delta + (row0 + j) * g.delta_row_stride, t, g.groups, c0, g.group_size, bt, coef);
-      }
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] = (t == 0) ? coef[e] * xv[e] : fmaf(coef[e], xv[e], acc[e]);
-    }
+    // taps that reach before the block start are zero (not taken)
+    conv_token<VEC, TAPS>(
+        j,
+        [&](int t, float (&coef)[VEC]) {
+          float bt[VEC];
+          unpack16(bw[t], bt);
+          if (ONE_GROUP) coef_one_group<VEC>(bt, dv[u][t], coef);
+          else add_delta<TIO, false, VEC>(delta + (row0 + j) * g.delta_row_stride, t, g.groups, c0, g.group_size, bt,
+                                          coef);
+        },
+        [&](int t, float (&xv)[VEC]) { unpack16(xw[u + TAPS - 1 - t], xv); }, acc);
     store_vec(out + (row0 + j) * H + c0, acc);
   }
 }

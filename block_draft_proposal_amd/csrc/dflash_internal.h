@@ -85,6 +85,14 @@ struct SelectArgs {
   float* scores;            // [n_req, slots, K, K]
 };
 hipError_t launch_proj(const SelectArgs& a, const ProjPlan& p, hipStream_t stream);
+// The propose step's conv and slot-row projection as workgroups of one
+// launch (bf16, blocks of 16, <= 8 taps, one group per vector, few rows);
+// the same conv_out and projection partials as launch_conv followed by
+// launch_proj ...
+bool conv_slot_proj_fits(const ConvArgs& c, const SelectArgs& s, const ProjPlan& p);
+// ... in the top-K's launch: one kernel for the propose step's first stage.
+hipError_t launch_topk_conv_proj(const TopkArgs& a, const TopkPlan& p, const ConvArgs& c, const SelectArgs& s,
+                                 const ProjPlan& pp, hipStream_t stream);
 hipError_t launch_lattice(const SelectArgs& a, const ProjPlan& p, hipStream_t stream);
 
 struct WalkArgs {

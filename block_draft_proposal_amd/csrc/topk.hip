@@ -44,6 +44,7 @@
 //  * The sorted per-wave lists are merged with one barrier: each entry's rank
 //    is its own index plus, per other list, a binary-searched count of larger
 //    entries.
+#include "conv_slot_proj.h"
 #include "dflash.h"
 #include "dflash_internal.h"
 
@@ -387,8 +388,9 @@ __device__ __forceinline__ uint32_t kth_largest_lane(uint32_t m, int K, int bits
   return t;
 }
 
+// One workgroup of the top-K: `block` = row * segs + segment.
 template <typename TIO, int NBUF>
-__device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, int64_t row_stride,
+__device__ __forceinline__ void topk_rows_body(int block, const TIO* __restrict__ logits, int64_t row_stride,
                                                int64_t valid_vocab, int32_t K, int32_t wchunks, int32_t segs,
                                                int32_t wchunks_per_seg, float mult, float cap,
                                                uint64_t* __restrict__ parts, int64_t* __restrict__ ids_out,
@@ -399,8 +401,8 @@ __device__ __forceinline__ void topk_rows_body(const TIO* __restrict__ logits, i
   // tests below are scalar and the loads need no exec masking
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   WaveLds& wl = sh.wave[wave];
-  const int64_t row = blockIdx.x / segs;
-  const int seg = (int)(blockIdx.x % segs);
+  const int64_t row = block / segs;
+  const int seg = (int)(block % segs);
   const int c_begin = seg * wchunks_per_seg;
   const int c_end = min(wchunks, c_begin + wchunks_per_seg);
   const TIO* rowp = logits + row * row_stride;
@@ -633,7 +635,7 @@ __global__ __launch_bounds__(kThreads, 4) void topk_rows_bf16(const uint16_t* __
                                                             float cap, uint64_t* __restrict__ parts,
                                                             int64_t* __restrict__ ids_out,
                                                             float* __restrict__ unary_out) {
-  topk_rows_body<uint16_t, 2>(logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap, parts,
+  topk_rows_body<uint16_t, 2>((int)blockIdx.x, logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap, parts,
                            ids_out, unary_out);
 }
 __global__ __launch_bounds__(kThreads) void topk_rows_f32(const float* __restrict__ logits, int64_t row_stride,
@@ -642,8 +644,28 @@ __global__ __launch_bounds__(kThreads) void topk_rows_f32(const float* __restric
                                                           float cap, uint64_t* __restrict__ parts,
                                                           int64_t* __restrict__ ids_out,
                                                           float* __restrict__ unary_out) {
-  topk_rows_body<float, 2>(logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap, parts,
+  topk_rows_body<float, 2>((int)blockIdx.x, logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap, parts,
                         ids_out, unary_out);
+}
+
+// The propose step's first stage in one launch (bf16): workgroups
+// [0, groups_x * ksplit) compute the conv and the slot projection
+// (conv_slot_proj.h), the rest the top-K rows.  Neither part reads what the
+// other writes, so they run side by side without a second stream; the
+// projection's workgroups come first so that they are dispatched first.
+template <int TAPS, int RT>
+__global__ __launch_bounds__(kThreads, 2) void topk_conv_proj_bf16(
+    const uint16_t* __restrict__ logits, int64_t row_stride, int64_t valid_vocab, int32_t K, int32_t wchunks,
+    int32_t segs, int32_t wchunks_per_seg, float mult, float cap, uint64_t* __restrict__ parts,
+    int64_t* __restrict__ ids_out, float* __restrict__ unary_out, SlotProjArgs sp) {
+  const int b = (int)blockIdx.x;
+  const int n_sp = sp.groups_x * sp.ksplit;
+  if (b < n_sp) {
+    conv_slot_proj_group<TAPS, RT>(b % sp.groups_x, b / sp.groups_x, sp);
+    return;
+  }
+  topk_rows_body<uint16_t, 2>(b - n_sp, logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult,
+                              cap, parts, ids_out, unary_out);
 }
 
 // Merge of the per-segment K best (rows split over several workgroups).
@@ -718,6 +740,53 @@ hipError_t launch_topk(const TopkArgs& a, const TopkPlan& p, hipStream_t stream)
   else
     hipLaunchKernelGGL(topk_merge_kernel<float>, dim3((unsigned)p.n_rows), dim3(kMergeThreads), 0, stream,
                        parts, a.top_k, p.segs, a.multiplier, a.softcap, a.ids_out, a.unary_out);
+  return hipGetLastError();
+}
+
+bool conv_slot_proj_fits(const ConvArgs& c, const SelectArgs& s, const ProjPlan& p) {
+  return c.dtype == DFLASH_BF16 && s.dtype == DFLASH_BF16 && c.block_size == kSpBlock && s.slots == kSpBlock - 1 &&
+         c.taps >= 1 && c.taps <= 8 && c.group_size % 8 == 0 && c.hidden % 8 == 0 && p.frags == 1 &&
+         s.rank >= 1 && s.rank <= 128 && c.n_tokens % kSpBlock == 0 && c.n_tokens / kSpBlock == s.n_req;
+}
+
+hipError_t launch_topk_conv_proj(const TopkArgs& a, const TopkPlan& p, const ConvArgs& c, const SelectArgs& s,
+                                 const ProjPlan& pp, hipStream_t stream) {
+  SlotProjArgs sp{static_cast<const uint16_t*>(c.x), static_cast<const uint16_t*>(c.base),
+                  static_cast<const uint16_t*>(c.delta), c.delta_row_stride, static_cast<uint16_t*>(c.out),
+                  (int32_t)(c.n_tokens / kSpBlock), c.hidden, c.group_size, static_cast<const uint16_t*>(s.proj),
+                  s.rank, s.slots, pp.kslice, pp.ksplit, s.u_parts, 0};
+  sp.groups_x = (sp.n_blocks + 3) / 4;
+  const int64_t n_sp = sp.n_blocks > 0 ? (int64_t)sp.groups_x * sp.ksplit : 0;
+  if (n_sp == 0) sp.groups_x = 0;
+  const int64_t n_tk = p.n_rows * p.segs;
+  if (n_sp + n_tk == 0) return hipSuccess;
+  uint64_t* parts = reinterpret_cast<uint64_t*>(static_cast<char*>(a.workspace) + p.parts_offset);
+  const dim3 grid((unsigned)(n_sp + n_tk));
+  const int tiles = s.rank > 64 ? 8 : 4;
+#define DFLASH_TCP(TAPS, RT)                                                                                      \
+  hipLaunchKernelGGL((topk_conv_proj_bf16<TAPS, RT>), grid, dim3(kThreads), 0, stream,                           \
+                     static_cast<const uint16_t*>(a.logits), a.row_stride, a.valid_vocab, a.top_k, p.chunks, p.segs, \
+                     p.chunks_per_seg, a.multiplier, a.softcap, parts, a.ids_out, a.unary_out, sp)
+#define DFLASH_TCP_T(TAPS)                 \
+  if (tiles == 4) DFLASH_TCP(TAPS, 4);     \
+  else DFLASH_TCP(TAPS, 8);
+  switch (c.taps) {
+    case 1: DFLASH_TCP_T(1) break;
+    case 2: DFLASH_TCP_T(2) break;
+    case 3: DFLASH_TCP_T(3) break;
+    case 4: DFLASH_TCP_T(4) break;
+    case 5: DFLASH_TCP_T(5) break;
+    case 6: DFLASH_TCP_T(6) break;
+    case 7: DFLASH_TCP_T(7) break;
+    case 8: DFLASH_TCP_T(8) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef DFLASH_TCP_T
+#undef DFLASH_TCP
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.segs == 1 || p.n_rows == 0) return e;
+  hipLaunchKernelGGL(topk_merge_kernel<uint16_t>, dim3((unsigned)p.n_rows), dim3(kMergeThreads), 0, stream, parts,
+                     a.top_k, p.segs, a.multiplier, a.softcap, a.ids_out, a.unary_out);
   return hipGetLastError();
 }
 

@@ -291,12 +291,16 @@ int dflash_verify(const void* target_logits, int64_t row_stride, int32_t n_req, 
  *   transform + top-K over the slot logits ->
  *   projection of each slot's hidden = conv-output row r*B + 1 + s (block
  *   position 0 is the verified anchor) -> lattice -> walk,
- * ordered on `stream` as one unit.  The conv and the projection, which do
- * not depend on the top-K, run beside it on an auxiliary stream of the
- * library (one per host thread and device, created on the first call with
- * default priority and kept until the process ends) that waits for the work
- * already on `stream` and that `stream` waits for before the lattice: the
- * call's outputs are ready for work enqueued on `stream` after it.  Results
+ * ordered on `stream` as one unit.  The conv and the projection do not
+ * depend on the top-K.  In bf16 with blocks of 16 tokens, at most 8 taps, a
+ * group size that is a multiple of 8, rank <= 128 and fewer than 4096 slot
+ * rows, they run as workgroups of the top-K's launch on `stream` (no second
+ * stream).  Otherwise they run beside the top-K on an auxiliary stream of the
+ * library (one per host thread and device, created on the first such call
+ * with default priority and kept until the process ends) that waits for the
+ * work already on `stream` and that `stream` waits for before the lattice.
+ * Either way the call's outputs are ready for work enqueued on `stream`
+ * after it.  Results
  * equal the chain dflash_conv -> dflash_topk -> dflash_lattice -> dflash_walk
  * on the same inputs bit for bit.
  * cfg: conv and selector must both be enabled; cfg->hidden_size = H. */
@@ -327,7 +331,9 @@ typedef struct {
   /* NULL, or 8 hipEvent_t handles (host array): events[2*k] is recorded before
    * and events[2*k+1] after stage k on the stream that runs it; stages:
    * 0 conv and 2 projection (auxiliary stream), 1 top-K and 3 lattice + walk
-   * (`stream`).  A NULL entry skips that record.  For timing only. */
+   * (`stream`).  When the conv and the projection share the top-K's launch,
+   * stages 0 and 1 both bracket that launch and stage 2 brackets nothing.  A
+   * NULL entry skips that record.  For timing only. */
   void* const* stage_events;
   int32_t n_req;
   int32_t dtype;
