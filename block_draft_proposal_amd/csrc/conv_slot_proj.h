@@ -174,7 +174,10 @@ __device__ __forceinline__ void conv_slot_proj_group(int gx, int split, const Sl
       const int p = 4 * (lane >> 4) + v;
       if (p >= 1 && p <= slots) {
         const int64_t srow = (int64_t)blk * slots + (p - 1);
-        u_parts[(srow * rank + col) * kstride + split] = acc[tt][v];
+        float* dst = u_parts + (srow * rank + col) * kstride;
+        dst[split] = acc[tt][v];
+        if (split == sp.ksplit - 1)
+          for (int q = split + 1; q < kstride; ++q) dst[q] = 0.f;   // pad slots: +0
       }
     }
   }

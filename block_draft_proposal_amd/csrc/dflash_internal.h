@@ -59,7 +59,7 @@ constexpr int kMaxTopK = 32;   // DFLASH_MAX_TOP_K
 constexpr int kMaxProjSplit = 16;
 // The partials are stored slice-minor, [n_rows][rank][kstride]: the slices of
 // one output sit together, kstride = ksplit rounded up to a multiple of 4
-// (one 16-byte vector per 4 slices; the padding is never read as a value).
+// (one 16-byte vector per 4 slices; the padding slots hold +0).
 __host__ __device__ inline int proj_slice_stride(int ksplit) { return (ksplit + 3) & ~3; }
 struct ProjPlan {
   int32_t n_rows, rank, hidden;

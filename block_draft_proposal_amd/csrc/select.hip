@@ -129,7 +129,12 @@ __global__ __launch_bounds__(kThreads) void proj_mfma_kernel(const uint16_t* __r
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = row_base + 16 * f + 4 * (lane >> 4) + v;
-        if (row < n_rows) u_parts[((int64_t)row * rank + col) * kstride + split] = acc[f][t][v];
+        if (row < n_rows) {
+          float* dst = u_parts + ((int64_t)row * rank + col) * kstride;
+          dst[split] = acc[f][t][v];
+          if (split == (int)gridDim.y - 1)
+            for (int sp = split + 1; sp < kstride; ++sp) dst[sp] = 0.f;   // pad slots: +0
+        }
       }
   }
 }
@@ -146,7 +151,9 @@ __global__ __launch_bounds__(kThreads) void proj_f32_kernel(const float* __restr
   const float* p = P + (int64_t)col * H;
   float acc = 0.f;
   for (int k = 0; k < H; ++k) acc = fmaf(h[k], p[k], acc);
-  u_parts[t * proj_slice_stride(1)] = acc;   // one slice, slice-minor layout
+  float* dst = u_parts + t * proj_slice_stride(1);   // one slice, slice-minor layout
+  dst[0] = acc;
+  dst[1] = dst[2] = dst[3] = 0.f;                      // pad slots: +0
 }
 
 // u[n][k] = sum over the projection slices sp = 0..ksplit-1 of the partial
@@ -171,11 +178,24 @@ __device__ __forceinline__ void load_proj_slices(const float* __restrict__ u_par
   }
 }
 
+// Adds whole 16-byte vectors of slices in order: the writers fill the slots
+// past the last slice with +0, which leaves every sum unchanged (a -0 sum
+// becomes +0, which no output depends on) and spares a test per slice.
 __device__ __forceinline__ float add_proj_slices(const float (&v)[kMaxProjSplit], int ksplit) {
+  const int nv = proj_slice_stride(ksplit) / 4;
   float u = v[0];
+  u += v[1];
+  u += v[2];
+  u += v[3];
 #pragma unroll
-  for (int sp = 1; sp < kMaxProjSplit; ++sp)
-    if (sp < ksplit) u += v[sp];
+  for (int q = 1; q < kMaxProjSplit / 4; ++q) {
+    if (q < nv) {
+      u += v[4 * q];
+      u += v[4 * q + 1];
+      u += v[4 * q + 2];
+      u += v[4 * q + 3];
+    }
+  }
   return u;
 }
 
@@ -827,7 +847,7 @@ ProjPlan plan_proj(int32_t n_rows, int32_t rank, int32_t hidden, int32_t dtype) 
     p.frags = n_rows >= 4096 ? 4 : 1;
     p.row_tiles = (n_rows + kRowsPerWG * p.frags - 1) / (kRowsPerWG * p.frags);
     int ks = p.row_tiles > 0 ? (512 + p.row_tiles - 1) / p.row_tiles : 1;
-    const int max_ks = hidden / 256 > 1 ? hidden / 256 : 1;
+    const int max_ks = hidden / 256 > 1 ? hidden / 256 : 1;   // slices of >= 8 k-steps
     if (ks > max_ks) ks = max_ks;
     if (ks < 1) ks = 1;
     if (ks > kMaxProjSplit) ks = kMaxProjSplit;
