@@ -389,7 +389,7 @@ __device__ __forceinline__ uint32_t kth_largest_lane(uint32_t m, int K, int bits
 }
 
 // One workgroup of the top-K: `block` = row * segs + segment.
-template <typename TIO, int NBUF>
+template <typename TIO>
 __device__ __forceinline__ void topk_rows_body(int block, const TIO* __restrict__ logits, int64_t row_stride,
                                                int64_t valid_vocab, int32_t K, int32_t wchunks, int32_t segs,
                                                int32_t wchunks_per_seg, float mult, float cap,
@@ -544,33 +544,13 @@ __device__ __forceinline__ void topk_rows_body(int block, const TIO* __restrict_
   Chunk<TIO> tail;
   bool tail_loaded = false;
   if (c < full_end) {
-    // NBUF register buffers in a ring, roles rotating so that no chunk is
-    // copied: while one chunk is processed, the next NBUF - 1 are in flight.
-    // Chunk indices past the prefetch end re-read its last one (a cache hit).
+    // two register buffers, roles alternating so that no chunk is copied:
+    // while one chunk is processed the next one is in flight (three buffers
+    // were measured slower).  Chunk indices past the prefetch end re-read its
+    // last one (a cache hit).
     auto idx = [&](int k) { return k < pre_end ? k : pre_end - 1; };
     int tail_in = 0;                              // the buffer holding the prefetched partial chunk
-    if constexpr (NBUF == 3) {
-      Chunk<TIO> a, b, d;
-      a.issue_clamped(rowp, c * kGroupChunk + wave_off32, last_vec);
-      b.issue_clamped(rowp, idx(c + 1) * kGroupChunk + wave_off32, last_vec);
-      while (true) {
-        d.issue_clamped(rowp, idx(c + 2) * kGroupChunk + wave_off32, last_vec);
-        process_full(a, (int64_t)c * kGroupChunk + wave_off, (int64_t)c * kGroupChunk);
-        if (++c >= full_end) { tail_in = 1; break; }
-        a.issue_clamped(rowp, idx(c + 2) * kGroupChunk + wave_off32, last_vec);
-        process_full(b, (int64_t)c * kGroupChunk + wave_off, (int64_t)c * kGroupChunk);
-        if (++c >= full_end) { tail_in = 2; break; }
-        b.issue_clamped(rowp, idx(c + 2) * kGroupChunk + wave_off32, last_vec);
-        process_full(d, (int64_t)c * kGroupChunk + wave_off, (int64_t)c * kGroupChunk);
-        if (++c >= full_end) { tail_in = 0; break; }
-      }
-      if (pre_end > full_end) {
-#pragma unroll
-        for (int j = 0; j < (int)(sizeof(tail.w) / sizeof(tail.w[0])); ++j)
-          tail.w[j] = tail_in == 0 ? a.w[j] : tail_in == 1 ? b.w[j] : d.w[j];
-        tail_loaded = true;
-      }
-    } else {
+    {
       Chunk<TIO> a, b;
       a.issue_clamped(rowp, c * kGroupChunk + wave_off32, last_vec);
       while (true) {
@@ -635,7 +615,7 @@ __global__ __launch_bounds__(kThreads, 4) void topk_rows_bf16(const uint16_t* __
                                                             float cap, uint64_t* __restrict__ parts,
                                                             int64_t* __restrict__ ids_out,
                                                             float* __restrict__ unary_out) {
-  topk_rows_body<uint16_t, 2>((int)blockIdx.x, logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap, parts,
+  topk_rows_body<uint16_t>((int)blockIdx.x, logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap, parts,
                            ids_out, unary_out);
 }
 __global__ __launch_bounds__(kThreads) void topk_rows_f32(const float* __restrict__ logits, int64_t row_stride,
@@ -644,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_f32(const float* __restric
                                                           float cap, uint64_t* __restrict__ parts,
                                                           int64_t* __restrict__ ids_out,
                                                           float* __restrict__ unary_out) {
-  topk_rows_body<float, 2>((int)blockIdx.x, logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap, parts,
+  topk_rows_body<float>((int)blockIdx.x, logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap, parts,
                         ids_out, unary_out);
 }
 
@@ -666,7 +646,7 @@ __global__ __launch_bounds__(kThreads, 2) void topk_conv_proj_bf16(
     conv_slot_proj_group<TAPS, RT>(g % sp.groups_x, g / sp.groups_x, sp);
     return;
   }
-  topk_rows_body<uint16_t, 2>(b, logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap,
+  topk_rows_body<uint16_t>(b, logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap,
                               parts, ids_out, unary_out);
 }
 
