@@ -250,7 +250,7 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
         g_temps, g_mask = inp["temperatures"].cpu(), inp["greedy_mask"].cpu()
         v_acc = torch.empty(R, dtype=torch.int32, device=dev)
         v_com = torch.empty((R, S + 1), dtype=torch.int64, device=dev)
-        v_ws = torch.empty(max(1, D.lib().dflash_verify_workspace_size(R, S)), dtype=torch.uint8, device=dev)
+        v_ws = torch.empty(max(1, D.lib().dflash_verify_workspace_size(R, S, w.valid_vocab)), dtype=torch.uint8, device=dev)
         coeff = torch.empty((w.n_tokens, 2, w.taps, w.groups), dtype=inp["x"].dtype, device=dev)
         prep_ws = torch.empty(max(1, D.lib().dflash_conv_prepare_workspace_size(
             w.n_tokens, H, w.group_size, w.taps, 1 if w.dtype == "bf16" else 0)), dtype=torch.uint8, device=dev)

@@ -68,7 +68,7 @@ _SIGNATURES = {
     "dflash_conv_prepare": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_vp, _c_size, _c_vp]),
     "dflash_philox_uniforms": (_c_i32, [_c_vp, _c_i64, _c_vp, _c_vp]),
-    "dflash_verify_workspace_size": (_c_size, [_c_i32, _c_i32]),
+    "dflash_verify_workspace_size": (_c_size, [_c_i32, _c_i32, _c_i64]),
     "dflash_verify": (_c_i32, [_c_vp, _c_i64, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp,
                                _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "dflash_topk_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i32]),
@@ -208,7 +208,7 @@ def dflash_verify(target_logits: torch.Tensor, cand_ids: torch.Tensor, q: torch.
     accepted_out = torch.empty(R, dtype=torch.int32, device=dev) if accepted_out is None else accepted_out
     committed_out = torch.empty((R, S1), dtype=torch.int64, device=dev) if committed_out is None else committed_out
     if workspace is None:
-        workspace = torch.empty(max(1, lib().dflash_verify_workspace_size(R, S)), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(1, lib().dflash_verify_workspace_size(R, S, valid_vocab)), dtype=torch.uint8, device=dev)
     for t, name in ((cand_ids, "cand_ids"), (q, "q"), (tokens, "tokens"), (u_accept, "u_accept"),
                     (u_residual, "u_residual"), (temperatures, "temperatures"), (greedy_mask, "greedy_mask")):
         if not t.is_contiguous():

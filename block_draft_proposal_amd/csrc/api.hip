@@ -319,9 +319,9 @@ int dflash_philox_uniforms(const uint64_t* seed_offset, int64_t n, float* out, d
   return st == DFLASH_OK ? ok() : st;
 }
 
-size_t dflash_verify_workspace_size(int32_t n_req, int32_t slots) {
-  if (n_req <= 0 || slots < 0) return 0;
-  return (size_t)n_req * (slots + 1) * dflash::kVerifySegs * sizeof(dflash::VerifyRowStats);
+size_t dflash_verify_workspace_size(int32_t n_req, int32_t slots, int64_t valid_vocab) {
+  if (n_req <= 0 || slots < 0 || valid_vocab <= 0) return 0;
+  return dflash::verify_workspace_bytes(n_req, slots, valid_vocab);
 }
 
 int dflash_verify(const void* target_logits, int64_t row_stride, int32_t n_req, int32_t slots, int64_t vocab,
@@ -342,7 +342,7 @@ int dflash_verify(const void* target_logits, int64_t row_stride, int32_t n_req, 
     return fail(DFLASH_ERR_INVALID_ARG, "%s: null pointer", who);
   if (reinterpret_cast<uintptr_t>(target_logits) % elem_bytes(dtype))
     return fail(DFLASH_ERR_INVALID_ARG, "%s: target_logits misaligned", who);
-  const size_t need = dflash_verify_workspace_size(n_req, slots);
+  const size_t need = dflash_verify_workspace_size(n_req, slots, valid_vocab);
   if (!workspace || workspace_bytes < need)
     return fail(DFLASH_ERR_WORKSPACE, "%s: workspace needs %zu bytes", who, need);
   if (reinterpret_cast<uintptr_t>(workspace) % 8)

@@ -179,9 +179,12 @@ struct VerifyArgs {
   int32_t dtype;
   int32_t* accepted_out;    // [n_req]
   int64_t* committed_out;   // [n_req, slots + 1]
-  void* workspace;          // VerifyRowStats [n_req * (slots + 1)][kVerifySegs]
+  void* workspace;          // VerifyRowStats [rows][kVerifySegs], then the chunk sums
 };
 constexpr int kVerifySegs = 4;   // workgroups (and statistics records) per target row
+// chunks per wave of a row segment at most, and the workspace for them
+int32_t verify_chunks_bound(int64_t valid_vocab);
+size_t verify_workspace_bytes(int32_t n_req, int32_t slots, int64_t valid_vocab);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 
 // Lattice and walk in one kernel (one workgroup per request) when the

@@ -276,9 +276,11 @@ int dflash_philox_uniforms(const uint64_t* seed_offset, int64_t n, float* out, d
  *   accepted_out   [n_req] int32: drafted tokens kept
  *   committed_out  [n_req, slots+1] int64: the kept tokens, then the
  *                  correction or bonus token, then -1
- * Scratch: dflash_verify_workspace_size(n_req, slots) bytes, 8-byte aligned.
- * n_req == 0 is a no-op. */
-size_t dflash_verify_workspace_size(int32_t n_req, int32_t slots);
+ * Scratch: dflash_verify_workspace_size(n_req, slots, valid_vocab) bytes,
+ * 8-byte aligned, owned by the caller (per-row statistics and per-chunk sums
+ * of the sampled rows; about valid_vocab / 8 bytes per target row); 0 when
+ * any argument is <= 0.  n_req == 0 is a no-op. */
+size_t dflash_verify_workspace_size(int32_t n_req, int32_t slots, int64_t valid_vocab);
 int dflash_verify(const void* target_logits, int64_t row_stride, int32_t n_req, int32_t slots, int64_t vocab,
                   int64_t valid_vocab, int32_t top_k, const int64_t* cand_ids, const float* q, const int64_t* tokens,
                   const float* u_accept, const float* u_residual, const float* temperatures,

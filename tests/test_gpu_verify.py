@@ -135,3 +135,40 @@ def test_verify_empty_is_a_no_op():
                                torch.zeros((0, 2), device=DEV), torch.zeros(0, device=DEV), torch.zeros(0, device=DEV),
                                torch.zeros(0, dtype=torch.uint8, device=DEV))
     assert acc.shape == (0,) and com.shape == (0, 3)
+
+
+def test_verify_large_vocab_ragged_rows():
+    # sampled requests whose chunk sums span every segment: fp32 rows with a
+    # ragged valid vocabulary, and bf16 rows of an odd length (so each row
+    # starts at a different offset from a 16-byte boundary)
+    _run(4, 3, 151936, 8, 10, dtype=torch.float32, valid=151001, greedy_frac=0.0)
+    _run(6, 3, 100003, 8, 11, greedy_frac=0.0)
+
+
+def test_verify_residual_falls_back_to_p():
+    # A sampled request at a temperature that makes p the point mass at the
+    # argmax, with q(argmax) = 1 and a drafted token of tiny q: the token is
+    # rejected, max(0, p - q) is zero everywhere, and the committed token is
+    # drawn from p (the argmax).
+    require_gpu()
+    R, S, V, K = 3, 2, 5000, 4
+    d = _inputs(R, S, V, K, 12, greedy_frac=0.0)
+    zf = d["z"].float()
+    d["temps"][:] = 1e-7
+    for r in range(R):
+        top = int(torch.argmax(zf[r, 0]))
+        others = [v for v in range(V) if v != top][:K - 1]
+        d["cand"][r, 0] = torch.tensor([top] + others)
+        d["q"][r, 0] = torch.tensor([1.0] + [1e-3] * (K - 1))
+        d["tok"][r, 0] = others[0]
+    say(f"dflash_verify residual fallback R={R} S={S} V={V}")
+    acc, com = D.dflash_verify(d["z"].to(DEV), d["cand"].to(DEV), d["q"].to(DEV), d["tok"].to(DEV),
+                               d["ua"].to(DEV), d["ur"].to(DEV), d["temps"].to(DEV), d["greedy"].to(DEV))
+    torch.cuda.synchronize()
+    ra, rc = O.verify(f64(d["z"]), V, d["cand"].numpy(), d["q"].double().numpy(), d["tok"].numpy(),
+                      d["ua"].double().numpy(), d["ur"].double().numpy(), d["temps"].double().numpy(),
+                      d["greedy"].numpy())
+    assert np.all(ra == 0)
+    assert np.array_equal(acc.cpu().numpy(), ra) and np.array_equal(com.cpu().numpy(), rc)
+    for r in range(R):
+        assert rc[r, 0] == int(torch.argmax(zf[r, 0]))
