@@ -81,13 +81,18 @@ __device__ __forceinline__ double exp_nonpos(double x) {
   return ldexp(p, (int)k);
 }
 
-// e^x for x <= 0, table-driven (Tang's method): x = (k / 256) ln2 + r with
-// |r| <= ln2 / 512, so e^x = 2^(k >> 8) 2^((k & 255) / 256) e^r.  The 256
-// powers 2^(j/256) sit in an LDS table (exp_table_fill), e^r is its Taylor
-// series to degree 4 (truncation below 2^-54 on that range); k (/ 256) ln2
+// e^x for x <= 0, table-driven (Tang's method), here with a 256-entry table:
+// x = (k / 256) ln2 + r with |r| <= ln2 / 512, so e^x = 2^(k >> 8)
+// 2^((k & 255) / 256) e^r.  The powers 2^(j/256) sit in an LDS table
+// (exp_table_fill), e^r is its Taylor series to degree 4 (truncation below
+// 2^-54 on that range; 32- and 64-entry tables with degrees 6 and 5 measured
+// the same); k (/ 256) ln2
 // is subtracted in the same two parts as in exp_nonpos.  About 3 ulp; zero
 // below -745.2 and for -inf or NaN, like exp_nonpos.
-constexpr int kExpTable = 256;
+constexpr int kExpBits = 8;                 // table of 2^(j / 2^kExpBits)
+constexpr int kExpTable = 1 << kExpBits;
+// Taylor degree for |r| <= ln2 / 2^(kExpBits+1): truncation below 2^-54
+constexpr int kExpDegree = kExpBits >= 8 ? 4 : kExpBits >= 6 ? 5 : kExpBits == 5 ? 6 : 7;
 
 __device__ __forceinline__ void exp_table_fill(double* t) {
   for (int j = threadIdx.x; j < kExpTable; j += blockDim.x)   // 2^(j/256) = 2 e^((j - 256) ln2 / 256)
@@ -116,11 +121,13 @@ __device__ __forceinline__ ExpReduced exp_tab_reduce(double x) {
 }
 
 __device__ __forceinline__ double exp_tab_finish(const ExpReduced& a, double table_value) {
-  double p = fma(a.r, 0x1.5555555555555p-5, 0x1.5555555555555p-3);   // 1/4!, 1/3!
-  p = fma(p, a.r, 0.5);
-  p = fma(p, a.r, 1.0);
-  p = fma(p, a.r, 1.0);
-  return ldexp(table_value * p, a.k >> 8);
+  // 1/d! for d = 0..7, rounded to double
+  constexpr double c[8] = {1.0, 1.0, 0.5, 0x1.5555555555555p-3, 0x1.5555555555555p-5, 0x1.1111111111111p-7,
+                           0x1.6c16c16c16c17p-10, 0x1.a01a01a01a01ap-13};
+  double p = fma(a.r, c[kExpDegree], c[kExpDegree - 1]);
+#pragma unroll
+  for (int d = kExpDegree - 2; d >= 0; --d) p = fma(p, a.r, c[d]);
+  return ldexp(table_value * p, a.k >> kExpBits);
 }
 
 __device__ __forceinline__ double exp_tab(double x, const double* t) {
@@ -365,20 +372,30 @@ __device__ __forceinline__ VerifyRowStats merge_segments(const VerifyRowStats* s
   return o;
 }
 
-// Inclusive scan of one double per thread over the workgroup, in thread order
-// (doubling steps in LDS); returns this thread's prefix, buf holds them all.
-__device__ __forceinline__ double block_scan(double v, double* buf) {
-  const int tid = threadIdx.x;
-  __syncthreads();
-  buf[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < kCommitThreads; o <<= 1) {
-    const double add = tid >= o ? buf[tid - o] : 0.0;
-    __syncthreads();
-    if (tid >= o) buf[tid] += add;
-    __syncthreads();
+// Inclusive scan of one double per thread over the workgroup, in thread
+// order: doubling steps within each wave (shuffles), then the totals of the
+// preceding waves added in wave order.  Returns this thread's prefix and the
+// workgroup's total; wtot holds kCommitThreads / 64 doubles.  Starts with a
+// barrier (so wtot may be reused right after a previous scan) and ends with
+// one.
+__device__ __forceinline__ double block_scan(double v, double* wtot, double& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
   }
-  return buf[tid];
+  __syncthreads();
+  if (lane == 63) wtot[wave] = v;
+  __syncthreads();
+  double before = 0.0, all = 0.0;
+  for (int w = 0; w < kCommitThreads / 64; ++w) {
+    if (w == wave) before = all;
+    all += wtot[w];
+  }
+  total = all;
+  __syncthreads();
+  return before + v;
 }
 
 template <typename TIO>
@@ -394,7 +411,9 @@ __global__ __launch_bounds__(kCommitThreads) void verify_commit_kernel(
   __shared__ int s_nc;
   __shared__ int64_t s_cid[kMaxTopK], s_rid[kMaxTopK];
   __shared__ double s_cq[kMaxTopK];
-  __shared__ double s_buf[kCommitThreads];
+  __shared__ double s_wtot[kCommitThreads / 64];
+  __shared__ VerifyRowStats s_st;
+  __shared__ double s_scale[kVerifySegs];
   __shared__ int s_block, s_lastblock;
   __shared__ double s_base;
   __shared__ int64_t s_ra, s_rb;
@@ -437,6 +456,15 @@ __global__ __launch_bounds__(kCommitThreads) void verify_commit_kernel(
       if (id < 0 || id >= valid) id = -1;
       s_rid[tid] = id;
     }
+    if (tid == kCommitThreads - 1) {               // the committed row's statistics, once
+      const VerifyRowStats* rs = stats + ((int64_t)r * (S + 1) + n) * kVerifySegs;
+      const VerifyRowStats st = merge_segments(rs, inv_t);
+      s_st = st;
+      // a chunk sum against its segment's maximum -> probability mass
+      for (int k = 0; k < kVerifySegs; ++k)
+        s_scale[k] = (!greedy && st.m > -INFINITY && rs[k].m > -INFINITY)
+                         ? exp_nonpos((rs[k].m - st.m) * inv_t) / st.s : 0.0;
+    }
     __syncthreads();
     if (n < S && !greedy && tid < K) {
       int rank = 0, nc = 0;
@@ -458,8 +486,7 @@ __global__ __launch_bounds__(kCommitThreads) void verify_commit_kernel(
   __syncthreads();
   const int n = s_n;
   const int64_t row = (int64_t)r * (S + 1) + n;
-  const VerifyRowStats* rst = stats + row * kVerifySegs;
-  const VerifyRowStats st = merge_segments(rst, inv_t);
+  const VerifyRowStats st = s_st;
   int64_t tok;
   if (greedy || !(st.m > -INFINITY)) {
     tok = st.arg;
@@ -503,12 +530,11 @@ __global__ __launch_bounds__(kCommitThreads) void verify_commit_kernel(
         g.wave_range(seg, w, wlo, whi);
         const int64_t i0 = wlo + j * kChunkVecs;
         a = b = 0;
-        if (i0 >= whi || !(rst[seg].m > -INFINITY)) return 0.0;
+        if (i0 >= whi || !(s_scale[seg] > 0.0)) return 0.0;
         const int64_t i1 = i0 + kChunkVecs < whi ? i0 + kChunkVecs : whi;
         a = g.head + i0 * VEC;
         b = g.head + i1 * VEC;
-        double s = chunk_sums[((row * kVerifySegs + seg) * kVerifyWaves + w) * nch_bound + j] *
-                   exp_nonpos((rst[seg].m - st.m) * inv_t) / st.s;
+        double s = chunk_sums[((row * kVerifySegs + seg) * kVerifyWaves + w) * nch_bound + j] * s_scale[seg];
         for (int c = 0; c < nc; ++c)                        // the residual at the candidate ids
           if (s_cid[c] >= a && s_cid[c] < b && (c == 0 || s_cid[c - 1] != s_cid[c]))
             s -= p_of(s_cid[c]) - weight(s_cid[c]);
@@ -523,8 +549,9 @@ __global__ __launch_bounds__(kCommitThreads) void verify_commit_kernel(
         s_block = kCommitThreads;
         s_lastblock = -1;
       }
-      const double incl = block_scan(bsum, s_buf);          // starts and ends with a barrier
-      const double target = u * s_buf[kCommitThreads - 1];
+      double total;
+      const double incl = block_scan(bsum, s_wtot, total);  // starts and ends with a barrier
+      const double target = u * total;
       // the first block whose cumulative weight passes the target; rounding
       // can leave the target at the very end: then the last block with weight
       if (bsum > 0.0) {
@@ -566,7 +593,8 @@ __global__ __launch_bounds__(kCommitThreads) void verify_commit_kernel(
       // scanned in id order; the first whose cumulative weight passes the
       // target, else the last with weight
       const double wv = (ra + tid < rb) ? weight(ra + tid) : 0.0;
-      const double vincl = block_scan(wv, s_buf) + base;
+      double vtotal;
+      const double vincl = block_scan(wv, s_wtot, vtotal) + base;
       if (wv > 0.0) {
         atomicMax(&s_lastid, (unsigned long long)(ra + tid + 1));
         if (vincl > target) atomicMin(&s_tok, (unsigned long long)(ra + tid));

@@ -107,9 +107,14 @@ def _run(R, S, V, K, seed, **kw):
 
 
 @pytest.mark.parametrize("R,S,V,K,seed", [(16, 5, 1000, 8, 1), (8, 3, 37, 4, 2), (5, 1, 300, 1, 3),
-                                          (12, 15, 5003, 32, 4), (4, 0, 64, 2, 5)])
+                                          (12, 15, 5003, 32, 4), (4, 0, 64, 2, 5), (9, 2, 5, 2, 13)])
 def test_verify_matches_the_oracle(R, S, V, K, seed):
+    # (V = 5: rows shorter than one 16-byte vector, all single elements)
     _run(R, S, V, K, seed)
+
+
+def test_verify_fp32_rows_shorter_than_a_vector():
+    _run(7, 2, 3, 2, 14, dtype=torch.float32)
 
 
 def test_verify_fp32_logits_and_padded_vocab():
