@@ -35,6 +35,7 @@ namespace {
 constexpr int kVerifyThreads = 256;   // 4 waves per (row, segment)
 constexpr int kVerifyWaves = kVerifyThreads / 64;
 constexpr int kCommitThreads = 1024;
+constexpr int kRowsLds = 64;          // target rows of a request whose statistics the commit keeps in LDS
 constexpr int kChunkVecs = 64;        // vectors of one chunk: one per lane of a wave
 constexpr int kBatch = 8;             // chunks whose per-lane sums a wave reduces together
 constexpr int kUnroll = 4;            // vectors per lane in flight (sums)
@@ -410,7 +411,9 @@ __global__ __launch_bounds__(kCommitThreads) void verify_commit_kernel(
   __shared__ int s_n;
   __shared__ int s_nc;
   __shared__ int64_t s_cid[kMaxTopK], s_rid[kMaxTopK];
-  __shared__ double s_cq[kMaxTopK];
+  __shared__ double s_cq[kMaxTopK], s_cz[kMaxTopK];
+  __shared__ VerifyRowStats s_rows[kRowsLds];
+  __shared__ double s_rscale[kRowsLds][kVerifySegs];
   __shared__ double s_wtot[kCommitThreads / 64];
   __shared__ VerifyRowStats s_st;
   __shared__ double s_scale[kVerifySegs];
@@ -423,12 +426,35 @@ __global__ __launch_bounds__(kCommitThreads) void verify_commit_kernel(
   const bool greedy = greedy_mask[r] != 0;
   const double inv_t = 1.0 / clamp_temperature(temperatures[r]);
   exp_table_fill(s_exp);
+  // Loads that do not wait for the decisions are all issued here: each of
+  // the first S K threads holds one candidate (id, q and its logit) of its
+  // slot, and thread t <= S merges row t's segment records (kept in LDS for
+  // the first kRowsLds rows, with the chunk scales of the sampled draw).
+  const int pslot = tid / K, pj = tid - pslot * K;
+  const bool pre = !greedy && (int64_t)S * K > tid;
+  int64_t pid = -1;
+  double pq = 0.0, pz = 0.0;
+  if (pre) {
+    pid = cand_ids[((int64_t)r * S + pslot) * K + pj];
+    pq = (double)q[((int64_t)r * S + pslot) * K + pj];
+    if (pid < 0 || pid >= valid) pid = -1;
+    else pz = logit_at(logits + ((int64_t)r * (S + 1) + pslot) * row_stride, pid);
+  }
   // the accept decisions of all slots at once; n = the first rejection
   if (tid == 0) s_n = S;
   __syncthreads();
-  for (int n = tid; n < S; n += kCommitThreads) {
+  for (int n = tid; n <= S; n += kCommitThreads) {
+    const VerifyRowStats* rs = stats + ((int64_t)r * (S + 1) + n) * kVerifySegs;
+    const VerifyRowStats st = merge_segments(rs, inv_t);
+    if (n < kRowsLds) {
+      s_rows[n] = st;
+      // a chunk sum against its segment's maximum -> probability mass
+      for (int k = 0; k < kVerifySegs; ++k)
+        s_rscale[n][k] = (!greedy && st.m > -INFINITY && rs[k].m > -INFINITY)
+                             ? exp_nonpos((rs[k].m - st.m) * inv_t) / st.s : 0.0;
+    }
+    if (n == S) continue;
     const int64_t x = tokens[(int64_t)r * S + n];
-    const VerifyRowStats st = merge_segments(stats + ((int64_t)r * (S + 1) + n) * kVerifySegs, inv_t);
     bool keep;
     if (greedy) {
       keep = x == st.arg;
@@ -445,41 +471,49 @@ __global__ __launch_bounds__(kCommitThreads) void verify_commit_kernel(
   }
   __syncthreads();
   // the rejected slot's candidates in id order (equal ids keep their order),
-  // for the residual max(0, p - q)
+  // for the residual max(0, p - q), with their logits
   {
     const int n = s_n;
-    int64_t id = -1;
-    double qj = 0.0;
-    if (n < S && !greedy && tid < K) {
-      id = cand_ids[((int64_t)r * S + n) * K + tid];
-      qj = (double)q[((int64_t)r * S + n) * K + tid];
+    const bool held = n < S && (int64_t)(n + 1) * K <= kCommitThreads;   // preloaded above
+    const int t0 = held ? n * K : 0;
+    const bool ranker = n < S && !greedy && tid >= t0 && tid < t0 + K;
+    const int j = tid - t0;
+    int64_t id = pid;
+    double qj = pq, zj = pz;
+    if (ranker && !held) {
+      id = cand_ids[((int64_t)r * S + n) * K + j];
+      qj = (double)q[((int64_t)r * S + n) * K + j];
       if (id < 0 || id >= valid) id = -1;
-      s_rid[tid] = id;
+      else zj = logit_at(logits + ((int64_t)r * (S + 1) + n) * row_stride, id);
     }
-    if (tid == kCommitThreads - 1) {               // the committed row's statistics, once
+    if (ranker) s_rid[j] = id;
+    if (n < kRowsLds) {
+      if (tid == kCommitThreads - 1) s_st = s_rows[n];
+      if (tid < kVerifySegs) s_scale[tid] = s_rscale[n][tid];
+    } else if (tid == kCommitThreads - 1) {         // the committed row's statistics
       const VerifyRowStats* rs = stats + ((int64_t)r * (S + 1) + n) * kVerifySegs;
       const VerifyRowStats st = merge_segments(rs, inv_t);
       s_st = st;
-      // a chunk sum against its segment's maximum -> probability mass
       for (int k = 0; k < kVerifySegs; ++k)
         s_scale[k] = (!greedy && st.m > -INFINITY && rs[k].m > -INFINITY)
                          ? exp_nonpos((rs[k].m - st.m) * inv_t) / st.s : 0.0;
     }
     __syncthreads();
-    if (n < S && !greedy && tid < K) {
+    if (ranker) {
       int rank = 0, nc = 0;
       for (int i = 0; i < K; ++i) {
         const int64_t o = s_rid[i];
         if (o < 0) continue;
         ++nc;
-        if (id >= 0 && (o < id || (o == id && i < tid))) ++rank;
+        if (id >= 0 && (o < id || (o == id && i < j))) ++rank;
       }
       if (id >= 0) {
         s_cid[rank] = id;
         s_cq[rank] = qj;
+        s_cz[rank] = zj;
       }
-      if (tid == 0) s_nc = nc;
-    } else if (tid == 0) {
+      if (j == 0) s_nc = nc;
+    } else if (tid == kCommitThreads - 1 && !(n < S && !greedy)) {
       s_nc = 0;
     }
   }
@@ -508,12 +542,12 @@ __global__ __launch_bounds__(kCommitThreads) void verify_commit_kernel(
     tok = -1;
     for (int attempt = 0; attempt < 2 && tok < 0; ++attempt) {
       const int nc = attempt == 0 ? s_nc : 0;
-      auto weight = [&](int64_t v) {
-        double w = p_of(v);
+      auto weight_from = [&](int64_t v, double w) {       // w = p(v)
         for (int c = 0; c < nc; ++c)
           if (s_cid[c] == v) w = w - s_cq[c] > 0.0 ? w - s_cq[c] : 0.0;
         return w;
       };
+      auto weight = [&](int64_t v) { return weight_from(v, p_of(v)); };
       auto region = [&](int64_t rg, int64_t& a, int64_t& b) -> double {
         if (rg == 0 || rg == n_regions - 1) {
           a = rg == 0 ? 0 : g.head + g.nvec * VEC;
@@ -536,14 +570,21 @@ __global__ __launch_bounds__(kCommitThreads) void verify_commit_kernel(
         b = g.head + i1 * VEC;
         double s = chunk_sums[((row * kVerifySegs + seg) * kVerifyWaves + w) * nch_bound + j] * s_scale[seg];
         for (int c = 0; c < nc; ++c)                        // the residual at the candidate ids
-          if (s_cid[c] >= a && s_cid[c] < b && (c == 0 || s_cid[c - 1] != s_cid[c]))
-            s -= p_of(s_cid[c]) - weight(s_cid[c]);
+          if (s_cid[c] >= a && s_cid[c] < b && (c == 0 || s_cid[c - 1] != s_cid[c])) {
+            const double pc = exp_tab(fma(s_cz[c], inv_t, -ms), s_exp) / st.s;   // p of that id
+            s -= pc - weight_from(s_cid[c], pc);
+          }
         return s > 0.0 ? s : 0.0;
       };
       double bsum = 0.0;
+      int64_t a0 = 0, b0 = 0;                              // this thread's first region
       for (int64_t rg = r0; rg < r1; ++rg) {
         int64_t a, b;
         bsum += region(rg, a, b);
+        if (rg == r0) {
+          a0 = a;
+          b0 = b;
+        }
       }
       if (tid == 0) {
         s_block = kCommitThreads;
@@ -567,9 +608,9 @@ __global__ __launch_bounds__(kCommitThreads) void verify_commit_kernel(
       // the block's owner finds the region the same way
       if (tid == blk) {
         double acc = incl - bsum;
-        int64_t ra = 0, rb = 0;
-        double rbase = 0.0;
-        for (int64_t rg = r0; rg < r1; ++rg) {
+        int64_t ra = a0, rb = b0;                          // a block of one region: that one
+        double rbase = acc;
+        for (int64_t rg = r0; per > 1 && rg < r1; ++rg) {
           int64_t a, b;
           const double w = region(rg, a, b);
           if (w > 0.0) {
