@@ -174,6 +174,14 @@ __device__ __forceinline__ void reduce_scatter(double (&v)[kBatch], int lane) {
   for (int m = 1; m < kLaneGroup; m <<= 1) v[0] += __shfl_xor(v[0], m, 64);
 }
 
+// The logits are streamed: non-temporal 16-byte loads do not allocate in the
+// caches, so they neither evict what other work keeps there nor force the
+// write-back of dirty lines (measured: the all-greedy 480-row call after a
+// 1 GiB write drops from 68 to 37 us, and is 2 us faster otherwise).
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // Geometry of one target row: `head` single elements up to the first 16-byte
 // boundary, nvec whole vectors, then single elements to `valid`; segment seg
 // takes its share of the vectors, wave w of it a contiguous quarter, read in
@@ -244,7 +252,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_stats_kernel(
 #pragma unroll
     for (int u = 0; u < kUnrollMax; ++u) {
       const int64_t i = i0 + (int64_t)u * 64;
-      raw[u] = ld16(zv + (i < whi ? i : wlo) * VEC);
+      raw[u] = ld16_stream(zv + (i < whi ? i : wlo) * VEC);
     }
 #pragma unroll
     for (int u = 0; u < kUnrollMax; ++u) {             // branch-free: a vector past the end counts as -inf
@@ -307,7 +315,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_stats_kernel(
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
           const int64_t i = wlo + (b0 + jj + u) * kChunkVecs + lane;
-          raw[u] = ld16(zv + (i < whi ? i : wlo) * VEC);
+          raw[u] = ld16_stream(zv + (i < whi ? i : wlo) * VEC);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
