@@ -76,9 +76,9 @@ def _margins_ok(d, r, got_n):
     return False
 
 
-def _run(R, S, V, K, seed, **kw):
+def _run(R, S, V, K, seed, d=None, **kw):
     require_gpu()
-    d = _inputs(R, S, V, K, seed, **kw)
+    d = _inputs(R, S, V, K, seed, **kw) if d is None else d
     say(f"dflash_verify R={R} S={S} V={V} K={K} valid={d['valid']} seed={seed}")
     acc, com = D.dflash_verify(d["z"].to(DEV), d["cand"].to(DEV), d["q"].to(DEV), d["tok"].to(DEV),
                                d["ua"].to(DEV), d["ur"].to(DEV), d["temps"].to(DEV), d["greedy"].to(DEV),
@@ -177,3 +177,30 @@ def test_verify_residual_falls_back_to_p():
     assert np.array_equal(acc.cpu().numpy(), ra) and np.array_equal(com.cpu().numpy(), rc)
     for r in range(R):
         assert rc[r, 0] == int(torch.argmax(zf[r, 0]))
+
+
+def test_verify_long_blocks():
+    # 70 slots x K = 16: more slots than the commit kernel keeps row
+    # statistics for in LDS (64) and more candidates than it preloads (1024
+    # threads), so the committed row and the rejected slot's candidates are
+    # fetched after the decisions.  Request 0 keeps every token (greedy, all
+    # argmax), request 1 keeps 66 tokens and rejects slot 66 (sampled, p a
+    # point mass at the argmax, q(argmax) = 1 before it), request 2 is random.
+    R, S, V, K = 3, 70, 400, 16
+    d = _inputs(R, S, V, K, 15, greedy_frac=0.0)
+    zf = d["z"].float()
+    d["greedy"][0], d["greedy"][1], d["greedy"][2] = 1, 0, 0
+    d["temps"][1] = 1e-7
+    for s in range(S):
+        top0 = int(torch.argmax(zf[0, s]))
+        d["cand"][0, s, 0] = top0 if not bool((d["cand"][0, s, 1:] == top0).any()) else d["cand"][0, s, 0]
+        d["tok"][0, s] = top0
+        top1 = int(torch.argmax(zf[1, s]))
+        others = [v for v in range(V) if v != top1][:K - 1]
+        d["cand"][1, s] = torch.tensor([top1] + others)
+        d["q"][1, s] = torch.tensor([1.0] + [1e-3] * (K - 1))
+        d["tok"][1, s] = top1 if s < 66 else others[0]
+    if not bool((d["cand"][0] == d["tok"][0].unsqueeze(-1)).any(-1).all()):
+        d["cand"][0, :, 0] = d["tok"][0]
+    a, _ = _run(R, S, V, K, 15, d=d)
+    assert a[0] == S and a[1] == 66
