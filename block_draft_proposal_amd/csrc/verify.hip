@@ -177,7 +177,11 @@ __device__ __forceinline__ void reduce_scatter(double (&v)[kBatch], int lane) {
 // The logits are streamed: non-temporal 16-byte loads do not allocate in the
 // caches, so they neither evict what other work keeps there nor force the
 // write-back of dirty lines (measured: the all-greedy 480-row call after a
-// 1 GiB write drops from 68 to 37 us, and is 2 us faster otherwise).
+// 1 GiB write drops from 68 to 37 us, and is 2 us faster otherwise).  A
+// sampled row is read twice; its second read then misses the caches, which
+// costs ~8% on a batch of 16384 sampled rows, less than a cached first read
+// costs the greedy rows (a per-row choice of load kind was merged away by
+// the compiler).
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
