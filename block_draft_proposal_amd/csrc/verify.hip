@@ -37,7 +37,7 @@ constexpr int kVerifyWaves = kVerifyThreads / 64;
 constexpr int kCommitThreads = 1024;
 constexpr int kRowsLds = 64;          // target rows of a request whose statistics the commit keeps in LDS
 constexpr int kChunkVecs = 64;        // vectors of one chunk: one per lane of a wave
-constexpr int kBatch = 8;             // chunks whose per-lane sums a wave reduces together
+constexpr int kBatch = 4;             // chunks whose per-lane sums a wave reduces together
 constexpr int kUnroll = 4;            // vectors per lane in flight (sums)
 constexpr int kUnrollMax = 8;         // vectors per lane in flight (maximum)
 
