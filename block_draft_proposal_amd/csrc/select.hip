@@ -623,7 +623,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_lds_kernel(const float* __r
   for (int base = 0; base < n_e; base += kWalkThreads * kBatch) {
     float v[kBatch];
 #pragma unroll
-    for (int q = 0; q < kBatch; ++q) v[q] = src[min(base + q * kWalkThreads + tid, n_e - 1)];
+    for (int q = 0; q < kBatch; ++q) v[q] = __builtin_nontemporal_load(src + min(base + q * kWalkThreads + tid, n_e - 1));
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       const int i = base + q * kWalkThreads + tid;
