@@ -35,7 +35,7 @@ if ROOT not in sys.path:
 METRIC = "draft tokens/s through conv+topK+lattice walk; conv/topK HBM GB/s % of peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFS = 2500.0      # MI355X dense bf16 matrix peak, TFLOP/s
-DEFAULT_WORKLOAD = "bf16_b16_v151936"
+DEFAULT_WORKLOAD = "stress_r1024_k32"
 MALL_BYTES = 256 * 1024 * 1024
 TIMED_EVERY = 4          # top-K events on every 4th timed step
 
@@ -313,35 +313,97 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
         torch.cuda.empty_cache()
 
 
-def cpu_baseline(w, n_req_sample: int, min_seconds: float = 10.0):
-    """Time the oracle (as it stands) on a bounded sample of the workload:
-    batches of n_req_sample requests (fresh seeds each) until min_seconds of
-    CPU work have been timed."""
-    import numpy as np
+def _oracle_host_inputs(name: str, n_req_sample: int, seed: int):
     import torch
     import workloads as W
+    ws = W.WORKLOADS[name].replace(n_req=n_req_sample)
+    inp = W.make_inputs(ws, device="cpu", seed=seed)
+    return ws, {k: (v.to(torch.float64).numpy() if v.is_floating_point() else v.numpy()) for k, v in inp.items()}
+
+
+def _run_oracle(ws, host):
     from oracle import dflash_oracle as O
+    O.propose_block(host, block_size=ws.block_size, group_size=ws.group_size, valid_vocab=ws.valid_vocab,
+                    top_k=ws.top_k, multiplier=ws.multiplier, softcap=ws.softcap, dtype=ws.dtype)
+
+
+def _single_thread():
+    import torch
     try:
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
+        threadpool_limits(limits=1)
     except Exception:   # pragma: no cover - threadpoolctl is optional
-        limiter = None
-    ws = w.replace(n_req=n_req_sample)
-    dt, batches = 0.0, 0
-    while dt < min_seconds:
-        inp = W.make_inputs(ws, device="cpu", seed=W.master_seed(ws) + 7919 * batches)
-        host = {k: (v.to(torch.float64).numpy() if v.is_floating_point() else v.numpy()) for k, v in inp.items()}
+        pass
+    torch.set_num_threads(1)
+
+
+_START = None
+
+
+def _worker_init(barrier):
+    global _START
+    _START = barrier
+    _single_thread()
+    import oracle.dflash_oracle  # noqa: F401
+    import workloads  # noqa: F401
+
+
+def _worker_batch(name: str, n_req_sample: int, seed: int):
+    """One batch in a worker: inputs first, then every worker starts the
+    oracle together (barrier); returns the oracle's wall-clock interval."""
+    ws, host = _oracle_host_inputs(name, n_req_sample, seed)
+    _START.wait()
+    t0 = time.time()
+    _run_oracle(ws, host)
+    return t0, time.time()
+
+
+def _host_cores() -> int:
+    """Cores this process may run on, capped at the 16 a one-GPU share gets."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:   # pragma: no cover - non-Linux
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(w, n_req_sample: int, min_seconds: float = 8.0):
+    """The oracle (as it stands, never tuned) on bounded samples of the
+    workload, on the host's cores: one single-threaded process, then one
+    single-threaded process per core, each on its own batch (fresh seeds),
+    all started together once their inputs exist and timed by wall clock
+    from the first start to the last end.  Input generation is not timed.
+    Called before the GPU is touched; the worker processes are spawned fresh."""
+    import concurrent.futures
+    import multiprocessing
+    import workloads as W
+    base_seed = W.master_seed(w)
+    per_batch = n_req_sample * w.slots
+    _single_thread()
+    dt1, b1 = 0.0, 0
+    while dt1 < min_seconds:
+        ws, host = _oracle_host_inputs(w.name, n_req_sample, base_seed + 7919 * b1)
         t0 = time.perf_counter()
-        O.propose_block(host, block_size=ws.block_size, group_size=ws.group_size, valid_vocab=ws.valid_vocab,
-                        top_k=ws.top_k, multiplier=ws.multiplier, softcap=ws.softcap, dtype=ws.dtype)
-        dt += time.perf_counter() - t0
-        batches += 1
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
-    tokens = batches * ws.n_slot_rows
-    return {"value": tokens / dt, "unit": "draft tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{batches} batches of {n_req_sample} of the {w.n_req} requests ({tokens} draft tokens), "
-                      f"full vocab/hidden; {dt:.1f} s single-threaded numpy float64 (walk in fp32)"}
+        _run_oracle(ws, host)
+        dt1 += time.perf_counter() - t0
+        b1 += 1
+    one = {"value": b1 * per_batch / dt1, "cores": 1,
+           "sample": f"{b1} batches of {n_req_sample} of the {w.n_req} requests ({b1 * per_batch} draft tokens), "
+                     f"{dt1:.1f} s in one single-threaded process"}
+    cores = _host_cores()
+    ctx = multiprocessing.get_context("spawn")
+    barrier = ctx.Barrier(cores)
+    with concurrent.futures.ProcessPoolExecutor(max_workers=cores, mp_context=ctx, initializer=_worker_init,
+                                                initargs=(barrier,)) as ex:
+        futs = [ex.submit(_worker_batch, w.name, n_req_sample, base_seed + 7919 * (1000 + c)) for c in range(cores)]
+        spans = [f.result() for f in futs]
+    wall = max(e for _, e in spans) - min(s for s, _ in spans)
+    tokens = cores * per_batch
+    return {"value": tokens / wall, "unit": "draft tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{cores} batches of {n_req_sample} of the {w.n_req} requests ({tokens} draft tokens), one "
+                      f"per single-threaded process on {cores} cores started together, {wall:.1f} s wall clock; "
+                      f"full vocab/hidden; numpy float64 (walk in fp32)",
+            "single_core": one}
 
 
 def main():
@@ -351,7 +413,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-requests", type=int, default=12)
+    ap.add_argument("--cpu-sample-requests", type=int, default=8)
     ap.add_argument("--sweep", action="store_true",
                     help="only time every C-ABI call on every workload (markdown table) and exit")
     ap.add_argument("--sweep-only", nargs="*", default=None, metavar="WORKLOAD",
@@ -375,11 +437,17 @@ def main():
         sweep(only=args.sweep_only)
         return
 
+    w = W.WORKLOADS[args.workload]
+    cpu = None
+    if not args.no_cpu_baseline:
+        # before the GPU is initialised: the oracle's worker processes start
+        # from a process with no GPU state
+        log("[bench] timing the CPU oracle on a sample")
+        cpu = cpu_baseline(w, min(args.cpu_sample_requests, w.n_req))
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    w = W.WORKLOADS[args.workload]
     cfg = D.make_config(taps=w.taps, group_size=w.group_size, rank=w.rank, top_k=w.top_k,
                         multiplier=w.multiplier, softcap=w.softcap, block_size=w.block_size, hidden=w.hidden)
     logits_bytes = w.n_slot_rows * w.vocab * w.elem_bytes
@@ -488,11 +556,8 @@ def main():
                      + ("conv and projection are workgroups of the top-K's launch (their events bracket it; "
                         "the projection stage is empty)" if fused else
                         "conv and projection run beside the top-K on a second stream")},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a sample")
-        line["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_requests, w.n_req))
     print(json.dumps(line), flush=True)
 
 

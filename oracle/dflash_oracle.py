@@ -281,26 +281,6 @@ def lattice(ids: np.ndarray, unary: np.ndarray, u: np.ndarray, anchor: np.ndarra
     return scores
 
 
-def lattice_error_scale(ids, unary, h, proj, anchor, sel_a, sel_b):
-    """Magnitudes that bound the rounding error of an fp32 evaluation of each
-    lattice entry (used by the tests to derive a tolerance, not part of the
-    method): M1[r,s,j,c] = sum_k |A_pk||B_ck| sum_h |P_kh h_h|,
-    M2[r,s,j,c] = sum_k |A_pk u_k B_ck| + |unary_c|."""
-    A = np.abs(np.asarray(sel_a, np.float64))
-    Bt = np.abs(np.asarray(sel_b, np.float64))
-    absu = np.abs(np.asarray(h, np.float64)) @ np.abs(np.asarray(proj, np.float64)).T
-    u = project(h, proj)
-    R, S, K = ids.shape
-    M1 = np.empty((R, S, K, K))
-    M2 = np.empty((R, S, K, K))
-    for r in range(R):
-        for s in range(S):
-            prev = np.full(K, anchor[r]) if s == 0 else ids[r, s - 1]
-            M1[r, s] = (A[prev] * absu[r, s]) @ Bt[ids[r, s]].T
-            M2[r, s] = (A[prev] * np.abs(u[r, s])) @ Bt[ids[r, s]].T + np.abs(unary[r, s])[None, :]
-    return M1, M2
-
-
 # ---------------------------------------------------------------------------
 # Step 6: the per-request walk  [DF2] walk-kernel code excerpt and executive
 # summary (greedy rows emit a point mass; sampled rows return the softmax q

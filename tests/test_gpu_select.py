@@ -2,11 +2,12 @@
 ("[Spec] DFlash2": executive summary edge formula and lossless-q contract;
 walk-kernel excerpt).
 
-Lattice bar (stepwise: the oracle gets the GPU's own ids, unary and hidden):
-each score within its fp32 rounding bound
-    (H + 8) u M1 + (r + 8) u M2,   u = 2^-24,
-M1 = sum_k |A_pk||B_ck| sum_h |P_kh h_h| (projection accumulation),
-M2 = sum_k |A_pk u_k B_ck| + |unary_c| (edge accumulation).
+Lattice bar (stepwise: the oracle gets the GPU's own ids, unary and hidden
+rows, and projects them exactly): every score within
+    1e-4 (1 + |unary_c| + sum_k |A_pk u_k B_ck|)
+of the exact value -- a bar an fp32 evaluation clears with a wide margin and
+a projection rounded to bf16 breaks (pinned on the CPU in
+tests/test_parity_bars.py).  The rigorous fp32 worst case is printed beside it.
 Walk bar: the oracle walks the GPU's own scores in the pages' fp32 order, so
 tokens and q must match bit for bit."""
 import numpy as np
@@ -17,9 +18,10 @@ import block_draft_proposal_amd as D
 import workloads as W
 from gpu_helpers import DEV, f64, require_gpu, sample_indices, say
 from oracle import dflash_oracle as O
+from parity_bars import fp32_sum_bound, lattice_bar
 
 pytestmark = pytest.mark.gpu
-U = 2.0 ** -24
+REQ_CHUNK = 64      # requests compared per host pass (bounds host memory)
 
 
 def _lattice_inputs(w: W.Workload, seed=None):
@@ -37,31 +39,36 @@ def _check_lattice(w, inp, hid, req_sample=None):
     scores = D.dflash_lattice(ids, unary, hid, inp["anchor"], inp["sel_a"], inp["sel_b"], inp["proj"])
     torch.cuda.synchronize()
     reqs = np.arange(w.n_req) if req_sample is None else sample_indices(w.n_req, req_sample, seed=1)
-    ri = torch.from_numpy(reqs).to(DEV)
-    ids_h = ids[ri].cpu().numpy()
-    un_h = f64(unary[ri])
-    h_h = f64(hid[ri])
-    anc = inp["anchor"][ri].cpu().numpy()
     A, B, P = f64(inp["sel_a"]), f64(inp["sel_b"]), f64(inp["proj"])
-    ref = O.lattice(ids_h, un_h, O.project(h_h, P), anc, A, B)
-    M1, M2 = O.lattice_error_scale(ids_h, un_h, h_h, P, anc, A, B)
-    tol = (w.hidden + 8) * U * M1 + (w.rank + 8) * U * M2
-    got = f64(scores[ri])
-    err = np.abs(got - ref)
-    assert np.all(err <= tol), (w.name, float(np.max(err / tol)))
+    worst, loose_worst = 0.0, 0.0
+    for c0 in range(0, len(reqs), REQ_CHUNK):
+        ri = torch.from_numpy(reqs[c0:c0 + REQ_CHUNK]).to(DEV)
+        ids_h = ids[ri].cpu().numpy()
+        un_h = f64(unary[ri])
+        h_h = f64(hid[ri])
+        anc = inp["anchor"][ri].cpu().numpy()
+        u = O.project(h_h, P)
+        ref = O.lattice(ids_h, un_h, u, anc, A, B)
+        err = np.abs(f64(scores[ri]) - ref)
+        ratio = err / lattice_bar(ids_h, un_h, u, anc, A, B)
+        worst = max(worst, float(np.max(ratio)))
+        assert np.all(ratio <= 1.0), (w.name, int(reqs[c0]), float(np.max(ratio)))
+        if c0 == 0:   # the fp32 worst-case bound, printed for comparison only
+            loose_worst = float(np.max(err / fp32_sum_bound(ids_h, un_h, h_h, P, anc, A, B)))
+    print(f"[lattice] {w.name}: {len(reqs)} of {w.n_req} requests, max err / bar {worst:.3e} "
+          f"(err / fp32 worst case {loose_worst:.3e} on the first {min(REQ_CHUNK, len(reqs))})", flush=True)
     # slot 0: every predecessor row is the anchor's, so the rows are identical
     assert torch.equal(scores[:, 0, :1, :].expand_as(scores[:, 0]), scores[:, 0])
     return ids, unary, scores
 
 
-@pytest.mark.parametrize("name,reqs", [("tiny_fp32", None), ("bf16_b16_v151936", None),
-                                       ("nonpow2_b10_v151936", None), ("padded_v201024_k16", 32),
-                                       ("stress_r1024_k32", 24)])
-def test_lattice_matches_oracle(name, reqs):
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_lattice_matches_oracle(name):
+    # every request of every workload, at full size
     require_gpu()
     w = W.WORKLOADS[name]
     inp, hid = _lattice_inputs(w)
-    _check_lattice(w, inp, hid, reqs)
+    _check_lattice(w, inp, hid)
 
 
 @pytest.mark.parametrize("dtype,H,r,K", [("bf16", 40, 8, 4), ("bf16", 200, 24, 5), ("bf16", 1032, 128, 32),

@@ -1,7 +1,10 @@
 """GPU parity of dflash_topk against the oracle's top-K ("[Spec] DFlash2",
 implementation breakdown: deterministic top-k over transformed unary logits;
 "DSpark padded-vocab d2t fix": padded ids never selected).  Bar: ids bit-exact
-(ties by lowest id); unary within 1e-5 * (1 + |ref|)."""
+(ties by lowest id); unary within 1e-5 * (1 + |ref|).  Large batches: the
+oracle's full sort on a seeded sample of rows, and every row of the batch
+through the sort-free validity check of tests/parity_bars.py, which pins the
+selected set and its order exactly."""
 import numpy as np
 import pytest
 import torch
@@ -10,6 +13,9 @@ import block_draft_proposal_amd as D
 import workloads as W
 from gpu_helpers import DEV, f64, require_gpu, sample_indices, say
 from oracle import dflash_oracle as O
+from parity_bars import topk_violations
+
+ROW_CHUNK = 256     # rows checked per host pass (bounds host memory)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,16 +36,37 @@ def _check(logits, valid, k, m, cap, rows=None, vocab=None, label=""):
     return ids, unary
 
 
+def _check_every_row(logits, ids, unary, valid, m, cap, label):
+    """Every row through the sort-free validity check; unary of every row
+    against the oracle's transform of the selected logits."""
+    n = logits.shape[0]
+    bad_rows = 0
+    for r0 in range(0, n, ROW_CHUNK):
+        z = logits[r0:r0 + ROW_CHUNK].float().cpu().numpy()           # bf16 and fp32 are exact in fp32
+        got = ids[r0:r0 + ROW_CHUNK].cpu().numpy()
+        bad = topk_violations(z, got, valid)
+        bad_rows += bad.size
+        assert bad.size == 0, (label, int(r0 + bad[0]))
+        ref_u = O.transform(np.take_along_axis(z.astype(np.float64), got, axis=1), m, cap)
+        got_u = f64(unary[r0:r0 + ROW_CHUNK])
+        fin = np.isfinite(ref_u)
+        assert np.array_equal(np.isneginf(got_u), ~fin)
+        assert np.all(np.abs(got_u[fin] - ref_u[fin]) <= 1e-5 * (1 + np.abs(ref_u[fin])))
+    print(f"[topk] {label}: all {n} rows valid", flush=True)
+
+
 @pytest.mark.parametrize("name,n_rows", [("tiny_fp32", None), ("bf16_b16_v151936", 48),
                                          ("nonpow2_b10_v151936", 48), ("padded_v201024_k16", 48),
                                          ("stress_r1024_k32", 48)])
 def test_topk_workloads(name, n_rows):
-    # Full-size launches; rows compared: all (tiny) or a seeded sample.
+    # Full-size launches: the oracle's sort on all (tiny) or a seeded sample
+    # of rows, then every row through the validity check.
     require_gpu()
     w = W.WORKLOADS[name]
     inp = W.make_inputs(w, device=DEV, parts=("logits",))
     rows = None if n_rows is None else sample_indices(w.n_slot_rows, n_rows, seed=3)
-    ids, _ = _check(inp["logits"], w.valid_vocab, w.top_k, w.multiplier, w.softcap, rows=rows, label=name)
+    ids, unary = _check(inp["logits"], w.valid_vocab, w.top_k, w.multiplier, w.softcap, rows=rows, label=name)
+    _check_every_row(inp["logits"], ids, unary, w.valid_vocab, w.multiplier, w.softcap, name)
     if w.plant_peak:
         assert torch.equal(ids[:, 0].cpu(), inp["planted"].cpu())
     if w.valid_vocab < w.vocab:
