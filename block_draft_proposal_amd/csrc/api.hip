@@ -44,12 +44,6 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 constexpr int64_t kMaxVocab = (int64_t)1 << 24;
-constexpr size_t kLatticeLdsMax = 64 * 1024;
-
-size_t lattice_lds(int K, int r) {
-  const size_t used = (size_t)(r + K * (r + 1) + r * K);
-  return ((used + 1) & ~(size_t)1) * sizeof(float) + 2 * (size_t)K * sizeof(int64_t);
-}
 
 // ---------------------------------------------------------------------------
 int check_conv(const void* x, const void* base, const void* delta, int64_t delta_row_stride,
@@ -123,8 +117,8 @@ int check_select(const int64_t* ids, const float* unary, const void* hidden, int
   const int vec = dtype == DFLASH_BF16 ? 8 : 4;
   if (hidden_size % vec) return fail(DFLASH_ERR_UNSUPPORTED, "%s: hidden_size must be a multiple of %d", who, vec);
   if (dtype == DFLASH_BF16 && rank > 128) return fail(DFLASH_ERR_UNSUPPORTED, "%s: bf16 rank > 128", who);
-  if (lattice_lds(top_k, rank) > kLatticeLdsMax)
-    return fail(DFLASH_ERR_UNSUPPORTED, "%s: top_k x rank too large for one workgroup's LDS", who);
+  if (rank > dflash::kMaxLatticeKpad || dflash::lattice_kpad_floats(top_k, rank, dtype) > dflash::kMaxLatticeKpad)
+    return fail(DFLASH_ERR_UNSUPPORTED, "%s: rank too large for the lattice kernels", who);
   if (vocab >= ((int64_t)1 << 31)) return fail(DFLASH_ERR_UNSUPPORTED, "%s: vocab must be < 2^31", who);
   if (req_stride < 0 || slot_stride < 0) return fail(DFLASH_ERR_INVALID_ARG, "%s: negative stride", who);
   if ((int64_t)n_req * slots == 0) return DFLASH_OK;

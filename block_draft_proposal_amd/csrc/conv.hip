@@ -165,8 +165,170 @@ __global__ __launch_bounds__(kThreads) void conv_kernel_any_taps(const TIO* __re
   }
 }
 
+// ---------------------------------------------------------------------------
+// Block walk (taps <= 8, blocks of <= 16 tokens, each 16-byte vector inside
+// one group, whole groups per wave): a wave owns one block and 64 channel
+// vectors (512 bf16 / 256 fp32 channels).  Lane l walks the block's tokens in
+// order for its vector: every input row of the block is loaded once (no halo
+// re-reads), the static rows once per block, and the last TAPS inputs stay in
+// fp32 registers as the tap history.  The block's dynamic coefficients for
+// the wave's groups -- [token][tap][group] in memory -- are loaded as 16-byte
+// pieces by the whole wave and transposed through LDS to [token][group][tap],
+// so that each token's TAPS coefficients of a lane's group are one 16-byte
+// (bf16) or two (fp32) LDS reads.  Arithmetic: conv_core.h (shared with every
+// conv producer).
+// ---------------------------------------------------------------------------
+constexpr int kWalkMaxBlock = 16;
+constexpr int kWalkWaves = 4;                       // waves (independent units) per workgroup
+// Groups per wave slice: one 16-byte piece of coefficients per (token, tap)
+// (8 bf16 / 4 fp32 groups, i.e. 64-channel groups).
+template <typename TIO> constexpr int kPieceGroups = 16 / (int)sizeof(TIO);
+constexpr int kWalkMaxPieces = kWalkMaxBlock * 8 / 64;   // pieces per lane: tokens x taps / 64
+// LDS per wave: [token][group][8 tap slots]
+constexpr int kWalkLdsPerWave = kWalkMaxBlock * 16 * 8;   // bytes (bf16: 8 groups x 2 B; fp32: 4 x 4 B)
+
+struct WalkGeom {
+  int64_t units;              // waves with work: blocks * slices
+  int64_t delta_row_stride;   // elements
+  int32_t hidden, groups, block_size, slices;
+  int32_t vec_per_group;      // 16-byte vectors per group
+};
+
+template <typename TIO, int TAPS>
+__global__ __launch_bounds__(kWalkWaves * 64) __attribute__((amdgpu_waves_per_eu(TAPS >= 8 ? 2 : 3, 8))) void conv_walk_kernel(const TIO* __restrict__ x,
+                                                                    const TIO* __restrict__ base,
+                                                                    const TIO* __restrict__ delta,
+                                                                    TIO* __restrict__ out, WalkGeom g) {
+  constexpr int VEC = Elem<TIO>::kVec;
+  constexpr int E = (int)sizeof(TIO);
+  constexpr int PV = 16 / E;                        // elements per 16-byte piece
+  constexpr int TS = 8;                             // tap slots per (token, group) in LDS
+  extern __shared__ __align__(16) unsigned char cw_smem[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t unit_raw = (int64_t)blockIdx.x * kWalkWaves + wave;
+  const bool active = unit_raw < g.units;
+  const int64_t unit = active ? unit_raw : g.units - 1;   // a spare wave repeats the last unit, unstored
+  const int slice = (int)(unit % g.slices);
+  const int64_t blk = unit / g.slices;
+  const int H = g.hidden, B = g.block_size;
+  const int64_t row0 = blk * B;
+  const int v = slice * 64 + lane;                  // this lane's vector (slices are full)
+  const int c0 = v * VEC;
+  const int gl = lane / g.vec_per_group;            // this lane's group within the slice
+  TIO* s_d = reinterpret_cast<TIO*>(cw_smem) + (size_t)wave * (kWalkLdsPerWave / E);
+
+  // ---- every load of the block first: inputs, static rows, coefficients --
+  u32x4 xr[kWalkMaxBlock];
+#pragma unroll
+  for (int j = 0; j < kWalkMaxBlock; ++j)
+    if (j < B) xr[j] = ld16(x + (row0 + j) * H + c0);
+  u32x4 br[TAPS];
+#pragma unroll
+  for (int t = 0; t < TAPS; ++t) br[t] = ld16(base + (int64_t)t * H + c0);
+  // the block's coefficients for the slice's groups: one 16-byte piece per
+  // (token j, tap t), piece i = j * TAPS + t
+  const int64_t g0 = (int64_t)slice * kPieceGroups<TIO>;
+  const int n_pieces = B * TAPS;
+  u32x4 dr[kWalkMaxPieces];
+#pragma unroll
+  for (int p = 0; p < kWalkMaxPieces; ++p) {
+    const int i = min(p * 64 + lane, n_pieces - 1);
+    const int t = i % TAPS, j = i / TAPS;
+    if (p * 64 < n_pieces) dr[p] = ld16(delta + (row0 + j) * g.delta_row_stride + (int64_t)t * g.groups + g0);
+  }
+  // transpose to [token][group][tap slot] (slots past TAPS are never read)
+#pragma unroll
+  for (int p = 0; p < kWalkMaxPieces; ++p) {
+    const int i = p * 64 + lane;
+    if (i < n_pieces) {
+      const int t = i % TAPS, j = i / TAPS;
+      TIO* dst = s_d + (size_t)j * kPieceGroups<TIO> * TS + t;
+#pragma unroll
+      for (int k = 0; k < PV; ++k) {
+        if constexpr (E == 2) *reinterpret_cast<uint16_t*>(dst + k * TS) = (uint16_t)(dr[p][k >> 1] >> (16 * (k & 1)));
+        else *reinterpret_cast<uint32_t*>(dst + k * TS) = dr[p][k];
+      }
+    }
+  }
+  __syncthreads();
+
+  float bt[TAPS][VEC];
+#pragma unroll
+  for (int t = 0; t < TAPS; ++t) unpack16(br[t], bt[t]);
+  float hist[TAPS][VEC];                            // hist[t] = input row j - t
+#pragma unroll
+  for (int j = 0; j < kWalkMaxBlock; ++j) {
+    // a constant trip count (guarded) keeps the loop unrolled, so xr and
+    // hist stay in registers
+    if (j < B) {
+      // a compiler-only barrier: each token's LDS reads stay in its own
+      // iteration (hoisting all of them ahead of the loop spills registers)
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int t = TAPS - 1; t > 0; --t)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) hist[t][e] = hist[t - 1][e];
+      unpack16(xr[j], hist[0]);
+      // this token's coefficients of the lane's group, tap slots 0..TS-1
+      const TIO* dj = s_d + ((size_t)j * kPieceGroups<TIO> + gl) * TS;
+      float d[TS];
+      if constexpr (E == 2) {
+        unpack16(ld16(dj), d);
+      } else {
+        float lo[4], hi[4];
+        unpack16(ld16(dj), lo);
+        unpack16(ld16(dj + 4), hi);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { d[k] = lo[k]; d[4 + k] = hi[k]; }
+      }
+      float acc[VEC];
+      conv_token<VEC, TAPS>(
+          j, [&](int t, float (&coef)[VEC]) { coef_one_group<VEC>(bt[t], d[t], coef); },
+          [&](int t, float (&xv)[VEC]) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) xv[e] = hist[t][e];
+          },
+          acc);
+      if (active) store_vec(out + (row0 + j) * H + c0, acc);
+    }
+  }
+}
+
+// The block walk's plan, or units == 0 when it does not apply: <= 8 taps,
+// blocks of <= 16 tokens, whole 64-vector slices, each slice's groups one
+// 16-byte piece of a coefficient row (64-channel groups), 16-byte aligned
+// coefficient pieces.
+WalkGeom plan_walk(const ConvArgs& a) {
+  WalkGeom w{};
+  const int vec = a.dtype == DFLASH_BF16 ? 8 : 4, e = a.dtype == DFLASH_BF16 ? 2 : 4;
+  const int nvec = a.hidden / vec;
+  const int G = a.hidden / a.group_size;
+  if (a.taps > 8 || a.block_size > kWalkMaxBlock || nvec % 64) return w;
+  if (64 * vec != (16 / e) * a.group_size) return w;
+  if ((a.delta_row_stride * e) % 16 || ((int64_t)G * e) % 16 || (reinterpret_cast<uintptr_t>(a.delta) & 15)) return w;
+  w.hidden = a.hidden;
+  w.groups = G;
+  w.block_size = a.block_size;
+  w.slices = nvec / 64;
+  w.vec_per_group = a.group_size / vec;
+  w.delta_row_stride = a.delta_row_stride;
+  w.units = (a.n_tokens / a.block_size) * w.slices;
+  return w;
+}
+
+template <typename TIO, int TAPS>
+hipError_t launch_walk_t(const ConvArgs& a, const WalkGeom& w, hipStream_t s) {
+  const dim3 grid((unsigned)((w.units + kWalkWaves - 1) / kWalkWaves));
+  hipLaunchKernelGGL((conv_walk_kernel<TIO, TAPS>), grid, dim3(kWalkWaves * 64), kWalkWaves * kWalkLdsPerWave, s,
+                     static_cast<const TIO*>(a.x), static_cast<const TIO*>(a.base), static_cast<const TIO*>(a.delta),
+                     static_cast<TIO*>(a.out), w);
+  return hipGetLastError();
+}
+
 template <typename TIO, int TAPS>
 hipError_t launch_t(const ConvArgs& a, const ConvGeom& g, hipStream_t s) {
+  const WalkGeom w = plan_walk(a);
+  if (w.units > 0) return launch_walk_t<TIO, TAPS>(a, w, s);
   const dim3 grid((unsigned)((g.units + kThreads - 1) / kThreads));
   const bool one_group = (a.group_size % Elem<TIO>::kVec) == 0;
   const TIO* x = static_cast<const TIO*>(a.x);

@@ -6,7 +6,7 @@
 // for bit: the coefficient is base + delta in fp32, the taps are taken in
 // order 0, 1, ..., the first product is rounded on its own and every later
 // one is fused into the sum, and the result is rounded once to the storage
-// dtype.
+// dtype (bf16: to nearest, ties to even).
 #pragma once
 
 #include "device_common.h"
@@ -37,13 +37,21 @@ __device__ __forceinline__ void coef_one_group(const float (&bt)[VEC], float d, 
   for (int e = 0; e < VEC; ++e) coef[e] = bt[e] + d;
 }
 
-// Eight fp32 conv outputs rounded to bf16 (nearest, ties to even), packed.
+// Eight fp32 conv outputs rounded to bf16 (nearest, ties to even), packed:
+// v_cvt_pk_bf16_f32 rounds two values per instruction in the default
+// round-to-nearest-even mode.
+typedef __bf16 conv_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float conv_f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const conv_f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, conv_bf16x2_t));
+}
 __device__ __forceinline__ uint4 pack_bf16x8(const float (&a)[8]) {
   uint4 v;
-  v.x = f32_to_bf16_rne(a[0]) | (f32_to_bf16_rne(a[1]) << 16);
-  v.y = f32_to_bf16_rne(a[2]) | (f32_to_bf16_rne(a[3]) << 16);
-  v.z = f32_to_bf16_rne(a[4]) | (f32_to_bf16_rne(a[5]) << 16);
-  v.w = f32_to_bf16_rne(a[6]) | (f32_to_bf16_rne(a[7]) << 16);
+  v.x = pack_bf16x2(a[0], a[1]);
+  v.y = pack_bf16x2(a[2], a[3]);
+  v.z = pack_bf16x2(a[4], a[5]);
+  v.w = pack_bf16x2(a[6], a[7]);
   return v;
 }
 

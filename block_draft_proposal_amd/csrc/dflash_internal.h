@@ -188,13 +188,22 @@ size_t verify_workspace_bytes(int32_t n_req, int32_t slots, int64_t valid_vocab)
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 
 // Lattice and walk in one kernel (one workgroup per request) when the
-// request's lattice and its staging fit in LDS; bit-identical to
-// launch_lattice followed by launch_walk.  scores_out may be null.
+// request's scores and staging fit in LDS; bit-identical to launch_lattice
+// followed by launch_walk.  scores_out may be null.
 // gfx950 lets one workgroup address 160 KB of LDS
 constexpr size_t kLatticeWalkLdsMax = 160 * 1024;
 constexpr size_t kWalkLdsMax = 160 * 1024;
 size_t lattice_walk_lds_bytes(int slots, int top_k, int rank, int dtype);
-bool lattice_walk_fits(const struct SelectArgs& a);   // LDS size, rank multiple of a vector, 16-byte tables
+bool lattice_walk_fits(const struct SelectArgs& a);   // one kernel can take the request (see below)
+// Requests at which the fused lattice + walk switches from one workgroup per
+// request (every row decided in parallel) to one wave per request (only the
+// walked rows decided, requests overlapping each other).
+constexpr int kLatticeWalkWaveMinReq = 512;
+bool lattice_walk_per_wave(const struct SelectArgs& a);
+// Floats of one slot's zero-padded u row in the lattice kernels (the fp32
+// matrix-core tile's k extent for top_k candidates and this rank).
+int lattice_kpad_floats(int32_t top_k, int32_t rank, int32_t dtype);
+constexpr int kMaxLatticeKpad = 4096;   // keeps the standalone lattice's LDS (4 waves' u rows) at 64 KB
 hipError_t launch_lattice_walk(const SelectArgs& a, const ProjPlan& p, const WalkArgs& w, float* scores_out,
                                hipStream_t stream);
 

@@ -206,208 +206,200 @@ __device__ __forceinline__ float sum_proj_slices(const float* __restrict__ u_par
   return add_proj_slices(v, ksplit);
 }
 
-template <typename TIO>
-__device__ __forceinline__ float load_f32(const TIO* p, int64_t i) { return Elem<TIO>::to_f32(p[i]); }
 
-// One lattice block (K x K) for slot row n = req * slots + s, evaluated into
-// `dst` (global or LDS) with row stride K.  All threads of the workgroup call.
-template <typename TIO>
-__device__ void lattice_block(const int64_t* __restrict__ ids, const float* __restrict__ unary,
-                              const int64_t* __restrict__ anchor, const TIO* __restrict__ A,
-                              const TIO* __restrict__ B, const float* __restrict__ u_parts,
-                              int ksplit, int n_rows, int req, int s, int slots, int K, int r,
-                              int64_t vocab, float* s_u, float* s_w, float* s_bt, int64_t* s_pred,
-                              int64_t* s_cand, float* dst) {
-  const int tid = threadIdx.x;
-  const int n = req * slots + s;
-  const int wstride = r + 1;                         // padded row of w (LDS banks)
-  for (int k = tid; k < r; k += kThreads) s_u[k] = sum_proj_slices(u_parts, ksplit, r, n, k);
-  for (int j = tid; j < K; j += kThreads) {
-    s_pred[j] = (s == 0) ? anchor[req] : ids[((int64_t)req * slots + s - 1) * K + j];
-    s_cand[j] = ids[(int64_t)n * K + j];
-  }
-  __syncthreads();
-  for (int i = tid; i < K * r; i += kThreads) {
-    const int j = i / r, k = i % r;
-    const int64_t p = s_pred[j], c = s_cand[j];
-    const float a = (p >= 0 && p < vocab) ? load_f32(A, p * r + k) : __builtin_nanf("");
-    const float b = (c >= 0 && c < vocab) ? load_f32(B, c * r + k) : __builtin_nanf("");
-    s_w[j * wstride + k] = a * s_u[k];               // A[p] (.) project(h)
-    s_bt[k * K + j] = b;
-  }
-  __syncthreads();
-  for (int e = tid; e < K * K; e += kThreads) {
-    const int j = e / K, c = e % K;
-    const float* w = s_w + j * wstride;
-    float acc = 0.f;
-    for (int k = 0; k < r; ++k) acc = fmaf(w[k], s_bt[k * K + c], acc);
-    dst[j * K + c] = acc + unary[(int64_t)n * K + c];
-  }
-  __syncthreads();
-}
+// ---------------------------------------------------------------------------
+// The K x K lattice block of one slot as one fp32 matrix-core tile.
+//
+// scores[j][c] = sum_k w[j][k] B[c][k] + unary[c],  w[j] = A[pred_j] (.) u
+// is a (K x r) by (r x K) product: one v_mfma_f32_16x16x4_f32 tile for
+// K <= 16, one v_mfma_f32_32x32x2_f32 tile for K <= 32.  Lane l serves row /
+// column e = l % MT (predecessor row j of the A operand, candidate c of the B
+// operand) and k-group g = l / MT of G = 64 / MT groups; group g owns the
+// contiguous range k in [g L, g L + L) (L a multiple of the 16-byte vector,
+// G L >= r; k >= r enters as zero), so each lane gathers one contiguous
+// piece of its two table rows with 16-byte loads.  MFMA step kk takes
+// k = g L + kk from every group.  Operands are fp32 (A * u rounded once to
+// fp32, B exact), never bf16: rounding A (.) u to bf16 would blur near-ties.
+// Every lattice evaluation (standalone or fused with the walk) runs this same
+// sequence, so they agree bit for bit.
+// ---------------------------------------------------------------------------
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-template <typename TIO>
-__global__ __launch_bounds__(kThreads) void lattice_kernel(const int64_t* __restrict__ ids,
-                                                           const float* __restrict__ unary,
-                                                           const int64_t* __restrict__ anchor,
-                                                           const TIO* __restrict__ A,
-                                                           const TIO* __restrict__ B,
-                                                           const float* __restrict__ u_parts,
-                                                           int32_t ksplit, int32_t slots, int32_t K,
-                                                           int32_t r, int64_t vocab, int32_t n_rows,
-                                                           float* __restrict__ scores) {
-  extern __shared__ float smem[];
-  float* s_u = smem;                                     // r
-  float* s_w = s_u + r;                                  // K * (r + 1)
-  float* s_bt = s_w + K * (r + 1);                       // r * K
-  const int used = r + K * (r + 1) + r * K;
-  int64_t* s_ids = reinterpret_cast<int64_t*>(smem + ((used + 1) & ~1));  // 2K, 8-byte aligned
-  const int n = blockIdx.x;
-  const int req = n / slots, s = n % slots;
-  lattice_block<TIO>(ids, unary, anchor, A, B, u_parts, ksplit, n_rows, req, s, slots, K, r, vocab,
-                     s_u, s_w, s_bt, s_ids, s_ids + K, scores + (int64_t)n * K * K);
-}
-
-// The same lattice block for the common case (rank a multiple of the 16-byte
-// vector, 16-byte aligned tables): 16-byte gathers of the A and B rows, B
-// kept one row per candidate in LDS, and each thread evaluates a TJ x TC
-// tile of entries, so that every LDS read feeds TJ or TC chains.  Every
-// entry is still one fma chain over k from 0 with w = A * u, so the result
-// equals lattice_block's bit for bit.
-// LDS: pred, cand [K] (int64), u [r], w [K][r+4] (fp32), B rows [K][r + 16 B].
-struct LatticeTileLds {
-  size_t pred, cand, u, w, b, bytes;
-  int wstride, bstride;
+template <int MT> struct LatTile;
+template <> struct LatTile<16> {
+  typedef f32x4_t acc_t;
+  static constexpr int kAcc = 4;
+  __device__ static acc_t mfma(float a, float b, acc_t c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
+  // row of accumulator i in this lane (its column is lane % 16)
+  __device__ static int row(int lane, int i) { return 4 * (lane >> 4) + i; }
 };
-__host__ __device__ inline LatticeTileLds lattice_tile_layout(int K, int r, int elem) {
-  LatticeTileLds L;
-  L.wstride = r + 4;
-  L.bstride = r + 16 / elem;
-  size_t o = 0;
-  L.pred = o; o += (size_t)K * 8;
-  L.cand = o; o += (size_t)K * 8;
-  L.u = o;    o += (((size_t)r * 4) + 15) & ~(size_t)15;
-  L.w = o;    o += (size_t)K * L.wstride * 4;
-  L.b = o;    o += (size_t)K * L.bstride * elem;
-  L.bytes = o;
-  return L;
+template <> struct LatTile<32> {
+  typedef f32x16_t acc_t;
+  static constexpr int kAcc = 16;
+  __device__ static acc_t mfma(float a, float b, acc_t c) { return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0); }
+  __device__ static int row(int lane, int i) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+};
+
+// Tile size and k-range length per lane group for K candidates, rank r and
+// `vec` elements per 16-byte vector (the shape every kernel and the host use).
+__host__ __device__ inline int lattice_mt(int K) { return K <= 16 ? 16 : 32; }
+__host__ __device__ inline int lattice_group_len(int K, int r, int vec) {
+  const int G = 64 / lattice_mt(K);
+  return (r + G * vec - 1) / (G * vec) * vec;
+}
+// k extent of the padded u row (G L floats, zeros past r).
+__host__ __device__ inline int lattice_kpad(int K, int r, int vec) {
+  return (64 / lattice_mt(K)) * lattice_group_len(K, r, vec);
 }
 
-template <typename TIO, int TJ, int TC>
-__global__ __launch_bounds__(kThreads) void lattice_tiled_kernel(
+// Table rows are gathered with 16-byte loads when every row and the tables
+// are 16-byte aligned; otherwise element by element into the same packed
+// vectors (odd ranks), with the same arithmetic afterwards.
+template <typename TIO>
+__device__ __forceinline__ u32x4 gather_piece(const TIO* __restrict__ row, int k, int r, bool vload) {
+  constexpr int VEC = Elem<TIO>::kVec;
+  if (vload) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    return k < r ? ld16(row + k) : zero;          // a vector lies wholly inside or past r
+  }
+  TIO e[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) e[i] = (k + i < r) ? row[k + i] : TIO(0);
+  return *reinterpret_cast<const u32x4*>(e);
+}
+
+// The two table rows a lane gathers for one slot: A[pred] and B[cand]
+// (row 0 for an id outside [0, vocab), whose products become NaN).
+template <typename TIO>
+struct TileRows {
+  const TIO* arow;
+  const TIO* brow;
+  bool pok, cok;
+};
+template <typename TIO>
+__device__ __forceinline__ TileRows<TIO> tile_rows(const TIO* __restrict__ A, const TIO* __restrict__ B,
+                                                   int64_t vocab, int r, int64_t pred, int64_t cand) {
+  TileRows<TIO> t;
+  t.pok = pred >= 0 && pred < vocab;
+  t.cok = cand >= 0 && cand < vocab;
+  t.arow = A + (t.pok ? pred : 0) * (int64_t)r;
+  t.brow = B + (t.cok ? cand : 0) * (int64_t)r;
+  return t;
+}
+
+// Gathers pieces v0 .. v0 + NB - 1 (those below nv) of the lane's k-range
+// (starting at kg) of both rows.
+template <typename TIO, int NB>
+__device__ __forceinline__ void tile_gather(const TileRows<TIO>& t, int kg, int v0, int nv, int r, bool vload,
+                                            u32x4 (&av)[NB], u32x4 (&bv)[NB]) {
+  constexpr int VEC = Elem<TIO>::kVec;
+#pragma unroll
+  for (int v = 0; v < NB; ++v) {
+    if (v0 + v < nv) {
+      av[v] = gather_piece(t.arow, kg + (v0 + v) * VEC, r, vload);
+      bv[v] = gather_piece(t.brow, kg + (v0 + v) * VEC, r, vload);
+    }
+  }
+}
+
+// The MFMA steps of those pieces: k = kg + (v0 + v) VEC + e in order, with
+// w = A * u rounded to fp32 (NaN for an out-of-range predecessor) against B
+// (NaN for an out-of-range candidate).
+template <typename TIO, int MT, int NB>
+__device__ __forceinline__ void tile_mfma(typename LatTile<MT>::acc_t& acc, const u32x4 (&av)[NB],
+                                          const u32x4 (&bv)[NB], bool pok, bool cok, int kg, int v0, int nv,
+                                          const float* s_u) {
+  constexpr int VEC = Elem<TIO>::kVec;
+  const float nan = __builtin_nanf("");
+#pragma unroll
+  for (int v = 0; v < NB; ++v) {
+    if (v0 + v < nv) {
+      float a[VEC], b[VEC];
+      unpack16(av[v], a);
+      unpack16(bv[v], b);
+      const float* u = s_u + kg + (v0 + v) * VEC;
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) {
+        const float4 u4 = *reinterpret_cast<const float4*>(u + e);
+        const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float w = pok ? a[e + i] * uu[i] : nan;        // A[p] (.) project(h)
+          acc = LatTile<MT>::mfma(w, cok ? b[e + i] : nan, acc);
+        }
+      }
+    }
+  }
+}
+
+// One slot's tile on one wave.  pred / cand: this lane's predecessor and
+// candidate token ids (lanes past K pass any in-range id; their rows and
+// columns are not used); s_u: the slot's u, G L floats (zeros past r), in LDS.
+// An id outside [0, vocab) turns its whole row (pred) or column (cand) NaN.
+// NB: 16-byte pieces of each table row gathered per round (register budget
+// only: the MFMA sequence is the same for every NB).
+template <typename TIO, int MT, int NB>
+__device__ __forceinline__ typename LatTile<MT>::acc_t lattice_slot_tile(
+    const TIO* __restrict__ A, const TIO* __restrict__ B, int64_t vocab, int r, int L, bool vload, int64_t pred,
+    int64_t cand, const float* s_u) {
+  constexpr int VEC = Elem<TIO>::kVec;
+  const int lane = threadIdx.x & 63;
+  const int kg = (lane / MT) * L;
+  const TileRows<TIO> t = tile_rows(A, B, vocab, r, pred, cand);
+  typename LatTile<MT>::acc_t acc = {};
+  const int nv = L / VEC;
+  for (int v0 = 0; v0 < nv; v0 += NB) {
+    u32x4 av[NB], bv[NB];
+    tile_gather<TIO, NB>(t, kg, v0, nv, r, vload, av, bv);
+    tile_mfma<TIO, MT, NB>(acc, av, bv, t.pok, t.cok, kg, v0, nv, s_u);
+  }
+  return acc;
+}
+
+// Stores one slot's tile plus unary: row j, column c of the block goes to
+// dst[j * row_stride + c] (global or LDS); rows and columns past K are not
+// stored.  un: the slot's unary [K] (global).
+template <int MT>
+__device__ __forceinline__ void lattice_store(const typename LatTile<MT>::acc_t& acc, const float* __restrict__ un,
+                                              int K, float* dst, int row_stride) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane % MT;
+  if (c >= K) return;
+  const float uc = un[c];
+#pragma unroll
+  for (int i = 0; i < LatTile<MT>::kAcc; ++i) {
+    const int j = LatTile<MT>::row(lane, i);
+    if (j < K) dst[j * row_stride + c] = acc[i] + uc;
+  }
+}
+
+// Standalone lattice: one wave per slot row, four per workgroup.  LDS: each
+// wave's u row (G L floats).
+constexpr int kLatWaves = 4;
+
+template <typename TIO, int MT>
+__global__ __launch_bounds__(kLatWaves * 64) void lattice_mfma_kernel(
     const int64_t* __restrict__ ids, const float* __restrict__ unary, const int64_t* __restrict__ anchor,
     const TIO* __restrict__ A, const TIO* __restrict__ B, const float* __restrict__ u_parts, int32_t ksplit,
-    int32_t slots, int32_t K, int32_t r, int64_t vocab, int32_t n_rows, float* __restrict__ scores) {
-  constexpr int VEC = Elem<TIO>::kVec;
-  extern __shared__ __align__(16) unsigned char lt_smem[];
-  const LatticeTileLds L = lattice_tile_layout(K, r, (int)sizeof(TIO));
-  int64_t* s_pred = reinterpret_cast<int64_t*>(lt_smem + L.pred);
-  int64_t* s_cand = reinterpret_cast<int64_t*>(lt_smem + L.cand);
-  float* s_u = reinterpret_cast<float*>(lt_smem + L.u);
-  float* s_w = reinterpret_cast<float*>(lt_smem + L.w);
-  TIO* s_b = reinterpret_cast<TIO*>(lt_smem + L.b);
-  const int tid = threadIdx.x;
-  const int n = blockIdx.x;
-  const int req = n / slots, s = n % slots;
-
-  for (int k = tid; k < r; k += kThreads) s_u[k] = sum_proj_slices(u_parts, ksplit, r, n, k);
-  for (int j = tid; j < K; j += kThreads) {
-    s_pred[j] = (s == 0) ? anchor[req] : ids[((int64_t)req * slots + s - 1) * K + j];
-    s_cand[j] = ids[(int64_t)n * K + j];
-  }
+    int32_t slots, int32_t K, int32_t r, int32_t L, int32_t vload, int64_t vocab, int32_t n_rows,
+    float* __restrict__ scores) {
+  extern __shared__ __align__(16) float lat_smem[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kpad = (64 / MT) * L;
+  float* s_u = lat_smem + wave * kpad;
+  const int n_raw = blockIdx.x * kLatWaves + wave;
+  const bool row_ok = n_raw < n_rows;
+  const int n = row_ok ? n_raw : n_rows - 1;        // a wave past the rows repeats the last one, unstored
+  const int req = n / slots, s = n - req * slots;
+  for (int k = lane; k < kpad; k += 64) s_u[k] = k < r ? sum_proj_slices(u_parts, ksplit, r, n, k) : 0.f;
+  const int e = lane % MT;
+  const int ec = e < K ? e : 0;
+  const int64_t pred = (s == 0) ? anchor[req] : ids[((int64_t)n - 1) * K + ec];
+  const int64_t cand = ids[(int64_t)n * K + ec];
   __syncthreads();
-
-  // gather: 16-byte pieces, unconditional loads (ids clamped into range),
-  // out-of-range ids become NaN afterwards
-  {
-    constexpr int kPer = 4;
-    const int ppr = r / VEC;
-    const int n_pieces = K * ppr;                   // per table
-    const int total = 2 * n_pieces;
-    for (int base = 0; base < total; base += kThreads * kPer) {
-      u32x4 raw[kPer];
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const int i = min(base + q * kThreads + tid, total - 1);
-        const bool is_b = i >= n_pieces;
-        const int ii = is_b ? i - n_pieces : i;
-        const int j = ii / ppr, v = ii - j * ppr;
-        const int64_t t = is_b ? s_cand[j] : s_pred[j];
-        const int64_t tc = (t >= 0 && t < vocab) ? t : 0;
-        raw[q] = ld16((is_b ? B : A) + tc * r + v * VEC);
-      }
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const int i = base + q * kThreads + tid;
-        if (i >= total) continue;
-        const bool is_b = i >= n_pieces;
-        const int ii = is_b ? i - n_pieces : i;
-        const int j = ii / ppr, v = ii - j * ppr;
-        const int64_t t = is_b ? s_cand[j] : s_pred[j];
-        const bool ok = t >= 0 && t < vocab;
-        if (is_b) {
-          TIO nanrow[VEC];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) nanrow[e] = Elem<TIO>::nan_value();
-          st16(s_b + (size_t)j * L.bstride + v * VEC, ok ? raw[q] : ld16(nanrow));
-        } else {
-          float a[VEC];
-          unpack16(raw[q], a);
-#pragma unroll
-          for (int e = 0; e < VEC; e += 4)
-            *reinterpret_cast<float4*>(s_w + j * L.wstride + v * VEC + e) =
-                make_float4((ok ? a[e] : __builtin_nanf("")) * s_u[v * VEC + e],
-                            (ok ? a[e + 1] : __builtin_nanf("")) * s_u[v * VEC + e + 1],
-                            (ok ? a[e + 2] : __builtin_nanf("")) * s_u[v * VEC + e + 2],
-                            (ok ? a[e + 3] : __builtin_nanf("")) * s_u[v * VEC + e + 3]);
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  // TJ x TC tiles of the K x K block; rows and columns past K are clamped
-  // (computed, not stored)
-  const int ntc = (K + TC - 1) / TC, ntiles = ((K + TJ - 1) / TJ) * ntc;
-  for (int t = tid; t < ntiles; t += kThreads) {
-    const int j0 = (t / ntc) * TJ, c0 = (t % ntc) * TC;
-    const float* w[TJ];
-    const TIO* b[TC];
-#pragma unroll
-    for (int a = 0; a < TJ; ++a) w[a] = s_w + min(j0 + a, K - 1) * L.wstride;
-#pragma unroll
-    for (int c = 0; c < TC; ++c) b[c] = s_b + (size_t)min(c0 + c, K - 1) * L.bstride;
-    float acc[TJ][TC];
-#pragma unroll
-    for (int a = 0; a < TJ; ++a)
-#pragma unroll
-      for (int c = 0; c < TC; ++c) acc[a][c] = 0.f;
-    for (int k0 = 0; k0 < r; k0 += VEC) {
-      float bv[TC][VEC];
-#pragma unroll
-      for (int c = 0; c < TC; ++c) unpack16(ld16(b[c] + k0), bv[c]);
-#pragma unroll
-      for (int a = 0; a < TJ; ++a) {
-#pragma unroll
-        for (int e4 = 0; e4 < VEC; e4 += 4) {
-          const float4 wv = *reinterpret_cast<const float4*>(w[a] + k0 + e4);
-#pragma unroll
-          for (int c = 0; c < TC; ++c) {
-            acc[a][c] = fmaf(wv.x, bv[c][e4 + 0], acc[a][c]);
-            acc[a][c] = fmaf(wv.y, bv[c][e4 + 1], acc[a][c]);
-            acc[a][c] = fmaf(wv.z, bv[c][e4 + 2], acc[a][c]);
-            acc[a][c] = fmaf(wv.w, bv[c][e4 + 3], acc[a][c]);
-          }
-        }
-      }
-    }
-    float* dst = scores + (int64_t)n * K * K;
-#pragma unroll
-    for (int a = 0; a < TJ; ++a)
-#pragma unroll
-      for (int c = 0; c < TC; ++c)
-        if (j0 + a < K && c0 + c < K) dst[(j0 + a) * K + c0 + c] = acc[a][c] + unary[(int64_t)n * K + c0 + c];
-  }
+  const typename LatTile<MT>::acc_t acc =
+      lattice_slot_tile<TIO, MT, 8>(A, B, vocab, r, L, vload != 0, pred, cand, s_u);
+  if (row_ok) lattice_store<MT>(acc, unary + (int64_t)n * K, K, scores + (int64_t)n * K * K, K);
 }
 
 // Lane j's value of v, as a wave-uniform value.
@@ -639,200 +631,219 @@ __global__ __launch_bounds__(kWalkThreads) void walk_lds_kernel(const float* __r
                                 row0, ids + row0 * K, tokens, q_out);
 }
 
-// Lattice + walk for one request in one workgroup of 1024 threads, when the
-// request's whole lattice and its staging fit in LDS.  Same per-entry
-// arithmetic as lattice_block (u summed over the projection slices in order,
-// w = A * u, fma chain over k from 0, + unary) and the same decision
-// arithmetic as walk_decide, so the result is bit-identical to lattice_kernel
-// followed by walk_kernel.  Phases, each one round of global loads or pure
-// LDS work:
-//   1. ids of every slot and its predecessor, u, unary, uniforms -> LDS
-//   2. w = A[pred] (.) u (fp32) and the B[cand] rows -> LDS
-//   3. one thread per lattice entry: its fma chain over k
-//   4, 5. decide_and_walk: every row's decision in parallel, then the walked
+
+// Lattice + walk for one request in one workgroup of 1024 threads (16
+// waves).  The lattice is lattice_slot_tile's (bit-identical to
+// lattice_mfma_kernel) and the decisions decide_and_walk's (bit-identical to
+// the walk kernels), so the result equals dflash_lattice followed by
+// dflash_walk.  Phases:
+//   1. candidate ids of every slot, uniforms, and u of every slot (the
+//      projection slices summed in order, zero past r) -> LDS, one round of
+//      loads;
+//   2. wave w evaluates slots w, w + 16, ...: its table gathers, the fp32
+//      matrix-core tile, + unary -> the score rows in LDS (and scores_out);
+//   3, 4. decide_and_walk: every row's decision in parallel, then the walked
 //      path by pointer jumping, q rows and tokens written in parallel.
-// LDS layout: pred ids [S][K], cand ids [S][K] (int64), w [S][K][r+4] (fp32;
-// rows 16-byte aligned and 4 banks apart), B rows [S][K][r + 16 bytes]
-// (storage dtype, one row per candidate), unary [S][K], scores [S][K][K+1]
-// (then exponentials, then q), u [S][r] during the gather (the scan's
-// second buffer during the walk), row maxima [S][K], uniforms [S], chosen
+// LDS: candidate ids [S][K] (int64), u [S][G L] (the scan's second buffer
+// afterwards), scores [S][K][K+1], row maxima [S][K], uniforms [S], chosen
 // index per row [S][K].
 constexpr int kLWThreads = 1024;
 
 struct LatticeWalkLds {
-  size_t pred, cand, w, b, unary, sc, e, mx, un, next, bytes;
-  int wstride, bstride;   // row strides of w (floats) and B rows (elements)
+  size_t cand, u, sc, mx, un, next, bytes;
 };
 
-__host__ __device__ inline LatticeWalkLds lattice_walk_layout(int S, int K, int r, int elem) {
+__host__ __device__ inline LatticeWalkLds lattice_walk_layout(int S, int K, int kpad) {
   LatticeWalkLds L;
-  L.wstride = r + 4;
-  L.bstride = r + 16 / elem;
-  const size_t u_bytes = (size_t)S * r * 4, g_bytes = (size_t)S * K * 4;
+  const size_t u_floats = (size_t)S * (kpad > K ? kpad : K);
   size_t o = 0;
-  L.pred = o;  o += (size_t)S * K * 8;
-  L.cand = o;  o += (size_t)S * K * 8;
-  L.w = o;     o += (size_t)S * K * L.wstride * 4;
-  L.b = o;     o += (size_t)S * K * L.bstride * elem;
-  L.unary = o; o += (size_t)S * K * 4;
-  L.sc = o;    o += (size_t)S * K * (K + 1) * 4;
-  L.e = o;     o += u_bytes > g_bytes ? u_bytes : g_bytes;
-  L.mx = o;    o += (size_t)S * K * 4;
-  L.un = o;    o += (size_t)S * 4;
-  L.next = o;  o += (size_t)S * K * 4;
+  L.cand = o; o += (size_t)S * K * 8;
+  L.u = o;    o += (u_floats * 4 + 15) & ~(size_t)15;
+  L.sc = o;   o += (size_t)S * K * (K + 1) * 4;
+  L.mx = o;   o += (size_t)S * K * 4;
+  L.next = o; o += (size_t)S * K * 4;
+  L.un = o;   o += (size_t)S * 4;
   L.bytes = o;
   return L;
 }
 
-template <typename TIO>
+template <typename TIO, int MT>
 __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
     const int64_t* __restrict__ ids, const float* __restrict__ unary, const int64_t* __restrict__ anchor,
     const TIO* __restrict__ A, const TIO* __restrict__ B, const float* __restrict__ u_parts, int32_t ksplit,
-    int32_t slots, int32_t K, int32_t r, int64_t vocab, int32_t n_rows, const float* __restrict__ uniforms,
-    const float* __restrict__ temperatures, const uint8_t* __restrict__ greedy_mask,
-    float* __restrict__ scores_out, int64_t* __restrict__ tokens, float* __restrict__ q_out) {
+    int32_t slots, int32_t K, int32_t r, int32_t L, int32_t vload, int64_t vocab,
+    const float* __restrict__ uniforms, const float* __restrict__ temperatures,
+    const uint8_t* __restrict__ greedy_mask, float* __restrict__ scores_out, int64_t* __restrict__ tokens,
+    float* __restrict__ q_out) {
   extern __shared__ __align__(16) unsigned char lw_smem[];
   const int req = blockIdx.x;
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int S = slots;
-  const LatticeWalkLds L = lattice_walk_layout(S, K, r, (int)sizeof(TIO));
-  int64_t* s_pred = reinterpret_cast<int64_t*>(lw_smem + L.pred);
-  int64_t* s_cand = reinterpret_cast<int64_t*>(lw_smem + L.cand);
-  float* s_u = reinterpret_cast<float*>(lw_smem + L.e);      // u during the gather, the scan buffer afterwards
-  float* s_w = reinterpret_cast<float*>(lw_smem + L.w);
-  TIO* s_b = reinterpret_cast<TIO*>(lw_smem + L.b);
-  float* s_unary = reinterpret_cast<float*>(lw_smem + L.unary);
-  float* s_sc = reinterpret_cast<float*>(lw_smem + L.sc);
-  float* s_mx = reinterpret_cast<float*>(lw_smem + L.mx);
-  float* s_un = reinterpret_cast<float*>(lw_smem + L.un);
-  int* s_next = reinterpret_cast<int*>(lw_smem + L.next);
+  const int kpad = (64 / MT) * L;
+  const LatticeWalkLds Ly = lattice_walk_layout(S, K, kpad);
+  int64_t* s_cand = reinterpret_cast<int64_t*>(lw_smem + Ly.cand);
+  float* s_u = reinterpret_cast<float*>(lw_smem + Ly.u);
+  float* s_sc = reinterpret_cast<float*>(lw_smem + Ly.sc);
+  float* s_mx = reinterpret_cast<float*>(lw_smem + Ly.mx);
+  float* s_un = reinterpret_cast<float*>(lw_smem + Ly.un);
+  int* s_next = reinterpret_cast<int*>(lw_smem + Ly.next);
   const int64_t row0 = (int64_t)req * S;            // first slot row of this request
-  const int wstride = L.wstride, bstride = L.bstride;
-  const FastDiv div_k(K), div_r(r);                 // every index below is < 2^16 (LDS bound)
+  const FastDiv div_k(K), div_kp(kpad);             // every index below is < 2^16 (LDS bound)
 
-  // ---- 1. ids, u (projection slices summed in order), unary, uniforms ----
-  // Each pass issues every load of its items (uniform, ids, unary, all u
-  // slices) before the first LDS write or add, so the phase costs one memory
-  // round trip per pass (one pass whenever S * max(K, r) <= 1024).
+  // ---- 1. candidate ids, uniforms, u -----------------------------------
+  // Each pass issues every load of its items before the first LDS write or
+  // add, so the phase costs one memory round trip per pass (one pass
+  // whenever S * max(K, G L) <= 1024).
   {
-    const int n_e = S * K, n_u = S * r;
+    const int n_e = S * K, n_u = S * kpad;
     const int n_all = max(max(n_e, n_u), S);
     for (int i = tid; i < n_all; i += kLWThreads) {
-      const bool has_e = i < n_e, has_u = i < n_u, has_s = i < S;
-      float uni = 0.f, un = 0.f;
-      int64_t pred = 0, cand = 0;
+      const bool has_e = i < n_e, has_s = i < S;
+      bool has_u = i < n_u;
+      float uni = 0.f;
+      int64_t cand = 0;
       float v[kMaxProjSplit];
+      int s_u_row = 0, k = 0;
       if (has_s) uni = uniforms[row0 + i];
-      if (has_e) {
-        const int s = div_k.quot(i), j = i - s * K;
-        pred = (s == 0) ? anchor[req] : ids[(row0 + s - 1) * K + j];
-        cand = ids[row0 * K + i];
-        un = unary[row0 * K + i];
-      }
+      if (has_e) cand = ids[row0 * K + i];
       if (has_u) {
-        const int s = div_r.quot(i);
-        load_proj_slices(u_parts, ksplit, r, row0 + s, i - s * r, v);
+        s_u_row = div_kp.quot(i);
+        k = i - s_u_row * kpad;
+        if (k < r) load_proj_slices(u_parts, ksplit, r, row0 + s_u_row, k, v);
       }
       // keep the compiler from sinking the slice loads below the LDS writes
       // (which would start a second round trip after the first one drained)
       asm volatile("" ::: "memory");
       if (has_s) s_un[i] = uni;
-      if (has_e) {
-        s_pred[i] = pred;
-        s_cand[i] = cand;
-        s_unary[i] = un;
-      }
-      if (has_u) s_u[i] = add_proj_slices(v, ksplit);
+      if (has_e) s_cand[i] = cand;
+      if (has_u) s_u[i] = k < r ? add_proj_slices(v, ksplit) : 0.f;
     }
   }
   __syncthreads();
 
-  // ---- 2. gather: w = A[pred] (.) u (fp32), B[cand] rows ------------------
-  // 16-byte pieces of the table rows (r is a multiple of VEC, rows 16-byte
-  // aligned).  Loads are unconditional (indices clamped into range) so that
-  // every thread issues all of its loads before the first use; out-of-range
-  // ids become NaN afterwards.
+  // ---- 2. one slot per wave: gathers, matrix-core tile, + unary ---------
   {
-    constexpr int VEC = Elem<TIO>::kVec;
-    constexpr int kPer = 2;                          // pieces per thread per pass
-    const int pieces_per_row = r / VEC;
-    const int n_pieces = S * K * pieces_per_row;     // per table
-    const int total = 2 * n_pieces;
-    const FastDiv div_ppr(pieces_per_row);
-    for (int base = 0; base < total; base += kLWThreads * kPer) {
-      u32x4 raw[kPer];
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const int i = min(base + q * kLWThreads + tid, total - 1);
-        const bool is_b = i >= n_pieces;
-        const int ii = is_b ? i - n_pieces : i;
-        const int sj = div_ppr.quot(ii), v = ii - sj * pieces_per_row;
-        const int64_t t = is_b ? s_cand[sj] : s_pred[sj];
-        const int64_t tc = (t >= 0 && t < vocab) ? t : 0;
-        raw[q] = ld16((is_b ? B : A) + tc * r + v * VEC);
-      }
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const int i = base + q * kLWThreads + tid;
-        if (i >= total) continue;
-        const bool is_b = i >= n_pieces;
-        const int ii = is_b ? i - n_pieces : i;
-        const int sj = div_ppr.quot(ii), v = ii - sj * pieces_per_row;
-        const int s = div_k.quot(sj);
-        const int64_t t = is_b ? s_cand[sj] : s_pred[sj];
-        const bool ok = t >= 0 && t < vocab;
-        if (is_b) {
-          // the candidate's row piece as it is (NaN for an out-of-range id)
-          TIO nanrow[VEC];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) nanrow[e] = Elem<TIO>::nan_value();
-          st16(s_b + (size_t)sj * bstride + v * VEC, ok ? raw[q] : ld16(nanrow));
-        } else {
-          float a[VEC];
-          unpack16(raw[q], a);
-          float wv[VEC];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e)
-            wv[e] = (ok ? a[e] : __builtin_nanf("")) * s_u[s * r + v * VEC + e];   // A[p] (.) project(h)
-#pragma unroll
-          for (int e = 0; e < VEC; e += 4)
-            *reinterpret_cast<float4*>(s_w + sj * wstride + v * VEC + e) = make_float4(wv[e], wv[e + 1], wv[e + 2], wv[e + 3]);
-        }
-      }
+    const int e = lane % MT;
+    const int ec = e < K ? e : 0;
+    const int64_t anc = anchor[req];
+    for (int s = wave; s < S; s += kLWThreads / 64) {
+      const int64_t pred = (s == 0) ? anc : s_cand[(s - 1) * K + ec];
+      const int64_t cand = s_cand[s * K + ec];
+      const typename LatTile<MT>::acc_t acc =
+          lattice_slot_tile<TIO, MT, 4>(A, B, vocab, r, L, vload != 0, pred, cand, s_u + s * kpad);
+      const float* un = unary + (row0 + s) * K;
+      lattice_store<MT>(acc, un, K, s_sc + s * K * (K + 1), K + 1);
+      if (scores_out) lattice_store<MT>(acc, un, K, scores_out + (row0 + s) * K * K, K);
     }
   }
   __syncthreads();
 
-  // ---- 3. one thread per entry (s, j, c): fma chain over k from 0 ---------
-  const int n_entries = S * K * K;
-  for (int e = tid; e < n_entries; e += kLWThreads) {
-    constexpr int VEC = Elem<TIO>::kVec;
-    const int sj = div_k.quot(e), c = e - sj * K;
-    const int s = div_k.quot(sj);
-    const float* w = s_w + sj * wstride;
-    const TIO* b = s_b + (size_t)(s * K + c) * bstride;
-    float acc = 0.f;
-    for (int k0 = 0; k0 < r; k0 += VEC) {
-      float bv[VEC];
-      unpack16(ld16(b + k0), bv);
-#pragma unroll
-      for (int e4 = 0; e4 < VEC; e4 += 4) {
-        const float4 wv = *reinterpret_cast<const float4*>(w + k0 + e4);
-        acc = fmaf(wv.x, bv[e4 + 0], acc);
-        acc = fmaf(wv.y, bv[e4 + 1], acc);
-        acc = fmaf(wv.z, bv[e4 + 2], acc);
-        acc = fmaf(wv.w, bv[e4 + 3], acc);
-      }
-    }
-    const float v = acc + s_unary[s * K + c];
-    s_sc[sj * (K + 1) + c] = v;
-    if (scores_out) scores_out[row0 * K * K + e] = v;
-  }
-  __syncthreads();
-
-  // ---- 4, 5. every row's decision, then the walked path --------------------
-  decide_and_walk<kLWThreads>(s_sc, s_mx, s_next, reinterpret_cast<int*>(lw_smem + L.e), s_un, S, K,
+  // ---- 3, 4. every row's decision, then the walked path -----------------
+  decide_and_walk<kLWThreads>(s_sc, s_mx, s_next, reinterpret_cast<int*>(s_u), s_un, S, K,
                               greedy_mask[req] != 0, temperatures[req], div_k, row0, s_cand, tokens, q_out);
+}
+
+// Lattice + walk with one wave per request, for batches with requests
+// enough to occupy every SIMD.  Slot by slot the wave evaluates the slot's
+// tile on the matrix cores (lattice_slot_tile's gathers and MFMA sequence),
+// takes the walked row -- the one chosen at the previous slot -- straight
+// from the accumulators (one lane shuffle), and decides it with walk_decide
+// (the serial walk's arithmetic).  Only the S walked rows are decided, not
+// all S x K; the next slot's table gathers and u are in flight while the
+// current slot is evaluated and decided.  Bit-identical to dflash_lattice
+// followed by dflash_walk.  Needs the tile's k-range in one gather round
+// (L <= 8 VEC) and G L <= 128; LDS: one u row (G L floats) per wave.
+constexpr int kLWWaves = 4;   // requests (waves) per workgroup
+
+template <typename TIO, int MT>
+__global__ __launch_bounds__(kLWWaves * 64) void lattice_walk_wave_kernel(
+    const int64_t* __restrict__ ids, const float* __restrict__ unary, const int64_t* __restrict__ anchor,
+    const TIO* __restrict__ A, const TIO* __restrict__ B, const float* __restrict__ u_parts, int32_t ksplit,
+    int32_t slots, int32_t K, int32_t r, int32_t L, int32_t vload, int64_t vocab, int32_t n_req,
+    const float* __restrict__ uniforms, const float* __restrict__ temperatures,
+    const uint8_t* __restrict__ greedy_mask, float* __restrict__ scores_out, int64_t* __restrict__ tokens,
+    float* __restrict__ q_out) {
+  constexpr int VEC = Elem<TIO>::kVec;
+  constexpr int NB = 8;
+  typedef LatTile<MT> Tile;
+  extern __shared__ __align__(16) float lww_smem[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int req = blockIdx.x * kLWWaves + wave;
+  if (req >= n_req) return;                          // waves are independent: no workgroup barrier
+  const int S = slots;
+  const int kpad = (64 / MT) * L;
+  float* s_u = lww_smem + wave * kpad;
+  const int64_t row0 = (int64_t)req * S;
+  const bool greedy = greedy_mask[req] != 0;
+  const float temp = temperatures[req];
+  const int e = lane % MT, ec = e < K ? e : 0;
+  const int kg = (lane / MT) * L;
+  const int nv = L / VEC;
+  const bool vl = vload != 0;
+
+  // slot 0's operands: the anchor for every row, then the slot's candidates
+  int64_t cand = ids[row0 * K + ec];
+  TileRows<TIO> tr = tile_rows(A, B, vocab, r, anchor[req], cand);
+  u32x4 av[NB], bv[NB];
+  tile_gather<TIO, NB>(tr, kg, 0, nv, r, vl, av, bv);
+  float uv[2][kMaxProjSplit];                        // this lane's u values k = lane, lane + 64
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = lane + 64 * h;
+    if (k < r) load_proj_slices(u_parts, ksplit, r, row0, k, uv[h]);
+  }
+  int prev = 0;
+  for (int s = 0; s < S; ++s) {
+    const int64_t n = row0 + s;
+    // u of slot s -> this wave's LDS row (in program order with the reads
+    // of the previous slot's tile and the next one's: one wave, in-order LDS)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = lane + 64 * h;
+      if (k < kpad) s_u[k] = k < r ? add_proj_slices(uv[h], ksplit) : 0.f;
+    }
+    asm volatile("" ::: "memory");
+    // keep slot s's operands; start slot s + 1's loads (the candidates of
+    // slot s are its predecessors)
+    u32x4 cav[NB], cbv[NB];
+#pragma unroll
+    for (int v = 0; v < NB; ++v) { cav[v] = av[v]; cbv[v] = bv[v]; }
+    const TileRows<TIO> cur = tr;
+    const int64_t cand_s = cand;
+    if (s + 1 < S) {
+      cand = ids[(n + 1) * K + ec];
+      tr = tile_rows(A, B, vocab, r, cand_s, cand);
+      tile_gather<TIO, NB>(tr, kg, 0, nv, r, vl, av, bv);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = lane + 64 * h;
+        if (k < r) load_proj_slices(u_parts, ksplit, r, n + 1, k, uv[h]);
+      }
+    }
+    typename Tile::acc_t acc = {};
+    tile_mfma<TIO, MT, NB>(acc, cav, cbv, cur.pok, cur.cok, kg, 0, nv, s_u);
+    const float* un = unary + n * K;
+    if (scores_out) lattice_store<MT>(acc, un, K, scores_out + n * K * K, K);
+    // row prev of the tile: its column c sits in lane (prev's lane group) * MT + c,
+    // accumulator i(prev); + unary[c] as lattice_store adds it
+    int src_grp, ai;
+    if (MT == 32) { src_grp = (prev >> 2) & 1; ai = 4 * (prev >> 3) + (prev & 3); }
+    else          { src_grp = prev >> 2;       ai = prev & 3; }
+    float x = acc[0];
+#pragma unroll
+    for (int i = 1; i < Tile::kAcc; ++i) x = (ai == i) ? acc[i] : x;
+    const float row_v = __shfl(x, src_grp * MT + e, 64);
+    const float v = lane < K ? row_v + un[e] : 0.f;
+    float q;
+    const int idx = walk_decide(v, lane, K, greedy, temp, uniforms[n], q);
+    if (lane < K) q_out[n * K + lane] = q;
+    const int64_t tok = (int64_t)__builtin_amdgcn_readlane((int)(uint64_t)cand_s, idx) |
+                        ((int64_t)__builtin_amdgcn_readlane((int)((uint64_t)cand_s >> 32), idx) << 32);
+    if (lane == 0) tokens[n] = tok;
+    prev = idx;
+  }
 }
 
 }  // namespace
@@ -900,41 +911,39 @@ hipError_t launch_proj(const SelectArgs& a, const ProjPlan& p, hipStream_t strea
   return hipGetLastError();
 }
 
-size_t lattice_lds_bytes(int K, int r) {
-  const size_t used = (size_t)(r + K * (r + 1) + r * K);
-  return ((used + 1) & ~(size_t)1) * sizeof(float) + 2 * (size_t)K * sizeof(int64_t);
+
+namespace {
+// 16-byte gathers of the table rows need 16-byte aligned rows and tables.
+bool lattice_vload(const SelectArgs& a) {
+  const int e = a.dtype == DFLASH_BF16 ? 2 : 4;
+  return ((int64_t)a.rank * e) % 16 == 0 && (reinterpret_cast<uintptr_t>(a.sel_a) & 15) == 0 &&
+         (reinterpret_cast<uintptr_t>(a.sel_b) & 15) == 0;
+}
+int lattice_vec(int32_t dtype) { return dtype == DFLASH_BF16 ? 8 : 4; }
+}  // namespace
+
+int lattice_kpad_floats(int32_t top_k, int32_t rank, int32_t dtype) {
+  return lattice_kpad(top_k, rank, lattice_vec(dtype));
 }
 
 hipError_t launch_lattice(const SelectArgs& a, const ProjPlan& p, hipStream_t stream) {
   const int n_rows = a.n_req * a.slots;
   if (n_rows == 0) return hipSuccess;
-  const int vec = a.dtype == DFLASH_BF16 ? 8 : 4;
-  if (a.rank % vec == 0 && (reinterpret_cast<uintptr_t>(a.sel_a) & 15) == 0 &&
-      (reinterpret_cast<uintptr_t>(a.sel_b) & 15) == 0) {
-    const size_t lds = lattice_tile_layout(a.top_k, a.rank, a.dtype == DFLASH_BF16 ? 2 : 4).bytes;
-    // 2 x 2 tiles once the block has enough entries to keep the threads busy
-    const bool big = a.top_k >= 16;
-#define DFLASH_LT(TIO, TJ, TC)                                                                                    \
-  hipLaunchKernelGGL((lattice_tiled_kernel<TIO, TJ, TC>), dim3(n_rows), dim3(kThreads), lds, stream, a.ids, a.unary, \
-                     a.anchor, static_cast<const TIO*>(a.sel_a), static_cast<const TIO*>(a.sel_b), a.u_parts,       \
-                     p.ksplit, a.slots, a.top_k, a.rank, a.vocab, n_rows, a.scores)
-    if (a.dtype == DFLASH_BF16) {
-      if (big) DFLASH_LT(uint16_t, 2, 2); else DFLASH_LT(uint16_t, 1, 1);
-    } else {
-      if (big) DFLASH_LT(float, 2, 2); else DFLASH_LT(float, 1, 1);
-    }
-#undef DFLASH_LT
-    return hipGetLastError();
+  const int MT = lattice_mt(a.top_k);
+  const int L = lattice_group_len(a.top_k, a.rank, lattice_vec(a.dtype));
+  const size_t lds = (size_t)kLatWaves * (64 / MT) * L * sizeof(float);
+  const int vload = lattice_vload(a) ? 1 : 0;
+  const dim3 grid((n_rows + kLatWaves - 1) / kLatWaves);
+#define DFLASH_LAT(TIO, MTV)                                                                                   \
+  hipLaunchKernelGGL((lattice_mfma_kernel<TIO, MTV>), grid, dim3(kLatWaves * 64), lds, stream, a.ids, a.unary, \
+                     a.anchor, static_cast<const TIO*>(a.sel_a), static_cast<const TIO*>(a.sel_b), a.u_parts,   \
+                     p.ksplit, a.slots, a.top_k, a.rank, L, vload, a.vocab, n_rows, a.scores)
+  if (a.dtype == DFLASH_BF16) {
+    if (MT == 16) DFLASH_LAT(uint16_t, 16); else DFLASH_LAT(uint16_t, 32);
+  } else {
+    if (MT == 16) DFLASH_LAT(float, 16); else DFLASH_LAT(float, 32);
   }
-  const size_t lds = lattice_lds_bytes(a.top_k, a.rank);
-  if (a.dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(lattice_kernel<uint16_t>, dim3(n_rows), dim3(kThreads), lds, stream, a.ids, a.unary,
-                       a.anchor, static_cast<const uint16_t*>(a.sel_a), static_cast<const uint16_t*>(a.sel_b),
-                       a.u_parts, p.ksplit, a.slots, a.top_k, a.rank, a.vocab, n_rows, a.scores);
-  else
-    hipLaunchKernelGGL(lattice_kernel<float>, dim3(n_rows), dim3(kThreads), lds, stream, a.ids, a.unary,
-                       a.anchor, static_cast<const float*>(a.sel_a), static_cast<const float*>(a.sel_b),
-                       a.u_parts, p.ksplit, a.slots, a.top_k, a.rank, a.vocab, n_rows, a.scores);
+#undef DFLASH_LAT
   return hipGetLastError();
 }
 
@@ -954,32 +963,62 @@ hipError_t launch_walk(const WalkArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+
 size_t lattice_walk_lds_bytes(int slots, int K, int r, int dtype) {
-  return lattice_walk_layout(slots, K, r, dtype == DFLASH_BF16 ? 2 : 4).bytes;
+  return lattice_walk_layout(slots, K, lattice_kpad(K, r, lattice_vec(dtype))).bytes;
 }
 
 bool lattice_walk_fits(const SelectArgs& a) {
-  const int vec = a.dtype == DFLASH_BF16 ? 8 : 4;
-  return lattice_walk_lds_bytes(a.slots, a.top_k, a.rank, a.dtype) <= kLatticeWalkLdsMax && a.rank % vec == 0 &&
-         (reinterpret_cast<uintptr_t>(a.sel_a) & 15) == 0 && (reinterpret_cast<uintptr_t>(a.sel_b) & 15) == 0;
+  return lattice_walk_per_wave(a) || lattice_walk_lds_bytes(a.slots, a.top_k, a.rank, a.dtype) <= kLatticeWalkLdsMax;
+}
+
+// One wave per request once the batch has a request for every SIMD (the
+// serial decisions then hide behind each other); the tile's k-range must fit
+// one gather round and two u values per lane.
+bool lattice_walk_per_wave(const SelectArgs& a) {
+  const int vec = lattice_vec(a.dtype);
+  const int L = lattice_group_len(a.top_k, a.rank, vec);
+  return a.n_req >= kLatticeWalkWaveMinReq && L <= 8 * vec && lattice_kpad(a.top_k, a.rank, vec) <= 128;
 }
 
 hipError_t launch_lattice_walk(const SelectArgs& a, const ProjPlan& p, const WalkArgs& w, float* scores_out,
                                hipStream_t stream) {
   if (a.n_req == 0 || a.slots == 0) return hipSuccess;
+  if (lattice_walk_per_wave(a)) {
+    const int MT = lattice_mt(a.top_k);
+    const int L = lattice_group_len(a.top_k, a.rank, lattice_vec(a.dtype));
+    const int vload = lattice_vload(a) ? 1 : 0;
+    const size_t lds = (size_t)kLWWaves * (64 / MT) * L * sizeof(float);
+    const dim3 grid((a.n_req + kLWWaves - 1) / kLWWaves);
+#define DFLASH_LWW(TIO, MTV)                                                                                        \
+  hipLaunchKernelGGL((lattice_walk_wave_kernel<TIO, MTV>), grid, dim3(kLWWaves * 64), lds, stream, a.ids, a.unary,  \
+                     a.anchor, static_cast<const TIO*>(a.sel_a), static_cast<const TIO*>(a.sel_b), a.u_parts,      \
+                     p.ksplit, a.slots, a.top_k, a.rank, L, vload, a.vocab, a.n_req, w.uniforms, w.temperatures,   \
+                     w.greedy, scores_out, w.tokens, w.q)
+    if (a.dtype == DFLASH_BF16) {
+      if (MT == 16) DFLASH_LWW(uint16_t, 16); else DFLASH_LWW(uint16_t, 32);
+    } else {
+      if (MT == 16) DFLASH_LWW(float, 16); else DFLASH_LWW(float, 32);
+    }
+#undef DFLASH_LWW
+    return hipGetLastError();
+  }
   if (!lattice_walk_fits(a)) return hipErrorInvalidValue;
   const size_t lds = lattice_walk_lds_bytes(a.slots, a.top_k, a.rank, a.dtype);
-  const int n_rows = a.n_req * a.slots;
-  if (a.dtype == DFLASH_BF16)
-    hipLaunchKernelGGL((lattice_walk_kernel<uint16_t>), dim3(a.n_req), dim3(kLWThreads), lds, stream, a.ids, a.unary,
-                       a.anchor, static_cast<const uint16_t*>(a.sel_a), static_cast<const uint16_t*>(a.sel_b),
-                       a.u_parts, p.ksplit, a.slots, a.top_k, a.rank, a.vocab, n_rows, w.uniforms, w.temperatures,
-                       w.greedy, scores_out, w.tokens, w.q);
-  else
-    hipLaunchKernelGGL((lattice_walk_kernel<float>), dim3(a.n_req), dim3(kLWThreads), lds, stream, a.ids, a.unary,
-                       a.anchor, static_cast<const float*>(a.sel_a), static_cast<const float*>(a.sel_b), a.u_parts,
-                       p.ksplit, a.slots, a.top_k, a.rank, a.vocab, n_rows, w.uniforms, w.temperatures, w.greedy,
-                       scores_out, w.tokens, w.q);
+  const int MT = lattice_mt(a.top_k);
+  const int L = lattice_group_len(a.top_k, a.rank, lattice_vec(a.dtype));
+  const int vload = lattice_vload(a) ? 1 : 0;
+#define DFLASH_LW(TIO, MTV)                                                                                      \
+  hipLaunchKernelGGL((lattice_walk_kernel<TIO, MTV>), dim3(a.n_req), dim3(kLWThreads), lds, stream, a.ids, a.unary, \
+                     a.anchor, static_cast<const TIO*>(a.sel_a), static_cast<const TIO*>(a.sel_b), a.u_parts,      \
+                     p.ksplit, a.slots, a.top_k, a.rank, L, vload, a.vocab, w.uniforms, w.temperatures, w.greedy,  \
+                     scores_out, w.tokens, w.q)
+  if (a.dtype == DFLASH_BF16) {
+    if (MT == 16) DFLASH_LW(uint16_t, 16); else DFLASH_LW(uint16_t, 32);
+  } else {
+    if (MT == 16) DFLASH_LW(float, 16); else DFLASH_LW(float, 32);
+  }
+#undef DFLASH_LW
   return hipGetLastError();
 }
 

@@ -1,7 +1,10 @@
 """GPU parity of dflash_conv against the oracle's block-causal grouped conv
 ("[Spec] DFlash2", code excerpt of the grouped conv).  Bar: max relative
 error (|got - ref| / max(|ref|, RMS(ref))) <= 1e-2 for bf16 output and 1e-5 for
-fp32; the identity initialisation must be reproduced bit for bit."""
+fp32; the identity initialisation must be reproduced bit for bit.  bf16
+outputs must also be the exact sum rounded once to nearest: within half a
+bf16 spacing of the exact value, widened only by the fp32 accumulation bound
+(a truncating or twice-rounding conversion fails this)."""
 import numpy as np
 import pytest
 import torch
@@ -29,7 +32,22 @@ def _run_and_check(w: W.Workload, side: int, blocks=None):
     got = f64(out[idx])
     err = conv_rel_err(got, ref)
     assert err <= CONV_TOL[w.dtype], (w.name, side, err)
+    if w.dtype == "bf16":
+        _check_rounded_once(got, ref, f64(x[idx]), f64(base), f64(delta[idx]), B, w.group_size)
     return err
+
+
+def _check_rounded_once(got, ref, x, base, delta, B, gs):
+    """|got - exact| <= half the bf16 spacing at got's magnitude (taken on
+    the larger side, 2^(e-8) for 2^e <= |got| < 2^(e+1)) + the fp32
+    accumulation bound (T + 2) 2^-24 sum_t |coef_t x_t|."""
+    mag = np.abs(O.conv(np.abs(x), np.abs(base), np.abs(delta), B, gs))   # >= sum_t |coef_t x_t|
+    e = np.floor(np.log2(np.maximum(np.abs(got), 2.0 ** -126)))
+    half = 2.0 ** (e - 8)
+    T = base.shape[0]
+    bound = half + (T + 2) * 2.0 ** -24 * mag
+    ratio = np.abs(got - ref) / bound
+    assert np.all(ratio <= 1.0), float(np.max(ratio))
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "bf16_b16_v151936", "nonpow2_b10_v151936"])
