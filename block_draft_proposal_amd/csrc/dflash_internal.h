@@ -64,9 +64,12 @@ __host__ __device__ inline int proj_slice_stride(int ksplit) { return (ksplit + 
 struct ProjPlan {
   int32_t n_rows, rank, hidden;
   int32_t row_tiles, ksplit, kslice;   // split of the contraction over workgroups
-  int32_t frags;                       // row fragments of 16 per wave (bf16)
+  int32_t frags;                       // row fragments of 16 per wave (bf16, per-wave kernel)
+  int32_t tiled;                       // 128 x 128 tiles of the shared tile product (bf16, large batches)
   size_t bytes;                        // fp32 partials [n_rows][rank][proj_slice_stride(ksplit)]
 };
+// Slot rows from which the bf16 projection runs as LDS-staged 128 x 128 tiles.
+constexpr int kProjTileMinRows = 2048;
 ProjPlan plan_proj(int32_t n_rows, int32_t rank, int32_t hidden, int32_t dtype);
 
 struct SelectArgs {

@@ -68,23 +68,36 @@ __device__ __forceinline__ void tile_of(int id, int n_mb, int& mb, int& nb) {
   mb = slot % n_mb;
 }
 
+// Row addresses of a [rows, H] operand whose rows sit at a fixed stride.
+struct StridedRows {
+  const uint16_t* base;
+  int64_t stride;
+  __device__ __forceinline__ const uint16_t* operator()(int r) const { return base + (int64_t)r * stride; }
+};
+
 // Issues the direct global -> LDS loads of one stage: rows [r0, r0 + ROWS)
-// x k [k0, k0 + BK) of a [rows, H] matrix, in 1 KB blocks of kBlockRows rows
-// dealt round the waves; lane l of a block fills slot l % kChunks of row
-// l / kChunks with the chunk the swizzle puts there.  Addresses are clamped
-// into the matrix: rows past the end repeat the last row (their results are
-// never used) and k past H is zeroed by zero_tail before use.
-template <class Cfg, int ROWS>
-__device__ __forceinline__ void issue_stage(const uint16_t* __restrict__ base, int64_t stride, int rows, int H,
-                                            int r0, int k0, unsigned char* dst) {
+// x k [k0, k0 + BK) of a [rows, H] matrix (row r at row_at(r)), in 1 KB
+// blocks of kBlockRows rows dealt round the waves; lane l of a block fills
+// slot l % kChunks of row l / kChunks with the chunk the swizzle puts there.
+// Addresses are clamped into the matrix: rows past the end repeat the last
+// row (their results are never used) and k past H is zeroed by zero_tail
+// before use.
+template <class Cfg, int ROWS, class RowAt>
+__device__ __forceinline__ void issue_stage(const RowAt& row_at, int rows, int H, int r0, int k0,
+                                            unsigned char* dst) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
   for (int q = 0; q < ROWS / Cfg::kBlockRows / Cfg::kWaves; ++q) {
     const int blk = q * Cfg::kWaves + wave, r = blk * Cfg::kBlockRows + lane / Cfg::kChunks;
     const int k = k0 + 8 * ((lane % Cfg::kChunks) ^ Cfg::swz(r));
-    const uint16_t* src = base + (int64_t)min(r0 + r, rows - 1) * stride + min(k, H - 8);
+    const uint16_t* src = row_at(min(r0 + r, rows - 1)) + min(k, H - 8);
     __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(dst + blk * 1024), 16, 0, 0);
   }
+}
+template <class Cfg, int ROWS>
+__device__ __forceinline__ void issue_stage(const uint16_t* __restrict__ base, int64_t stride, int rows, int H,
+                                            int r0, int k0, unsigned char* dst) {
+  issue_stage<Cfg, ROWS>(StridedRows{base, stride}, rows, H, r0, k0, dst);
 }
 
 // After the stage has landed: zeroes this thread's chunks of it whose k is at
@@ -121,7 +134,9 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 // The kBM x kBN fp32 tile at (m0, n0) summed over k blocks [kb0, kb0 + nkb)
-// of the H-long contraction (nk = ceil(H / BK) blocks in all); each wave
+// of the H-long contraction (nk = ceil(H / BK) blocks in all), A's and B's
+// rows addressed by row functors (row r -> pointer to its first element;
+// StridedRows for a plain row stride); each wave
 // holds its kWM x kWN block in kFragM x kFragN accumulators.  D layout of one
 // 16 x 16 MFMA: lane l holds column l % 16 and rows 4 (l / 16) + v, v = 0..3.
 // Stage t lives in ring slot t % kStages; each iteration waits for its own
@@ -129,10 +144,9 @@ __device__ __forceinline__ void ring_barrier() {
 // free) and refills that slot with stage t + kStages - 1 before computing.
 // The k blocks are summed in increasing order.  Ends with a barrier, so the
 // LDS may be reused.
-template <class Cfg>
-__device__ __forceinline__ void tile_product(const uint16_t* __restrict__ A, int64_t a_stride,
-                                             const uint16_t* __restrict__ B, int64_t b_stride, int M, int N, int H,
-                                             int m0, int n0, int kb0, int nkb, unsigned char* smem,
+template <class Cfg, class RowA, class RowB>
+__device__ __forceinline__ void tile_product(const RowA& A, const RowB& B, int M, int N, int H, int m0, int n0,
+                                             int kb0, int nkb, unsigned char* smem,
                                              f32x4_t (&acc)[Cfg::kFragM][Cfg::kFragN]) {
   constexpr int S = Cfg::kStages;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -147,8 +161,8 @@ __device__ __forceinline__ void tile_product(const uint16_t* __restrict__ A, int
 #pragma unroll
   for (int t = 0; t < S - 1; ++t) {
     if (t < nkb) {
-      issue_stage<Cfg, Cfg::kBM>(A, a_stride, M, H, m0, (kb0 + t) * Cfg::kBK, stage(t));
-      issue_stage<Cfg, Cfg::kBN>(B, b_stride, N, H, n0, (kb0 + t) * Cfg::kBK, stage(t) + Cfg::kBOff);
+      issue_stage<Cfg, Cfg::kBM>(A, M, H, m0, (kb0 + t) * Cfg::kBK, stage(t));
+      issue_stage<Cfg, Cfg::kBN>(B, N, H, n0, (kb0 + t) * Cfg::kBK, stage(t) + Cfg::kBOff);
     }
   }
   // fragment reads: row (lane & 15) of a 16-row group, chunk (lane >> 4) of a
@@ -171,8 +185,8 @@ __device__ __forceinline__ void tile_product(const uint16_t* __restrict__ A, int
     ring_barrier();
     if (kt + S - 1 < nkb) {
       unsigned char* nxt = stage(kt + S - 1);
-      issue_stage<Cfg, Cfg::kBM>(A, a_stride, M, H, m0, (kb0 + kt + S - 1) * Cfg::kBK, nxt);
-      issue_stage<Cfg, Cfg::kBN>(B, b_stride, N, H, n0, (kb0 + kt + S - 1) * Cfg::kBK, nxt + Cfg::kBOff);
+      issue_stage<Cfg, Cfg::kBM>(A, M, H, m0, (kb0 + kt + S - 1) * Cfg::kBK, nxt);
+      issue_stage<Cfg, Cfg::kBN>(B, N, H, n0, (kb0 + kt + S - 1) * Cfg::kBK, nxt + Cfg::kBOff);
     }
     const unsigned char* sa = cur;
     const unsigned char* sb = cur + Cfg::kBOff;
@@ -194,6 +208,13 @@ __device__ __forceinline__ void tile_product(const uint16_t* __restrict__ A, int
     }
   }
   __syncthreads();
+}
+template <class Cfg>
+__device__ __forceinline__ void tile_product(const uint16_t* __restrict__ A, int64_t a_stride,
+                                             const uint16_t* __restrict__ B, int64_t b_stride, int M, int N, int H,
+                                             int m0, int n0, int kb0, int nkb, unsigned char* smem,
+                                             f32x4_t (&acc)[Cfg::kFragM][Cfg::kFragN]) {
+  tile_product<Cfg>(StridedRows{A, a_stride}, StridedRows{B, b_stride}, M, N, H, m0, n0, kb0, nkb, smem, acc);
 }
 
 // The wave's accumulators rounded to bf16 (nearest, ties to even), two per

@@ -26,12 +26,12 @@
 //    touches LDS.
 #include "dflash.h"
 #include "dflash_internal.h"
+#include "conv_core.h"
+#include "gemm_tile.h"
 
 namespace dflash {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kRowsPerWG = 64;       // 4 waves x 16 rows
@@ -139,6 +139,64 @@ __global__ __launch_bounds__(kThreads) void proj_mfma_kernel(const uint16_t* __r
   }
 }
 
+
+// Large batches: the projection as 128 x 128 output tiles of the shared
+// tile product (gemm_tile.h: direct global -> LDS stages, 64-deep k blocks,
+// v_mfma_f32_16x16x32_bf16 with operand lane groups at k + 8 (lane >> 4),
+// k-steps in order), over one slice of the contraction per workgroup.  Each
+// output is the MFMA chain over its slice's k-steps from zero, exactly as in
+// proj_mfma_kernel and the conv + slot projection, so every producer of the
+// partials agrees bit for bit.  Rank columns past `rank` repeat the last P
+// row and are not stored.
+using ProjTileCfg = TileCfg<4, 4, 2, 2, 64, 2>;
+
+// Slot row n of a request-major [R][S] view with strides in elements.
+struct SlotRows {
+  const uint16_t* h;
+  int64_t req_stride, slot_stride;
+  int32_t slots;
+  __device__ __forceinline__ const uint16_t* operator()(int n) const {
+    const int req = n / slots, s = n - req * slots;
+    return h + (int64_t)req * req_stride + (int64_t)s * slot_stride;
+  }
+};
+
+__global__ __launch_bounds__(ProjTileCfg::kThreads) void proj_tile_kernel(
+    const uint16_t* __restrict__ hidden, int64_t req_stride, int64_t slot_stride, int32_t slots,
+    const uint16_t* __restrict__ P, int32_t n_rows, int32_t rank, int32_t H, int32_t kb_per_slice,
+    float* __restrict__ u_parts) {
+  typedef ProjTileCfg Cfg;
+  extern __shared__ __align__(16) unsigned char pt_smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int split = blockIdx.y, ksplit = gridDim.y;
+  const int kstride = proj_slice_stride(ksplit);
+  const int nk = (H + Cfg::kBK - 1) / Cfg::kBK;
+  const int kb0 = split * kb_per_slice;
+  const int nkb = min(kb_per_slice, nk - kb0);
+  const int m0 = blockIdx.x * Cfg::kBM;
+  f32x4_t acc[Cfg::kFragM][Cfg::kFragN];
+  tile_product<Cfg>(SlotRows{hidden, req_stride, slot_stride, slots}, StridedRows{P, H}, n_rows, rank, H, m0, 0,
+                    kb0, nkb, pt_smem, acc);
+  const int wm = (wave / Cfg::kWavesN) * Cfg::kWM, wn = (wave % Cfg::kWavesN) * Cfg::kWN;
+#pragma unroll
+  for (int j = 0; j < Cfg::kFragN; ++j) {
+    const int col = wn + 16 * j + (lane & 15);
+    if (col >= rank) continue;
+#pragma unroll
+    for (int i = 0; i < Cfg::kFragM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = m0 + wm + 16 * i + 4 * (lane >> 4) + v;
+        if (row < n_rows) {
+          float* dst = u_parts + ((int64_t)row * rank + col) * kstride;
+          dst[split] = acc[i][j][v];
+          if (split == ksplit - 1)
+            for (int sp = split + 1; sp < kstride; ++sp) dst[sp] = 0.f;   // pad slots: +0
+        }
+      }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void proj_f32_kernel(const float* __restrict__ hidden,
                                                             int64_t req_stride, int64_t slot_stride,
                                                             int32_t slots, const float* __restrict__ P,
@@ -230,6 +288,9 @@ template <> struct LatTile<16> {
   typedef f32x4_t acc_t;
   static constexpr int kAcc = 4;
   __device__ static acc_t mfma(float a, float b, acc_t c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
+  __device__ static acc_t mfma(bf16x8_t a, bf16x8_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
   // row of accumulator i in this lane (its column is lane % 16)
   __device__ static int row(int lane, int i) { return 4 * (lane >> 4) + i; }
 };
@@ -237,6 +298,9 @@ template <> struct LatTile<32> {
   typedef f32x16_t acc_t;
   static constexpr int kAcc = 16;
   __device__ static acc_t mfma(float a, float b, acc_t c) { return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0); }
+  __device__ static acc_t mfma(bf16x8_t a, bf16x8_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
   __device__ static int row(int lane, int i) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 };
 
@@ -302,9 +366,16 @@ __device__ __forceinline__ void tile_gather(const TileRows<TIO>& t, int kg, int 
   }
 }
 
-// The MFMA steps of those pieces: k = kg + (v0 + v) VEC + e in order, with
-// w = A * u rounded to fp32 (NaN for an out-of-range predecessor) against B
-// (NaN for an out-of-range candidate).
+// The MFMA steps of those pieces.  fp32 tables: one v_mfma_f32_*_f32 step
+// per k = kg + (v0 + v) VEC + e, in order, with w = A * u rounded to fp32
+// (NaN for an out-of-range predecessor) against B (NaN for an out-of-range
+// candidate).  bf16 tables: w (the same fp32 product) is split as
+// hi = bf16(w), lo = bf16(w - hi) (w - hi is exact in fp32), and each 16-byte
+// piece of 8 k values takes two bf16 MFMA steps, hi x B then lo x B: bf16 x
+// bf16 products are exact in fp32 and hi + lo carries w to within
+// 2^-18 |w|, so every term is within 2^-18 of A u B (a single bf16 rounding
+// of w would be 2^-9).  The 8 k values of a piece sit in the instruction's k
+// positions 8 g .. 8 g + 7 of lane group g, in order.
 template <typename TIO, int MT, int NB>
 __device__ __forceinline__ void tile_mfma(typename LatTile<MT>::acc_t& acc, const u32x4 (&av)[NB],
                                           const u32x4 (&bv)[NB], bool pok, bool cok, int kg, int v0, int nv,
@@ -314,19 +385,36 @@ __device__ __forceinline__ void tile_mfma(typename LatTile<MT>::acc_t& acc, cons
 #pragma unroll
   for (int v = 0; v < NB; ++v) {
     if (v0 + v < nv) {
-      float a[VEC], b[VEC];
+      float a[VEC];
       unpack16(av[v], a);
-      unpack16(bv[v], b);
       const float* u = s_u + kg + (v0 + v) * VEC;
+      float w[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; e += 4) {
         const float4 u4 = *reinterpret_cast<const float4*>(u + e);
-        const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
+        w[e] = a[e] * u4.x;                                         // A[p] (.) project(h)
+        w[e + 1] = a[e + 1] * u4.y;
+        w[e + 2] = a[e + 2] * u4.z;
+        w[e + 3] = a[e + 3] * u4.w;
+      }
+      if constexpr (sizeof(TIO) == 2) {
+        u32x4 hi, lo;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float w = pok ? a[e + i] * uu[i] : nan;        // A[p] (.) project(h)
-          acc = LatTile<MT>::mfma(w, cok ? b[e + i] : nan, acc);
+        for (int q = 0; q < 4; ++q) {
+          hi[q] = pack_bf16x2(w[2 * q], w[2 * q + 1]);
+          const float r0 = w[2 * q] - __uint_as_float(hi[q] << 16);
+          const float r1 = w[2 * q + 1] - __uint_as_float(hi[q] & 0xffff0000u);
+          lo[q] = pack_bf16x2(r0, r1);
         }
+        const u32x4 qnan = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, cok ? bv[v] : qnan);
+        acc = LatTile<MT>::mfma(__builtin_bit_cast(bf16x8_t, pok ? hi : qnan), b, acc);
+        acc = LatTile<MT>::mfma(__builtin_bit_cast(bf16x8_t, pok ? lo : qnan), b, acc);
+      } else {
+        float b[VEC];
+        unpack16(bv[v], b);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc = LatTile<MT>::mfma(pok ? w[e] : nan, cok ? b[e] : nan, acc);
       }
     }
   }
@@ -744,90 +832,186 @@ __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
                               greedy_mask[req] != 0, temperatures[req], div_k, row0, s_cand, tokens, q_out);
 }
 
+// walk_decide's arithmetic (the same operations in the same order, so the
+// same bits) with short dependency chains, for one wave whose lanes 0..K-1
+// hold the row and whose other lanes hold -inf (they add 0 to every sum and
+// never win; a count past K - 1 is capped as before).  The values summed in
+// order are read into uniform registers all at once before each ordered sum,
+// and the row maximum is a wave reduction (fmaxf is exact in any order).
+template <int MT>
+__device__ __forceinline__ int walk_decide_wave(float v, int lane, int K, bool greedy, float temp, float u,
+                                                float& q) {
+  constexpr int BT = 8;                             // lanes read per batch
+  const bool on = lane < K;
+  if (greedy) {
+    // first maximum in candidate order = lowest index among ties
+    float best = lane_value(v, 0);
+    int idx = 0;
+#pragma unroll
+    for (int j0 = 0; j0 < MT; j0 += BT) {
+      float r[BT];
+#pragma unroll
+      for (int b = 0; b < BT; ++b) r[b] = lane_value(v, j0 + b);
+#pragma unroll
+      for (int b = 0; b < BT; ++b)
+        if (j0 + b > 0 && r[b] > best) { best = r[b]; idx = j0 + b; }
+    }
+    q = (lane == idx) ? 1.f : 0.f;
+    return idx;
+  }
+  const float t = fmaxf(temp, 1e-5f);
+  const float xs = v / t;
+  const float mx = wave_max_f32(xs);
+  // exp rounded once to fp32 (from the fp64 exponential)
+  const float e = on ? (float)exp((double)(xs - mx)) : 0.f;
+  float total = 0.f;
+#pragma unroll
+  for (int j0 = 0; j0 < MT; j0 += BT) {
+    float r[BT];
+#pragma unroll
+    for (int b = 0; b < BT; ++b) r[b] = lane_value(e, j0 + b);
+#pragma unroll
+    for (int b = 0; b < BT; ++b) total += r[b];                    // left to right
+  }
+  const float p = e / total;
+  float cdf = 0.f;
+  int cnt = 0;
+#pragma unroll
+  for (int j0 = 0; j0 < MT; j0 += BT) {
+    float r[BT];
+#pragma unroll
+    for (int b = 0; b < BT; ++b) r[b] = lane_value(p, j0 + b);
+#pragma unroll
+    for (int b = 0; b < BT; ++b) {                                 // C_j left to right
+      cdf += r[b];
+      cnt += (u >= cdf) ? 1 : 0;
+    }
+  }
+  q = on ? p : 0.f;
+  return cnt < K - 1 ? cnt : K - 1;
+}
+
 // Lattice + walk with one wave per request, for batches with requests
 // enough to occupy every SIMD.  Slot by slot the wave evaluates the slot's
-// tile on the matrix cores (lattice_slot_tile's gathers and MFMA sequence),
-// takes the walked row -- the one chosen at the previous slot -- straight
-// from the accumulators (one lane shuffle), and decides it with walk_decide
-// (the serial walk's arithmetic).  Only the S walked rows are decided, not
-// all S x K; the next slot's table gathers and u are in flight while the
-// current slot is evaluated and decided.  Bit-identical to dflash_lattice
-// followed by dflash_walk.  Needs the tile's k-range in one gather round
-// (L <= 8 VEC) and G L <= 128; LDS: one u row (G L floats) per wave.
-constexpr int kLWWaves = 4;   // requests (waves) per workgroup
+// tile on the matrix cores (tile_mfma: the sequence every lattice kernel
+// runs), takes the walked row -- the one chosen at the previous slot --
+// straight from the accumulators (one lane shuffle), and decides it with
+// walk_decide's arithmetic.  Only the S walked rows are decided, not all
+// S x K.  Pipelining: every small per-slot input (candidate ids, unary,
+// uniforms) is staged in LDS up front, so inside the loop the wave issues
+// only the next slot's u and table loads -- the vector-memory counter
+// retires in order, so waiting for a later small load would wait for those
+// prefetches too; slot s + 1's loads are in flight while slot s is decided,
+// and slot s + 1's MFMA chain is issued in the same stretch of code as slot
+// s's decision.  The two register sets for table pieces alternate roles
+// (two slots per loop turn), so nothing is copied.  Bit-identical to
+// dflash_lattice followed by dflash_walk.  Needs S <= 16, bf16 or fp32
+// tables with 16-byte aligned rows, rank a multiple of the tile's k-groups
+// (G VEC) so that every gathered piece lies inside the row, NV = L / VEC
+// pieces per lane (1, 2, 4 or 8) and G L <= 128.  LDS per wave: two u rows,
+// the candidate ids [S][MT] (int64), unary [S][MT] and uniforms [S].
+constexpr int kLWWaves = 4;          // requests (waves) per workgroup
+constexpr int kWaveMaxSlots = 16;
 
-template <typename TIO, int MT>
+template <typename TIO, int MT, int NV>
 __global__ __launch_bounds__(kLWWaves * 64) void lattice_walk_wave_kernel(
     const int64_t* __restrict__ ids, const float* __restrict__ unary, const int64_t* __restrict__ anchor,
     const TIO* __restrict__ A, const TIO* __restrict__ B, const float* __restrict__ u_parts, int32_t ksplit,
-    int32_t slots, int32_t K, int32_t r, int32_t L, int32_t vload, int64_t vocab, int32_t n_req,
-    const float* __restrict__ uniforms, const float* __restrict__ temperatures,
-    const uint8_t* __restrict__ greedy_mask, float* __restrict__ scores_out, int64_t* __restrict__ tokens,
-    float* __restrict__ q_out) {
+    int32_t slots, int32_t K, int32_t r, int64_t vocab, int32_t n_req, const float* __restrict__ uniforms,
+    const float* __restrict__ temperatures, const uint8_t* __restrict__ greedy_mask,
+    float* __restrict__ scores_out, int64_t* __restrict__ tokens, float* __restrict__ q_out) {
   constexpr int VEC = Elem<TIO>::kVec;
-  constexpr int NB = 8;
+  constexpr int L = NV * VEC;
+  constexpr int KPAD = (64 / MT) * L;
   typedef LatTile<MT> Tile;
   extern __shared__ __align__(16) float lww_smem[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int req = blockIdx.x * kLWWaves + wave;
   if (req >= n_req) return;                          // waves are independent: no workgroup barrier
   const int S = slots;
-  const int kpad = (64 / MT) * L;
-  float* s_u = lww_smem + wave * kpad;
+  float* s_u2 = lww_smem + wave * 2 * KPAD;          // u rows of two slots (alternating)
   const int64_t row0 = (int64_t)req * S;
   const bool greedy = greedy_mask[req] != 0;
   const float temp = temperatures[req];
-  const int e = lane % MT, ec = e < K ? e : 0;
+  const int e = lane % MT;
   const int kg = (lane / MT) * L;
-  const int nv = L / VEC;
-  const bool vl = vload != 0;
 
-  // slot 0's operands: the anchor for every row, then the slot's candidates
-  int64_t cand = ids[row0 * K + ec];
-  TileRows<TIO> tr = tile_rows(A, B, vocab, r, anchor[req], cand);
-  u32x4 av[NB], bv[NB];
-  tile_gather<TIO, NB>(tr, kg, 0, nv, r, vl, av, bv);
-  float uv[2][kMaxProjSplit];                        // this lane's u values k = lane, lane + 64
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int k = lane + 64 * h;
-    if (k < r) load_proj_slices(u_parts, ksplit, r, row0, k, uv[h]);
+  // Every small per-slot input to the wave's LDS up front: candidate ids (as
+  // given), unary, uniforms.
+  int64_t* s_id = reinterpret_cast<int64_t*>(lww_smem + kLWWaves * 2 * KPAD) + wave * kWaveMaxSlots * MT;
+  float* s_un = reinterpret_cast<float*>(reinterpret_cast<int64_t*>(lww_smem + kLWWaves * 2 * KPAD) +
+                                         kLWWaves * kWaveMaxSlots * MT) + wave * (kWaveMaxSlots * MT + kWaveMaxSlots);
+  float* s_uni = s_un + kWaveMaxSlots * MT;
+  for (int i = lane; i < S * MT; i += 64) {
+    const int si = i / MT, ei = i - si * MT;
+    const int64_t src = (row0 + si) * K + (ei < K ? ei : 0);
+    s_id[i] = ids[src];
+    s_un[i] = unary[src];
   }
-  int prev = 0;
-  for (int s = 0; s < S; ++s) {
-    const int64_t n = row0 + s;
-    // u of slot s -> this wave's LDS row (in program order with the reads
-    // of the previous slot's tile and the next one's: one wave, in-order LDS)
+  if (lane < S) s_uni[lane] = uniforms[row0 + lane];
+  const int64_t anc = anchor[req];
+  asm volatile("" ::: "memory");
+  // slot s's predecessor / candidate id of this lane's row / column index
+  // (an id outside [0, vocab) is out of range for tile_rows as it is)
+  auto pred_of = [&](int s) -> int64_t { return s == 0 ? anc : s_id[(s - 1) * MT + e]; };
+  auto cand_of = [&](int s) -> int64_t { return s_id[s * MT + e]; };
+  auto load_u = [&](int s, float (&uv)[2][kMaxProjSplit]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = lane + 64 * h;
+      if (k < KPAD) load_proj_slices(u_parts, ksplit, r, row0 + s, k, uv[h]);
+    }
+  };
+  auto store_u = [&](const float (&uv)[2][kMaxProjSplit], float* dst) {
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int k = lane + 64 * h;
-      if (k < kpad) s_u[k] = k < r ? add_proj_slices(uv[h], ksplit) : 0.f;
+      if (k < KPAD) dst[k] = add_proj_slices(uv[h], ksplit);
     }
     asm volatile("" ::: "memory");
-    // keep slot s's operands; start slot s + 1's loads (the candidates of
-    // slot s are its predecessors)
-    u32x4 cav[NB], cbv[NB];
+  };
+  // the table pieces of slot s (rank is a multiple of G VEC: every piece lies
+  // inside its row, so the loads are unconditional)
+  auto gather = [&](int s, u32x4 (&ga)[NV], u32x4 (&gb)[NV]) -> TileRows<TIO> {
+    const TileRows<TIO> t = tile_rows(A, B, vocab, r, pred_of(s), cand_of(s));
 #pragma unroll
-    for (int v = 0; v < NB; ++v) { cav[v] = av[v]; cbv[v] = bv[v]; }
-    const TileRows<TIO> cur = tr;
-    const int64_t cand_s = cand;
-    if (s + 1 < S) {
-      cand = ids[(n + 1) * K + ec];
-      tr = tile_rows(A, B, vocab, r, cand_s, cand);
-      tile_gather<TIO, NB>(tr, kg, 0, nv, r, vl, av, bv);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int k = lane + 64 * h;
-        if (k < r) load_proj_slices(u_parts, ksplit, r, n + 1, k, uv[h]);
-      }
+    for (int v = 0; v < NV; ++v) {
+      ga[v] = ld16(t.arow + kg + v * VEC);
+      gb[v] = ld16(t.brow + kg + v * VEC);
     }
-    typename Tile::acc_t acc = {};
-    tile_mfma<TIO, MT, NB>(acc, cav, cbv, cur.pok, cur.cok, kg, 0, nv, s_u);
-    const float* un = unary + n * K;
+    return t;
+  };
+
+  // slot 0: u to LDS and its tile; slot 1's operands in flight
+  float uv[2][kMaxProjSplit];
+  load_u(0, uv);
+  u32x4 a0[NV], b0[NV], a1[NV], b1[NV];
+  TileRows<TIO> t0 = gather(0, a0, b0);
+  store_u(uv, s_u2);
+  load_u(S > 1 ? 1 : 0, uv);
+  TileRows<TIO> t1 = gather(S > 1 ? 1 : 0, a1, b1);
+  typename Tile::acc_t acc = {};
+  tile_mfma<TIO, MT, NV>(acc, a0, b0, t0.pok, t0.cok, kg, 0, NV, s_u2);
+
+  int prev = 0;
+  // One slot: (xa, xb, tx) hold slot s + 1's pieces, (ya, yb, ty) receive slot
+  // s + 2's.  Slots past S - 1 are clamped (their results are not used).
+  auto step = [&](int s, u32x4 (&xa)[NV], u32x4 (&xb)[NV], const TileRows<TIO>& tx, u32x4 (&ya)[NV],
+                  u32x4 (&yb)[NV], TileRows<TIO>& ty) {
+    const int64_t n = row0 + s;
+    const int sa = min(s + 2, S - 1);
+    float* un_lds = s_u2 + ((s + 1) & 1) * KPAD;
+    store_u(uv, un_lds);
+    load_u(sa, uv);
+    ty = gather(sa, ya, yb);
+    // slot s + 1's MFMA chain and slot s's decision, in one stretch of code
+    typename Tile::acc_t acc_n = {};
+    tile_mfma<TIO, MT, NV>(acc_n, xa, xb, tx.pok, tx.cok, kg, 0, NV, un_lds);
+    const float* un = s_un + s * MT;
     if (scores_out) lattice_store<MT>(acc, un, K, scores_out + n * K * K, K);
-    // row prev of the tile: its column c sits in lane (prev's lane group) * MT + c,
-    // accumulator i(prev); + unary[c] as lattice_store adds it
+    // row prev of slot s's tile: its column c sits in lane (prev's lane
+    // group) * MT + c, accumulator i(prev); + unary[c] as lattice_store adds it
     int src_grp, ai;
     if (MT == 32) { src_grp = (prev >> 2) & 1; ai = 4 * (prev >> 3) + (prev & 3); }
     else          { src_grp = prev >> 2;       ai = prev & 3; }
@@ -835,14 +1019,17 @@ __global__ __launch_bounds__(kLWWaves * 64) void lattice_walk_wave_kernel(
 #pragma unroll
     for (int i = 1; i < Tile::kAcc; ++i) x = (ai == i) ? acc[i] : x;
     const float row_v = __shfl(x, src_grp * MT + e, 64);
-    const float v = lane < K ? row_v + un[e] : 0.f;
+    const float v = lane < K ? row_v + un[e] : -INFINITY;
     float q;
-    const int idx = walk_decide(v, lane, K, greedy, temp, uniforms[n], q);
+    const int idx = walk_decide_wave<MT>(v, lane, K, greedy, temp, s_uni[s], q);
     if (lane < K) q_out[n * K + lane] = q;
-    const int64_t tok = (int64_t)__builtin_amdgcn_readlane((int)(uint64_t)cand_s, idx) |
-                        ((int64_t)__builtin_amdgcn_readlane((int)((uint64_t)cand_s >> 32), idx) << 32);
-    if (lane == 0) tokens[n] = tok;
+    if (lane == 0) tokens[n] = s_id[s * MT + idx];   // the chosen candidate's id as given
     prev = idx;
+    acc = acc_n;
+  };
+  for (int s = 0; s < S; s += 2) {
+    step(s, a1, b1, t1, a0, b0, t0);
+    if (s + 1 < S) step(s + 1, a0, b0, t0, a1, b1, t1);
   }
 }
 
@@ -853,10 +1040,24 @@ ProjPlan plan_proj(int32_t n_rows, int32_t rank, int32_t hidden, int32_t dtype) 
   p.n_rows = n_rows;
   p.rank = rank;
   p.hidden = hidden;
-  if (dtype == DFLASH_BF16) {
-    // four row fragments per wave once there are rows enough to fill the chip
-    p.frags = n_rows >= 4096 ? 4 : 1;
-    p.row_tiles = (n_rows + kRowsPerWG * p.frags - 1) / (kRowsPerWG * p.frags);
+  if (dtype == DFLASH_BF16 && n_rows >= kProjTileMinRows && rank <= ProjTileCfg::kBN) {
+    // 128-row tiles; the contraction split so that ~480 workgroups exist
+    // (a split above 4 costs nothing more in partials up to the next
+    // multiple of 4, so it is rounded up to one)
+    p.tiled = 1;
+    p.row_tiles = (n_rows + ProjTileCfg::kBM - 1) / ProjTileCfg::kBM;
+    const int nk = (hidden + ProjTileCfg::kBK - 1) / ProjTileCfg::kBK;
+    int ks = (480 + p.row_tiles - 1) / p.row_tiles;
+    if (ks > 4) ks = (ks + 3) & ~3;
+    if (ks > kMaxProjSplit) ks = kMaxProjSplit;
+    if (ks > nk) ks = nk;
+    if (ks < 1) ks = 1;
+    const int kb = (nk + ks - 1) / ks;
+    p.kslice = kb * ProjTileCfg::kBK;
+    p.ksplit = (nk + kb - 1) / kb;
+  } else if (dtype == DFLASH_BF16) {
+    p.frags = 1;
+    p.row_tiles = (n_rows + kRowsPerWG - 1) / kRowsPerWG;
     int ks = p.row_tiles > 0 ? (512 + p.row_tiles - 1) / p.row_tiles : 1;
     const int max_ks = hidden / 256 > 1 ? hidden / 256 : 1;   // slices of >= 8 k-steps
     if (ks > max_ks) ks = max_ks;
@@ -879,6 +1080,13 @@ ProjPlan plan_proj(int32_t n_rows, int32_t rank, int32_t hidden, int32_t dtype) 
 hipError_t launch_proj(const SelectArgs& a, const ProjPlan& p, hipStream_t stream) {
   const int n_rows = a.n_req * a.slots;
   if (n_rows == 0 || a.rank == 0) return hipSuccess;
+  if (a.dtype == DFLASH_BF16 && p.tiled) {
+    hipLaunchKernelGGL(proj_tile_kernel, dim3(p.row_tiles, p.ksplit), dim3(ProjTileCfg::kThreads),
+                       ProjTileCfg::kSmemBytes, stream, static_cast<const uint16_t*>(a.hidden), a.hidden_req_stride,
+                       a.hidden_slot_stride, a.slots, static_cast<const uint16_t*>(a.proj), n_rows, a.rank,
+                       a.hidden_size, p.kslice / ProjTileCfg::kBK, a.u_parts);
+    return hipGetLastError();
+  }
   if (a.dtype == DFLASH_BF16) {
     const dim3 grid(p.row_tiles, p.ksplit);
     const uint16_t* h = static_cast<const uint16_t*>(a.hidden);
@@ -894,11 +1102,7 @@ hipError_t launch_proj(const SelectArgs& a, const ProjPlan& p, hipStream_t strea
   else if (tiles <= 4) DFLASH_PROJ(4, FR);  \
   else if (tiles <= 8) DFLASH_PROJ(8, FR);  \
   else return hipErrorInvalidValue;   /* rank > 128 is rejected by the API layer */
-    if (p.frags == 4) {
-      DFLASH_PROJ_RT(4)
-    } else {
-      DFLASH_PROJ_RT(1)
-    }
+    DFLASH_PROJ_RT(1)
 #undef DFLASH_PROJ_RT
 #undef DFLASH_PROJ
   } else {
@@ -973,12 +1177,17 @@ bool lattice_walk_fits(const SelectArgs& a) {
 }
 
 // One wave per request once the batch has a request for every SIMD (the
-// serial decisions then hide behind each other); the tile's k-range must fit
-// one gather round and two u values per lane.
+// serial decisions then hide behind each other); the tile's k-range must be
+// whole 16-byte pieces inside the rank, one gather round and two u values
+// per lane.
 bool lattice_walk_per_wave(const SelectArgs& a) {
   const int vec = lattice_vec(a.dtype);
+  const int MT = lattice_mt(a.top_k);
   const int L = lattice_group_len(a.top_k, a.rank, vec);
-  return a.n_req >= kLatticeWalkWaveMinReq && L <= 8 * vec && lattice_kpad(a.top_k, a.rank, vec) <= 128;
+  const int nv = L / vec;
+  return a.n_req >= kLatticeWalkWaveMinReq && a.slots <= kWaveMaxSlots && lattice_vload(a) &&
+         a.rank % ((64 / MT) * vec) == 0 && (nv == 1 || nv == 2 || nv == 4 || nv == 8) &&
+         lattice_kpad(a.top_k, a.rank, vec) <= 128;
 }
 
 hipError_t launch_lattice_walk(const SelectArgs& a, const ProjPlan& p, const WalkArgs& w, float* scores_out,
@@ -986,20 +1195,28 @@ hipError_t launch_lattice_walk(const SelectArgs& a, const ProjPlan& p, const Wal
   if (a.n_req == 0 || a.slots == 0) return hipSuccess;
   if (lattice_walk_per_wave(a)) {
     const int MT = lattice_mt(a.top_k);
-    const int L = lattice_group_len(a.top_k, a.rank, lattice_vec(a.dtype));
-    const int vload = lattice_vload(a) ? 1 : 0;
-    const size_t lds = (size_t)kLWWaves * (64 / MT) * L * sizeof(float);
+    const int vec = lattice_vec(a.dtype);
+    const int L = lattice_group_len(a.top_k, a.rank, vec);
+    const int nv = L / vec;
+    const size_t lds = (size_t)kLWWaves * (2 * (64 / MT) * L * sizeof(float) + kWaveMaxSlots * MT * sizeof(int64_t) +
+                                           (kWaveMaxSlots * MT + kWaveMaxSlots) * sizeof(float));
     const dim3 grid((a.n_req + kLWWaves - 1) / kLWWaves);
-#define DFLASH_LWW(TIO, MTV)                                                                                        \
-  hipLaunchKernelGGL((lattice_walk_wave_kernel<TIO, MTV>), grid, dim3(kLWWaves * 64), lds, stream, a.ids, a.unary,  \
-                     a.anchor, static_cast<const TIO*>(a.sel_a), static_cast<const TIO*>(a.sel_b), a.u_parts,      \
-                     p.ksplit, a.slots, a.top_k, a.rank, L, vload, a.vocab, a.n_req, w.uniforms, w.temperatures,   \
+#define DFLASH_LWW(TIO, MTV, NVV)                                                                                 \
+  hipLaunchKernelGGL((lattice_walk_wave_kernel<TIO, MTV, NVV>), grid, dim3(kLWWaves * 64), lds, stream, a.ids,      \
+                     a.unary, a.anchor, static_cast<const TIO*>(a.sel_a), static_cast<const TIO*>(a.sel_b),         \
+                     a.u_parts, p.ksplit, a.slots, a.top_k, a.rank, a.vocab, a.n_req, w.uniforms, w.temperatures,   \
                      w.greedy, scores_out, w.tokens, w.q)
+#define DFLASH_LWW_NV(TIO, MTV)                                     \
+  if (nv == 1) DFLASH_LWW(TIO, MTV, 1);                             \
+  else if (nv == 2) DFLASH_LWW(TIO, MTV, 2);                        \
+  else if (nv == 4) DFLASH_LWW(TIO, MTV, 4);                        \
+  else DFLASH_LWW(TIO, MTV, 8);
     if (a.dtype == DFLASH_BF16) {
-      if (MT == 16) DFLASH_LWW(uint16_t, 16); else DFLASH_LWW(uint16_t, 32);
+      if (MT == 16) { DFLASH_LWW_NV(uint16_t, 16) } else { DFLASH_LWW_NV(uint16_t, 32) }
     } else {
-      if (MT == 16) DFLASH_LWW(float, 16); else DFLASH_LWW(float, 32);
+      if (MT == 16) { DFLASH_LWW_NV(float, 16) } else { DFLASH_LWW_NV(float, 32) }
     }
+#undef DFLASH_LWW_NV
 #undef DFLASH_LWW
     return hipGetLastError();
   }

@@ -94,6 +94,39 @@ def test_lattice_bar_holds_fp32_and_rejects_bf16_projection(name, n_req):
           f"bf16 err / fp32 worst-case bound {float(np.max(np.abs(got_bf - ref) / loose)):.3f}")
 
 
+def _split_bf16_lattice(ids, unary, u32, anchor, A, B):
+    """The edge formula with w = A * u rounded to fp32 and then split as
+    hi = bf16(w), lo = bf16(w - hi); each of hi * B and lo * B is exact (bf16
+    x bf16), summed here exactly (float64) -- the arithmetic of a matrix-core
+    tile that keeps the terms bf16 but carries w to ~16 significant bits."""
+    A32 = A.astype(np.float32)
+    R, S, K = ids.shape
+    out = np.empty((R, S, K, K))
+    for r in range(R):
+        for s in range(S):
+            prev = np.full(K, anchor[r]) if s == 0 else ids[r, s - 1]
+            w = (A32[prev] * u32[r, s]).astype(np.float32).astype(np.float64)
+            hi = O.round_to_bf16(w)
+            lo = O.round_to_bf16(w - hi)
+            out[r, s] = (hi + lo) @ B[ids[r, s]].T + unary[r, s][None, :].astype(np.float32)
+    return out
+
+
+@pytest.mark.parametrize("name,n_req", [("bf16_b16_v151936", 4), ("stress_r1024_k32", 2)])
+def test_lattice_bar_holds_the_split_bf16_tile(name, n_req):
+    # The two-term bf16 split of w keeps each product within 2^-18 |w B| of
+    # w B: far inside the bar (a single bf16 rounding, 2^-9, breaks it).
+    w, h, A, B, P, ids, unary, anchor = _selector_case(name, n_req, seed=99)
+    u = O.project(h, P)
+    ref = O.lattice(ids, unary, u, anchor, A, B)
+    bar = lattice_bar(ids, unary, u, anchor, A, B)
+    u32 = (h.astype(np.float32) @ P.astype(np.float32).T).astype(np.float32)
+    got = _split_bf16_lattice(ids, unary, u32, anchor, A, B)
+    ratio = float(np.max(np.abs(got - ref) / bar))
+    assert ratio <= 0.1, ratio
+    print(f"[bar] {name}: split-bf16 tile err/bar {ratio:.4f}")
+
+
 def test_softmax_shift_bounds_random_perturbations():
     rng = np.random.default_rng(7)
     for _ in range(200):
