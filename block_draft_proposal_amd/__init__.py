@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     dflash_lm_head,
     dflash_lm_head_topk,
     dflash_propose_block,
+    dflash_propose_block_noalloc,
     ProposeBlock,
     ProposeGraph,
     dflash_philox_uniforms,

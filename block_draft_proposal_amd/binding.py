@@ -84,6 +84,7 @@ _SIGNATURES = {
                                      _c_i32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "dflash_propose_block_workspace_size": (_c_size, [ctypes.POINTER(DraftConfig), _c_i32, _c_i64]),
     "dflash_propose_block": (_c_i32, [ctypes.POINTER(DraftConfig), ctypes.POINTER(BlockArgs), _c_vp]),
+    "dflash_propose_block_noalloc": (_c_i32, [ctypes.POINTER(DraftConfig), ctypes.POINTER(BlockArgs), _c_vp]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -335,12 +336,14 @@ class ProposeBlock:
     buffers: built once, then each call only hands the prepared struct to the
     library (what a serving loop whose buffers stay put does every step).
     Inputs as for dflash_propose_block; the outputs dict and the workspace are
-    allocated here unless given, and are rewritten by every call."""
+    allocated here unless given, and are rewritten by every call.  noalloc:
+    call dflash_propose_block_noalloc instead (no workspace: the library's
+    own scratch; the call itself allocates nothing)."""
 
     def __init__(self, cfg: DraftConfig, *, x, conv_base, conv_delta, logits, anchor, sel_a, sel_b, proj,
                  uniforms, temperatures, greedy_mask, valid_vocab: Optional[int] = None,
                  vocab: Optional[int] = None, keep_scores: bool = False,
-                 outputs: Optional[Dict[str, torch.Tensor]] = None, workspace=None):
+                 outputs: Optional[Dict[str, torch.Tensor]] = None, workspace=None, noalloc: bool = False):
         B, K = cfg.block_size, cfg.selector_top_k
         S = B - 1
         N = x.shape[0]
@@ -360,7 +363,9 @@ class ProposeBlock:
         for k, (shape, dt) in shapes.items():
             if k not in o:
                 o[k] = torch.empty(shape, dtype=dt, device=dev)
-        if workspace is None:
+        if noalloc:
+            workspace = None                 # the library's own scratch (dflash_propose_block_noalloc)
+        elif workspace is None:
             nbytes = propose_block_workspace_size(cfg, max(R, 1), valid_vocab)
             workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
         self.outputs = o
@@ -375,10 +380,10 @@ class ProposeBlock:
             _p(anchor), _p(sel_a), _p(sel_b), _p(proj),
             _p(uniforms), _p(temperatures), _p(greedy_mask),
             _p(o["conv_out"]), _p(o["ids"]), _p(o["unary"]), _p(o["tokens"]), _p(o["q"]), _p(o.get("scores")),
-            _p(workspace), workspace.numel(), None, R, _dtype_code(x))
+            _p(workspace), 0 if workspace is None else workspace.numel(), None, R, _dtype_code(x))
         self._cfg_ref = ctypes.byref(cfg)
         self._args_ref = ctypes.byref(self._args)
-        self._fn = lib().dflash_propose_block
+        self._fn = lib().dflash_propose_block_noalloc if noalloc else lib().dflash_propose_block
 
     @staticmethod
     def event_array(stage_events: Sequence):
@@ -515,6 +520,13 @@ class ProposeGraph:
             raise RuntimeError("staging copy failed")
         self.graph.replay()
         return self.call.outputs
+
+
+def dflash_propose_block_noalloc(cfg: DraftConfig, *, stage_events: Optional[Sequence] = None, stream=None,
+                                 **kw) -> Dict[str, torch.Tensor]:
+    """dflash_propose_block through the entry point that allocates nothing
+    (its scratch is the library's own); same inputs and outputs."""
+    return dflash_propose_block(cfg, stage_events=stage_events, stream=stream, noalloc=True, **kw)
 
 
 def dflash_propose_block(cfg: DraftConfig, *, stage_events: Optional[Sequence] = None, stream=None,

@@ -1,6 +1,8 @@
 // C ABI of the DFlash2 draft-block library: host-side validation and launch
 // sequencing.  Every check runs on the host before anything is enqueued.
+#include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -205,15 +207,49 @@ BlockLayout block_layout(const dflash_draft_config* cfg, int32_t n_req, int64_t 
   BlockLayout L{};
   const int32_t slots = cfg->block_size - 1;
   const int64_t rows = (int64_t)n_req * slots;
-  const int32_t K = cfg->selector_top_k;
+  const int32_t K = cfg->selector_top_k, r = cfg->selector_rank;
   L.topk = dflash::plan_topk(rows, valid_vocab, K);
-  // dtype only changes the projection split; size for the larger (bf16) plan
-  const dflash::ProjPlan pb = dflash::plan_proj((int32_t)rows, cfg->selector_rank, cfg->hidden_size, DFLASH_BF16);
-  const dflash::ProjPlan pf = dflash::plan_proj((int32_t)rows, cfg->selector_rank, cfg->hidden_size, DFLASH_F32);
+  // dtype only changes the projection split; size for the larger plan
+  const dflash::ProjPlan pb = dflash::plan_proj((int32_t)rows, r, cfg->hidden_size, DFLASH_BF16);
+  const dflash::ProjPlan pf = dflash::plan_proj((int32_t)rows, r, cfg->hidden_size, DFLASH_F32);
   L.proj_off = align256(L.topk.bytes);
   L.scores_off = L.proj_off + align256(pb.bytes > pf.bytes ? pb.bytes : pf.bytes);
-  L.bytes = L.scores_off + align256((size_t)rows * K * K * sizeof(float));
+  // the scores need workspace only when no lattice + walk kernel keeps a
+  // request's scores on chip (its LDS need, for the larger dtype)
+  const size_t lw = std::max(dflash::lattice_walk_lds_bytes(slots, K, r, DFLASH_BF16),
+                             dflash::lattice_walk_lds_bytes(slots, K, r, DFLASH_F32));
+  const bool scores_in_ws = lw > dflash::kLatticeWalkLdsMax;
+  L.bytes = L.scores_off + (scores_in_ws ? align256((size_t)rows * K * K * sizeof(float)) : 0);
   return L;
+}
+
+// Scratch of dflash_propose_block_noalloc: device storage of the library
+// itself (each GPU holds its own copy from the library's first use on it
+// until the process ends).  In host code `scratch` names a host-side stand-in,
+// not device memory: the device address comes from hipGetSymbolAddress, once
+// per device (scratch_ptr), and only that address is ever handed to kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) static unsigned char scratch[kNoAllocScratchBytes];
+
+struct DeviceScratch {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+
+int scratch_ptr(void** out, const char* who) {
+  static DeviceScratch per_device[kMaxDevices];
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DFLASH_ERR_LAUNCH, "%s: hipGetDevice failed: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DFLASH_ERR_UNSUPPORTED, "%s: device index %d", who, dev);
+  DeviceScratch& d = per_device[dev];
+  // with device `dev` current: its copy of the array
+  std::call_once(d.once, [&] { d.err = hipGetSymbolAddress(&d.ptr, HIP_SYMBOL(scratch)); });
+  if (d.err != hipSuccess || !d.ptr)
+    return fail(DFLASH_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch) failed: %s", who, hipGetErrorString(d.err));
+  *out = d.ptr;
+  return DFLASH_OK;
 }
 
 }  // namespace
@@ -489,8 +525,16 @@ size_t dflash_propose_block_workspace_size(const dflash_draft_config* cfg, int32
   return block_layout(cfg, n_req, valid_vocab).bytes;
 }
 
-int dflash_propose_block(const dflash_draft_config* cfg, const dflash_block_args* a, dflash_stream_t stream) {
-  const char* who = "dflash_propose_block";
+}  // extern "C"
+
+namespace {
+
+// The draft block on `stream` with workspace [ws, ws + ws_bytes).  aux_ok:
+// the conv and the projection may run on the library's auxiliary stream
+// beside the top-K (created on first use); otherwise every stage runs on
+// `stream`, in the order conv, projection, top-K, lattice + walk.
+int propose_impl(const dflash_draft_config* cfg, const dflash_block_args* a, dflash_stream_t stream, void* ws_ptr,
+                 size_t ws_bytes, bool aux_ok, const char* who) {
   if (!a) return fail(DFLASH_ERR_INVALID_ARG, "%s: null args", who);
   int st = dflash_validate_config(cfg);
   if (st != DFLASH_OK) return st;
@@ -506,8 +550,7 @@ int dflash_propose_block(const dflash_draft_config* cfg, const dflash_block_args
   if (st != DFLASH_OK) return st;
   const BlockLayout L = block_layout(cfg, a->n_req > 0 ? a->n_req : 1, a->valid_vocab > 0 ? a->valid_vocab : 1);
   st = check_topk(a->logits, a->logits_row_stride, rows, a->vocab, a->valid_vocab, K, cfg->output_multiplier,
-                  cfg->final_logit_softcapping, a->dtype, a->ids_out, a->unary_out, L.topk, a->workspace,
-                  a->workspace_bytes, who);
+                  cfg->final_logit_softcapping, a->dtype, a->ids_out, a->unary_out, L.topk, ws_ptr, ws_bytes, who);
   if (st != DFLASH_OK) return st;
   st = check_select(a->ids_out, a->unary_out, a->conv_out, (int64_t)B * H, H, a->anchor_ids, a->sel_a, a->sel_b,
                     a->proj, a->n_req, S, K, H, r, a->vocab, a->dtype, who);
@@ -516,17 +559,17 @@ int dflash_propose_block(const dflash_draft_config* cfg, const dflash_block_args
                   a->temperatures, a->greedy_mask, a->n_req, S, K, a->tokens_out, a->q_out, who);
   if (st != DFLASH_OK) return st;
   if (a->n_req == 0) return ok();
-  if (a->workspace_bytes < L.bytes || !a->workspace)
-    return fail(DFLASH_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu needed", who, a->workspace_bytes, L.bytes);
-  if (reinterpret_cast<uintptr_t>(a->workspace) & 255)
+  if (ws_bytes < L.bytes || (L.bytes && !ws_ptr))
+    return fail(DFLASH_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu needed", who, ws_bytes, L.bytes);
+  if (reinterpret_cast<uintptr_t>(ws_ptr) & 255)
     return fail(DFLASH_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", who);
 
   hipStream_t s = as_hip(stream);
-  char* ws = static_cast<char*>(a->workspace);
+  char* ws = static_cast<char*>(ws_ptr);
   float* scores = a->scores_out ? a->scores_out : reinterpret_cast<float*>(ws + L.scores_off);
   void* const* ev = a->stage_events;
   dflash::TopkArgs ta{a->logits, a->logits_row_stride, rows, a->vocab, a->valid_vocab, K, cfg->output_multiplier,
-                      cfg->final_logit_softcapping, a->dtype, a->ids_out, a->unary_out, a->workspace};
+                      cfg->final_logit_softcapping, a->dtype, a->ids_out, a->unary_out, ws_ptr};
   dflash::ConvArgs ca{a->x, a->conv_base, a->conv_delta, a->delta_row_stride, a->conv_out, N, H, gs, T, B,
                       a->dtype};
   const dflash::ProjPlan pp = dflash::plan_proj((int32_t)rows, r, H, a->dtype);
@@ -544,6 +587,17 @@ int dflash_propose_block(const dflash_draft_config* cfg, const dflash_block_args
     if ((st = record(ev, 3, s)) != DFLASH_OK) return st;
     if ((st = record(ev, 4, s)) != DFLASH_OK) return st;
     if ((st = record(ev, 5, s)) != DFLASH_OK) return st;
+  } else if (!aux_ok) {
+    // every stage on `stream`: conv, projection, then the top-K
+    if ((st = record(ev, 0, s)) != DFLASH_OK) return st;
+    if ((st = launch_status(dflash::launch_conv(ca, s), who)) != DFLASH_OK) return st;
+    if ((st = record(ev, 1, s)) != DFLASH_OK) return st;
+    if ((st = record(ev, 4, s)) != DFLASH_OK) return st;
+    if ((st = launch_status(dflash::launch_proj(sa, pp, s), who)) != DFLASH_OK) return st;
+    if ((st = record(ev, 5, s)) != DFLASH_OK) return st;
+    if ((st = record(ev, 2, s)) != DFLASH_OK) return st;
+    if ((st = launch_status(dflash::launch_topk(ta, L.topk, s), who)) != DFLASH_OK) return st;
+    if ((st = record(ev, 3, s)) != DFLASH_OK) return st;
   } else {
     ForkJoin* fj = nullptr;
     if ((st = fork_join(&fj, who)) != DFLASH_OK) return st;
@@ -579,6 +633,34 @@ int dflash_propose_block(const dflash_draft_config* cfg, const dflash_block_args
   }
   if ((st = record(ev, 7, s)) != DFLASH_OK) return st;
   return ok();
+}
+
+
+}  // namespace
+
+extern "C" {
+
+int dflash_propose_block(const dflash_draft_config* cfg, const dflash_block_args* a, dflash_stream_t stream) {
+  if (!a) return fail(DFLASH_ERR_INVALID_ARG, "dflash_propose_block: null args");
+  return propose_impl(cfg, a, stream, a->workspace, a->workspace_bytes, true, "dflash_propose_block");
+}
+
+int dflash_propose_block_noalloc(const dflash_draft_config* cfg, const dflash_block_args* a,
+                                 dflash_stream_t stream) {
+  const char* who = "dflash_propose_block_noalloc";
+  if (!a) return fail(DFLASH_ERR_INVALID_ARG, "%s: null args", who);
+  if (!cfg) return fail(DFLASH_ERR_INVALID_ARG, "%s: null config", who);
+  if (cfg->block_size >= 2 && cfg->selector_top_k > 0 && cfg->selector_rank > 0 && cfg->hidden_size > 0 &&
+      a->n_req > 0 && a->valid_vocab > 0) {
+    const size_t need = block_layout(cfg, a->n_req, a->valid_vocab).bytes;
+    if (need > kNoAllocScratchBytes)
+      return fail(DFLASH_ERR_WORKSPACE, "%s: needs %zu bytes of scratch, more than the %zu-byte static scratch", who,
+                  need, kNoAllocScratchBytes);
+  }
+  void* ptr = nullptr;
+  int st = scratch_ptr(&ptr, who);
+  if (st != DFLASH_OK) return st;
+  return propose_impl(cfg, a, stream, ptr, kNoAllocScratchBytes, false, who);
 }
 
 }  // extern "C"

@@ -34,7 +34,12 @@
  *     floats (unary, scores, q) are always fp32.
  *   - Vector loads need 16-byte alignment of the tensors and row strides named
  *     in each entry point; a violation is DFLASH_ERR_INVALID_ARG.
- *   - Thread safety: no mutable global state; the error string is per thread.
+ *   - Thread safety: the error string is per thread.  The library's mutable
+ *     state is set up on first use and kept until the process ends: the
+ *     auxiliary stream and two ordering events of dflash_propose_block (one
+ *     set per host thread and device) and the device address of the
+ *     no-allocation scratch (one per device); calls from several threads are
+ *     safe as long as they share no workspace or output buffers.
  *   - Sizes: 1 <= top_k <= 32; vocab < 2^24; everything else bounded by int64.
  */
 #ifndef DFLASH_H
@@ -345,6 +350,26 @@ size_t dflash_propose_block_workspace_size(const dflash_draft_config* cfg, int32
                                            int64_t valid_vocab);
 int dflash_propose_block(const dflash_draft_config* cfg, const dflash_block_args* args,
                          dflash_stream_t stream);
+
+/*
+ * dflash_propose_block_noalloc -- dflash_propose_block for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same computation and
+ * results, with no hipMalloc, hipFree or other allocating call inside.
+ *   - Scratch: a 64 MiB array of device storage inside the library (each GPU
+ *     the library runs on holds its own copy from the first use on it until
+ *     the process ends); args->workspace and args->workspace_bytes are
+ *     ignored.  A batch whose workspace (dflash_propose_block_workspace_size)
+ *     exceeds 64 MiB is rejected with DFLASH_ERR_WORKSPACE, nothing enqueued.
+ *   - Every stage runs on `stream` (conv, projection, top-K, lattice + walk),
+ *     never on the auxiliary stream; stage events as for dflash_propose_block.
+ *   - The scratch is shared by every call on a GPU and keeps whatever the
+ *     last call left (no call relies on its contents): two calls that may
+ *     overlap in time on the same GPU race.  Serialise them (one stream, or
+ *     events).
+ */
+int dflash_propose_block_noalloc(const dflash_draft_config* cfg, const dflash_block_args* args,
+                                 dflash_stream_t stream);
 
 #ifdef __cplusplus
 }

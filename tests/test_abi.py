@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_entry_point():
     names = _declared_functions()
-    assert "dflash_propose_block" in names and len(names) == 19
+    assert "dflash_propose_block" in names and len(names) == 20
     lib = D.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -276,3 +276,19 @@ def test_error_message_is_per_call():
     cfg = _cfg()
     assert L.dflash_validate_config(ctypes.byref(cfg)) == 0
     assert D.last_error() == ""
+
+
+def test_propose_block_noalloc_rejects_batches_beyond_its_scratch():
+    # Host-side checks only (nothing reaches the GPU): a batch whose
+    # workspace exceeds the 64 MiB static scratch is refused up front.
+    L = D.lib()
+    cfg = D.make_config(taps=4, group_size=64, rank=128, top_k=32, multiplier=1.0, softcap=30.0, block_size=16,
+                        hidden=4096)
+    n_req = 8192                                        # 122880 slot rows: far more than 64 MiB of partials
+    assert L.dflash_propose_block_workspace_size(ctypes.byref(cfg), n_req, 201024) > 64 << 20
+    args = Bd.BlockArgs()
+    args.n_req, args.valid_vocab, args.vocab, args.dtype = n_req, 201024, 201024, 1
+    st = L.dflash_propose_block_noalloc(ctypes.byref(cfg), ctypes.byref(args), None)
+    assert st == Bd.DFLASH_ERR_WORKSPACE
+    assert b"static scratch" in L.dflash_last_error()
+    assert L.dflash_propose_block_noalloc(ctypes.byref(cfg), None, None) == Bd.DFLASH_ERR_INVALID_ARG
