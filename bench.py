@@ -67,10 +67,11 @@ TOPK_SOURCES = tuple(os.path.join(ROOT, "block_draft_proposal_amd", "csrc", f)
 def single_launch_stage1(w) -> bool:
     """Whether dflash_propose_block runs the conv and the slot projection as
     workgroups of the top-K's launch (bf16, blocks of 16 tokens, <= 8 taps,
-    one group per 16-byte vector, rank <= 128, fewer than 4096 slot rows);
-    otherwise they run beside it on a second stream."""
+    one group per 16-byte vector, rank <= 128, fewer than 2048 slot rows --
+    beyond that the projection runs as its own tiled kernel); otherwise they
+    run beside it on a second stream."""
     return (w.dtype == "bf16" and w.block_size == 16 and 1 <= w.taps <= 8 and w.group_size % 8 == 0
-            and w.rank <= 128 and w.n_slot_rows < 4096)
+            and w.rank <= 128 and w.n_slot_rows < 2048)
 
 
 def sources_sha256(paths) -> str:
@@ -529,6 +530,21 @@ def main():
     else:
         stage1_bytes, stage1_name = nbytes["topk"], "topk_rows"
     topk_gbs = stage1_bytes / (avg_ms[1] * 1e-3) / 1e9
+    # The conv's own rate: dflash_conv alone on the same rotating inputs (beside
+    # the top-K its events are stretched by the shared HBM), median of 20.
+    conv_out = torch.empty_like(sets[0]["x"])
+    conv_ev = []
+    for i in range(25):
+        st = sets[i % n_sets]
+        a, b = TimingEvent(), TimingEvent()
+        a.record(stream)
+        D.dflash_conv(st["x"], st["base"][0], st["delta"][:, 0], block_size=w.block_size, group_size=w.group_size,
+                      out=conv_out)
+        b.record(stream)
+        conv_ev.append((a, b))
+    torch.cuda.synchronize()
+    conv_us = sorted(a.elapsed_time(b) for a, b in conv_ev[5:])[10] * 1e3
+    conv_gbs = nbytes["conv"] / (conv_us * 1e-6) / 1e9
     tokens = w.n_slot_rows * args.steps
     line = {
         "metric": METRIC,
@@ -550,6 +566,12 @@ def main():
         "roofline": {"bound": "hbm", "kernel": stage1_name, "achieved": topk_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": topk_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                      "algorithmic_bytes_per_launch": stage1_bytes, "avg_launch_us": avg_ms[1] * 1e3},
+        "hbm_kernels": {
+            "topk": {"achieved": topk_gbs, "frac": topk_gbs / HBM_PEAK_GBS, "unit": "GB/s",
+                     "how": "the roofline kernel above (events around it inside the timed steps)"},
+            "conv": {"achieved": conv_gbs, "frac": conv_gbs / HBM_PEAK_GBS, "unit": "GB/s", "us": conv_us,
+                     "algorithmic_bytes": nbytes["conv"],
+                     "how": "dflash_conv alone on the same rotating inputs, median of 20 calls by HIP events"}},
         "stage_us": {"conv": avg_ms[0] * 1e3, "topk": avg_ms[1] * 1e3, "proj": avg_ms[2] * 1e3,
                      "lattice_walk": avg_ms[3] * 1e3, "note": f"top-K from every {TIMED_EVERY}th timed step, the other stages "
                      f"from {n_stage} further steps with all stage events; "

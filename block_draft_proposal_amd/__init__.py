@@ -28,4 +28,7 @@ from .binding import (  # noqa: F401
     ProposeGraph,
     dflash_philox_uniforms,
     propose_block_workspace_size,
+    propose_block_schedule,
+    SCHEDULE_ONE_LAUNCH,
+    SCHEDULE_AUX_STREAM,
 )

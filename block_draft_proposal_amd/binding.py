@@ -85,6 +85,7 @@ _SIGNATURES = {
     "dflash_propose_block_workspace_size": (_c_size, [ctypes.POINTER(DraftConfig), _c_i32, _c_i64]),
     "dflash_propose_block": (_c_i32, [ctypes.POINTER(DraftConfig), ctypes.POINTER(BlockArgs), _c_vp]),
     "dflash_propose_block_noalloc": (_c_i32, [ctypes.POINTER(DraftConfig), ctypes.POINTER(BlockArgs), _c_vp]),
+    "dflash_propose_block_schedule": (_c_i32, [ctypes.POINTER(DraftConfig), _c_i32, _c_i32]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -329,6 +330,20 @@ def dflash_lm_head_topk(hidden: torch.Tensor, weight: torch.Tensor, *, top_k: in
 
 def propose_block_workspace_size(cfg: DraftConfig, n_req: int, valid_vocab: int) -> int:
     return lib().dflash_propose_block_workspace_size(ctypes.byref(cfg), n_req, valid_vocab)
+
+
+SCHEDULE_ONE_LAUNCH = 1    # conv + projection inside the top-K's launch
+SCHEDULE_AUX_STREAM = 2    # conv + projection on the auxiliary stream beside the top-K
+
+
+def propose_block_schedule(cfg: DraftConfig, n_req: int, dtype: str) -> int:
+    """The schedule dflash_propose_block takes for this config, batch and
+    dtype ("bf16" or "f32"): SCHEDULE_ONE_LAUNCH or SCHEDULE_AUX_STREAM."""
+    code = {"f32": 0, "bf16": 1}[dtype]
+    got = lib().dflash_propose_block_schedule(ctypes.byref(cfg), n_req, code)
+    if got == 0:
+        raise DFlashError(DFLASH_ERR_INVALID_ARG, last_error() or "dflash_propose_block_schedule: rejected shape")
+    return got
 
 
 class ProposeBlock:

@@ -525,6 +525,22 @@ size_t dflash_propose_block_workspace_size(const dflash_draft_config* cfg, int32
   return block_layout(cfg, n_req, valid_vocab).bytes;
 }
 
+int dflash_propose_block_schedule(const dflash_draft_config* cfg, int32_t n_req, int32_t dtype) {
+  if (dflash_validate_config(cfg) != DFLASH_OK) return 0;
+  if (cfg->conv_kernel_size == 0 || cfg->selector_top_k == 0 || cfg->block_size < 2 || n_req < 1 ||
+      (dtype != DFLASH_F32 && dtype != DFLASH_BF16))
+    return 0;
+  // the shape fields propose_impl hands to the same decision
+  const int32_t B = cfg->block_size, S = B - 1, H = cfg->hidden_size;
+  const dflash::ConvArgs ca{nullptr, nullptr, nullptr, 0, nullptr, (int64_t)n_req * B, H,
+                            cfg->conv_group_size, cfg->conv_kernel_size, B, dtype};
+  const dflash::SelectArgs sa{nullptr, nullptr, nullptr, (int64_t)B * H, (int64_t)H, nullptr, nullptr, nullptr,
+                              nullptr, n_req, S, cfg->selector_top_k, H, cfg->selector_rank, 0, dtype,
+                              nullptr, nullptr};
+  const dflash::ProjPlan pp = dflash::plan_proj(n_req * S, cfg->selector_rank, H, dtype);
+  return dflash::conv_slot_proj_fits(ca, sa, pp) ? DFLASH_SCHEDULE_ONE_LAUNCH : DFLASH_SCHEDULE_AUX_STREAM;
+}
+
 }  // extern "C"
 
 namespace {

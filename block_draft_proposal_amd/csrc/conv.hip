@@ -205,7 +205,9 @@ __global__ __launch_bounds__(kWalkWaves * 64) __attribute__((amdgpu_waves_per_eu
   constexpr int TS = 8;                             // tap slots per (token, group) in LDS
   extern __shared__ __align__(16) unsigned char cw_smem[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t unit_raw = (int64_t)blockIdx.x * kWalkWaves + wave;
+  // the slices of one token block read the same coefficient lines: keep
+  // them on one XCD
+  const int64_t unit_raw = (int64_t)xcd_contiguous(blockIdx.x, gridDim.x) * kWalkWaves + wave;
   const bool active = unit_raw < g.units;
   const int64_t unit = active ? unit_raw : g.units - 1;   // a spare wave repeats the last unit, unstored
   const int slice = (int)(unit % g.slices);

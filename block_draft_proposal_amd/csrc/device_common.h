@@ -115,6 +115,16 @@ __device__ __forceinline__ int count_greater(const uint64_t* l, int n, uint64_t 
 // ---------------------------------------------------------------------------
 // Wave (64-lane) reductions
 // ---------------------------------------------------------------------------
+// Workgroups of a launch are dealt to the chip's 8 XCDs in turn (workgroup
+// w runs on XCD w % 8), each XCD with its own L2.  This renumbers them so
+// that consecutive numbers share an XCD: XCD x takes the contiguous range
+// starting at x * (n / 8) + min(x, n % 8).  Work that neighbouring numbers
+// share (the same cache lines) is then fetched into one L2, not several.
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t w, uint32_t n) {
+  const uint32_t q = n >> 3, rem = n & 7, x = w & 7;
+  return x * q + (x < rem ? x : rem) + (w >> 3);
+}
+
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -300,7 +300,7 @@ int dflash_verify(const void* target_logits, int64_t row_stride, int32_t n_req, 
  *   position 0 is the verified anchor) -> lattice -> walk,
  * ordered on `stream` as one unit.  The conv and the projection do not
  * depend on the top-K.  In bf16 with blocks of 16 tokens, at most 8 taps, a
- * group size that is a multiple of 8, rank <= 128 and fewer than 4096 slot
+ * group size that is a multiple of 8, rank <= 128 and fewer than 2048 slot
  * rows, they run as workgroups of the top-K's launch on `stream` (no second
  * stream).  Otherwise they run beside the top-K on an auxiliary stream of the
  * library (one per host thread and device, created on the first such call
@@ -348,6 +348,19 @@ typedef struct {
 
 size_t dflash_propose_block_workspace_size(const dflash_draft_config* cfg, int32_t n_req,
                                            int64_t valid_vocab);
+
+/* Which schedule dflash_propose_block takes for this config, batch size and
+ * dtype, decided on the host from these alone (no GPU work, no allocation):
+ *   DFLASH_SCHEDULE_ONE_LAUNCH: conv and projection are workgroups of the
+ *     top-K's launch on `stream`;
+ *   DFLASH_SCHEDULE_AUX_STREAM: conv then projection on the auxiliary stream,
+ *     beside the top-K on `stream` (dflash_propose_block_noalloc runs them on
+ *     `stream` before the top-K instead).
+ * Returns 0 for a config or size dflash_propose_block would reject on shape
+ * alone (invalid config, conv or selector disabled, block_size < 2, n_req < 1,
+ * unknown dtype). */
+typedef enum { DFLASH_SCHEDULE_ONE_LAUNCH = 1, DFLASH_SCHEDULE_AUX_STREAM = 2 } dflash_schedule;
+int dflash_propose_block_schedule(const dflash_draft_config* cfg, int32_t n_req, int32_t dtype);
 int dflash_propose_block(const dflash_draft_config* cfg, const dflash_block_args* args,
                          dflash_stream_t stream);
 

@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_entry_point():
     names = _declared_functions()
-    assert "dflash_propose_block" in names and len(names) == 20
+    assert "dflash_propose_block" in names and len(names) == 21
     lib = D.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -175,6 +175,30 @@ def test_propose_block_validation():
     bad = _cfg(block_size=1)
     assert L.dflash_propose_block(ctypes.byref(bad), ctypes.byref(args), None) == -1
     assert L.dflash_propose_block_workspace_size(ctypes.byref(cfg), 32, 151936) > 0
+
+
+@pytest.mark.parametrize("kw,n_req,dtype,want", [
+    (dict(), 32, "bf16", D.SCHEDULE_ONE_LAUNCH),                   # 480 slot rows, blocks of 16, 4 taps
+    (dict(), 136, "bf16", D.SCHEDULE_ONE_LAUNCH),                  # 2040 slot rows: still one launch
+    (dict(), 137, "bf16", D.SCHEDULE_AUX_STREAM),                  # 2055 rows: the tiled projection
+    (dict(), 32, "f32", D.SCHEDULE_AUX_STREAM),                    # fp32 never shares the top-K's launch
+    (dict(block_size=10, hidden=5120, taps=5), 64, "bf16", D.SCHEDULE_AUX_STREAM),   # blocks of 10
+    (dict(taps=9), 32, "bf16", D.SCHEDULE_AUX_STREAM),             # more than 8 taps
+    (dict(taps=8, rank=128, top_k=32, hidden=7168), 1024, "bf16", D.SCHEDULE_AUX_STREAM),
+    (dict(rank=256), 32, "bf16", D.SCHEDULE_AUX_STREAM),           # rank above 128
+])
+def test_propose_block_schedule(kw, n_req, dtype, want):
+    # host-only decision: which branch dflash_propose_block takes
+    assert D.propose_block_schedule(_cfg(**kw), n_req, dtype) == want
+
+
+def test_propose_block_schedule_rejects_what_propose_rejects():
+    L = D.lib()
+    for cfg, n_req, dt in [(_cfg(taps=0, group_size=0), 32, 1), (_cfg(block_size=1), 32, 1), (_cfg(), 0, 1),
+                           (_cfg(), 32, 7), (_cfg(top_k=33), 32, 1)]:
+        assert L.dflash_propose_block_schedule(ctypes.byref(cfg), n_req, dt) == 0
+    with pytest.raises(D.DFlashError):
+        D.propose_block_schedule(_cfg(block_size=1), 32, "bf16")
 
 
 def test_lm_head_validation():

@@ -181,25 +181,38 @@ def test_end_to_end_against_oracle(name, reqs):
     print(f"[e2e] {name}: decisions inside the rounding band: {near}", flush=True)
 
 
-def test_auxiliary_stream_is_ordered_with_the_callers_stream():
-    """The conv and the projection run on the library's auxiliary stream: they
-    must see inputs written on the caller's stream just before the call, and
-    work the caller enqueues on that stream after it must see every output."""
+@pytest.mark.parametrize("name,n_req,schedule", [
+    ("bf16_b16_v151936", None, D.SCHEDULE_ONE_LAUNCH),
+    ("nonpow2_b10_v151936", None, D.SCHEDULE_AUX_STREAM),       # blocks of 10: fork/join
+    ("bf16_b16_v151936", 288, D.SCHEDULE_AUX_STREAM),           # 4320 slot rows: tiled projection, fork/join
+])
+def test_stream_ordering_on_either_schedule(name, n_req, schedule):
+    """Whichever schedule the call takes (asserted first), its kernels must
+    see inputs written on the caller's stream just before the call, and work
+    the caller enqueues on that stream after it must see every output: on the
+    fork/join schedule the conv and the projection run on the library's
+    auxiliary stream.  Outputs start poisoned (NaN, -1) so that a read before
+    the write that should precede it shows."""
     require_gpu()
-    w = W.WORKLOADS["bf16_b16_v151936"]
+    w = W.WORKLOADS[name]
+    if n_req is not None:
+        w = w.replace(n_req=n_req)
+    assert D.propose_block_schedule(_cfg(w), w.n_req, w.dtype) == schedule
     inp = W.make_inputs(w, device=DEV)
-    ref = _propose(w, inp)
+    say(f"stream ordering {name} n_req={w.n_req} schedule={schedule}: chain reference")
+    ref = _chain(w, inp)
     x_late = torch.zeros_like(inp["x"])
+    outs = {k: torch.full_like(v, -1 if v.dtype == torch.int64 else float("nan")) for k, v in ref.items()}
     busy = torch.empty(1 << 28, dtype=torch.uint8, device=DEV)
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
-    say("dflash_propose_block on a side stream after a late input write")
+    say(f"stream ordering {name}: dflash_propose_block on a side stream after a late input write")
     with torch.cuda.stream(side):
         for _ in range(4):
             busy.fill_(1)                 # keeps the side stream busy before the write
         x_late.copy_(inp["x"])
-        out = _propose(w, dict(inp, x=x_late))
-        got = {k: out[k].clone() for k in ("conv_out", "ids", "scores", "tokens", "q")}
+        out = _propose(w, dict(inp, x=x_late), outputs=outs)
+        got = {k: out[k].clone() for k in ref}
     torch.cuda.synchronize()
     for k, v in got.items():
         assert torch.equal(v, ref[k]), k
