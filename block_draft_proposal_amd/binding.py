@@ -333,7 +333,7 @@ def propose_block_workspace_size(cfg: DraftConfig, n_req: int, valid_vocab: int)
 
 
 SCHEDULE_ONE_LAUNCH = 1    # conv + projection inside the top-K's launch
-SCHEDULE_AUX_STREAM = 2    # conv + projection on the auxiliary stream beside the top-K
+SCHEDULE_AUX_STREAM = 2    # conv then projection on the auxiliary stream beside the top-K
 
 
 def propose_block_schedule(cfg: DraftConfig, n_req: int, dtype: str) -> int:

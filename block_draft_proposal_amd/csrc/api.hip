@@ -545,6 +545,19 @@ int dflash_propose_block_schedule(const dflash_draft_config* cfg, int32_t n_req,
 
 namespace {
 
+// Stages 0 and 2 on `st`: the conv, then the projection of the slot rows of
+// its output.
+int conv_and_proj(const dflash::ConvArgs& ca, const dflash::SelectArgs& sa, const dflash::ProjPlan& pp,
+                  void* const* ev, hipStream_t st, const char* who) {
+  int rc;
+  if ((rc = record(ev, 0, st)) != DFLASH_OK) return rc;
+  if ((rc = launch_status(dflash::launch_conv(ca, st), who)) != DFLASH_OK) return rc;
+  if ((rc = record(ev, 1, st)) != DFLASH_OK) return rc;
+  if ((rc = record(ev, 4, st)) != DFLASH_OK) return rc;
+  if ((rc = launch_status(dflash::launch_proj(sa, pp, st), who)) != DFLASH_OK) return rc;
+  return record(ev, 5, st);
+}
+
 // The draft block on `stream` with workspace [ws, ws + ws_bytes).  aux_ok:
 // the conv and the projection may run on the library's auxiliary stream
 // beside the top-K (created on first use); otherwise every stage runs on
@@ -605,12 +618,7 @@ int propose_impl(const dflash_draft_config* cfg, const dflash_block_args* a, dfl
     if ((st = record(ev, 5, s)) != DFLASH_OK) return st;
   } else if (!aux_ok) {
     // every stage on `stream`: conv, projection, then the top-K
-    if ((st = record(ev, 0, s)) != DFLASH_OK) return st;
-    if ((st = launch_status(dflash::launch_conv(ca, s), who)) != DFLASH_OK) return st;
-    if ((st = record(ev, 1, s)) != DFLASH_OK) return st;
-    if ((st = record(ev, 4, s)) != DFLASH_OK) return st;
-    if ((st = launch_status(dflash::launch_proj(sa, pp, s), who)) != DFLASH_OK) return st;
-    if ((st = record(ev, 5, s)) != DFLASH_OK) return st;
+    if ((st = conv_and_proj(ca, sa, pp, ev, s, who)) != DFLASH_OK) return st;
     if ((st = record(ev, 2, s)) != DFLASH_OK) return st;
     if ((st = launch_status(dflash::launch_topk(ta, L.topk, s), who)) != DFLASH_OK) return st;
     if ((st = record(ev, 3, s)) != DFLASH_OK) return st;
@@ -627,12 +635,7 @@ int propose_impl(const dflash_draft_config* cfg, const dflash_block_args* a, dfl
     // stages 0 and 2 on the auxiliary stream: conv, then the projection of
     // the slot rows of its output
     if ((st = stream_op(hipStreamWaitEvent(aux, fj->fork, 0), who)) != DFLASH_OK) return st;
-    if ((st = record(ev, 0, aux)) != DFLASH_OK) return st;
-    if ((st = launch_status(dflash::launch_conv(ca, aux), who)) != DFLASH_OK) return st;
-    if ((st = record(ev, 1, aux)) != DFLASH_OK) return st;
-    if ((st = record(ev, 4, aux)) != DFLASH_OK) return st;
-    if ((st = launch_status(dflash::launch_proj(sa, pp, aux), who)) != DFLASH_OK) return st;
-    if ((st = record(ev, 5, aux)) != DFLASH_OK) return st;
+    if ((st = conv_and_proj(ca, sa, pp, ev, aux, who)) != DFLASH_OK) return st;
     // join: `stream` waits for the auxiliary chain
     if ((st = stream_op(hipEventRecord(fj->join, aux), who)) != DFLASH_OK) return st;
     if ((st = stream_op(hipStreamWaitEvent(s, fj->join, 0), who)) != DFLASH_OK) return st;

@@ -14,6 +14,7 @@
 // token, so every load and store of a wave is one contiguous 1 KiB (bf16)
 // segment.
 #include "conv_core.h"
+#include "conv_walk.h"
 #include "dflash.h"
 #include "dflash_internal.h"
 
@@ -167,25 +168,10 @@ __global__ __launch_bounds__(kThreads) void conv_kernel_any_taps(const TIO* __re
 
 // ---------------------------------------------------------------------------
 // Block walk (taps <= 8, blocks of <= 16 tokens, each 16-byte vector inside
-// one group, whole groups per wave): a wave owns one block and 64 channel
-// vectors (512 bf16 / 256 fp32 channels).  Lane l walks the block's tokens in
-// order for its vector: every input row of the block is loaded once (no halo
-// re-reads), the static rows once per block, and the last TAPS inputs stay in
-// fp32 registers as the tap history.  The block's dynamic coefficients for
-// the wave's groups -- [token][tap][group] in memory -- are loaded as 16-byte
-// pieces by the whole wave and transposed through LDS to [token][group][tap],
-// so that each token's TAPS coefficients of a lane's group are one 16-byte
-// (bf16) or two (fp32) LDS reads.  Arithmetic: conv_core.h (shared with every
-// conv producer).
+// one group, whole groups per wave; conv_walk.h): each wave of a workgroup
+// is an independent unit, one block x one chunk of 64 channel vectors.
 // ---------------------------------------------------------------------------
-constexpr int kWalkMaxBlock = 16;
 constexpr int kWalkWaves = 4;                       // waves (independent units) per workgroup
-// Groups per wave slice: one 16-byte piece of coefficients per (token, tap)
-// (8 bf16 / 4 fp32 groups, i.e. 64-channel groups).
-template <typename TIO> constexpr int kPieceGroups = 16 / (int)sizeof(TIO);
-constexpr int kWalkMaxPieces = kWalkMaxBlock * 8 / 64;   // pieces per lane: tokens x taps / 64
-// LDS per wave: [token][group][8 tap slots]
-constexpr int kWalkLdsPerWave = kWalkMaxBlock * 16 * 8;   // bytes (bf16: 8 groups x 2 B; fp32: 4 x 4 B)
 
 struct WalkGeom {
   int64_t units;              // waves with work: blocks * slices
@@ -201,10 +187,10 @@ __global__ __launch_bounds__(kWalkWaves * 64) __attribute__((amdgpu_waves_per_eu
                                                                     TIO* __restrict__ out, WalkGeom g) {
   constexpr int VEC = Elem<TIO>::kVec;
   constexpr int E = (int)sizeof(TIO);
-  constexpr int PV = 16 / E;                        // elements per 16-byte piece
-  constexpr int TS = 8;                             // tap slots per (token, group) in LDS
   extern __shared__ __align__(16) unsigned char cw_smem[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index as a scalar: the unit's block, slice and row addresses
+  // are then computed once per wave in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   // the slices of one token block read the same coefficient lines: keep
   // them on one XCD
   const int64_t unit_raw = (int64_t)xcd_contiguous(blockIdx.x, gridDim.x) * kWalkWaves + wave;
@@ -218,82 +204,13 @@ __global__ __launch_bounds__(kWalkWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int c0 = v * VEC;
   const int gl = lane / g.vec_per_group;            // this lane's group within the slice
   TIO* s_d = reinterpret_cast<TIO*>(cw_smem) + (size_t)wave * (kWalkLdsPerWave / E);
-
-  // ---- every load of the block first: inputs, static rows, coefficients --
-  u32x4 xr[kWalkMaxBlock];
-#pragma unroll
-  for (int j = 0; j < kWalkMaxBlock; ++j)
-    if (j < B) xr[j] = ld16(x + (row0 + j) * H + c0);
-  u32x4 br[TAPS];
-#pragma unroll
-  for (int t = 0; t < TAPS; ++t) br[t] = ld16(base + (int64_t)t * H + c0);
-  // the block's coefficients for the slice's groups: one 16-byte piece per
-  // (token j, tap t), piece i = j * TAPS + t
-  const int64_t g0 = (int64_t)slice * kPieceGroups<TIO>;
-  const int n_pieces = B * TAPS;
-  u32x4 dr[kWalkMaxPieces];
-#pragma unroll
-  for (int p = 0; p < kWalkMaxPieces; ++p) {
-    const int i = min(p * 64 + lane, n_pieces - 1);
-    const int t = i % TAPS, j = i / TAPS;
-    if (p * 64 < n_pieces) dr[p] = ld16(delta + (row0 + j) * g.delta_row_stride + (int64_t)t * g.groups + g0);
-  }
-  // transpose to [token][group][tap slot] (slots past TAPS are never read)
-#pragma unroll
-  for (int p = 0; p < kWalkMaxPieces; ++p) {
-    const int i = p * 64 + lane;
-    if (i < n_pieces) {
-      const int t = i % TAPS, j = i / TAPS;
-      TIO* dst = s_d + (size_t)j * kPieceGroups<TIO> * TS + t;
-#pragma unroll
-      for (int k = 0; k < PV; ++k) {
-        if constexpr (E == 2) *reinterpret_cast<uint16_t*>(dst + k * TS) = (uint16_t)(dr[p][k >> 1] >> (16 * (k & 1)));
-        else *reinterpret_cast<uint32_t*>(dst + k * TS) = dr[p][k];
-      }
-    }
-  }
+  u32x4 xr[kWalkMaxBlock], br[TAPS];
+  walk_load<TIO, TAPS>(x, base, delta, g.delta_row_stride, H, g.groups, B, row0, c0,
+                       (int64_t)slice * kPieceGroups<TIO>, s_d, xr, br);
   __syncthreads();
-
-  float bt[TAPS][VEC];
-#pragma unroll
-  for (int t = 0; t < TAPS; ++t) unpack16(br[t], bt[t]);
-  float hist[TAPS][VEC];                            // hist[t] = input row j - t
-#pragma unroll
-  for (int j = 0; j < kWalkMaxBlock; ++j) {
-    // a constant trip count (guarded) keeps the loop unrolled, so xr and
-    // hist stay in registers
-    if (j < B) {
-      // a compiler-only barrier: each token's LDS reads stay in its own
-      // iteration (hoisting all of them ahead of the loop spills registers)
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int t = TAPS - 1; t > 0; --t)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) hist[t][e] = hist[t - 1][e];
-      unpack16(xr[j], hist[0]);
-      // this token's coefficients of the lane's group, tap slots 0..TS-1
-      const TIO* dj = s_d + ((size_t)j * kPieceGroups<TIO> + gl) * TS;
-      float d[TS];
-      if constexpr (E == 2) {
-        unpack16(ld16(dj), d);
-      } else {
-        float lo[4], hi[4];
-        unpack16(ld16(dj), lo);
-        unpack16(ld16(dj + 4), hi);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) { d[k] = lo[k]; d[4 + k] = hi[k]; }
-      }
-      float acc[VEC];
-      conv_token<VEC, TAPS>(
-          j, [&](int t, float (&coef)[VEC]) { coef_one_group<VEC>(bt[t], d[t], coef); },
-          [&](int t, float (&xv)[VEC]) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) xv[e] = hist[t][e];
-          },
-          acc);
-      if (active) store_vec(out + (row0 + j) * H + c0, acc);
-    }
-  }
+  walk_tokens<TIO, TAPS>(xr, br, s_d, B, gl, [&](int j, float (&acc)[VEC]) {
+    if (active) store_vec(out + (row0 + j) * H + c0, acc);
+  });
 }
 
 // The block walk's plan, or units == 0 when it does not apply: <= 8 taps,

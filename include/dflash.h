@@ -354,11 +354,11 @@ size_t dflash_propose_block_workspace_size(const dflash_draft_config* cfg, int32
  *   DFLASH_SCHEDULE_ONE_LAUNCH: conv and projection are workgroups of the
  *     top-K's launch on `stream`;
  *   DFLASH_SCHEDULE_AUX_STREAM: conv then projection on the auxiliary stream,
- *     beside the top-K on `stream` (dflash_propose_block_noalloc runs them on
- *     `stream` before the top-K instead).
- * Returns 0 for a config or size dflash_propose_block would reject on shape
- * alone (invalid config, conv or selector disabled, block_size < 2, n_req < 1,
- * unknown dtype). */
+ *     beside the top-K on `stream`.
+ * dflash_propose_block_noalloc runs the auxiliary-stream work on `stream`
+ * before the top-K instead.  Returns 0 for a config or size
+ * dflash_propose_block would reject on shape alone (invalid config, conv or
+ * selector disabled, block_size < 2, n_req < 1, unknown dtype). */
 typedef enum { DFLASH_SCHEDULE_ONE_LAUNCH = 1, DFLASH_SCHEDULE_AUX_STREAM = 2 } dflash_schedule;
 int dflash_propose_block_schedule(const dflash_draft_config* cfg, int32_t n_req, int32_t dtype);
 int dflash_propose_block(const dflash_draft_config* cfg, const dflash_block_args* args,

@@ -180,9 +180,10 @@ def test_propose_block_validation():
 @pytest.mark.parametrize("kw,n_req,dtype,want", [
     (dict(), 32, "bf16", D.SCHEDULE_ONE_LAUNCH),                   # 480 slot rows, blocks of 16, 4 taps
     (dict(), 136, "bf16", D.SCHEDULE_ONE_LAUNCH),                  # 2040 slot rows: still one launch
-    (dict(), 137, "bf16", D.SCHEDULE_AUX_STREAM),                  # 2055 rows: the tiled projection
+    (dict(), 137, "bf16", D.SCHEDULE_AUX_STREAM),               # 2055 rows: the tiled projection
     (dict(), 32, "f32", D.SCHEDULE_AUX_STREAM),                    # fp32 never shares the top-K's launch
-    (dict(block_size=10, hidden=5120, taps=5), 64, "bf16", D.SCHEDULE_AUX_STREAM),   # blocks of 10
+    (dict(block_size=10, hidden=5120, taps=5), 64, "bf16", D.SCHEDULE_AUX_STREAM),   # blocks of 10, 576 rows
+    (dict(block_size=10, hidden=5120, taps=5), 240, "bf16", D.SCHEDULE_AUX_STREAM),   # 2160 rows
     (dict(taps=9), 32, "bf16", D.SCHEDULE_AUX_STREAM),             # more than 8 taps
     (dict(taps=8, rank=128, top_k=32, hidden=7168), 1024, "bf16", D.SCHEDULE_AUX_STREAM),
     (dict(rank=256), 32, "bf16", D.SCHEDULE_AUX_STREAM),           # rank above 128

@@ -184,7 +184,8 @@ def test_end_to_end_against_oracle(name, reqs):
 @pytest.mark.parametrize("name,n_req,schedule", [
     ("bf16_b16_v151936", None, D.SCHEDULE_ONE_LAUNCH),
     ("nonpow2_b10_v151936", None, D.SCHEDULE_AUX_STREAM),       # blocks of 10: fork/join
-    ("bf16_b16_v151936", 288, D.SCHEDULE_AUX_STREAM),           # 4320 slot rows: tiled projection, fork/join
+    ("bf16_b16_v151936", 288, D.SCHEDULE_AUX_STREAM),        # 4320 slot rows: the tiled projection
+    ("nonpow2_b10_v151936", 240, D.SCHEDULE_AUX_STREAM),     # blocks of 10, 2160 slot rows
 ])
 def test_stream_ordering_on_either_schedule(name, n_req, schedule):
     """Whichever schedule the call takes (asserted first), its kernels must
