@@ -446,24 +446,30 @@ __device__ __forceinline__ void topk_rows_body(int block, const TIO* __restrict_
   // After the survivors of one chunk are in the pool: exact narrowing if they
   // overflowed, then merge them into the held list, 64 at a time (one per
   // lane).  Ranks: a held entry's is its index plus the new ones above it; a
-  // new one's is the held ones above it plus the new ones above it (counted
-  // with readlane over the lanes, no LDS reads); composites are unique, so
-  // ranks are distinct.  The K best are reordered through LDS.  A chunk
-  // without survivors costs nothing here.
+  // new one's is the held ones above it plus the new ones above it.  Per new
+  // candidate j (read with readlane): the held lanes it beats come from one
+  // compare, whose ballot also gives, by complement over the held lanes, the
+  // count of held entries above it (composites are unique) -- no pass over
+  // the held list.  Ranks are distinct.  The K best are reordered through
+  // LDS.  A chunk without survivors costs nothing here.
   auto update = [&](int64_t lb, int64_t c_start) {
     if (n_new == 0) return;
     if (n_new > kWaveCap) n_new = (int)narrow_exact<TIO>(rowp, lb, c_start, valid_vocab, lane, K, 0, wl);
     wave_sync();
     for (int b0 = 0; b0 < n_new; b0 += 64) {
       const int m = min(64, n_new - b0);
+      const uint64_t held = (1ull << nbest) - 1ull;   // lanes holding an entry (nbest <= K <= 32)
       const uint64_t cv = lane < m ? wl.pool[b0 + lane] : 0ull;
-      int rank_h = lane, rank_c = 0;
+      int rank_h = lane, rank_c = 0, above_c = 0;
       for (int j = 0; j < m; ++j) {
         const uint64_t cj = readlane64(cv, j);
-        rank_h += cj > hv ? 1 : 0;
+        const bool beats = cj > hv;
+        rank_h += beats ? 1 : 0;
         rank_c += cj > cv ? 1 : 0;
+        const int above = (int)__popcll(held & ~__ballot(beats));
+        if (lane == j) above_c = above;
       }
-      for (int j = 0; j < nbest; ++j) rank_c += readlane64(hv, j) > cv ? 1 : 0;
+      rank_c += above_c;
       if (lane < nbest && rank_h < K) wl.tmp[rank_h] = hv;
       if (lane < m && rank_c < K) wl.tmp[rank_c] = cv;
       wave_sync();
