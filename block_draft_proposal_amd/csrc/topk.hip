@@ -302,10 +302,16 @@ struct WaveLds {
 
 struct Shared {
   WaveLds wave[kWaves];
-  // Largest K-th held key of any wave of the workgroup: K values of the row
-  // reach it, so every wave may drop values below it (not ties: another
-  // wave's values can have smaller ids).
+  // Keys below which every wave may drop values (not ties: another wave's
+  // values can have smaller ids), each valid because at least K values of
+  // the row reach it:
+  //  * bound: the largest K-th held key of any wave;
+  //  * qkey[w]: wave w's ceil(K/4)-th held key (0 until it holds that many);
+  //    the smallest of the four is reached by 4 ceil(K/4) >= K values, and
+  //    sits near the K-th best of the values seen so far (the largest K-th
+  //    key only near the 4K-th).
   uint32_t bound;
+  uint32_t qkey[kWaves];
 };
 
 template <int VEC>
@@ -414,12 +420,17 @@ __device__ __forceinline__ void topk_rows_body(int block, const TIO* __restrict_
   uint32_t kth_key = 0;                          // key of the K-th held one once nbest == K
   int n_new = 0;                                 // this chunk's survivors in wl.pool[0, n_new) (wave-uniform)
   if (threadIdx.x == 0) sh.bound = 0;
+  if (threadIdx.x < kWaves) sh.qkey[threadIdx.x] = 0;
   __syncthreads();
   // The workgroup's shared bound (a key; 0 = none yet), read without ordering:
   // any value another wave has published is valid.
   auto shared_bound = [&]() -> uint32_t {
-    return __builtin_amdgcn_readfirstlane(__hip_atomic_load(&sh.bound, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_WORKGROUP));
+    uint32_t q = __hip_atomic_load(&sh.qkey[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+      q = min(q, __hip_atomic_load(&sh.qkey[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    const uint32_t b = __hip_atomic_load(&sh.bound, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readfirstlane(max(b, q));
   };
   // (readlane returns a signed int: widen each half through uint32_t)
   auto readlane64 = [](uint64_t v, int j) -> uint64_t {
@@ -478,6 +489,11 @@ __device__ __forceinline__ void topk_rows_body(int block, const TIO* __restrict_
       wave_sync();
     }
     n_new = 0;
+    const int q = (K + 3) / 4;
+    if (nbest >= q) {
+      const uint32_t qk = composite_key(readlane64(hv, q - 1));
+      if (lane == 0) __hip_atomic_store(&sh.qkey[wave], qk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     if (nbest == K) {
       kth_key = composite_key(readlane64(hv, K - 1));
       if (lane == 0) atomicMax(&sh.bound, kth_key);
