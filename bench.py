@@ -64,16 +64,6 @@ TOPK_SOURCES = tuple(os.path.join(ROOT, "block_draft_proposal_amd", "csrc", f)
                      for f in ("topk.hip", "device_common.h", "conv_slot_proj.h", "conv_core.h", "gemm_tile.h"))
 
 
-def single_launch_stage1(w) -> bool:
-    """Whether dflash_propose_block runs the conv and the slot projection as
-    workgroups of the top-K's launch (bf16, blocks of 16 tokens, <= 8 taps,
-    one group per 16-byte vector, rank <= 128, fewer than 2048 slot rows --
-    beyond that the projection runs as its own tiled kernel); otherwise they
-    run beside it on a second stream."""
-    return (w.dtype == "bf16" and w.block_size == 16 and 1 <= w.taps <= 8 and w.group_size % 8 == 0
-            and w.rank <= 128 and w.n_slot_rows < 2048)
-
-
 def sources_sha256(paths) -> str:
     import hashlib
     h = hashlib.sha256()
@@ -519,7 +509,8 @@ def main():
     avg_ms = [sum(x[k] for x in stage_ms) / n_stage for k in range(4)]
     avg_ms[1] = topk_ms
     nbytes = algorithmic_bytes(w)
-    fused = single_launch_stage1(w)
+    # the schedule the library takes for this batch (host-only query)
+    fused = D.propose_block_schedule(cfg, w.n_req, w.dtype) == D.SCHEDULE_ONE_LAUNCH
     # the dominant kernel: the first stage (top-K, plus conv and slot
     # projection when they share its launch: x, base, delta and P read,
     # conv_out and u written)

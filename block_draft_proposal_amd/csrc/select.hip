@@ -10,20 +10,28 @@
 //   uniform and emit the softmax q they drew from.
 //
 // Kernels
-//  * proj_mfma_kernel: u = P h for every slot row, the one dense contraction
-//    on the path, on the matrix cores (v_mfma_f32_16x16x32_bf16; bf16 x bf16
-//    products are exact in fp32).  A workgroup owns 64 slot rows x all rank
-//    columns and one slice of the hidden axis; slices are summed later in a
-//    fixed order, so the result is deterministic.  proj_f32_kernel is the
-//    fp32-storage path (VALU fma chain).
-//  * lattice_kernel: one workgroup per (request, slot); stages w = A[p] * u
-//    and B[c] in LDS as fp32 and evaluates the K x K block as fp32 fma chains
-//    in fixed k order (never bf16: rounding A * u to bf16 would blur
-//    near-ties).
-//  * walk_kernel: one workgroup per request; the request's S x K x K scores
-//    are staged in LDS with coalesced loads, then one wave walks the slots
-//    (lane j = candidate j) with wave reductions; the serial chain only
-//    touches LDS.
+//  * Projection u = P h for every slot row, the one dense contraction on the
+//    path, on the matrix cores (v_mfma_f32_16x16x32_bf16; bf16 x bf16
+//    products are exact in fp32), split over slices of the hidden axis whose
+//    partials the consumer adds in a fixed order (deterministic):
+//    proj_mfma_kernel (few rows: a wave owns 16 rows x all rank columns of one
+//    slice) and proj_tile_kernel (2048 slot rows or more: LDS-staged 128 x 128
+//    tiles of the shared tile product, gemm_tile.h).  Each output is the same
+//    MFMA chain over its slice's 32-wide k steps whatever the grouping, so the
+//    two agree with the propose step's fused projection bit for bit.
+//    proj_f32_kernel is the fp32-storage path (VALU fma chain).
+//  * The lattice block of one slot on one wave's matrix cores (tile_mfma):
+//    w = A[p] (.) u in fp32, then against B[c] -- fp32 tables by fp32 MFMA
+//    steps, bf16 tables by two bf16 MFMA steps per 8 k values (w split into a
+//    bf16 hi and lo part), every term within 2^-18 of A u B.  Kernels:
+//    lattice_mfma_kernel (standalone: one wave per slot row),
+//    lattice_walk_kernel (one workgroup per request, the lattice in LDS, then
+//    every row decided in parallel and the path found by pointer jumping),
+//    lattice_walk_wave_kernel (one wave per request for large batches: only
+//    the walked rows are decided, slot by slot, pipelined).
+//  * walk_kernel / walk_lds_kernel: the standalone walk over given scores.
+// Every lattice and walk evaluation runs the same arithmetic, so the fused
+// kernels equal dflash_lattice followed by dflash_walk bit for bit.
 #include "dflash.h"
 #include "dflash_internal.h"
 #include "conv_core.h"
