@@ -169,6 +169,7 @@ def call_bytes(w):
     verify = R * (w.slots + 1) * V * e + 12 * Ns * K + 12 * Ns + 4 * R + 9 * R + 4 * R + 8 * R * (w.slots + 1)
     return {"dflash_conv": conv, "dflash_conv_prepare": prepare, "dflash_topk": topk, "dflash_lattice": lattice,
             "dflash_walk": walk, "dflash_verify": verify, "dflash_propose_block": propose,
+            "ProposeGraph.step_eager": propose + 4 * Ns + 5 * R + 16,
             "ProposeGraph.replay": propose + 4 * Ns + 5 * R + 16}
 
 
@@ -263,6 +264,7 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
                                                      valid_vocab=w.valid_vocab, accepted_out=v_acc,
                                                      committed_out=v_com, workspace=v_ws),
             "dflash_propose_block": lambda: call(stream),
+            "ProposeGraph.step_eager": lambda: graph.step_eager(g_temps, g_mask, 1234, 0),
             "ProposeGraph.replay": lambda: graph.replay(g_temps, g_mask, 1234, 0),
         }
         nbytes = call_bytes(w)

@@ -519,11 +519,8 @@ class ProposeGraph:
             raise DFlashError(st, last_error())
         self.call(stream_handle)
 
-    def replay(self, temperatures, greedy_mask, seed: int, offset: int) -> Dict[str, torch.Tensor]:
-        """Stage the sampling parameters and {seed, offset} (host values), then
-        replay on torch's current stream.  Returns the outputs dict."""
+    def _stage(self, temperatures, greedy_mask, seed: int, offset: int, stream) -> None:
         hip = _hip()
-        stream = torch.cuda.current_stream().cuda_stream
         if hip.hipEventSynchronize(self._staged) != 0:     # the previous staging copy has read the pinned buffer
             raise RuntimeError("hipEventSynchronize failed")
         self._h_temp[:] = np.asarray(temperatures, dtype=np.float32)
@@ -533,7 +530,21 @@ class ProposeGraph:
         dst, src, nbytes = self._stage_args
         if hip.hipMemcpyAsync(dst, src, nbytes, 1, stream) != 0 or hip.hipEventRecord(self._staged, stream) != 0:
             raise RuntimeError("staging copy failed")
+
+    def replay(self, temperatures, greedy_mask, seed: int, offset: int) -> Dict[str, torch.Tensor]:
+        """Stage the sampling parameters and {seed, offset} (host values), then
+        replay on torch's current stream.  Returns the outputs dict."""
+        self._stage(temperatures, greedy_mask, seed, offset, torch.cuda.current_stream().cuda_stream)
         self.graph.replay()
+        return self.call.outputs
+
+    def step_eager(self, temperatures, greedy_mask, seed: int, offset: int) -> Dict[str, torch.Tensor]:
+        """The same step without the graph: the same staging copy, then the
+        uniforms and the propose call launched one by one on torch's current
+        stream (the like-for-like comparison for replay)."""
+        stream = torch.cuda.current_stream().cuda_stream
+        self._stage(temperatures, greedy_mask, seed, offset, stream)
+        self._step(stream)
         return self.call.outputs
 
 

@@ -79,6 +79,12 @@ def test_graph_replays_equal_eager_steps(name):
         seen.append((seed, offset, temps, mask, out["tokens"].clone()))
     # the first counter again: the same draw
     seed, offset, temps, mask, tokens = seen[0]
-    again = g.replay(temps, mask, seed, offset)
+    again = {k: v.clone() for k, v in g.replay(temps, mask, seed, offset).items()}
     torch.cuda.synchronize()
     assert torch.equal(again["tokens"], tokens)
+    # the same step launched without the graph (the sweep's like-for-like row)
+    say(f"ProposeGraph {name}: step_eager")
+    eager_step = g.step_eager(temps, mask, seed, offset)
+    torch.cuda.synchronize()
+    for k in ("conv_out", "ids", "unary", "tokens", "q"):
+        assert torch.equal(eager_step[k], again[k]), (name, "step_eager", k)
