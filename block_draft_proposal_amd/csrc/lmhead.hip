@@ -17,13 +17,14 @@
 // written through LDS as 16-byte row pieces.
 //
 // Fused head + top-K (compute_candidates without the logits reaching HBM):
-// each workgroup computes one column tile of its row block (a few when a
-// row's lists would not fit the merge) with the same tile product; the
-// rounded tile is staged in LDS and two threads per row fold its values into
-// small sorted lists, skipping values below a per-row bound on the K-th best
-// key that finished tiles publish.  The row's lists are merged after every
-// tile into the K best composites (value descending, id ascending) of the
-// column group, and a second kernel merges the groups of each row.  Both
+// each workgroup computes a group of consecutive column tiles of its row
+// block with the same tile product; each rounded tile is staged in LDS and
+// two threads per row fold its values into small sorted lists, skipping
+// values below the row's group list (kept in LDS across the group's tiles)
+// and below a per-row bound on the K-th best key that finished tiles
+// publish.  After its last tile a group stores its K best composites (value
+// descending, id ascending), and a second kernel merges the groups of each
+// row.  Both
 // paths rank the same bf16 logits, so the fused result equals the head
 // followed by the streaming top-K bit for bit.
 #include "dflash.h"
@@ -102,32 +103,49 @@ __device__ __forceinline__ void list_insert(uint32_t (&best)[KB], uint32_t c) {
   }
 }
 
-// Within one tile a value's order is carried by a 32-bit key: its 16-bit
-// value key above 255 - (column within the tile), so larger is better and
-// equal values rank by column; 0 marks an empty slot.
-static_assert(kBN <= 256, "tile columns fit the 8-bit column field");
-__device__ __forceinline__ uint32_t tile_key(uint32_t key, int col_in_tile) {
-  return (key << 8) | (uint32_t)(255 - col_in_tile);
+// Within a group of column tiles a value's order is carried by a 32-bit key:
+// its 16-bit value key above 65535 - (column within the group), so larger is
+// better and equal values rank by column; 0 marks an empty slot.  A group
+// spans at most 65536 columns.
+constexpr int kMaxGroupCols = 65536;
+__device__ __forceinline__ uint32_t group_key(uint32_t key, int col_in_group) {
+  return (key << 16) | (uint32_t)(0xFFFF - col_in_group);
 }
-__device__ __forceinline__ uint64_t tile_key_composite(uint32_t tk, int n0) {
-  return composite(tk >> 8, n0 + 255 - (int)(tk & 255u));
+__device__ __forceinline__ uint64_t group_key_composite(uint32_t gk, int g0) {
+  return composite(gk >> 16, g0 + 0xFFFF - (int)(gk & 0xFFFFu));
 }
 
 constexpr int kRowThreads = kLmThreads / kBM;   // scan threads per tile row
 constexpr int kScanCols = kOutCols / kRowThreads;   // columns each of them folds in per output pass
 static_assert(kLmThreads % kBM == 0 && kScanCols % 8 == 0, "scan threads split the rows evenly");
 static_assert(sizeof(uint32_t) * kBM * (kRowThreads - 1) * 32 <= kLmSmem, "list exchange fits the ring");
+// the group lists ([kBM][KB] keys) sit in LDS past the tile ring
+template <int KB> constexpr size_t lm_topk_smem() { return kLmSmem + sizeof(uint32_t) * kBM * KB; }
+static_assert(lm_topk_smem<32>() <= 160 * 1024, "ring + group lists fit a workgroup's LDS");
+// Each scan thread's pending candidates: kCandCap keys in the ring past the
+// staged output pass (which the scan reads), inserted into its list when the
+// buffer fills and at the end of each pass.
+constexpr int kCandCap = 16;
+constexpr size_t kCandOff = sizeof(uint16_t) * kBM * kCPad;
+static_assert(kCandOff % 16 == 0 && kCandOff + sizeof(uint32_t) * kLmThreads * kCandCap <= kLmSmem,
+              "candidate buffers fit the ring beside the staged pass");
 
+// A workgroup walks a group of consecutive column tiles of its row block.
 // kRowThreads threads per row: thread t takes row t / kRowThreads and, of
 // every output pass of a tile, the kScanCols columns from p kScanCols on,
-// p = t % kRowThreads, folding them into a sorted list of its own.  After
-// the tile the lists of a row meet in LDS and the row's p = 0 thread merges
-// them, with the group's list so far (from the workspace, for the second
-// tile of a group on), and stores the group's list.  No list is live across
-// a tile product.
+// p = t % kRowThreads, folding them into a sorted list of its own -- the p = 0
+// thread starting from the row's group list (in LDS), the others empty; a
+// value enters only above the group list's K-th entry.  A value that passes
+// is first appended to the thread's candidate buffer (one store), and the
+// buffer is inserted into the list when it fills or the pass ends: inserting
+// on the spot would run the K-step insertion for every lane of the wave
+// whenever any one lane had a value to insert.  After the tile the
+// lists of a row meet in LDS and the p = 0 thread merges them and stores the
+// group list back.  No list is live across a tile product.  After the
+// group's last tile its K best go to the workspace as composites.
 //
 // bound[r] is a lower bound on the key of row r's K-th best value: once a
-// merged list holds K values the bound is raised (atomic max) to the key of
+// group list holds K values the bound is raised (atomic max) to the key of
 // its K-th, since K values of the row have at least that key.  Values with a
 // smaller key cannot place and are skipped before any list work; the bound
 // only grows, so a stale read filters less but never wrongly.
@@ -145,9 +163,16 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_topk_kernel(
   const bool row_ok = m0 + row < M;
   const int nb0 = grp * tiles_per_group, nb1 = min(n_nb, nb0 + tiles_per_group);
   uint16_t* cs = reinterpret_cast<uint16_t*>(lm_smem);
-  uint64_t* dst = parts + ((int64_t)(m0 + row) * n_grp + grp) * K;
+  uint32_t* glist = reinterpret_cast<uint32_t*>(lm_smem + kLmSmem) + row * KB;   // the row's group list
+  // KB - K sentinels (above every entry) ahead of the K real slots, so the
+  // K-th entry is always the last slot; visible after the tile product's
+  // first barrier
+  if (part == 0) {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) glist[i] = (i < KB - K) ? ~0u : 0u;
+  }
   for (int nb = nb0; nb < nb1; ++nb) {
-    const int n0 = nb * kBN;
+    const int n0 = nb * kBN, cg0 = (nb - nb0) * kBN;   // the tile's first column, in the row and in the group
     uint32_t pk[kFragM][kFragN][2];
     {
       f32x4_t acc[kFragM][kFragN];
@@ -157,15 +182,31 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_topk_kernel(
     }
     uint32_t lo = 0;
     if (row_ok) lo = __hip_atomic_load(bound + m0 + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t gk = glist[KB - 1];           // the group list's K-th (0 until it holds K)
     uint32_t tl[KB];
 #pragma unroll
-    for (int i = 0; i < KB; ++i) tl[i] = (i < KB - K) ? ~0u : 0u;
+    for (int i = 0; i < KB; ++i) tl[i] = part == 0 ? glist[i] : ((i < KB - K) ? ~0u : 0u);
     for (int pass = 0; pass < kOutPasses; ++pass) {
       tile_to_lds<LmCfg>(pk, cs, pass);
       __syncthreads();
       const int t_lo = pass * kOutCols + kScanCols * part;   // first column within the tile
       if (row_ok && n0 + t_lo < valid) {
         const uint16_t* rowp = cs + row * kCPad + kScanCols * part;
+        uint32_t* cand = reinterpret_cast<uint32_t*>(lm_smem + kCandOff) + tid * kCandCap;
+        int n_cand = 0;
+        // a value is appended when its full key (value, then column) beats
+        // the thread's list and the group list: stale between flushes, so
+        // it lets more through, never fewer; bf16 values tie often, so the
+        // column takes part in the test
+        uint32_t thr = max(tl[KB - 1], gk);
+        auto flush = [&]() {
+          for (int i = 0; i < n_cand; ++i) {
+            const uint32_t c = cand[i];
+            if (c > tl[KB - 1]) list_insert(tl, c);
+          }
+          n_cand = 0;
+          thr = max(tl[KB - 1], gk);
+        };
 #pragma unroll 2
         for (int c8 = 0; c8 < kScanCols; c8 += 8) {
           if (n0 + t_lo + c8 >= valid) break;
@@ -174,18 +215,18 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_topk_kernel(
           for (int e = 0; e < 8; ++e) {
             const int tc = t_lo + c8 + e;
             const uint32_t key = bf16_key((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu));
-            if (key >= lo && n0 + tc < valid) {
-              const uint32_t c = tile_key(key, tc);
-              if (c > tl[KB - 1]) list_insert(tl, c);
-            }
+            const uint32_t c = group_key(key, cg0 + tc);
+            if (key >= lo && n0 + tc < valid && c > thr) cand[n_cand++] = c;
           }
+          if (n_cand > kCandCap - 8) flush();       // room for the next 8 values
         }
+        flush();
       }
       __syncthreads();                         // the pass's LDS is reused next
     }
     // row merge: the other threads' lists to LDS, the p = 0 thread folds them
-    // in, widens its list to composites and adds the group's earlier tiles
-    uint32_t* xch = reinterpret_cast<uint32_t*>(lm_smem);   // [kBM][kRowThreads - 1][KB]
+    // into its list (the group list and this thread's values) and stores it
+    uint32_t* xch = reinterpret_cast<uint32_t*>(lm_smem);   // [kBM][kRowThreads - 1][KB], in the ring
     if (part > 0) {
 #pragma unroll
       for (int i = 0; i < KB; ++i) xch[(row * (kRowThreads - 1) + part - 1) * KB + i] = tl[i];
@@ -199,30 +240,19 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_topk_kernel(
           if (c != ~0u && c > tl[KB - 1]) list_insert(tl, c);
         }
       }
-      uint64_t kth;                            // the group list's K-th entry
-      if (nb == nb0) {
 #pragma unroll
-        for (int i = 0; i < KB; ++i)
-          if (i >= KB - K) dst[i - (KB - K)] = tl[i] == 0u ? 0ull : tile_key_composite(tl[i], n0);
-        kth = tl[KB - 1] == 0u ? 0ull : tile_key_composite(tl[KB - 1], n0);
-      } else {                                 // with the group's earlier tiles (stored by this thread)
-        uint64_t best[KB];
-#pragma unroll
-        for (int i = 0; i < KB; ++i)
-          best[i] = (i < KB - K) ? ~0ull : (tl[i] == 0u ? 0ull : tile_key_composite(tl[i], n0));
-        for (int i = K - 1; i >= 0; --i) {
-          const uint64_t c = dst[i];
-          if (c > best[KB - 1]) list_insert(best, c);
-        }
-#pragma unroll
-        for (int i = 0; i < KB; ++i)
-          if (i >= KB - K) dst[i - (KB - K)] = best[i];
-        kth = best[KB - 1];
-      }
-      if (kth != 0 && composite_key(kth) > lo)
-        __hip_atomic_fetch_max(bound + m0 + row, composite_key(kth), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < KB; ++i) glist[i] = tl[i];
+      if (tl[KB - 1] != 0u && (tl[KB - 1] >> 16) > lo)
+        __hip_atomic_fetch_max(bound + m0 + row, tl[KB - 1] >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();                           // xch lies in the ring the next tile refills
+  }
+  if (part == 0 && row_ok) {
+    uint64_t* dst = parts + ((int64_t)(m0 + row) * n_grp + grp) * K;
+    for (int i = KB - K; i < KB; ++i) {
+      const uint32_t c = glist[i];
+      dst[i - (KB - K)] = c == 0u ? 0ull : group_key_composite(c, nb0 * kBN);
+    }
   }
 }
 
@@ -290,10 +320,17 @@ LmTopkPlan plan_lm_head_topk(int64_t n_rows, int64_t vocab, int32_t top_k) {
   LmTopkPlan p{};
   p.n_mb = (int32_t)((n_rows + kBM - 1) / kBM);
   p.n_nb = (int32_t)((vocab + kBN - 1) / kBN);
-  // one tile per workgroup unless a row's merge candidates could overflow
-  // (K threads of the merge, ceil(n_grp / 256) lists of K each)
+  // groups of column tiles per workgroup: about 4096 workgroups (16 per CU,
+  // one resident at a time), so that a group's later tiles are filtered by
+  // its own list and the per-row bound; at least enough tiles that a row's
+  // merge candidates fit (K threads of the merge, ceil(n_grp / 256) lists of
+  // K each); a group spans at most 65536 columns
   int t = 1;
   while ((int64_t)top_k * top_k * (((p.n_nb + t - 1) / t + 255) / 256) > kLmMergeCand) ++t;
+  const int64_t tiles = (int64_t)p.n_mb * p.n_nb;
+  const int t_par = (int)(tiles / 4096);
+  if (t_par > t) t = t_par;
+  if (t > kMaxGroupCols / kBN) t = kMaxGroupCols / kBN;
   p.tiles_per_group = t;
   p.n_grp = (p.n_nb + t - 1) / t;
   const size_t lists = (size_t)n_rows * p.n_grp * top_k * sizeof(uint64_t);
@@ -313,7 +350,7 @@ hipError_t launch_lm_head_topk(const LmHeadArgs& a, const LmTopkPlan& p, int64_t
   const int64_t slots = (int64_t)((p.n_grp + 7) / 8) * p.n_mb;
   const dim3 grid((unsigned)(slots * 8));
 #define DFLASH_LMTK(KB)                                                                                    \
-  hipLaunchKernelGGL((lm_head_topk_kernel<KB>), grid, dim3(kLmThreads), kLmSmem, stream,                \
+  hipLaunchKernelGGL((lm_head_topk_kernel<KB>), grid, dim3(kLmThreads), lm_topk_smem<KB>(), stream,     \
                      static_cast<const uint16_t*>(a.hidden), a.hidden_row_stride,                          \
                      static_cast<const uint16_t*>(a.weight), (int32_t)a.n_rows, a.hidden_size,             \
                      (int32_t)a.vocab, (int32_t)valid_vocab, top_k, p.n_mb, p.n_nb, p.tiles_per_group,     \

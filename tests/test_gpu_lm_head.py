@@ -120,6 +120,27 @@ def test_fused_head_topk_equals_head_then_topk(M, H, V, valid, K, m, cap):
     np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
 
 
+@pytest.mark.parametrize("M,H,V,valid,K", [
+    (4096, 128, 131144, 131000, 32),      # 16 x 513 tiles: groups of 2 tiles, a last group of one
+    (4000, 64, 262144, 262144, 8),        # 16 x 1024 tiles: groups of 4, ragged last row block
+])
+def test_fused_head_topk_multi_tile_groups_equal_chain(M, H, V, valid, K):
+    # batches with many tiles walk groups of column tiles per workgroup, the
+    # group's list carried in LDS from tile to tile
+    require_gpu()
+    w = W.WORKLOADS["bf16_b16_v151936"].replace(hidden=H, vocab=V, valid_vocab=valid, n_req=1)
+    hid, wt = _head(w, rows=M, seed=M + V)
+    say(f"dflash_lm_head_topk groups M={M} H={H} V={V} valid={valid} K={K}")
+    ids, unary = D.dflash_lm_head_topk(hid, wt, top_k=K, valid_vocab=valid, multiplier=1.0, softcap=30.0)
+    logits = D.dflash_lm_head(hid, wt)
+    ids2, unary2 = D.dflash_topk(logits, top_k=K, valid_vocab=valid, multiplier=1.0, softcap=30.0)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(unary, unary2)
+    rows = sample_indices(M, 24, seed=5)
+    ref_ids, _ = O.topk(f64(logits[torch.from_numpy(rows).to(DEV)]), valid, K, 1.0, 30.0)
+    np.testing.assert_array_equal(ids[torch.from_numpy(rows).to(DEV)].cpu().numpy(), ref_ids)
+
+
 def test_fused_head_topk_ties_go_to_the_lower_id():
     # identical head rows give equal logits in every row: the lower id first
     require_gpu()
