@@ -46,6 +46,9 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 constexpr int64_t kMaxVocab = (int64_t)1 << 24;
+// the dense head addresses a 256-row tile of either operand with 32-bit byte
+// offsets: row strides (the weight's is hidden_size) stay below 2^22 elements
+constexpr int64_t kMaxHeadStride = (int64_t)1 << 22;
 
 // ---------------------------------------------------------------------------
 int check_conv(const void* x, const void* base, const void* delta, int64_t delta_row_stride,
@@ -462,6 +465,8 @@ int dflash_lm_head(const void* hidden, int64_t hidden_row_stride, const void* we
     return fail(DFLASH_ERR_INVALID_ARG, "%s: row strides shorter than the rows", who);
   if (hidden_row_stride % 8 || logits_row_stride % 8)
     return fail(DFLASH_ERR_INVALID_ARG, "%s: row strides must be multiples of 8 elements", who);
+  if (hidden_row_stride >= kMaxHeadStride)
+    return fail(DFLASH_ERR_UNSUPPORTED, "%s: hidden_row_stride and hidden_size must be < 2^22", who);
   if (n_rows == 0 || vocab == 0) return ok();
   if (!hidden || !weight || !logits_out) return fail(DFLASH_ERR_INVALID_ARG, "%s: null pointer", who);
   if (!aligned16(hidden) || !aligned16(weight) || !aligned16(logits_out))
@@ -501,6 +506,8 @@ int dflash_lm_head_topk(const void* hidden, int64_t hidden_row_stride, const voi
     return fail(DFLASH_ERR_UNSUPPORTED, "%s: hidden_size must be a positive multiple of 8", who);
   if (hidden_row_stride < hidden_size || hidden_row_stride % 8)
     return fail(DFLASH_ERR_INVALID_ARG, "%s: hidden_row_stride must be >= hidden_size and a multiple of 8", who);
+  if (hidden_row_stride >= kMaxHeadStride)
+    return fail(DFLASH_ERR_UNSUPPORTED, "%s: hidden_row_stride and hidden_size must be < 2^22", who);
   if (n_rows == 0) return ok();
   if (!hidden || !weight || !ids_out || !unary_out) return fail(DFLASH_ERR_INVALID_ARG, "%s: null pointer", who);
   if (!aligned16(hidden) || !aligned16(weight))

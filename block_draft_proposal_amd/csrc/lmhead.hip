@@ -10,10 +10,9 @@
 //
 // Design: one workgroup (8 waves) per 256 x 256 output tile, the tile
 // product of gemm_tile.h (direct global -> LDS staging into a two-stage
-// swizzled ring, 128 x 64 per wave).  Workgroups are dealt to the 8 XCDs in
-// turn and the two row blocks that share a head tile land on the same XCD,
-// so each head tile is fetched from HBM about once and re-read from that
-// XCD's L2.  The fp32 tile is rounded to bf16 (nearest, ties to even) and
+// swizzled ring, 128 x 64 per wave, pipelined by 32-wide k slices).  Each
+// XCD walks its column blocks in groups of 8 row blocks, so the workgroups
+// it runs together share head tiles and hidden rows in its L2.  The fp32 tile is rounded to bf16 (nearest, ties to even) and
 // written through LDS as 16-byte row pieces.
 //
 // Fused head + top-K (compute_candidates without the logits reaching HBM):
@@ -42,6 +41,8 @@ constexpr int kFragM = LmCfg::kFragM, kFragN = LmCfg::kFragN;
 constexpr int kLmThreads = LmCfg::kThreads;
 constexpr int kOutCols = LmCfg::kOutCols, kOutPasses = LmCfg::kOutPasses, kCPad = LmCfg::kCPad;
 constexpr size_t kLmSmem = LmCfg::kSmemBytes;
+// row blocks per group of the XCD-local tile order (tile_of_grouped)
+constexpr int kGroupRows = 8;
 
 __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const uint16_t* __restrict__ h, int64_t h_stride,
                                                              const uint16_t* __restrict__ W, int32_t M, int32_t H,
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const uint16_t* __r
                                                              int64_t l_stride, int32_t n_mb, int32_t n_nb) {
   extern __shared__ __align__(16) unsigned char lm_smem[];
   int mb, nb;
-  tile_of(blockIdx.x, n_mb, mb, nb);
+  tile_of_grouped<kGroupRows>(blockIdx.x, n_mb, n_nb, mb, nb);
   if (nb >= n_nb) return;
   const int m0 = mb * kBM, n0 = nb * kBN;
   uint32_t pk[kFragM][kFragN][2];
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_topk_kernel(
     uint64_t* __restrict__ parts, uint32_t* __restrict__ bound) {
   extern __shared__ __align__(16) unsigned char lm_smem[];
   int mb, grp;
-  tile_of(blockIdx.x, n_mb, mb, grp);
+  tile_of_grouped<kGroupRows>(blockIdx.x, n_mb, n_grp, mb, grp);
   if (grp >= n_grp) return;
   const int m0 = mb * kBM, tid = threadIdx.x;
   const int row = tid / kRowThreads, part = tid % kRowThreads;
@@ -347,8 +348,7 @@ hipError_t launch_lm_head_topk(const LmHeadArgs& a, const LmTopkPlan& p, int64_t
   uint32_t* bound = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) + p.bound_offset);
   hipLaunchKernelGGL(clear_u32_kernel, dim3((unsigned)((a.n_rows + 255) / 256)), dim3(256), 0, stream, bound,
                      a.n_rows);
-  const int64_t slots = (int64_t)((p.n_grp + 7) / 8) * p.n_mb;
-  const dim3 grid((unsigned)(slots * 8));
+  const dim3 grid((unsigned)grouped_grid(p.n_mb, p.n_grp));
 #define DFLASH_LMTK(KB)                                                                                    \
   hipLaunchKernelGGL((lm_head_topk_kernel<KB>), grid, dim3(kLmThreads), lm_topk_smem<KB>(), stream,     \
                      static_cast<const uint16_t*>(a.hidden), a.hidden_row_stride,                          \
@@ -370,8 +370,7 @@ hipError_t launch_lm_head(const LmHeadArgs& a, hipStream_t stream) {
   if (a.n_rows == 0 || a.vocab == 0) return hipSuccess;
   const int n_mb = (int)((a.n_rows + kBM - 1) / kBM);
   const int n_nb = (int)((a.vocab + kBN - 1) / kBN);
-  const int64_t slots = (int64_t)((n_nb + 7) / 8) * n_mb;
-  hipLaunchKernelGGL(lm_head_kernel, dim3((unsigned)(slots * 8)), dim3(kLmThreads), kLmSmem, stream,
+  hipLaunchKernelGGL(lm_head_kernel, dim3((unsigned)grouped_grid(n_mb, n_nb)), dim3(kLmThreads), kLmSmem, stream,
                      static_cast<const uint16_t*>(a.hidden), a.hidden_row_stride,
                      static_cast<const uint16_t*>(a.weight), (int32_t)a.n_rows, a.hidden_size, (int32_t)a.vocab,
                      static_cast<uint16_t*>(a.logits), a.logits_row_stride, n_mb, n_nb);

@@ -220,7 +220,9 @@ int dflash_walk(const float* scores, const int64_t* ids, const float* uniforms,
  * fp32 and summed in fp32 on the matrix cores; each sum is rounded once to
  * bf16 (nearest, ties to even).  hidden_size must be a multiple of 8;
  * hidden, weight, logits_out and both row strides 16-byte aligned;
- * logits_out must not overlap the inputs; n_rows and vocab below 2^31. */
+ * logits_out must not overlap the inputs; n_rows and vocab below 2^31;
+ * hidden_row_stride (hence hidden_size) below 2^22 elements
+ * (DFLASH_ERR_UNSUPPORTED otherwise). */
 int dflash_lm_head(const void* hidden, int64_t hidden_row_stride, const void* weight, int64_t n_rows,
                    int32_t hidden_size, int64_t vocab, void* logits_out, int64_t logits_row_stride,
                    int32_t dtype, dflash_stream_t stream);
@@ -235,7 +237,8 @@ int dflash_lm_head(const void* hidden, int64_t hidden_row_stride, const void* we
  * arguments.  Arguments as for those two calls (bf16 only; valid_vocab <=
  * vocab; 1 <= top_k <= DFLASH_MAX_TOP_K, top_k <= valid_vocab).  Scratch:
  * dflash_lm_head_topk_workspace_size(n_rows, vocab, top_k) bytes, 256-byte
- * aligned (per row, the K best of every group of 128-column tiles). */
+ * aligned (per row, the K best of every group of consecutive 256-column
+ * tiles, plus a per-row bound). */
 size_t dflash_lm_head_topk_workspace_size(int64_t n_rows, int64_t vocab, int32_t top_k);
 int dflash_lm_head_topk(const void* hidden, int64_t hidden_row_stride, const void* weight, int64_t n_rows,
                         int32_t hidden_size, int64_t vocab, int64_t valid_vocab, int32_t top_k,

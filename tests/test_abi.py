@@ -215,6 +215,7 @@ def test_lm_head_validation():
     assert call(os=130) == Bd.DFLASH_ERR_INVALID_ARG           # stride not a multiple of 8
     assert call(n=-1) == Bd.DFLASH_ERR_INVALID_ARG
     assert call(V=1 << 31, os=1 << 31) == Bd.DFLASH_ERR_UNSUPPORTED
+    assert call(hs=1 << 22) == Bd.DFLASH_ERR_UNSUPPORTED       # tile offsets are 32-bit
     assert call(h=ctypes.c_void_p(18)) == Bd.DFLASH_ERR_INVALID_ARG   # misaligned
     assert call(o=ctypes.c_void_p(16)) == Bd.DFLASH_ERR_INVALID_ARG   # overlaps the inputs
     assert call(n=0) == Bd.DFLASH_OK and call(V=0, os=0) == Bd.DFLASH_OK   # nothing to do
@@ -237,6 +238,7 @@ def test_lm_head_topk_validation():
     assert call(cap=-1.0) == Bd.DFLASH_ERR_INVALID_ARG
     assert call(wsb=ws_need - 1) == Bd.DFLASH_ERR_WORKSPACE
     assert call(ws=ctypes.c_void_p(128)) == Bd.DFLASH_ERR_INVALID_ARG   # not 256-byte aligned
+    assert call(hs=1 << 22) == Bd.DFLASH_ERR_UNSUPPORTED       # tile offsets are 32-bit
     assert call(n=0) == Bd.DFLASH_OK
 
 
