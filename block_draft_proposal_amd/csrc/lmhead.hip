@@ -17,13 +17,13 @@
 //
 // Fused head + top-K (compute_candidates without the logits reaching HBM):
 // each workgroup computes a group of consecutive column tiles of its row
-// block with the same tile product; each rounded tile is staged in LDS and
-// two threads per row fold its values into small sorted lists, skipping
-// values below the row's group list (kept in LDS across the group's tiles)
-// and below a per-row bound on the K-th best key that finished tiles
-// publish.  After its last tile a group stores its K best composites (value
-// descending, id ascending), and a second kernel merges the groups of each
-// row.  Both
+// block with the same tile product and keeps each row's K best of the group
+// in LDS.  Once a row has a threshold (its group list's K-th, or a per-row
+// bound on the K-th best key that finished group lists publish), the
+// rounded values are tested in registers and only the few that pass reach
+// the lists; tiles without thresholds are staged in LDS and scanned.  After
+// its last tile a group stores its K best composites (value descending, id
+// ascending), and a second kernel merges the groups of each row.  Both
 // paths rank the same bf16 logits, so the fused result equals the head
 // followed by the streaming top-K bit for bit.
 #include "dflash.h"
@@ -43,6 +43,7 @@ constexpr int kOutCols = LmCfg::kOutCols, kOutPasses = LmCfg::kOutPasses, kCPad 
 constexpr size_t kLmSmem = LmCfg::kSmemBytes;
 // row blocks per group of the XCD-local tile order (tile_of_grouped)
 constexpr int kGroupRows = 8;
+typedef short i16x2 __attribute__((ext_vector_type(2)));
 
 __global__ __launch_bounds__(kLmThreads) void lm_head_kernel(const uint16_t* __restrict__ h, int64_t h_stride,
                                                              const uint16_t* __restrict__ W, int32_t M, int32_t H,
@@ -130,6 +131,13 @@ constexpr int kCandCap = 16;
 constexpr size_t kCandOff = sizeof(uint16_t) * kBM * kCPad;
 static_assert(kCandOff % 16 == 0 && kCandOff + sizeof(uint32_t) * kLmThreads * kCandCap <= kLmSmem,
               "candidate buffers fit the ring beside the staged pass");
+// The filter from registers: per tile row a threshold and a buffer of up to
+// kRowCap passing keys with its count, all in the ring after the tile
+// product, then an overflow flag.
+constexpr int kRowCap = 112;
+constexpr size_t kThrOff = sizeof(uint32_t) * (kBM * kRowCap + kBM);
+constexpr size_t kOverOff = kThrOff + sizeof(uint32_t) * kBM;
+static_assert(kThrOff % 16 == 0 && kOverOff + 16 <= kLmSmem, "row buffers, counts and thresholds fit the ring");
 
 // A workgroup walks a group of consecutive column tiles of its row block.
 // kRowThreads threads per row: thread t takes row t / kRowThreads and, of
@@ -150,6 +158,16 @@ static_assert(kCandOff % 16 == 0 && kCandOff + sizeof(uint32_t) * kLmThreads * k
 // its K-th, since K values of the row have at least that key.  Values with a
 // smaller key cannot place and are skipped before any list work; the bound
 // only grows, so a stale read filters less but never wrongly.
+//
+// Most tiles skip the staging: once every row of the tile has a threshold
+// (its group list's K-th key, or the bound), each lane tests the 128
+// rounded values it holds against their rows' thresholds and appends the
+// few that pass to their row's buffer in LDS (an LDS atomic gives the
+// slot); the p = 0 thread of each row then inserts its row's entries into
+// the group list.  A tile where some row has no threshold yet (a group's
+// first tiles) or a row's buffer overflows takes the staged scan instead.
+// Both paths let exactly the values above the same thresholds reach the
+// lists, so the result does not depend on which one a tile takes.
 template <int KB>
 __global__ __launch_bounds__(kLmThreads) void lm_head_topk_kernel(
     const uint16_t* __restrict__ h, int64_t h_stride, const uint16_t* __restrict__ W, int32_t M, int32_t H,
@@ -180,6 +198,114 @@ __global__ __launch_bounds__(kLmThreads) void lm_head_topk_kernel(
       tile_product<LmCfg>(h, h_stride, W, H, M, V, H, m0, n0, 0, (H + LmCfg::kBK - 1) / LmCfg::kBK, lm_smem,
                           acc);                  // ends with a barrier
       pack_tile<LmCfg>(acc, pk);
+    }
+    {
+      // thresholds: a value passes iff its group key exceeds its row's
+      // (the group list's K-th, and key >= bound); rows past M take none
+      uint32_t* s_cnt = reinterpret_cast<uint32_t*>(lm_smem) + kBM * kRowCap;
+      uint32_t* s_thr = reinterpret_cast<uint32_t*>(lm_smem + kThrOff);
+      uint32_t* s_over = reinterpret_cast<uint32_t*>(lm_smem + kOverOff);
+      if (tid == 0) *s_over = 0u;
+      __syncthreads();
+      if (tid < kBM) {
+        uint32_t t = ~0u;
+        if (m0 + tid < M) {
+          const uint32_t b = __hip_atomic_load(bound + m0 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          t = max(reinterpret_cast<const uint32_t*>(lm_smem + kLmSmem)[tid * KB + KB - 1], b ? (b << 16) - 1u : 0u);
+          if (t == 0u) *s_over = 1u;              // no threshold yet: stage the tile
+        }
+        s_thr[tid] = t;
+        s_cnt[tid] = 0u;
+      }
+      __syncthreads();
+      // the flag is one LDS word read by every thread after a barrier: uniform
+      if (__builtin_amdgcn_readfirstlane(*s_over) == 0u) {
+        // lane-dependent values are derived here from an opaque copy of the
+        // thread index, so the compiler forms them per tile instead of
+        // keeping them across the tile product (where they would spill)
+        uint32_t tq = (uint32_t)tid;
+        asm volatile("" : "+v"(tq));
+        const int wave = tid >> 6, lane = (int)(tq & 63u);
+        const int wm = (wave / LmCfg::kWavesN) * LmCfg::kWM, wn = (wave % LmCfg::kWavesN) * LmCfg::kWN;
+        uint32_t* s_cand = reinterpret_cast<uint32_t*>(lm_smem);
+        // A pre-filter over the packed values: pk[i][j][h] holds rows
+        // r4 + 2h (low half) and r4 + 2h + 1 (high half) of fragment row i
+        // at column j.  For a strictly positive threshold value a value can
+        // only pass if its bf16 bits, read as a signed 16-bit integer, are
+        // >= the threshold's (negative values are negative integers), so the
+        // packed signed maximum over the four columns against the packed
+        // thresholds flags the row pairs worth an exact look (ties included;
+        // any other threshold flags its pair).
+        u32x4 t4[kFragM];
+#pragma unroll
+        for (int i = 0; i < kFragM; ++i) t4[i] = ld16(s_thr + wm + 16 * i + 4 * (lane >> 4));
+        uint32_t flags = 0u;                     // bit 2 i + h: row pair (i, h) has a candidate
+#pragma unroll
+        for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t ka = t4[i][2 * h] >> 16, kb = t4[i][2 * h + 1] >> 16;
+            const i16x2 thm = {(short)((ka & 0x7fffu) - 1u), (short)((kb & 0x7fffu) - 1u)};
+            i16x2 mx = __builtin_bit_cast(i16x2, pk[i][0][h]);
+#pragma unroll
+            for (int j = 1; j < kFragN; ++j) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(i16x2, pk[i][j][h]));
+            const i16x2 m2 = __builtin_elementwise_max(mx, thm);
+            const bool above = __builtin_bit_cast(uint32_t, m2) != __builtin_bit_cast(uint32_t, thm);
+            flags |= ((ka > 0x8000u && kb > 0x8000u) ? above : true) ? (1u << (2 * i + h)) : 0u;
+          }
+        // the exact test for flagged pairs: group key against the row's
+        // threshold, valid columns only, then an LDS slot in the row's buffer
+#pragma unroll
+        for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            if ((flags >> (2 * i + h)) & 1u) {
+              // opaque copies: keys and addresses are formed here, not
+              // hoisted out of the tile loop and kept (or spilled)
+              uint32_t lq = (uint32_t)tid, w[kFragN];
+#pragma unroll
+              for (int j = 0; j < kFragN; ++j) w[j] = pk[i][j][h];
+              asm volatile("" : "+v"(lq), "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+              const uint32_t l = lq & 63u, wv = lq >> 6;
+              const uint32_t r0 = (wv / LmCfg::kWavesN) * LmCfg::kWM + (uint32_t)(16 * i + 2 * h) + 4u * (l >> 4);
+#pragma unroll
+              for (int j = 0; j < kFragN; ++j) {
+                const uint32_t tc = (wv % LmCfg::kWavesN) * LmCfg::kWN + (uint32_t)(16 * j) + (l & 15u);
+                const uint32_t ck = 0xFFFFu - ((uint32_t)cg0 + tc);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                  const uint32_t c = (bf16_key(e ? (w[j] >> 16) : (w[j] & 0xffffu)) << 16) | ck;
+                  if (n0 + (int)tc < valid && c > t4[i][2 * h + e]) {
+                    const uint32_t slot = atomicAdd(s_cnt + r0 + e, 1u);
+                    if (slot < (uint32_t)kRowCap) s_cand[(r0 + e) * kRowCap + slot] = c;
+                  }
+                }
+              }
+            }
+          }
+        __syncthreads();
+        if (tid < kBM && s_cnt[tid] > (uint32_t)kRowCap) *s_over = 1u;
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(*s_over) == 0u) {
+          if (part == 0 && row_ok) {
+            uint32_t tl[KB];
+#pragma unroll
+            for (int i = 0; i < KB; ++i) tl[i] = glist[i];
+            const uint32_t lo_r = __hip_atomic_load(bound + m0 + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int n = (int)s_cnt[row];
+            for (int e = 0; e < n; ++e) {
+              const uint32_t c = s_cand[row * kRowCap + e];
+              if (c > tl[KB - 1]) list_insert(tl, c);
+            }
+#pragma unroll
+            for (int i = 0; i < KB; ++i) glist[i] = tl[i];
+            if (tl[KB - 1] != 0u && (tl[KB - 1] >> 16) > lo_r)
+              __hip_atomic_fetch_max(bound + m0 + row, tl[KB - 1] >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          __syncthreads();                       // the buffers lie in the ring the next tile refills
+          continue;
+        }
+      }
     }
     uint32_t lo = 0;
     if (row_ok) lo = __hip_atomic_load(bound + m0 + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
