@@ -41,6 +41,13 @@ template <> struct Elem<float> {
 // demoted to scratch memory by such a select).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Buffer resources: word 3 of a raw dword buffer (32-bit data format, no
+// swizzle).  A load through a buffer resource past num_records bytes returns
+// zeros and reads no memory.
+constexpr int kBufferFlags = 0x00020000;
+// cache policy of a streaming (non-temporal) buffer load
+constexpr int kBufferStream = 2;
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 __device__ __forceinline__ void unpack16(u32x4 v, float (&o)[8]) {

@@ -165,7 +165,8 @@ hipError_t launch_philox_uniforms(const uint64_t* seed_offset, int64_t n, float*
 // Verify and commit of a drafted block.
 struct VerifyRowStats {
   double m;                 // maximum logit of the row (valid ids), -inf if none is finite
-  double s;                 // sum_v exp((z_v - m) / T) (sampled requests)
+  double s;                 // sum_v exp((z_v - m) / T) (sampled requests), approximate
+  double b;                 // bound on |s - the exact sum|
   int64_t arg;              // lowest id of the maximum
 };
 struct VerifyArgs {

@@ -143,7 +143,6 @@ __device__ __forceinline__ void issue_stage(const uint16_t* __restrict__ base, i
 // of a stage differ from its first by whole row blocks).  Row strides and
 // contraction lengths stay below 2^22 elements, which keeps every offset of
 // a 256-row tile within 32 bits.
-constexpr int kBufferFlags = 0x00020000;   // raw dword buffer: 32-bit data format, no swizzle
 template <class Cfg, int ROWS>
 struct BufRows {
   static constexpr int kLoads = ROWS / Cfg::kBlockRows / Cfg::kWaves;

@@ -284,10 +284,15 @@ int dflash_philox_uniforms(const uint64_t* seed_offset, int64_t n, float* out, d
  *   accepted_out   [n_req] int32: drafted tokens kept
  *   committed_out  [n_req, slots+1] int64: the kept tokens, then the
  *                  correction or bonus token, then -1
+ * The sums behind p are first taken in fp32 with a bound on their error; a
+ * decision or draw that the bound cannot settle is taken again from the
+ * row's fp64 sums, so results are those of the fp64 rule either way.
  * Scratch: dflash_verify_workspace_size(n_req, slots, valid_vocab) bytes,
- * 8-byte aligned, owned by the caller (per-row statistics and per-chunk sums
- * of the sampled rows; about valid_vocab / 8 bytes per target row); 0 when
- * any argument is <= 0.  n_req == 0 is a no-op. */
+ * 8-byte aligned, owned by the caller (per-row statistics, per-chunk sums and
+ * their reference maxima for the sampled rows -- about valid_vocab / 80 bytes
+ * per target row -- and a list of the requests whose draw needs the fp64
+ * sums); calls that share it must be ordered on one stream.  0 when any
+ * argument is <= 0.  n_req == 0 is a no-op. */
 size_t dflash_verify_workspace_size(int32_t n_req, int32_t slots, int64_t valid_vocab);
 int dflash_verify(const void* target_logits, int64_t row_stride, int32_t n_req, int32_t slots, int64_t vocab,
                   int64_t valid_vocab, int32_t top_k, const int64_t* cand_ids, const float* q, const int64_t* tokens,

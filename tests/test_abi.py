@@ -274,9 +274,9 @@ def test_verify_validation():
     need = L.dflash_verify_workspace_size(R, S, V)
     assert need >= R * (S + 1) * 24 and L.dflash_verify_workspace_size(0, S, V) == 0
     assert L.dflash_verify_workspace_size(R, S, 0) == 0
-    # the chunk sums cover every vector of a row: at least 8 bytes per 256 ids
+    # the chunk sums cover every vector of a row: at least 8 bytes per 1024 ids
     big = 151936
-    assert L.dflash_verify_workspace_size(R, S, big) >= R * (S + 1) * (4 * 24 + 8 * (big // 256))
+    assert L.dflash_verify_workspace_size(R, S, big) >= R * (S + 1) * (4 * 24 + 8 * (big // 1024))
     call = lambda **kw: L.dflash_verify(*[kw.get(k, d) for k, d in (
         ("z", A(1 << 20)), ("rs", V), ("R", R), ("S", S), ("V", V), ("vv", V), ("K", K), ("ids", A(2 << 20)),
         ("q", A(3 << 20)), ("tok", A(4 << 20)), ("ua", A(5 << 20)), ("ur", A(6 << 20)), ("t", A(7 << 20)),

@@ -204,3 +204,63 @@ def test_verify_long_blocks():
         d["cand"][0, :, 0] = d["tok"][0]
     a, _ = _run(R, S, V, K, 15, d=d)
     assert a[0] == S and a[1] == 66
+
+
+def _near_ties(d, S, seed):
+    """Sets u_accept so that each request's slot r % S sits 3e-7 (relative)
+    from its accept edge (alternately just rejected and just kept; earlier
+    slots kept outright), then u_residual so that the committed draw's target
+    sits 2e-7 of the total from an interval boundary in the middle of the
+    drawn distribution (alternately just inside and just before it)."""
+    z = f64(d["z"])
+    R = z.shape[0]
+    temps = d["temps"].double().numpy()
+    cand, tok, valid = d["cand"].numpy(), d["tok"].numpy(), d["valid"]
+    for r in range(R):
+        n = r % S
+        d["ua"][r, :n] = 0.0                      # u q(x) = 0 < p(x): kept
+        x = int(tok[r, n])
+        p = O.target_distribution(z[r, n], valid, temps[r], False)
+        qx = float(d["q"][r, n, np.flatnonzero(cand[r, n] == x)[0]])
+        u = p[x] / qx * (1 + (3e-7 if r % 2 == 0 else -3e-7))
+        if u >= 1.0:
+            u = p[x] / qx * (1 - 3e-7)
+        d["ua"][r, n] = float(np.float32(u))
+    ra, _ = O.verify(z, valid, cand, d["q"].double().numpy(), tok, d["ua"].double().numpy(),
+                     d["ur"].double().numpy(), temps, d["greedy"].numpy())
+    for r in range(R):
+        n = int(ra[r])
+        p = O.target_distribution(z[r, n], valid, temps[r], False)
+        w = p
+        if n < S:
+            w = p.copy()
+            for jj, v in enumerate(cand[r, n]):
+                w[v] = max(0.0, w[v] - float(d["q"][r, n, jj]))
+            if not np.any(w > 0):
+                w = p
+        c = np.cumsum(w)
+        k = int(np.searchsorted(c, 0.5 * c[-1]))
+        lo = c[k - 1] if k > 0 else 0.0
+        side = 1.0 if (r // 2) % 2 == 0 else -1.0
+        d["ur"][r] = float(np.float32((lo + side * 2e-7 * c[-1]) / c[-1]))
+    return d
+
+
+@pytest.mark.parametrize("dtype,V,valid,seed", [(torch.bfloat16, 151936, 151936, 16),
+                                                (torch.float32, 5003, 4999, 17)])
+def test_verify_near_ties_take_the_exact_path(dtype, V, valid, seed):
+    # Decisions and draws a few 1e-7 (relative) from their edges: inside the
+    # error bound of the fp32 sums, so the kernels take each near-tie
+    # decision from its row's exact fp64 sums inside the commit pass (a draw
+    # after a rejection there comes from those sums too), and leave a draw
+    # from a later row to the exact-sum and fix-up passes (half the requests
+    # here); far outside the comparison's 1e-9 edge allowance, so the outcome
+    # must equal the oracle's.
+    R, S, K = 12, 3, 8
+    d = _near_ties(_inputs(R, S, V, K, seed, dtype=dtype, valid=valid, greedy_frac=0.0), S, seed)
+    acc, com = _run(R, S, V, K, seed, d=d)
+    ra, rc = O.verify(f64(d["z"]), valid, d["cand"].numpy(), d["q"].double().numpy(), d["tok"].numpy(),
+                      d["ua"].double().numpy(), d["ur"].double().numpy(), d["temps"].double().numpy(),
+                      d["greedy"].numpy())
+    assert np.array_equal(acc, ra) and np.array_equal(com, rc)
+    assert 0 < int((ra < np.arange(R) % S + 1).sum()) < R   # both sides of the accept edge occur
