@@ -37,7 +37,7 @@ namespace {
 
 constexpr int kVerifyThreads = 256;   // 4 waves per (row, segment)
 constexpr int kVerifyWaves = kVerifyThreads / 64;
-constexpr int kCommitThreads = 1024;
+constexpr int kCommitThreads = 256;   // 4 waves per request: four requests per CU at once
 constexpr int kRowsLds = 64;          // target rows of a request whose statistics the commit keeps in LDS
 constexpr int kChunkLoads = 4;        // vectors per lane of one chunk
 constexpr int kChunkVecs = 64 * kChunkLoads;   // vectors of one chunk, contiguous in the row
@@ -554,8 +554,7 @@ __device__ __forceinline__ double exact_singles(const TIO* z, const RowGeom& g, 
 // whole commit workgroup: every chunk's sum is overwritten with its fp64
 // value and its reference with m, and the row's total (chunks and singles)
 // is returned to every thread.  Wave w of the workgroup takes the row's
-// (segment, wave) range w.
-static_assert(kCommitThreads / 64 == kVerifySegs * kVerifyWaves, "one commit wave per (segment, wave) range");
+// (segment, wave) ranges w, w + waves, ...
 template <typename TIO>
 __device__ double exact_row_sums(const TIO* z, int64_t valid, double m, double inv_t, const double* s_exp,
                                  double* cs_row, float* cr_row, int32_t nch_bound, double* red) {
@@ -563,19 +562,21 @@ __device__ double exact_row_sums(const TIO* z, int64_t valid, double m, double i
   const TIO* zv = z + g.head;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const double ms = m * inv_t;
-  int64_t wlo, whi;
-  g.wave_range(wv / kVerifyWaves, wv % kVerifyWaves, wlo, whi);
-  const int64_t nch = (whi - wlo + kChunkVecs - 1) / kChunkVecs;
-  double* cs = cs_row + (int64_t)wv * nch_bound;
-  float* cr = cr_row + (int64_t)wv * nch_bound;
   double lacc = 0.0;
-  for (int64_t j = 0; j < nch; ++j) {
-    const double cj = exact_chunk_sum(zv, wlo, whi, j, ms, inv_t, s_exp);
-    if (lane == 0) {
-      cs[j] = cj;
-      cr[j] = (float)m;
+  for (int part = wv; part < kVerifySegs * kVerifyWaves; part += kCommitThreads / 64) {
+    int64_t wlo, whi;
+    g.wave_range(part / kVerifyWaves, part % kVerifyWaves, wlo, whi);
+    const int64_t nch = (whi - wlo + kChunkVecs - 1) / kChunkVecs;
+    double* cs = cs_row + (int64_t)part * nch_bound;
+    float* cr = cr_row + (int64_t)part * nch_bound;
+    for (int64_t j = 0; j < nch; ++j) {
+      const double cj = exact_chunk_sum(zv, wlo, whi, j, ms, inv_t, s_exp);
+      if (lane == 0) {
+        cs[j] = cj;
+        cr[j] = (float)m;
+      }
+      lacc += cj;
     }
-    lacc += cj;
   }
   if (wv == 0) lacc += exact_singles(z, g, valid, ms, inv_t, s_exp, true, true);
   __syncthreads();                                        // red is free
@@ -1034,7 +1035,10 @@ __device__ void commit_body(const CommitArgs<TIO>& ca, const int r) {
 }
 
 template <typename TIO>
-__global__ __launch_bounds__(kCommitThreads) void verify_commit_kernel(CommitArgs<TIO> ca) {
+// (capped at 4 waves per SIMD, 128 registers: four requests per CU at once,
+// a few spills on the rare paths; 166 registers let three in and ran 1.5x
+// slower on 1024 requests)
+__global__ __launch_bounds__(kCommitThreads) __attribute__((amdgpu_waves_per_eu(4))) void verify_commit_kernel(CommitArgs<TIO> ca) {
   commit_body<TIO, false>(ca, blockIdx.x);
 }
 
@@ -1093,7 +1097,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_exact_kernel(CommitArgs
 
 // The draws left pending, taken again from the exact sums: one workgroup
 // per listed request, over a fixed grid of kFixupGroups workgroups.
-constexpr int kFixupGroups = 128;
+constexpr int kFixupGroups = 256;
 template <typename TIO>
 __global__ __launch_bounds__(kCommitThreads) void verify_fixup_kernel(CommitArgs<TIO> ca) {
   const uint32_t cnt = *ca.count;
