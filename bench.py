@@ -7,8 +7,8 @@ projection -> lattice -> walk; the library runs conv and projection beside
 the top-K on a second stream) over one batch of synthetic draft blocks,
 issued through a prepared call whose arguments were marshalled once per input
 set, as a serving loop with fixed buffers does.  The
-default workload is the bf16 batch of 32 requests x block 16 (hidden 4096 =
-64 x 64, 4 taps, vocab 151936, K = 8, rank 64, all greedy).  Activations (x,
+default workload is the largest one, 1024 requests x block 16 (hidden 7168 =
+112 x 64, 8 taps, vocab 201024, K = 32, rank 128, all sampled at T = 0.7).  Activations (x,
 delta, logits, uniforms) rotate over several independent input sets whose
 logits total more than twice the 256 MB Infinity Cache, so every step streams
 its logits from HBM; selector tables and projection weights stay fixed like

@@ -43,7 +43,7 @@ __device__ __forceinline__ void walk_load(const TIO* __restrict__ x, const TIO* 
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int j = 0; j < kWalkMaxBlock; ++j)
-    if (j < B) xr[j] = ld16(x + (row0 + j) * H + c0);
+    if (j < B) xr[j] = ld16_nt(x + (row0 + j) * H + c0);   // each input row is read once
 #pragma unroll
   for (int t = 0; t < TAPS; ++t) br[t] = ld16(base + (int64_t)t * H + c0);
   // one 16-byte piece per (token j, tap t), piece i = j * TAPS + t

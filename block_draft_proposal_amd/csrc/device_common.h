@@ -49,6 +49,13 @@ constexpr int kBufferFlags = 0x00020000;
 // cache policy of a streaming (non-temporal) buffer load
 constexpr int kBufferStream = 2;
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Streaming (non-temporal) forms, for data read or written once: on this
+// chip a stream of them runs well above the plain forms' rate (a 16-byte-lane
+// copy: ~5.9 against ~5.0 TB/s).
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p)); }
 
 __device__ __forceinline__ void unpack16(u32x4 v, float (&o)[8]) {
 #pragma unroll
