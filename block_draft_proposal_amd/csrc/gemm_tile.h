@@ -106,6 +106,11 @@ struct StridedRows {
   __device__ __forceinline__ const uint16_t* operator()(int r) const { return base + (int64_t)r * stride; }
 };
 
+// Cache policy of an operand's direct loads: a row functor may declare
+// kAux (kBufferStream for rows read once); 0 (default caching) otherwise.
+template <class R, class = void> struct RowAux { static constexpr int value = 0; };
+template <class R> struct RowAux<R, std::void_t<decltype(R::kAux)>> { static constexpr int value = R::kAux; };
+
 // Issues the direct global -> LDS loads of one stage: rows [r0, r0 + ROWS)
 // x k [k0, k0 + BK) of a [rows, H] matrix (row r at row_at(r)), in 1 KB
 // blocks of kBlockRows rows dealt round the waves; lane l of a block fills
@@ -122,7 +127,7 @@ __device__ __forceinline__ void issue_stage(const RowAt& row_at, int rows, int H
     const int blk = q * Cfg::kWaves + wave, r = blk * Cfg::kBlockRows + lane / Cfg::kChunks;
     const int k = k0 + 8 * ((lane % Cfg::kChunks) ^ Cfg::swz(r));
     const uint16_t* src = row_at(min(r0 + r, rows - 1)) + min(k, H - 8);
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(dst + blk * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(dst + blk * 1024), 16, 0, RowAux<RowAt>::value);
   }
 }
 template <class Cfg, int ROWS>

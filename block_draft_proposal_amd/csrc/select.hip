@@ -160,6 +160,7 @@ using ProjTileCfg = TileCfg<4, 4, 2, 2, 64, 2>;
 
 // Slot row n of a request-major [R][S] view with strides in elements.
 struct SlotRows {
+  static constexpr int kAux = kBufferStream;        // each slot row is read once: streaming loads
   const uint16_t* h;
   int64_t req_stride, slot_stride;
   int32_t slots;
