@@ -170,7 +170,8 @@ def call_bytes(w):
     return {"dflash_conv": conv, "dflash_conv_prepare": prepare, "dflash_topk": topk, "dflash_lattice": lattice,
             "dflash_walk": walk, "dflash_verify": verify, "dflash_propose_block": propose,
             "ProposeGraph.step_eager": propose + 4 * Ns + 5 * R + 16,
-            "ProposeGraph.replay": propose + 4 * Ns + 5 * R + 16}
+            "ProposeGraph.replay": propose + 4 * Ns + 5 * R + 16,
+            "hbm_ceiling.read": Ns * w.vocab * e, "hbm_ceiling.copy": 2 * N * H * e}
 
 
 def sweep(iters: int = 50, warm: int = 5, only=None):
@@ -199,13 +200,22 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
         pick = lambda q: t[min(len(t) - 1, int(q * (len(t) - 1) + 0.5))]
         return pick(0.5), pick(0.1), pick(0.9)
 
-    # copy ceiling: 1 GiB device-to-device (reads 1 GiB, writes 1 GiB)
+    # copy ceiling: 1 GiB device-to-device (reads 1 GiB, writes 1 GiB), by
+    # torch's copy and by the library's streaming copy; and a 1 GiB read
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).uniform_()
     dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
     med, _, _ = timed(lambda: dst.copy_(src))
     copy_gbs = 2 * (1 << 30) / (med * 1e-6) / 1e9
+    med_s, _, _ = timed(lambda: D.dflash_hbm_ceiling(D.CEILING_COPY, src, dst))
+    med_r, _, _ = timed(lambda: D.dflash_hbm_ceiling(D.CEILING_READ, src, sink))
     del src, dst
-    print(f"copy ceiling: 1 GiB device copy {med:.1f} us -> {copy_gbs:.0f} GB/s (read + write)\n")
+    print(f"copy ceiling: 1 GiB torch device copy {med:.1f} us -> {copy_gbs:.0f} GB/s (read + write); "
+          f"streaming copy (dflash_hbm_ceiling) {med_s:.1f} us -> {2 * (1 << 30) / (med_s * 1e-6) / 1e9:.0f} GB/s; "
+          f"streaming read of 1 GiB {med_r:.1f} us -> {(1 << 30) / (med_r * 1e-6) / 1e9:.0f} GB/s\n")
+    print("Rows hbm_ceiling.read / hbm_ceiling.copy: dflash_hbm_ceiling streams of the workload's logits (the "
+          "top-K's bytes) and of its x copied into the conv output (the conv's rows), for reading the kernels "
+          "against a plain stream of the same size.\n")
     print("| workload | call | median us | p10 us | p90 us | algorithmic MB | GB/s | % of 8 TB/s | % of copy |")
     print("|---|---|---|---|---|---|---|---|---|")
     for name, w in W.WORKLOADS.items():
@@ -266,6 +276,8 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
             "dflash_propose_block": lambda: call(stream),
             "ProposeGraph.step_eager": lambda: graph.step_eager(g_temps, g_mask, 1234, 0),
             "ProposeGraph.replay": lambda: graph.replay(g_temps, g_mask, 1234, 0),
+            "hbm_ceiling.read": lambda: D.dflash_hbm_ceiling(D.CEILING_READ, inp["logits"], sink),
+            "hbm_ceiling.copy": lambda: D.dflash_hbm_ceiling(D.CEILING_COPY, inp["x"], conv_out),
         }
         nbytes = call_bytes(w)
         for cname, fn in fns.items():
@@ -538,6 +550,28 @@ def main():
     torch.cuda.synchronize()
     conv_us = sorted(a.elapsed_time(b) for a, b in conv_ev[5:])[10] * 1e3
     conv_gbs = nbytes["conv"] / (conv_us * 1e-6) / 1e9
+    # What this chip sustains for plain streams of the same sizes, in the
+    # kernels' load and store forms: a read of one input set's logits (the
+    # top-K's bytes) and a copy of its x into conv_out (the conv's rows).
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def ceiling(kind, src_of, dst_of):
+        evs = []
+        for i in range(25):
+            a, b = TimingEvent(), TimingEvent()
+            a.record(stream)
+            D.dflash_hbm_ceiling(kind, src_of(sets[i % n_sets]), dst_of(sets[i % n_sets]))
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs[5:])[10] * 1e3
+
+    read_bytes = sets[0]["logits"].numel() * sets[0]["logits"].element_size()
+    copy_bytes = 2 * sets[0]["x"].numel() * sets[0]["x"].element_size()
+    read_us = ceiling(D.CEILING_READ, lambda st: st["logits"], lambda st: sink)
+    copy_us = ceiling(D.CEILING_COPY, lambda st: st["x"], lambda st: conv_out)
+    read_gbs = read_bytes / (read_us * 1e-6) / 1e9
+    copy_gbs = copy_bytes / (copy_us * 1e-6) / 1e9
     tokens = w.n_slot_rows * args.steps
     line = {
         "metric": METRIC,
@@ -561,10 +595,17 @@ def main():
                      "algorithmic_bytes_per_launch": stage1_bytes, "avg_launch_us": avg_ms[1] * 1e3},
         "hbm_kernels": {
             "topk": {"achieved": topk_gbs, "frac": topk_gbs / HBM_PEAK_GBS, "unit": "GB/s",
-                     "how": "the roofline kernel above (events around it inside the timed steps)"},
+                     "how": "the roofline kernel above (events around it inside the timed steps)",
+                     "read_ceiling": {"GBps": read_gbs, "us": read_us, "bytes": read_bytes,
+                                      "how": "dflash_hbm_ceiling read of one input set's logits, median of 20"},
+                     "of_read_ceiling": topk_gbs / read_gbs},
             "conv": {"achieved": conv_gbs, "frac": conv_gbs / HBM_PEAK_GBS, "unit": "GB/s", "us": conv_us,
                      "algorithmic_bytes": nbytes["conv"],
-                     "how": "dflash_conv alone on the same rotating inputs, median of 20 calls by HIP events"}},
+                     "how": "dflash_conv alone on the same rotating inputs, median of 20 calls by HIP events",
+                     "copy_ceiling": {"GBps": copy_gbs, "us": copy_us, "bytes": copy_bytes,
+                                      "how": "dflash_hbm_ceiling copy of one input set's x into the conv output, "
+                                             "median of 20"},
+                     "of_copy_ceiling": conv_gbs / copy_gbs}},
         "stage_us": {"conv": avg_ms[0] * 1e3, "topk": avg_ms[1] * 1e3, "proj": avg_ms[2] * 1e3,
                      "lattice_walk": avg_ms[3] * 1e3, "note": f"top-K from every {TIMED_EVERY}th timed step, the other stages "
                      f"from {n_stage} further steps with all stage events; "

@@ -27,6 +27,9 @@ from .binding import (  # noqa: F401
     ProposeBlock,
     ProposeGraph,
     dflash_philox_uniforms,
+    dflash_hbm_ceiling,
+    CEILING_READ,
+    CEILING_COPY,
     propose_block_workspace_size,
     propose_block_schedule,
     SCHEDULE_ONE_LAUNCH,

@@ -68,6 +68,7 @@ _SIGNATURES = {
     "dflash_conv_prepare": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
                                      _c_i32, _c_vp, _c_size, _c_vp]),
     "dflash_philox_uniforms": (_c_i32, [_c_vp, _c_i64, _c_vp, _c_vp]),
+    "dflash_hbm_ceiling": (_c_i32, [_c_i32, _c_vp, _c_vp, _c_i64, _c_vp]),
     "dflash_verify_workspace_size": (_c_size, [_c_i32, _c_i32, _c_i64]),
     "dflash_verify": (_c_i32, [_c_vp, _c_i64, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp,
                                _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
@@ -431,6 +432,23 @@ def dflash_philox_uniforms(seed_offset: torch.Tensor, n: int, *, out: Optional[t
         out = torch.empty(n, dtype=torch.float32, device=seed_offset.device)
     _check(lib().dflash_philox_uniforms(_p(seed_offset), n, _p(out), _stream(stream)))
     return out
+
+
+CEILING_READ, CEILING_COPY = 0, 1
+
+
+def dflash_hbm_ceiling(kind: int, src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Measurement support: streams src's bytes (kind CEILING_READ, dst a
+    4-byte sink) or copies them into dst (CEILING_COPY) with the path's
+    streaming load and store forms."""
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if kind == CEILING_COPY and dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    if kind == CEILING_READ and dst.numel() * dst.element_size() < 4:
+        raise ValueError("the read sink needs 4 bytes")
+    _check(lib().dflash_hbm_ceiling(kind, _p(src), _p(dst), nbytes, _stream(stream)))
 
 
 _hip_rt = None

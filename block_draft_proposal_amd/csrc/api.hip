@@ -352,6 +352,21 @@ int dflash_philox_uniforms(const uint64_t* seed_offset, int64_t n, float* out, d
   return st == DFLASH_OK ? ok() : st;
 }
 
+int dflash_hbm_ceiling(int32_t kind, const void* src, void* dst, int64_t bytes, dflash_stream_t stream) {
+  const char* who = "dflash_hbm_ceiling";
+  if (kind != DFLASH_CEILING_READ && kind != DFLASH_CEILING_COPY)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: unknown kind %d", who, kind);
+  if (bytes < 0 || bytes % 16) return fail(DFLASH_ERR_INVALID_ARG, "%s: bytes must be >= 0 and a multiple of 16", who);
+  if (bytes == 0) return ok();
+  if (!src || !dst) return fail(DFLASH_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!aligned16(src) || (kind == DFLASH_CEILING_COPY ? !aligned16(dst) : reinterpret_cast<uintptr_t>(dst) % 4))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: misaligned pointer", who);
+  if (overlaps(src, (size_t)bytes, dst, kind == DFLASH_CEILING_COPY ? (size_t)bytes : 4))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: dst overlaps src", who);
+  const int st = launch_status(dflash::launch_hbm_ceiling(kind, src, dst, bytes, as_hip(stream)), who);
+  return st == DFLASH_OK ? ok() : st;
+}
+
 size_t dflash_verify_workspace_size(int32_t n_req, int32_t slots, int64_t valid_vocab) {
   if (n_req <= 0 || slots < 0 || valid_vocab <= 0) return 0;
   return dflash::verify_workspace_bytes(n_req, slots, valid_vocab);

@@ -161,6 +161,9 @@ hipError_t launch_conv_prepare(const ConvPrepArgs& a, const ConvPrepPlan& p, hip
 
 // Philox-4x32-10 uniforms: seed_offset = {seed, offset} in device memory.
 hipError_t launch_philox_uniforms(const uint64_t* seed_offset, int64_t n, float* out, hipStream_t stream);
+// HBM ceilings (ceiling.hip): kind 0 reads bytes from src (dst: a 4-byte
+// sink), kind 1 copies them to dst; bytes a multiple of 16.
+hipError_t launch_hbm_ceiling(int kind, const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
 // Verify and commit of a drafted block.
 struct VerifyRowStats {

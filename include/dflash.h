@@ -261,6 +261,21 @@ int dflash_lm_head_topk(const void* hidden, int64_t hidden_row_stride, const voi
 int dflash_philox_uniforms(const uint64_t* seed_offset, int64_t n, float* out, dflash_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * dflash_hbm_ceiling -- measurement support, not a step of the method: the
+ * bandwidth this chip sustains for a plain stream of a given size, in the
+ * load and store forms the path's streaming kernels use (16-byte lanes,
+ * non-temporal), so that a kernel's achieved bandwidth can be read against
+ * a stream of the same byte count.
+ *   kind   DFLASH_CEILING_READ: reads `bytes` from src (dst: a device word
+ *          that receives a value only for one bit pattern of the data);
+ *          DFLASH_CEILING_COPY: copies `bytes` from src to dst
+ *   src    device, 16-byte aligned; dst 16-byte (copy) or 4-byte (read)
+ *          aligned, not overlapping src
+ *   bytes  a multiple of 16 (0 is a no-op) */
+enum { DFLASH_CEILING_READ = 0, DFLASH_CEILING_COPY = 1 };
+int dflash_hbm_ceiling(int32_t kind, const void* src, void* dst, int64_t bytes, dflash_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * dflash_verify -- verify and commit of a drafted block ("[Spec] DFlash2",
  * executive summary and walk-kernel excerpt: verify checks the drafted tokens
  * against the distribution the walk drew them from -- a point mass on greedy

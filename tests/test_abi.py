@@ -25,7 +25,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_entry_point():
     names = _declared_functions()
-    assert "dflash_propose_block" in names and len(names) == 21
+    assert "dflash_propose_block" in names and len(names) == 22
     lib = D.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -293,6 +293,21 @@ def test_verify_validation():
     assert call(wsb=need - 1) == Bd.DFLASH_ERR_WORKSPACE
     assert call(ws=A((11 << 20) + 4)) == Bd.DFLASH_ERR_INVALID_ARG   # not 8-byte aligned
     assert call(R=0) == Bd.DFLASH_OK
+
+
+def test_hbm_ceiling_validation():
+    L = Bd.lib()
+    A = ctypes.c_void_p
+    call = lambda kind=1, src=A(1 << 20), dst=A(2 << 20), n=1 << 16: L.dflash_hbm_ceiling(kind, src, dst, n, None)
+    assert call(kind=2) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(n=24) == Bd.DFLASH_ERR_INVALID_ARG               # not a multiple of 16
+    assert call(n=-16) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(src=None) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(src=A((1 << 20) + 8)) == Bd.DFLASH_ERR_INVALID_ARG
+    assert call(dst=A((2 << 20) + 4)) == Bd.DFLASH_ERR_INVALID_ARG   # a copy needs 16-byte alignment
+    assert call(dst=A((1 << 20) + 4096)) == Bd.DFLASH_ERR_INVALID_ARG   # overlaps src
+    assert call(kind=0, dst=A((1 << 20) + 4)) == Bd.DFLASH_ERR_INVALID_ARG   # sink inside src
+    assert call(n=0) == Bd.DFLASH_OK
 
 
 def test_error_message_is_per_call():
