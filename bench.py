@@ -38,6 +38,7 @@ MFMA_PEAK_TFS = 2500.0      # MI355X dense bf16 matrix peak, TFLOP/s
 DEFAULT_WORKLOAD = "stress_r1024_k32"
 MALL_BYTES = 256 * 1024 * 1024
 TIMED_EVERY = 4          # top-K events on every 4th timed step
+SPIN_CYCLES = 400_000    # GPU spin before each swept call (~0.2 ms): longer than any call's host enqueue
 
 
 def log(*a):
@@ -176,9 +177,10 @@ def call_bytes(w):
 
 def sweep(iters: int = 50, warm: int = 5, only=None):
     """Per-call GPU time of every C-ABI entry point on every workload: HIP
-    events around each call on one stream, a 1 GiB scratch write before each
-    call (flushes the 256 MB Infinity Cache and keeps the GPU busy while the
-    host enqueues the call), median and p10/p90 over the timed calls."""
+    events around each call on one stream; before each call a 1 GiB scratch
+    write (flushes the 256 MB Infinity Cache) and then a GPU spin without
+    memory traffic (the write drains, and the GPU stays busy while the host
+    enqueues the call); median and p10/p90 over the timed calls."""
     import torch
     import block_draft_proposal_amd as D
     import workloads as W
@@ -190,6 +192,9 @@ def sweep(iters: int = 50, warm: int = 5, only=None):
         out = []
         for it in range(warm + iters):
             scratch.fill_(it & 0xff)
+            # a spin with no memory traffic: the scratch write drains, and
+            # the GPU stays busy while the host enqueues the timed call
+            torch.cuda._sleep(SPIN_CYCLES)
             a, b = TimingEvent(), TimingEvent()
             a.record(stream)
             fn()
