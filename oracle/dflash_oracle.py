@@ -19,7 +19,7 @@ walk, whose precision the pages fix at fp32.  Sources (page titles; sections):
          200058 vs physical 201024, and the requirement that padded ids are
          never sampled.
 
-Readings where the pages are silent (each listed again in the design doc):
+Readings where the pages are silent:
   * conv: coefficient index is the OUTPUT token i with tap t, applied to
     x[i - t]; delta carries a tap axis, delta[i, t, g]; block position is the
     flat token index modulo the block size.
