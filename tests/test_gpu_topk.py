@@ -111,6 +111,30 @@ def test_topk_mass_ties_take_lowest_ids(dtype):
     _check(logits, 30000, 32, 0.5, 30.0, label=f"ties {dtype} valid=30000")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_topk_largest_vocab(dtype):
+    # The largest vocabulary the ids' 24-bit field allows (vocab < 2^24): few
+    # rows, so each is split into segments and merged; the row maxima and
+    # their ties sit at the top of the id range.
+    require_gpu()
+    V, rows = (1 << 24) - 1, 3
+    stride = (V + 7) // 8 * 8                     # 16-byte aligned rows
+    logits = W.normal((rows, stride), 3.0, dtype, 17, "maxvocab", DEV)[:, :V]
+    logits[0, V - 1] = 40.0                       # the largest id holds the maximum
+    logits[1, V - 1] = 40.0
+    logits[1, 7] = 40.0                           # a tie with id 7: id 7 first
+    logits[2, V - 40:] = 25.0                     # 40 ties in the last ids; K = 32 takes the lowest 32
+    for k in (32, 5):
+        say(f"dflash_topk max vocab {dtype} V={V} K={k}")
+        ids, unary = D.dflash_topk(logits, top_k=k, valid_vocab=V, multiplier=1.0, softcap=30.0, vocab=V)
+        torch.cuda.synchronize()
+        # the sort-free validity check pins the selected set and its order
+        _check_every_row(logits, ids, unary, V, 1.0, 30.0, f"max vocab {dtype} K={k}")
+        got = ids.cpu().numpy()
+        assert got[0, 0] == V - 1 and got[1, 0] == 7 and got[1, 1] == V - 1
+        assert np.array_equal(got[2], np.arange(V - 40, V - 40 + k))
+
+
 def test_topk_masked_tail_equals_logical_vocab():
     # Padded ids are never returned, whether they are masked by -inf or by
     # the logical vocabulary bound (config with 200058 of 201024).
