@@ -33,12 +33,15 @@
 namespace dflash {
 
 constexpr int kSpBlock = 16;      // tokens per block = rows of an MFMA tile
-// k-steps whose loads are issued together: one.  Every wave of a launch gets
-// the register count of its largest part, and these workgroups share the
-// top-K's launch: with one k-step in flight they stay within the top-K's
-// budget (~120 VGPRs at 4 taps x 4 column tiles), so its occupancy is
-// untouched; four in flight (224 VGPRs) made the launch 12 us slower.
-template <int TAPS, int RT> constexpr int sp_unroll() { return 1; }
+// k-steps whose loads are issued together.  Every wave of a launch gets the
+// register count of its largest part, and these workgroups share the
+// top-K's launch.  Their k-steps are chains of dependent loads that wait in
+// the queue the top-K's stream keeps full, so two in flight shorten the
+// launch (32 requests at 4 taps x 4 column tiles: 38.5 -> 37.1 us) as long
+// as the launch stays within three waves per SIMD (<= 168 VGPRs: 4 column
+// tiles and up to 7 taps); beyond that one (three in flight: 45 us; four,
+// at 224 VGPRs: 12 us slower).
+template <int TAPS, int RT> constexpr int sp_unroll() { return (RT == 4 && TAPS <= 7) ? 2 : 1; }
 
 // The 16-byte vector of lane (lane - t) of the same 16-lane row (row shift by
 // t; t is a compile-time constant after unrolling).
