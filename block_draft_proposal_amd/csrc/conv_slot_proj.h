@@ -11,9 +11,10 @@
 // with the slices of plan_proj, so that the result equals the chain
 // conv -> projection bit for bit.
 //
-// Design (bf16, blocks of 16 tokens, at most 8 taps, one group per 16-byte
-// channel vector, few rows): a wave owns one block -- its 16 tokens are the 16
-// rows of an MFMA A tile -- and one slice of the channels.  Per k-step each
+// Design (bf16, blocks of at most 16 tokens, at most 8 taps, one group per
+// 16-byte channel vector, few rows): a wave owns one block -- its tokens are
+// the first rows of a 16-row MFMA A tile, the rows past the block zeros --
+// and one slice of the channels.  Per k-step each
 // lane computes the conv output vector of its A-operand slot (token
 // lane & 15, channels kc .. kc + 7 with kc = k + 8 (lane >> 4)) with the conv
 // kernel's arithmetic (conv_core.h), stores it to conv_out, and feeds it to
@@ -32,7 +33,7 @@
 
 namespace dflash {
 
-constexpr int kSpBlock = 16;      // tokens per block = rows of an MFMA tile
+constexpr int kSpBlock = 16;      // most tokens per block = rows of an MFMA tile
 // k-steps whose loads are issued together.  Every wave of a launch gets the
 // register count of its largest part, and these workgroups share the
 // top-K's launch.  Their k-steps are chains of dependent loads that wait in
@@ -78,7 +79,7 @@ struct SlotProjArgs {
   const uint16_t* delta;
   int64_t delta_row_stride;
   uint16_t* conv_out;
-  int32_t n_blocks, H, group_size;
+  int32_t n_blocks, block_size, H, group_size;
   const uint16_t* P;
   int32_t rank, slots, kslice, ksplit;
   float* u_parts;
@@ -95,7 +96,7 @@ __device__ __forceinline__ void conv_slot_proj_group(int gx, int split, const Sl
   const uint16_t* __restrict__ delta = sp.delta;
   const int64_t delta_row_stride = sp.delta_row_stride;
   uint16_t* __restrict__ conv_out = sp.conv_out;
-  const int32_t n_blocks = sp.n_blocks, H = sp.H, group_size = sp.group_size;
+  const int32_t n_blocks = sp.n_blocks, B = sp.block_size, H = sp.H, group_size = sp.group_size;
   const uint16_t* __restrict__ P = sp.P;
   const int32_t rank = sp.rank, slots = sp.slots, kslice = sp.kslice;
   float* __restrict__ u_parts = sp.u_parts;
@@ -103,16 +104,20 @@ __device__ __forceinline__ void conv_slot_proj_group(int gx, int split, const Sl
   const int kstride = proj_slice_stride(sp.ksplit);
   const int blk = gx * 4 + wave;
   const bool blk_ok = blk < n_blocks;
-  const int64_t row0 = (int64_t)(blk_ok ? blk : n_blocks - 1) * kSpBlock;   // clamped for addressing
+  const int64_t row0 = (int64_t)(blk_ok ? blk : n_blocks - 1) * B;   // clamped for addressing
   const int pos = lane & 15;                        // token of this lane's A slot
-  const bool slot_ok = blk_ok && pos >= 1 && pos <= slots;
+  const bool tok_ok = blk_ok && pos < B;            // a token of the block (rows past it: zeros)
+  const bool slot_ok = tok_ok && pos >= 1 && pos <= slots;
   const int k0 = split * kslice;
   const int k1 = min(H, k0 + kslice);
   const int kofs = 8 * (lane >> 4);
   const int G = H / group_size;
-  const uint16_t* xrow = x + (row0 + pos) * H;
-  const uint16_t* drow = delta + (row0 + pos) * delta_row_stride;
-  uint16_t* orow = conv_out + (row0 + pos) * H;
+  // a lane past the block reads its block's last row (its results are never
+  // used: a token's taps come from lanes pos - t of the same block)
+  const int tok = pos < B ? pos : B - 1;
+  const uint16_t* xrow = x + (row0 + tok) * H;
+  const uint16_t* drow = delta + (row0 + tok) * delta_row_stride;
+  uint16_t* orow = conv_out + (row0 + tok) * H;
 
   f32x4_t acc[RT];
 #pragma unroll
@@ -154,7 +159,7 @@ __device__ __forceinline__ void conv_slot_proj_group(int gx, int split, const Sl
           },
           [&](int t, float (&xf)[8]) { unpack16(xs[t], xf); }, cv);
       const uint4 packed = pack_bf16x8(cv);
-      if (blk_ok && k_ok) *reinterpret_cast<uint4*>(orow + kc) = packed;
+      if (tok_ok && k_ok) *reinterpret_cast<uint4*>(orow + kc) = packed;
       const u32x4 pk = {packed.x, packed.y, packed.z, packed.w};
       const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (slot_ok && k_ok) ? pk : zero);
 #pragma unroll

@@ -748,16 +748,18 @@ hipError_t launch_topk(const TopkArgs& a, const TopkPlan& p, hipStream_t stream)
 }
 
 bool conv_slot_proj_fits(const ConvArgs& c, const SelectArgs& s, const ProjPlan& p) {
-  return c.dtype == DFLASH_BF16 && s.dtype == DFLASH_BF16 && c.block_size == kSpBlock && s.slots == kSpBlock - 1 &&
+  return c.dtype == DFLASH_BF16 && s.dtype == DFLASH_BF16 && c.block_size >= 2 && c.block_size <= kSpBlock &&
+         s.slots == c.block_size - 1 &&
          c.taps >= 1 && c.taps <= 8 && c.group_size % 8 == 0 && c.hidden % 8 == 0 && p.frags == 1 &&
-         s.rank >= 1 && s.rank <= 128 && c.n_tokens % kSpBlock == 0 && c.n_tokens / kSpBlock == s.n_req;
+         s.rank >= 1 && s.rank <= 128 && c.n_tokens % c.block_size == 0 && c.n_tokens / c.block_size == s.n_req;
 }
 
 hipError_t launch_topk_conv_proj(const TopkArgs& a, const TopkPlan& p, const ConvArgs& c, const SelectArgs& s,
                                  const ProjPlan& pp, hipStream_t stream) {
   SlotProjArgs sp{static_cast<const uint16_t*>(c.x), static_cast<const uint16_t*>(c.base),
                   static_cast<const uint16_t*>(c.delta), c.delta_row_stride, static_cast<uint16_t*>(c.out),
-                  (int32_t)(c.n_tokens / kSpBlock), c.hidden, c.group_size, static_cast<const uint16_t*>(s.proj),
+                  (int32_t)(c.n_tokens / c.block_size), c.block_size, c.hidden, c.group_size,
+                  static_cast<const uint16_t*>(s.proj),
                   s.rank, s.slots, pp.kslice, pp.ksplit, s.u_parts, 0};
   sp.groups_x = (sp.n_blocks + 3) / 4;
   const int64_t n_sp = sp.n_blocks > 0 ? (int64_t)sp.groups_x * sp.ksplit : 0;

@@ -322,7 +322,7 @@ int dflash_verify(const void* target_logits, int64_t row_stride, int32_t n_req, 
  *   projection of each slot's hidden = conv-output row r*B + 1 + s (block
  *   position 0 is the verified anchor) -> lattice -> walk,
  * ordered on `stream` as one unit.  The conv and the projection do not
- * depend on the top-K.  In bf16 with blocks of 16 tokens, at most 8 taps, a
+ * depend on the top-K.  In bf16 with blocks of 2 to 16 tokens, at most 8 taps, a
  * group size that is a multiple of 8, rank <= 128 and fewer than 2048 slot
  * rows, they run as workgroups of the top-K's launch on `stream` (no second
  * stream).  Otherwise they run beside the top-K on an auxiliary stream of the

@@ -182,7 +182,9 @@ def test_propose_block_validation():
     (dict(), 136, "bf16", D.SCHEDULE_ONE_LAUNCH),                  # 2040 slot rows: still one launch
     (dict(), 137, "bf16", D.SCHEDULE_AUX_STREAM),               # 2055 rows: the tiled projection
     (dict(), 32, "f32", D.SCHEDULE_AUX_STREAM),                    # fp32 never shares the top-K's launch
-    (dict(block_size=10, hidden=5120, taps=5), 64, "bf16", D.SCHEDULE_AUX_STREAM),   # blocks of 10, 576 rows
+    (dict(block_size=10, hidden=5120, taps=5), 64, "bf16", D.SCHEDULE_ONE_LAUNCH),   # blocks of 10, 576 rows
+    (dict(block_size=2, hidden=512, taps=1), 64, "bf16", D.SCHEDULE_ONE_LAUNCH),     # blocks of 2: one slot
+    (dict(block_size=20, hidden=512), 64, "bf16", D.SCHEDULE_AUX_STREAM),            # blocks above 16 tokens
     (dict(block_size=10, hidden=5120, taps=5), 240, "bf16", D.SCHEDULE_AUX_STREAM),   # 2160 rows
     (dict(taps=9), 32, "bf16", D.SCHEDULE_AUX_STREAM),             # more than 8 taps
     (dict(taps=8, rank=128, top_k=32, hidden=7168), 1024, "bf16", D.SCHEDULE_AUX_STREAM),

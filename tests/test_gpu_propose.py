@@ -73,6 +73,26 @@ def test_fused_equals_chain_and_repeats(name):
     assert torch.equal(a["tokens"], d["tokens"]) and torch.equal(a["q"], d["q"])
 
 
+@pytest.mark.parametrize("B,T,n_req", [(2, 1, 37), (3, 2, 21), (7, 3, 19), (10, 5, 13), (13, 8, 11), (16, 8, 9)])
+def test_one_launch_for_every_block_size(B, T, n_req):
+    # Blocks of 2 to 16 tokens share the top-K's launch (the block's tokens
+    # are the first rows of a 16-row matrix tile, the rest zeros): equal to
+    # the chain bit for bit and to the oracle, with a ragged last workgroup.
+    require_gpu()
+    w = W.WORKLOADS["nonpow2_b10_v151936"].replace(n_req=n_req, block_size=B, taps=T, vocab=4096,
+                                                  valid_vocab=4096, hidden=1024)
+    assert D.propose_block_schedule(_cfg(w), w.n_req, w.dtype) == D.SCHEDULE_ONE_LAUNCH
+    inp = W.make_inputs(w, device=DEV)
+    say(f"dflash_propose_block one launch B={B} T={T} n_req={n_req}")
+    a = _propose(w, inp)
+    c = _chain(w, inp)
+    torch.cuda.synchronize()
+    for k in ("conv_out", "ids", "unary", "scores", "tokens", "q"):
+        assert torch.equal(a[k], c[k]), (B, k)
+    ref = O.conv(f64(inp["x"]), f64(inp["base"][0]), f64(inp["delta"][:, 0]), B, w.group_size)
+    assert conv_rel_err(f64(a["conv_out"]), ref) <= CONV_TOL["bf16"]
+
+
 @pytest.mark.parametrize("modes", ["sampled:2.0", "alt:1.5", "greedy"])
 def test_fused_walk_follows_nonzero_choices(modes):
     """Lattices that fit the fused kernel, with walks that leave row 0: q of
@@ -183,7 +203,7 @@ def test_end_to_end_against_oracle(name, reqs):
 
 @pytest.mark.parametrize("name,n_req,schedule", [
     ("bf16_b16_v151936", None, D.SCHEDULE_ONE_LAUNCH),
-    ("nonpow2_b10_v151936", None, D.SCHEDULE_AUX_STREAM),       # blocks of 10: fork/join
+    ("nonpow2_b10_v151936", None, D.SCHEDULE_ONE_LAUNCH),       # blocks of 10 in the one launch
     ("bf16_b16_v151936", 288, D.SCHEDULE_AUX_STREAM),        # 4320 slot rows: the tiled projection
     ("nonpow2_b10_v151936", 240, D.SCHEDULE_AUX_STREAM),     # blocks of 10, 2160 slot rows
 ])
