@@ -34,15 +34,18 @@
 namespace dflash {
 
 constexpr int kSpBlock = 16;      // most tokens per block = rows of an MFMA tile
-// k-steps whose loads are issued together.  Every wave of a launch gets the
-// register count of its largest part, and these workgroups share the
-// top-K's launch.  Their k-steps are chains of dependent loads that wait in
-// the queue the top-K's stream keeps full, so two in flight shorten the
-// launch (32 requests at 4 taps x 4 column tiles: 38.5 -> 37.1 us) as long
-// as the launch stays within three waves per SIMD (<= 168 VGPRs: 4 column
-// tiles and up to 7 taps); beyond that one (three in flight: 45 us; four,
-// at 224 VGPRs: 12 us slower).
-template <int TAPS, int RT> constexpr int sp_unroll() { return (RT == 4 && TAPS <= 7) ? 2 : 1; }
+// k-steps whose loads are issued together (U): a launch-time choice.  Every
+// wave of a launch gets the register count of its largest part, and these
+// workgroups share the top-K's launch.  Their k-steps are chains of dependent
+// loads that wait in the queue the top-K's stream keeps full, so two in
+// flight shorten the launch (32 requests at 4 taps x 4 column tiles: 38.5 ->
+// 37.1 us) where the launch then still has a slot for every workgroup at
+// three waves per SIMD (<= 168 VGPRs: 4 column tiles and up to 7 taps); when
+// it has more workgroups than that, one in flight keeps four waves per SIMD
+// and every workgroup resident (64 requests of 10 tokens: 60.0 -> 55.7 us
+// per step).  Three in flight: 45 us; four, at 224 VGPRs: 12 us slower.
+template <int TAPS, int RT> constexpr bool sp_two_in_flight_fits() { return RT == 4 && TAPS <= 7; }
+constexpr int64_t kSpThreeWaveSlots = 256 * 3;    // resident workgroups of 4 waves at three waves per SIMD
 
 // The 16-byte vector of lane (lane - t) of the same 16-lane row (row shift by
 // t; t is a compile-time constant after unrolling).
@@ -88,7 +91,7 @@ struct SlotProjArgs {
 
 // One workgroup (4 waves) of the conv + slot projection: blocks 4 gx ..
 // 4 gx + 3, one per wave, channel slice `split`.
-template <int TAPS, int RT>
+template <int TAPS, int RT, int U>
 __device__ __forceinline__ void conv_slot_proj_group(int gx, int split, const SlotProjArgs& sp) {
   static_assert(TAPS >= 1 && TAPS <= 8, "taps");
   const uint16_t* __restrict__ x = sp.x;
@@ -123,7 +126,6 @@ __device__ __forceinline__ void conv_slot_proj_group(int gx, int split, const Sl
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  constexpr int U = sp_unroll<TAPS, RT>();
   for (int kk = k0; kk < k1; kk += 32 * U) {
     // every load of the round first: own input vector, static rows, the
     // group's dynamic scalars, P fragments (addresses clamped into the slice)

@@ -656,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void topk_rows_f32(const float* __restric
 // so they run side by side without a second stream.  The top-K's
 // workgroups are dispatched first so that they spread evenly over the CUs
 // (the other order left the top-K rows placed last 3 us behind).
-template <int TAPS, int RT>
+template <int TAPS, int RT, int U>
 __global__ __launch_bounds__(kThreads, 2) void topk_conv_proj_bf16(
     const uint16_t* __restrict__ logits, int64_t row_stride, int64_t valid_vocab, int32_t K, int32_t wchunks,
     int32_t segs, int32_t wchunks_per_seg, float mult, float cap, uint64_t* __restrict__ parts,
@@ -665,7 +665,7 @@ __global__ __launch_bounds__(kThreads, 2) void topk_conv_proj_bf16(
   const int n_tk = (int)gridDim.x - sp.groups_x * sp.ksplit;
   if (b >= n_tk) {
     const int g = b - n_tk;
-    conv_slot_proj_group<TAPS, RT>(g % sp.groups_x, g / sp.groups_x, sp);
+    conv_slot_proj_group<TAPS, RT, U>(g % sp.groups_x, g / sp.groups_x, sp);
     return;
   }
   topk_rows_body<uint16_t>(b, logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap,
@@ -770,9 +770,17 @@ hipError_t launch_topk_conv_proj(const TopkArgs& a, const TopkPlan& p, const Con
   const dim3 grid((unsigned)(n_sp + n_tk));
   const int tiles = s.rank > 64 ? 8 : 4;
 #define DFLASH_TCP(TAPS, RT)                                                                                      \
-  hipLaunchKernelGGL((topk_conv_proj_bf16<TAPS, RT>), grid, dim3(kThreads), 0, stream,                           \
-                     static_cast<const uint16_t*>(a.logits), a.row_stride, a.valid_vocab, a.top_k, p.chunks, p.segs, \
-                     p.chunks_per_seg, a.multiplier, a.softcap, parts, a.ids_out, a.unary_out, sp)
+  do {                                                                                                            \
+    if (sp_two_in_flight_fits<TAPS, RT>() && n_sp + n_tk <= kSpThreeWaveSlots)                                   \
+      hipLaunchKernelGGL((topk_conv_proj_bf16<TAPS, RT, sp_two_in_flight_fits<TAPS, RT>() ? 2 : 1>), grid,       \
+                         dim3(kThreads), 0, stream, static_cast<const uint16_t*>(a.logits), a.row_stride,        \
+                         a.valid_vocab, a.top_k, p.chunks, p.segs, p.chunks_per_seg, a.multiplier, a.softcap,    \
+                         parts, a.ids_out, a.unary_out, sp);                                                     \
+    else                                                                                                          \
+      hipLaunchKernelGGL((topk_conv_proj_bf16<TAPS, RT, 1>), grid, dim3(kThreads), 0, stream,                    \
+                         static_cast<const uint16_t*>(a.logits), a.row_stride, a.valid_vocab, a.top_k, p.chunks, \
+                         p.segs, p.chunks_per_seg, a.multiplier, a.softcap, parts, a.ids_out, a.unary_out, sp);  \
+  } while (0)
 #define DFLASH_TCP_T(TAPS)                 \
   if (tiles == 4) DFLASH_TCP(TAPS, 4);     \
   else DFLASH_TCP(TAPS, 8);
