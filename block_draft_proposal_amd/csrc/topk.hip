@@ -650,26 +650,30 @@ __global__ __launch_bounds__(kThreads) void topk_rows_f32(const float* __restric
                         ids_out, unary_out);
 }
 
-// The propose step's first stage in one launch (bf16): the first workgroups
-// compute the top-K rows, the last groups_x * ksplit the conv and the slot
-// projection (conv_slot_proj.h).  Neither part reads what the other writes,
-// so they run side by side without a second stream.  The top-K's
-// workgroups are dispatched first so that they spread evenly over the CUs
-// (the other order left the top-K rows placed last 3 us behind).
+// The propose step's first stage in one launch (bf16): workgroups that
+// compute the top-K rows and groups_x * ksplit that compute the conv and the
+// slot projection (conv_slot_proj.h).  Neither part reads what the other
+// writes, so they run side by side without a second stream.
 template <int TAPS, int RT, int U>
 __global__ __launch_bounds__(kThreads, 2) void topk_conv_proj_bf16(
     const uint16_t* __restrict__ logits, int64_t row_stride, int64_t valid_vocab, int32_t K, int32_t wchunks,
     int32_t segs, int32_t wchunks_per_seg, float mult, float cap, uint64_t* __restrict__ parts,
     int64_t* __restrict__ ids_out, float* __restrict__ unary_out, SlotProjArgs sp) {
   const int b = (int)blockIdx.x;
-  const int n_tk = (int)gridDim.x - sp.groups_x * sp.ksplit;
-  if (b >= n_tk) {
-    const int g = b - n_tk;
+  // Dispatch order: with two k-steps in flight the conv + projection chains
+  // end well inside the top-K's time and the top-K rows go first; with one,
+  // those chains are the longer ones and go first (measured both ways: 32
+  // requests 43.8 vs 47.2 us per step, 64 requests of 10 tokens 56.1 vs 54.4).
+  const int n_spw = sp.groups_x * sp.ksplit;
+  const int n_tk = (int)gridDim.x - n_spw;
+  const int sp_first = U == 1;
+  if (sp_first ? b < n_spw : b >= n_tk) {
+    const int g = sp_first ? b : b - n_tk;
     conv_slot_proj_group<TAPS, RT, U>(g % sp.groups_x, g / sp.groups_x, sp);
     return;
   }
-  topk_rows_body<uint16_t>(b, logits, row_stride, valid_vocab, K, wchunks, segs, wchunks_per_seg, mult, cap,
-                              parts, ids_out, unary_out);
+  topk_rows_body<uint16_t>(sp_first ? b - n_spw : b, logits, row_stride, valid_vocab, K, wchunks, segs,
+                           wchunks_per_seg, mult, cap, parts, ids_out, unary_out);
 }
 
 // Merge of the per-segment K best (rows split over several workgroups).
