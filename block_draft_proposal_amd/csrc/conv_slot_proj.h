@@ -6,7 +6,7 @@
 // conv output of the draft block feeds the selector's low-rank projection
 // u = P h of each slot's hidden row, slot s being block position 1 + s):
 //   conv_out = conv(x, base, delta)                     (every row)
-//   u_parts[slot row][k][slice] = the projection's partial sum over one slice
+//   u_parts[slice][slot row][k] = the projection's partial sum over one slice
 //                                  of the channels     (slot rows only)
 // with the slices of plan_proj, so that the result equals the chain
 // conv -> projection bit for bit.
@@ -104,7 +104,6 @@ __device__ __forceinline__ void conv_slot_proj_group(int gx, int split, const Sl
   const int32_t rank = sp.rank, slots = sp.slots, kslice = sp.kslice;
   float* __restrict__ u_parts = sp.u_parts;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int kstride = proj_slice_stride(sp.ksplit);
   const int blk = gx * 4 + wave;
   const bool blk_ok = blk < n_blocks;
   const int64_t row0 = (int64_t)(blk_ok ? blk : n_blocks - 1) * B;   // clamped for addressing
@@ -184,10 +183,7 @@ __device__ __forceinline__ void conv_slot_proj_group(int gx, int split, const Sl
       const int p = 4 * (lane >> 4) + v;
       if (p >= 1 && p <= slots) {
         const int64_t srow = (int64_t)blk * slots + (p - 1);
-        float* dst = u_parts + (srow * rank + col) * kstride;
-        dst[split] = acc[tt][v];
-        if (split == sp.ksplit - 1)
-          for (int q = split + 1; q < kstride; ++q) dst[q] = 0.f;   // pad slots: +0
+        u_parts[proj_part_index(split, (int64_t)n_blocks * slots, rank, srow, col)] = acc[tt][v];
       }
     }
   }

@@ -57,16 +57,19 @@ constexpr int kMaxTopK = 32;   // DFLASH_MAX_TOP_K
 // and adds every slice of each value it needs, and the projection runs beside
 // the top-K, off the critical path, so more workgroups would not pay.
 constexpr int kMaxProjSplit = 16;
-// The partials are stored slice-minor, [n_rows][rank][kstride]: the slices of
-// one output sit together, kstride = ksplit rounded up to a multiple of 4
-// (one 16-byte vector per 4 slices; the padding slots hold +0).
-__host__ __device__ inline int proj_slice_stride(int ksplit) { return (ksplit + 3) & ~3; }
+// The partials are stored slice-major, [ksplit][n_rows][rank]: a workgroup's
+// partials of its output tile are whole contiguous rows of one slice, written
+// once (no segment shared with another workgroup's slice, so no partial-line
+// writes), and a reader of one value takes its slices from ksplit places.
+__host__ __device__ inline int64_t proj_part_index(int split, int64_t n_rows, int rank, int64_t row, int col) {
+  return ((int64_t)split * n_rows + row) * rank + col;
+}
 struct ProjPlan {
   int32_t n_rows, rank, hidden;
   int32_t row_tiles, ksplit, kslice;   // split of the contraction over workgroups
   int32_t frags;                       // row fragments of 16 per wave (bf16, per-wave kernel)
   int32_t tiled;                       // 128 x 128 tiles of the shared tile product (bf16, large batches)
-  size_t bytes;                        // fp32 partials [n_rows][rank][proj_slice_stride(ksplit)]
+  size_t bytes;                        // fp32 partials [ksplit][n_rows][rank]
 };
 // Slot rows from which the bf16 projection runs as LDS-staged 128 x 128 tiles.
 constexpr int kProjTileMinRows = 2048;

@@ -72,7 +72,6 @@ __global__ __launch_bounds__(kThreads) void proj_mfma_kernel(const uint16_t* __r
                                                              int32_t n_rows, int32_t rank, int32_t H,
                                                              int32_t kslice, float* __restrict__ u_parts) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int kstride = proj_slice_stride((int)gridDim.y);   // gridDim.y = ksplit
   const int row_base = (blockIdx.x * 4 + wave) * 16 * FR;
   const int split = blockIdx.y;
   const int k0 = split * kslice;
@@ -137,12 +136,7 @@ __global__ __launch_bounds__(kThreads) void proj_mfma_kernel(const uint16_t* __r
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = row_base + 16 * f + 4 * (lane >> 4) + v;
-        if (row < n_rows) {
-          float* dst = u_parts + ((int64_t)row * rank + col) * kstride;
-          dst[split] = acc[f][t][v];
-          if (split == (int)gridDim.y - 1)
-            for (int sp = split + 1; sp < kstride; ++sp) dst[sp] = 0.f;   // pad slots: +0
-        }
+        if (row < n_rows) u_parts[proj_part_index(split, n_rows, rank, row, col)] = acc[f][t][v];
       }
   }
 }
@@ -177,8 +171,7 @@ __global__ __launch_bounds__(ProjTileCfg::kThreads) void proj_tile_kernel(
   typedef ProjTileCfg Cfg;
   extern __shared__ __align__(16) unsigned char pt_smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int split = blockIdx.y, ksplit = gridDim.y;
-  const int kstride = proj_slice_stride(ksplit);
+  const int split = blockIdx.y;
   const int nk = (H + Cfg::kBK - 1) / Cfg::kBK;
   const int kb0 = split * kb_per_slice;
   const int nkb = min(kb_per_slice, nk - kb0);
@@ -196,12 +189,7 @@ __global__ __launch_bounds__(ProjTileCfg::kThreads) void proj_tile_kernel(
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = m0 + wm + 16 * i + 4 * (lane >> 4) + v;
-        if (row < n_rows) {
-          float* dst = u_parts + ((int64_t)row * rank + col) * kstride;
-          dst[split] = acc[i][j][v];
-          if (split == ksplit - 1)
-            for (int sp = split + 1; sp < kstride; ++sp) dst[sp] = 0.f;   // pad slots: +0
-        }
+        if (row < n_rows) u_parts[proj_part_index(split, n_rows, rank, row, col)] = acc[i][j][v];
       }
   }
 }
@@ -218,58 +206,36 @@ __global__ __launch_bounds__(kThreads) void proj_f32_kernel(const float* __restr
   const float* p = P + (int64_t)col * H;
   float acc = 0.f;
   for (int k = 0; k < H; ++k) acc = fmaf(h[k], p[k], acc);
-  float* dst = u_parts + t * proj_slice_stride(1);   // one slice, slice-minor layout
-  dst[0] = acc;
-  dst[1] = dst[2] = dst[3] = 0.f;                      // pad slots: +0
+  u_parts[t] = acc;                                    // one slice: [0][row][col]
 }
 
 // u[n][k] = sum over the projection slices sp = 0..ksplit-1 of the partial
-// u_parts[n][k][sp] (slice-minor, stride proj_slice_stride(ksplit)), added in
-// slice order.  load_proj_slices issues every load of the value (16-byte
-// vectors of 4 slices) before add_proj_slices uses the first, so callers can
-// put other loads between the two and pay one memory round trip for all.
-__device__ __forceinline__ void load_proj_slices(const float* __restrict__ u_parts, int ksplit, int r, int64_t n,
-                                                 int k, float (&v)[kMaxProjSplit]) {
-  constexpr int NV = kMaxProjSplit / 4;
-  const int nv = proj_slice_stride(ksplit) / 4;   // 16-byte vectors holding slices
-  const float4* base = reinterpret_cast<const float4*>(u_parts + (n * r + k) * (int64_t)(4 * nv));
-  // every load unconditional (a vector past the last re-reads it), so none
-  // waits for another
+// u_parts[sp][n][k] (slice-major, n_rows slot rows per slice), added in slice
+// order.  load_proj_slices issues every load of the value before
+// add_proj_slices uses the first, so callers can put other loads between the
+// two and pay one memory round trip for all.
+__device__ __forceinline__ void load_proj_slices(const float* __restrict__ u_parts, int ksplit, int64_t n_rows,
+                                                 int r, int64_t n, int k, float (&v)[kMaxProjSplit]) {
+  const float* base = u_parts + n * r + k;
+  const int64_t slice = n_rows * r;
+  // every load unconditional (a slot past the last slice re-reads it), so
+  // none waits for another
 #pragma unroll
-  for (int q = 0; q < NV; ++q) {
-    const float4 a = base[q < nv ? q : nv - 1];
-    v[4 * q] = a.x;
-    v[4 * q + 1] = a.y;
-    v[4 * q + 2] = a.z;
-    v[4 * q + 3] = a.w;
-  }
+  for (int q = 0; q < kMaxProjSplit; ++q) v[q] = base[(q < ksplit ? q : ksplit - 1) * slice];
 }
 
-// Adds whole 16-byte vectors of slices in order: the writers fill the slots
-// past the last slice with +0, which leaves every sum unchanged (a -0 sum
-// becomes +0, which no output depends on) and spares a test per slice.
 __device__ __forceinline__ float add_proj_slices(const float (&v)[kMaxProjSplit], int ksplit) {
-  const int nv = proj_slice_stride(ksplit) / 4;
   float u = v[0];
-  u += v[1];
-  u += v[2];
-  u += v[3];
 #pragma unroll
-  for (int q = 1; q < kMaxProjSplit / 4; ++q) {
-    if (q < nv) {
-      u += v[4 * q];
-      u += v[4 * q + 1];
-      u += v[4 * q + 2];
-      u += v[4 * q + 3];
-    }
-  }
+  for (int q = 1; q < kMaxProjSplit; ++q)
+    if (q < ksplit) u += v[q];
   return u;
 }
 
-__device__ __forceinline__ float sum_proj_slices(const float* __restrict__ u_parts, int ksplit, int r, int64_t n,
-                                                 int k) {
+__device__ __forceinline__ float sum_proj_slices(const float* __restrict__ u_parts, int ksplit, int64_t n_rows,
+                                                 int r, int64_t n, int k) {
   float v[kMaxProjSplit];
-  load_proj_slices(u_parts, ksplit, r, n, k, v);
+  load_proj_slices(u_parts, ksplit, n_rows, r, n, k, v);
   return add_proj_slices(v, ksplit);
 }
 
@@ -488,7 +454,7 @@ __global__ __launch_bounds__(kLatWaves * 64) void lattice_mfma_kernel(
   const bool row_ok = n_raw < n_rows;
   const int n = row_ok ? n_raw : n_rows - 1;        // a wave past the rows repeats the last one, unstored
   const int req = n / slots, s = n - req * slots;
-  for (int k = lane; k < kpad; k += 64) s_u[k] = k < r ? sum_proj_slices(u_parts, ksplit, r, n, k) : 0.f;
+  for (int k = lane; k < kpad; k += 64) s_u[k] = k < r ? sum_proj_slices(u_parts, ksplit, n_rows, r, n, k) : 0.f;
   const int e = lane % MT;
   const int ec = e < K ? e : 0;
   const int64_t pred = (s == 0) ? anchor[req] : ids[((int64_t)n - 1) * K + ec];
@@ -807,7 +773,7 @@ __global__ __launch_bounds__(kLWThreads) void lattice_walk_kernel(
       if (has_u) {
         s_u_row = div_kp.quot(i);
         k = i - s_u_row * kpad;
-        if (k < r) load_proj_slices(u_parts, ksplit, r, row0 + s_u_row, k, v);
+        if (k < r) load_proj_slices(u_parts, ksplit, (int64_t)gridDim.x * S, r, row0 + s_u_row, k, v);
       }
       // keep the compiler from sinking the slice loads below the LDS writes
       // (which would start a second round trip after the first one drained)
@@ -968,7 +934,7 @@ __global__ __launch_bounds__(kLWWaves * 64) void lattice_walk_wave_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int k = lane + 64 * h;
-      if (k < KPAD) load_proj_slices(u_parts, ksplit, r, row0 + s, k, uv[h]);
+      if (k < KPAD) load_proj_slices(u_parts, ksplit, (int64_t)n_req * S, r, row0 + s, k, uv[h]);
     }
   };
   auto store_u = [&](const float (&uv)[2][kMaxProjSplit], float* dst) {
@@ -1081,7 +1047,7 @@ ProjPlan plan_proj(int32_t n_rows, int32_t rank, int32_t hidden, int32_t dtype) 
     p.kslice = hidden;
     p.ksplit = 1;
   }
-  p.bytes = (size_t)proj_slice_stride(p.ksplit) * n_rows * rank * sizeof(float);
+  p.bytes = (size_t)p.ksplit * n_rows * rank * sizeof(float);
   p.bytes = (p.bytes + 255) & ~(size_t)255;
   return p;
 }

@@ -328,7 +328,7 @@ def test_propose_block_noalloc_rejects_batches_beyond_its_scratch():
     L = D.lib()
     cfg = D.make_config(taps=4, group_size=64, rank=128, top_k=32, multiplier=1.0, softcap=30.0, block_size=16,
                         hidden=4096)
-    n_req = 8192                                        # 122880 slot rows: far more than 64 MiB of partials
+    n_req = 16384                                       # 245760 slot rows: 126 MB of partials at least
     assert L.dflash_propose_block_workspace_size(ctypes.byref(cfg), n_req, 201024) > 64 << 20
     args = Bd.BlockArgs()
     args.n_req, args.valid_vocab, args.vocab, args.dtype = n_req, 201024, 201024, 1
